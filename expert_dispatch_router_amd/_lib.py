@@ -1,0 +1,247 @@
+"""ctypes binding of ``libmoe.so`` (the C ABI declared in include/moe.h).
+
+Argument marshalling only: every step of the MoE forward path runs in the
+library's HIP kernels.  The functions keep the C names; tensors are torch
+tensors on the GPU (PyTorch provides device memory and streams only).
+
+The library is loaded from this package directory.  If it is missing the
+first call raises -- there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_SCORE_SOFTMAX = 0
+MOE_SCORE_SIGMOID = 1
+MOE_OK = 0
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_TOPK",
+          -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_UNSUPPORTED",
+          -7: "MOE_ERR_HIP"}
+
+# Every symbol include/moe.h declares, with its ctypes signature.
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SZ = ctypes.c_size_t
+SIGNATURES = {
+    "moe_abi_version": (_I, []),
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_workspace_size": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(_SZ)]),
+    "moe_workspace_size_ex": (_I, [_I, _I, _I, _I, _I, _P, ctypes.POINTER(_SZ)]),
+    "moe_plan": (_I, [_I, _I, _I, _I, _I, _P, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "moe_forward": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
+    "moe_forward_ex": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "moe_route_workspace_size": (_I, [_I, _I, _I, _P, ctypes.POINTER(_SZ)]),
+    "moe_route": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
+                       ctypes.POINTER(_I), _P, _SZ, _P]),
+    "moe_timer_create": (_I, [ctypes.POINTER(_P)]),
+    "moe_timer_destroy": (_I, [_P]),
+    "moe_timer_elapsed_ms": (_I, [_P, _P, ctypes.POINTER(ctypes.c_float)]),
+}
+
+
+class MoeOptions(ctypes.Structure):
+    """struct moe_options of include/moe.h."""
+    _fields_ = [("block_rows", ctypes.c_int), ("split_k", ctypes.c_int),
+                ("stage_events", ctypes.c_void_p)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(
+                    f"{LIB_PATH} is missing: build it with "
+                    "`python -m expert_dispatch_router_amd.build` (hipcc, gfx950)")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                f = getattr(L, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = L
+        return _lib
+
+
+def _check(fn: str, rc: int):
+    if rc != MOE_OK:
+        raise MoeError(fn, rc)
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def moe_abi_version() -> int:
+    return int(lib().moe_abi_version())
+
+
+def _opts(block_rows=0, split_k=0, stage_events=None):
+    if not block_rows and not split_k and stage_events is None:
+        return None, None
+    o = MoeOptions(int(block_rows), int(split_k), None)
+    keep = None
+    if stage_events is not None:
+        keep = (ctypes.c_void_p * len(stage_events))(*stage_events)
+        o.stage_events = ctypes.cast(keep, ctypes.c_void_p)
+    return o, keep
+
+
+def moe_workspace_size(T, d, ffn, E, top_k, block_rows=0, split_k=0) -> int:
+    o, _ = _opts(block_rows, split_k)
+    n = _SZ(0)
+    _check("moe_workspace_size_ex", lib().moe_workspace_size_ex(
+        T, d, ffn, E, top_k, ctypes.byref(o) if o else None, ctypes.byref(n)))
+    return int(n.value)
+
+
+def moe_plan(T, d, ffn, E, top_k, block_rows=0, split_k=0):
+    """(block_rows, split_k) the library uses for these sizes and options."""
+    o, _ = _opts(block_rows, split_k)
+    bm, sk = _I(0), _I(0)
+    _check("moe_plan", lib().moe_plan(T, d, ffn, E, top_k, ctypes.byref(o) if o else None,
+                                       ctypes.byref(bm), ctypes.byref(sk)))
+    return int(bm.value), int(sk.value)
+
+
+def moe_route_workspace_size(T, E, top_k, block_rows=0) -> int:
+    o, _ = _opts(block_rows)
+    n = _SZ(0)
+    _check("moe_route_workspace_size", lib().moe_route_workspace_size(
+        T, E, top_k, ctypes.byref(o) if o else None, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _score_code(score) -> int:
+    if isinstance(score, str):
+        return {"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}[score]
+    return int(score)
+
+
+def _dev_ptr(t, dtype, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_ptr(stream, device):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=None,
+                score="softmax", workspace=None, stream=None, block_rows=0, split_k=0,
+                stage_events=None):
+    """out[T,d] (bf16) = the MoE forward pass, enqueued on ``stream``.
+
+    x bf16 [T,d]; router_logits fp32 [T,E]; W_gate_up bf16 [E,2F,d];
+    W_down bf16 [E,d,F].  ``out`` and ``workspace`` (uint8) are allocated
+    with torch when not given.  ``stage_events``: 7 HIP event handles."""
+    T, d = x.shape
+    E = router_logits.shape[1]
+    F = W_down.shape[2]
+    if router_logits.shape[0] != T or tuple(W_gate_up.shape) != (E, 2 * F, d) or \
+            tuple(W_down.shape) != (E, d, F):
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
+    ws_need = moe_workspace_size(T, d, F, E, top_k, block_rows, split_k)
+    if workspace is None:
+        workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=x.device)
+    o, keep = _opts(block_rows, split_k, stage_events)
+    rc = lib().moe_forward_ex(
+        _dev_ptr(x, torch.bfloat16, "x"), _dev_ptr(router_logits, torch.float32, "router_logits"),
+        _dev_ptr(W_gate_up, torch.bfloat16, "W_gate_up"), _dev_ptr(W_down, torch.bfloat16, "W_down"),
+        int(top_k), int(bool(renormalize)), _dev_ptr(out, torch.bfloat16, "out"),
+        T, d, F, E, _score_code(score), ctypes.byref(o) if o else None,
+        _dev_ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream_ptr(stream, x.device))
+    del keep
+    _check("moe_forward_ex", rc)
+    return out
+
+
+def moe_route(router_logits, top_k, renormalize, score="softmax", x=None, block_rows=0,
+              workspace=None, stream=None):
+    """Runs the routing kernels and returns a dict of GPU tensors: ids, w,
+    counts, offsets, perm, inv, blocks [nb_max,2], nb [1], x_perm (if x is
+    given) and the host int bm."""
+    T, E = router_logits.shape
+    dev = router_logits.device
+    A = T * top_k
+    i32 = dict(dtype=torch.int32, device=dev)
+    res = dict(ids=torch.empty(T, top_k, **i32),
+               w=torch.empty(T, top_k, dtype=torch.float32, device=dev),
+               counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+               perm=torch.empty(A, **i32), inv=torch.empty(A, **i32))
+    o, _ = _opts(block_rows)
+    ws_need = moe_route_workspace_size(T, E, top_k, block_rows)
+    if workspace is None:
+        workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
+    bm, _ = moe_plan(T, 64, 64, E, top_k, block_rows)
+    nb_max = (A + bm - 1) // bm + min(E, A) if A > 0 else 0
+    res["blocks"] = torch.zeros(max(nb_max, 1), 2, **i32)
+    res["nb"] = torch.zeros(1, **i32)
+    d = 0
+    if x is not None:
+        d = x.shape[1]
+        res["x_perm"] = torch.empty(A, d, dtype=torch.bfloat16, device=dev)
+    bm_used = _I(0)
+    rc = lib().moe_route(
+        _dev_ptr(router_logits, torch.float32, "router_logits"), T, E, int(top_k),
+        int(bool(renormalize)), _score_code(score), ctypes.byref(o) if o else None,
+        res["ids"].data_ptr(), res["w"].data_ptr(), res["counts"].data_ptr(),
+        res["offsets"].data_ptr(), res["perm"].data_ptr(), res["inv"].data_ptr(),
+        res["blocks"].data_ptr(), res["nb"].data_ptr(),
+        _dev_ptr(x, torch.bfloat16, "x") if x is not None else None, d,
+        res["x_perm"].data_ptr() if x is not None else None, ctypes.byref(bm_used),
+        _dev_ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream_ptr(stream, dev))
+    _check("moe_route", rc)
+    res["bm"] = int(bm_used.value)
+    return res
+
+
+class Timer:
+    """A HIP event created and owned by the library (moe_timer_*)."""
+
+    def __init__(self):
+        h = _P(None)
+        _check("moe_timer_create", lib().moe_timer_create(ctypes.byref(h)))
+        self.handle = h.value
+
+    def elapsed_ms(self, stop: "Timer") -> float:
+        ms = ctypes.c_float(0.0)
+        _check("moe_timer_elapsed_ms", lib().moe_timer_elapsed_ms(self.handle, stop.handle,
+                                                                  ctypes.byref(ms)))
+        return float(ms.value)
+
+    def __del__(self):
+        try:
+            if self.handle and _lib is not None:
+                _lib.moe_timer_destroy(self.handle)
+        except Exception:
+            pass

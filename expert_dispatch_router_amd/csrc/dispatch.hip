@@ -1,0 +1,156 @@
+// dispatch.hip -- K2: expert histogram, LDS prefix scan and block schedule;
+//                 K3: stable reorder of the routed rows and the row gather.
+//
+// [R] = the Pith review of "Cross-Platform Fused MoE Dispatch in Triton".
+// Tokens are reordered onto experts ("The reading"; abstract: token
+// permutation) and fixed-size blocks of rows are mapped to (expert,
+// token-offset) pairs (Algorithm 1, "What carries the argument"; BLOCK_M is
+// fixed for one launch, "Assumptions & free parameters").  On the page the
+// schedule is built on the host (Limitations (5) in the "Referee Report");
+// here it is built on the device so the forward pass never waits for a
+// device-to-host copy.
+//
+// Readings: rows of one expert keep ascending flat index i = t*k + j, which
+// makes the reorder unique and deterministic; a block never spans two
+// experts; an expert with no rows gets no block; the token-offset of a block
+// is its first sorted row.
+#include "moe_internal.hpp"
+#include "../../include/moe.h"
+
+namespace moe {
+namespace {
+
+constexpr int kScanThreads = 1024;
+static_assert(kScanThreads == kChunk, "one thread per row of a chunk");
+static_assert(MOE_MAX_EXPERTS <= kScanThreads, "one thread per expert in the scans");
+
+// Inclusive scan of v over the first MOE_MAX_EXPERTS threads (Hillis-Steele
+// in LDS); threads beyond contribute nothing.  Ends with a barrier.
+__device__ int block_inclusive_scan(int v, int* sh) {
+  const int tid = threadIdx.x;
+  if (tid < MOE_MAX_EXPERTS) sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < MOE_MAX_EXPERTS; off <<= 1) {
+    int add = 0;
+    if (tid < MOE_MAX_EXPERTS && tid >= off) add = sh[tid - off];
+    __syncthreads();
+    if (tid < MOE_MAX_EXPERTS) sh[tid] += add;
+    __syncthreads();
+  }
+  return tid < MOE_MAX_EXPERTS ? sh[tid] : 0;
+}
+
+// One workgroup.  Per chunk c of kChunk flat rows: count each expert in LDS,
+// record the count and the number of earlier rows of that expert.  Then the
+// expert totals, their exclusive prefix (offsets), the number of blocks of
+// each expert, their prefix, and the block table.
+__global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
+    const int32_t* __restrict__ ids, int A, int E, int bm, int nchunks,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ chunk_cnt,
+    int32_t* __restrict__ chunk_base, int32_t* __restrict__ blocks, int32_t* __restrict__ nb) {
+  __shared__ int hist[MOE_MAX_EXPERTS];
+  __shared__ int run[MOE_MAX_EXPERTS];
+  __shared__ int sh[MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  if (tid < E) run[tid] = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    if (tid < E) hist[tid] = 0;
+    __syncthreads();
+    const int i = c * kChunk + tid;
+    if (i < A) atomicAdd(&hist[ids[i]], 1);
+    __syncthreads();
+    if (tid < E) {
+      chunk_cnt[(size_t)c * E + tid] = hist[tid];
+      chunk_base[(size_t)c * E + tid] = run[tid];
+      run[tid] += hist[tid];
+    }
+    __syncthreads();
+  }
+  const int cnt = tid < E ? run[tid] : 0;
+  const int incl = block_inclusive_scan(cnt, sh);
+  if (tid < E) {
+    counts[tid] = cnt;
+    offsets[tid + 1] = incl;
+  }
+  if (tid == 0) offsets[0] = 0;
+  const int row0 = incl - cnt;
+  const int nbk = (cnt + bm - 1) / bm;
+  const int bincl = block_inclusive_scan(nbk, sh);
+  if (tid < E) {
+    const int b0 = bincl - nbk;
+    for (int r = 0; r < nbk; ++r) {
+      blocks[2 * (b0 + r)] = tid;
+      blocks[2 * (b0 + r) + 1] = row0 + r * bm;
+    }
+  }
+  if (tid == E - 1) nb[0] = bincl;
+}
+
+// One wave per (chunk, expert).  The wave walks its chunk in order, 64 rows
+// at a time; a ballot of "row goes to my expert" ranks the matching lanes,
+// so rows land at consecutive sorted positions in ascending flat order.
+__global__ __launch_bounds__(256) void permute_kernel(
+    const int32_t* __restrict__ ids, int A, int E, int nchunks, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ chunk_cnt, const int32_t* __restrict__ chunk_base,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (gw >= E * nchunks) return;
+  const int c = gw / E;
+  const int e = gw - c * E;
+  const int cnt = chunk_cnt[(size_t)c * E + e];
+  if (cnt == 0) return;
+  const int lane = threadIdx.x & 63;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int pos = offsets[e] + chunk_base[(size_t)c * E + e];
+  const int end = pos + cnt;
+  const int i0 = c * kChunk;
+  for (int it = 0; it < kChunk / 64 && pos < end; ++it) {
+    const int i = i0 + it * 64 + lane;
+    const bool hit = i < A && ids[i] == e;
+    const unsigned long long mask = __ballot(hit);
+    if (hit) {
+      const int p = pos + __popcll(mask & below);
+      perm[p] = i;
+      inv[i] = p;
+    }
+    pos += __popcll(mask);
+  }
+}
+
+// x_perm[p] = x[perm[p] / k]: one workgroup per sorted row, 16-byte moves.
+__global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ x,
+                                                     const int32_t* __restrict__ perm, int d, int k,
+                                                     uint16_t* __restrict__ x_perm) {
+  const int p = blockIdx.x;
+  const int src = perm[p] / k;
+  const uint4* s = reinterpret_cast<const uint4*>(x + (size_t)src * d);
+  uint4* o = reinterpret_cast<uint4*>(x_perm + (size_t)p * d);
+  for (int c = threadIdx.x; c < d / 8; c += 256) o[c] = s[c];
+}
+
+}  // namespace
+
+hipError_t launch_hist_scan(const int32_t* ids, int A, int E, int bm, int nchunks, int32_t* counts,
+                            int32_t* offsets, int32_t* chunk_cnt, int32_t* chunk_base,
+                            int32_t* blocks, int32_t* nb, hipStream_t s) {
+  hist_scan_kernel<<<1, kScanThreads, 0, s>>>(ids, A, E, bm, nchunks, counts, offsets, chunk_cnt,
+                                              chunk_base, blocks, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const int32_t* ids, int A, int E, int nchunks, const int32_t* offsets,
+                          const int32_t* chunk_cnt, const int32_t* chunk_base, int32_t* perm,
+                          int32_t* inv, hipStream_t s) {
+  const int waves = E * nchunks;
+  permute_kernel<<<(waves + 3) / 4, 256, 0, s>>>(ids, A, E, nchunks, offsets, chunk_cnt,
+                                                 chunk_base, perm, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int A, int d, int k,
+                         uint16_t* x_perm, hipStream_t s) {
+  gather_kernel<<<A, 256, 0, s>>>(x, perm, d, k, x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,314 @@
+// grouped_gemm.hip -- K4: fused gate/up SwiGLU grouped GEMM; K5: down
+// grouped GEMM.  bf16 inputs, fp32 accumulation on gfx950 MFMA
+// (v_mfma_f32_16x16x32_bf16).
+//
+// [R] = the Pith review of "Cross-Platform Fused MoE Dispatch in Triton".
+// "What carries the argument": both SwiGLU projections are computed from one
+// shared load of each input tile and SiLU is applied in registers, so the
+// gate and up intermediates never reach global memory; the GEMMs are one
+// launch over a block schedule whose blocks map to (expert, token-offset)
+// pairs (Algorithm 1).  The down projection is the second expert GEMM of the
+// SwiGLU FFN (abstract: expert GEMMs).
+//
+// Design on gfx950 (weights are K-contiguous, "NT"):
+//   * One workgroup = one schedule block (expert e, up to BM sorted rows) x
+//     one column tile; a wave owns NWT 16-column subtiles (for K4: NWT gate
+//     subtiles and the NWT matching up subtiles) and all BM rows.
+//   * The activation tile (BM rows x 64 of K) is staged once per K step in
+//     LDS and shared by the workgroup's waves -- and, in K4, by the gate and
+//     the up operand of every wave: this is the "one shared load of each
+//     input tile" of the page, on LDS instead of L2.
+//   * Weights are streamed from HBM straight into VGPRs in the MFMA operand
+//     layout (16 bytes per lane per load), PF K steps ahead; the activation
+//     loads ride in the same ring, so waiting for the oldest stage never
+//     drains the younger prefetches.  Each weight element is read once per
+//     block; only LDS is shared, so no weight byte goes through LDS.
+//   * The MFMA's A operand is the weight (rows = output columns n), the B
+//     operand the activation (columns = rows m): lane l then holds outputs
+//     (n0 + 4*(l/16) + r, m0 + l%16), r = 0..3 -- four consecutive output
+//     columns of one row, stored as one 8-byte (bf16) or 16-byte (fp32)
+//     write.  Both operands take K elements [8*(l/16), 8*(l/16)+8) of each
+//     32-wide chunk, so the contraction pairs them whatever the hardware's
+//     internal K order.
+//   * Blocks whose rows end early skip the 16-row subtiles past the end;
+//     rows of the last partial subtile are masked at the store.  Subtiles
+//     past the last column are skipped whole (N % 16 == 0).
+//   * K5 may split its reduction into `split` contiguous parts, each written
+//     as its own fp32 partial; the combination kernel adds them in order.
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kBK = 64;               // K per pipeline step (two 32-wide MFMA chunks)
+constexpr int kLdsStride = kBK + 8;   // bf16 per LDS row: 144 bytes, conflict-free reads
+
+// Wait for this wave's LDS traffic, then a workgroup barrier.  Unlike
+// __syncthreads() it does not wait for outstanding global loads, so the
+// weight prefetches stay in flight across it.  The memory clobber keeps the
+// compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
+
+template <int BM, int NWT, int WAVES, int PF, bool SWIGLU>
+struct Gemm {
+  static constexpr int kMT = BM / 16;                        // 16-row subtiles
+  static constexpr int kNG = SWIGLU ? 2 : 1;                 // weight groups (gate, up)
+  static constexpr int kThreads = WAVES * 64;
+  static constexpr int kTileCols = WAVES * NWT * 16;         // output columns per workgroup
+  static constexpr int kXChunks = BM * (kBK / 8);            // 16-byte chunks per activation tile
+  static constexpr int kXPerThread = (kXChunks + kThreads - 1) / kThreads;
+  static_assert(BM % 16 == 0, "BM is a multiple of 16");
+};
+
+// X: activations [A, K] (sorted rows).  W: weights [E, NG*N, K].
+// out: K4 -> bf16 h [A, N];  K5 -> fp32 y [split, A, N].
+template <int BM, int NWT, int WAVES, int PF, bool SWIGLU>
+__global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+    const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
+    const int32_t* __restrict__ offsets, void* __restrict__ out, int A, int N, int K, int ksplit,
+    int tiles_per_block) {
+  using G = Gemm<BM, NWT, WAVES, PF, SWIGLU>;
+  constexpr int MT = G::kMT, NG = G::kNG, XPT = G::kXPerThread;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kLdsStride];
+
+  const int b = blockIdx.x / tiles_per_block;
+  if (b >= nb_dev[0]) return;  // beyond the schedule built on the device
+  const int rem = blockIdx.x - b * tiles_per_block;
+  const int e = blocks[2 * b];
+  const int r0 = blocks[2 * b + 1];
+  const int rows = min(BM, offsets[e + 1] - r0);
+  const int mt_act = (rows + 15) >> 4;
+
+  const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
+  const int tile = rem % n_tiles;
+  const int part = rem / n_tiles;
+  const int kb = part * ksplit;
+  const int nks = max(0, (min(K, kb + ksplit) - kb) / kBK);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: uniform branches
+  const int n0 = tile * G::kTileCols + wave * (NWT * 16);
+  const int lrow = lane & 15;
+  const int lk = (lane >> 4) * 8;
+
+  // Every global load below is unconditional, with its address clamped into
+  // the operands, so the compiler can count outstanding loads exactly and
+  // wait only for the oldest ring stage.  Subtiles past the last column load
+  // the last valid rows and are never stored; K steps past the end reload
+  // the last step (an L2 hit).
+  const uint16_t* wrow[NG][NWT];
+  bool jok[NWT];
+#pragma unroll
+  for (int j = 0; j < NWT; ++j) {
+    jok[j] = n0 + 16 * j < N;
+    const int nr = (jok[j] ? n0 + 16 * j : N - 16) + lrow;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      wrow[g][j] = W + ((size_t)e * NG * N + (size_t)g * N + nr) * K + kb + lk;
+  }
+
+  // Activation chunks this thread stages: chunk c -> (row c/8, 16-byte
+  // column chunk c%8).  When the tile has fewer chunks than threads, extra
+  // threads repeat a chunk (same data, same LDS slot).  Rows past the
+  // block's end read its last row and store zeros.
+  const uint16_t* xsrc[XPT];
+  int xdst[XPT];
+  bool xreal[XPT];
+#pragma unroll
+  for (int q = 0; q < XPT; ++q) {
+    const int c = (tid + q * G::kThreads) % G::kXChunks;
+    const int row = c >> 3;
+    const int ch = c & 7;
+    xreal[q] = row < rows;
+    xsrc[q] = X + (size_t)(r0 + (xreal[q] ? row : rows - 1)) * K + kb + ch * 8;
+    xdst[q] = row * kLdsStride + ch * 8;
+  }
+
+  bf16x8 wr[PF][NG][NWT][2];
+  u32x4 xr[PF][XPT];
+  f32x4 acc[NG][MT][NWT];
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < NWT; ++j) acc[g][mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_x = [&](u32x4(&dst)[XPT], int ks) {
+#pragma unroll
+    for (int q = 0; q < XPT; ++q)
+      dst[q] = *reinterpret_cast<const u32x4*>(xsrc[q] + (size_t)ks * kBK);
+  };
+  auto load_w = [&](bf16x8(&dst)[NG][NWT][2], int ks) {
+#pragma unroll
+    for (int j = 0; j < NWT; ++j)
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const uint16_t* p = wrow[g][j] + (size_t)ks * kBK;
+        dst[g][j][0] = *reinterpret_cast<const bf16x8*>(p);
+        dst[g][j][1] = *reinterpret_cast<const bf16x8*>(p + 32);
+      }
+  };
+  auto store_x = [&](int buf, const u32x4(&src)[XPT]) {
+#pragma unroll
+    for (int q = 0; q < XPT; ++q) {
+      const uint32_t keep = xreal[q] ? 0xffffffffu : 0u;
+      *reinterpret_cast<u32x4*>(&xs[buf][xdst[q]]) = src[q] & keep;
+    }
+  };
+  auto compute = [&](int buf, const bf16x8(&wv)[NG][NWT][2]) {
+    const uint16_t* xb = &xs[buf][0];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt < mt_act) {
+        const uint16_t* xp = xb + (mt * 16 + lrow) * kLdsStride + lk;
+        const bf16x8 xa0 = *reinterpret_cast<const bf16x8*>(xp);
+        const bf16x8 xa1 = *reinterpret_cast<const bf16x8*>(xp + 32);
+#pragma unroll
+        for (int j = 0; j < NWT; ++j)
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            acc[g][mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[g][j][0], xa0,
+                                                                    acc[g][mt][j], 0, 0, 0);
+            acc[g][mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[g][j][1], xa1,
+                                                                    acc[g][mt][j], 0, 0, 0);
+          }
+      }
+    }
+  };
+
+  if (nks > 0) {
+    // Prologue: stages 0..PF-1 in flight (activation, then weights, per stage).
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      load_x(xr[s], min(s, nks - 1));
+      load_w(wr[s], min(s, nks - 1));
+    }
+    // Full groups of PF steps; ring slot s is a fixed register set.  Step
+    // ks: stage its activation tile in LDS, barrier, refill the slot's
+    // activation part, multiply, refill the slot's weight part.
+    int ks0 = 0;
+    for (; ks0 + PF <= nks; ks0 += PF) {
+#pragma unroll
+      for (int s = 0; s < PF; ++s) {
+        const int ks = ks0 + s;
+        const int nxt = min(ks + PF, nks - 1);
+        const int buf = ks & 1;
+        store_x(buf, xr[s]);
+        lds_barrier();
+        load_x(xr[s], nxt);
+        compute(buf, wr[s]);
+        load_w(wr[s], nxt);
+      }
+    }
+    // Remaining (< PF) steps are already in flight: no further loads.
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int ks = ks0 + s;
+      if (ks < nks) {
+        const int buf = ks & 1;
+        store_x(buf, xr[s]);
+        lds_barrier();
+        compute(buf, wr[s]);
+      }
+    }
+  }
+
+  // Epilogue.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    if (mt < mt_act) {
+      const int m = mt * 16 + lrow;
+      if (m < rows) {
+        const size_t orow = (size_t)(r0 + m);
+#pragma unroll
+        for (int j = 0; j < NWT; ++j) {
+          if (!jok[j]) continue;
+          const int n = n0 + 16 * j + 4 * (lane >> 4);
+          if constexpr (SWIGLU) {
+            const f32x4 gv = acc[0][mt][j];
+            const f32x4 uv = acc[NG - 1][mt][j];
+            bf16x4 hv;
+            hv[0] = (__bf16)(silu_f32(gv[0]) * uv[0]);
+            hv[1] = (__bf16)(silu_f32(gv[1]) * uv[1]);
+            hv[2] = (__bf16)(silu_f32(gv[2]) * uv[2]);
+            hv[3] = (__bf16)(silu_f32(gv[3]) * uv[3]);
+            *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(out) + orow * N + n) = hv;
+          } else {
+            float* y = static_cast<float*>(out) + ((size_t)part * A + orow) * N + n;
+            *reinterpret_cast<f32x4*>(y) = acc[0][mt][j];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int NWT, int WAVES, int PF, bool SWIGLU>
+hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, const int32_t* blocks,
+                      const int32_t* nb, const int32_t* offsets, void* out, int A, int N, int K,
+                      int split, int ksplit, int nb_max, hipStream_t s) {
+  using G = Gemm<BM, NWT, WAVES, PF, SWIGLU>;
+  const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
+  const int tiles_per_block = n_tiles * split;
+  const long long grid = (long long)tiles_per_block * nb_max;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  grouped_gemm_kernel<BM, NWT, WAVES, PF, SWIGLU><<<(unsigned)grid, G::kThreads, 0, s>>>(
+      X, W, blocks, nb, offsets, out, A, N, K, ksplit, tiles_per_block);
+  return hipGetLastError();
+}
+
+// Tile shapes per block size.  NWT*16 columns per wave (x2 for gate+up in
+// K4), 4 waves, PF K steps of prefetch; register budget ~ acc + PF stages.
+#define MOE_GU_CFGS(X) X(16, 4, 4, 2) X(32, 4, 4, 2) X(64, 4, 4, 2) X(128, 2, 4, 2) X(192, 2, 4, 2)
+#define MOE_DN_CFGS(X) X(16, 4, 4, 3) X(32, 4, 4, 3) X(64, 4, 4, 3) X(128, 4, 4, 2) X(192, 4, 4, 2)
+
+}  // namespace
+
+int gate_up_tile_cols(int bm) {
+#define X(BM, NWT, WV, PF) \
+  if (bm == BM) return Gemm<BM, NWT, WV, PF, true>::kTileCols;
+  MOE_GU_CFGS(X)
+#undef X
+  return 0;
+}
+
+int down_tile_cols(int bm) {
+#define X(BM, NWT, WV, PF) \
+  if (bm == BM) return Gemm<BM, NWT, WV, PF, false>::kTileCols;
+  MOE_DN_CFGS(X)
+#undef X
+  return 0;
+}
+
+hipError_t launch_gate_up(int bm, const uint16_t* x_perm, const uint16_t* w_gate_up,
+                          const int32_t* blocks, const int32_t* nb, const int32_t* offsets,
+                          uint16_t* h, int A, int d, int ffn, int nb_max, hipStream_t s) {
+#define X(BM, NWT, WV, PF)                                                                   \
+  if (bm == BM)                                                                              \
+    return launch_cfg<BM, NWT, WV, PF, true>(x_perm, w_gate_up, blocks, nb, offsets, h, A,   \
+                                             ffn, d, 1, d, nb_max, s);
+  MOE_GU_CFGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_down(int bm, const uint16_t* h, const uint16_t* w_down, const int32_t* blocks,
+                       const int32_t* nb, const int32_t* offsets, float* y, int A, int d, int ffn,
+                       int split, int ksplit, int nb_max, hipStream_t s) {
+#define X(BM, NWT, WV, PF)                                                                  \
+  if (bm == BM)                                                                             \
+    return launch_cfg<BM, NWT, WV, PF, false>(h, w_down, blocks, nb, offsets, y, A, d, ffn, \
+                                              split, ksplit, nb_max, s);
+  MOE_DN_CFGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -1,0 +1,341 @@
+// moe_api.cpp -- host side of the C ABI declared in include/moe.h:
+// argument checks (host only, before any HIP call), the plan (block size,
+// split of the down projection, workspace carve-up) and the launches of the
+// six kernels on the caller's stream.  No device allocation, no
+// synchronisation.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "moe_internal.hpp"
+
+namespace moe {
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kBlockRows[] = {16, 32, 64, 128, 192};
+constexpr int kMaxSplit = 8;
+constexpr int kTargetDownWorkgroups = 1024;  // ~4 per CU on 256 CUs
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool is_block_rows(int bm) {
+  for (int b : kBlockRows)
+    if (b == bm) return true;
+  return false;
+}
+
+// Checks that only depend on sizes.  dims: d and ffn are used.
+int check_sizes(int T, int d, int ffn, int E, int k, bool dims) {
+  if (T < 0 || E < 1) return MOE_ERR_SHAPE;
+  if (dims && (d < 1 || ffn < 1)) return MOE_ERR_SHAPE;
+  if (k < 1 || k > E) return MOE_ERR_TOPK;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (dims && (d % 64 != 0 || ffn % 64 != 0)) return MOE_ERR_ALIGN;
+  if ((long long)T * k > MOE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_options(const moe_options* opt) {
+  if (!opt) return MOE_OK;
+  if (opt->block_rows != 0 && !is_block_rows(opt->block_rows)) return MOE_ERR_UNSUPPORTED;
+  if (opt->split_k < 0 || opt->split_k > kMaxSplit) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Block size: the smallest supported BM that holds the mean rows per expert
+// plus three standard deviations of a uniform router (binomial counts), so
+// that under near-uniform routing almost every expert is one block and its
+// weights are streamed once.  Larger loads use the largest BM.
+int auto_block_rows(int A, int E) {
+  const double mean = (double)A / E;
+  const double want = mean + 3.0 * sqrt(mean) + 1.0;
+  for (int b : kBlockRows)
+    if (b >= want) return b;
+  return kBlockRows[sizeof(kBlockRows) / sizeof(kBlockRows[0]) - 1];
+}
+
+// Split of the down projection's reduction: enough workgroups to fill the
+// chip when blocks x column tiles are few (few experts, wide d).
+int auto_split(int A, int E, int d, int ffn, int bm) {
+  const int tile_cols = down_tile_cols(bm);
+  const long long n_tiles = (d + tile_cols - 1) / tile_cols;
+  const long long blocks_est = (long long)((A + bm - 1) / bm) < (long long)(E < A ? E : A)
+                                   ? (long long)(E < A ? E : A)
+                                   : (long long)((A + bm - 1) / bm);
+  const long long wg = n_tiles * (blocks_est > 0 ? blocks_est : 1);
+  int s = (int)((kTargetDownWorkgroups + wg - 1) / wg);
+  const int max_by_k = ffn / (8 * 64);  // keep at least 8 K steps per part
+  if (s > max_by_k) s = max_by_k;
+  if (s > kMaxSplit) s = kMaxSplit;
+  return s < 1 ? 1 : s;
+}
+
+void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan* p) {
+  memset(p, 0, sizeof(*p));
+  p->T = T;
+  p->d = d;
+  p->ffn = ffn;
+  p->E = E;
+  p->k = k;
+  p->A = T * k;
+  const int A = p->A;
+  p->bm = (opt && opt->block_rows) ? opt->block_rows : auto_block_rows(A > 0 ? A : 1, E);
+  p->nb_max = (A + p->bm - 1) / p->bm + (E < A ? E : A);
+  p->nchunks = (A + kChunk - 1) / kChunk;
+  if (ffn > 0) {
+    int s = (opt && opt->split_k) ? opt->split_k : auto_split(A, E, d, ffn, p->bm);
+    const int ksteps = ffn / 64;
+    const int per = (ksteps + s - 1) / s;
+    p->ksplit = per * 64;
+    p->split = (ksteps + per - 1) / per;  // every part has at least one K step
+  }
+  size_t o = 0;
+  auto seg = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  const size_t nck = (size_t)p->nchunks * E;
+  p->o_ids = seg((size_t)A * 4);
+  p->o_w = seg((size_t)A * 4);
+  p->o_counts = seg((size_t)E * 4);
+  p->o_offsets = seg((size_t)(E + 1) * 4);
+  p->o_ccnt = seg(nck * 4);
+  p->o_cbase = seg(nck * 4);
+  p->o_perm = seg((size_t)A * 4);
+  p->o_inv = seg((size_t)A * 4);
+  p->o_blocks = seg((size_t)p->nb_max * 2 * 4);
+  p->o_nb = seg(4);
+  p->route_bytes = o;
+  p->o_xperm = seg((size_t)A * d * 2);
+  p->o_h = seg((size_t)A * ffn * 2);
+  p->o_y = seg((size_t)p->split * A * d * 4);
+  p->total_bytes = o;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+template <class T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int record(const moe_options* opt, int i, hipStream_t s) {
+  if (!opt || !opt->stage_events) return MOE_OK;
+  hipEvent_t ev = static_cast<hipEvent_t>(opt->stage_events[i]);
+  if (!ev) return MOE_OK;
+  return hipEventRecord(ev, s) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+#define MOE_TRY_HIP(expr)                     \
+  do {                                        \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+#define MOE_TRY(expr)           \
+  do {                          \
+    const int rc_ = (expr);     \
+    if (rc_ != MOE_OK) return rc_; \
+  } while (0)
+
+// K1..K3 into the workspace's routing section.
+int run_routing(const float* logits, const Plan& p, int renorm, int score, void* ws,
+                const moe_options* opt, hipStream_t s) {
+  int32_t* ids = at<int32_t>(ws, p.o_ids);
+  float* w = at<float>(ws, p.o_w);
+  int32_t* offsets = at<int32_t>(ws, p.o_offsets);
+  MOE_TRY(record(opt, 0, s));
+  MOE_TRY_HIP(launch_route(logits, p.T, p.E, p.k, renorm, score, ids, w, s));
+  MOE_TRY(record(opt, 1, s));
+  MOE_TRY_HIP(launch_hist_scan(ids, p.A, p.E, p.bm, p.nchunks, at<int32_t>(ws, p.o_counts),
+                               offsets, at<int32_t>(ws, p.o_ccnt), at<int32_t>(ws, p.o_cbase),
+                               at<int32_t>(ws, p.o_blocks), at<int32_t>(ws, p.o_nb), s));
+  MOE_TRY(record(opt, 2, s));
+  MOE_TRY_HIP(launch_permute(ids, p.A, p.E, p.nchunks, offsets, at<int32_t>(ws, p.o_ccnt),
+                             at<int32_t>(ws, p.o_cbase), at<int32_t>(ws, p.o_perm),
+                             at<int32_t>(ws, p.o_inv), s));
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "invalid size";
+    case MOE_ERR_TOPK: return "top_k must be in [1, E]";
+    case MOE_ERR_ALIGN: return "d and ffn must be multiples of 64; pointers 16-byte aligned, workspace 256";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_UNSUPPORTED: return "outside this build's limits or an unsupported option";
+    case MOE_ERR_HIP: return "a HIP call failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_workspace_size_ex(int T, int d, int ffn, int E, int top_k, const moe_options* opt,
+                          size_t* bytes) {
+  MOE_TRY(check_sizes(T, d, ffn, E, top_k, true));
+  MOE_TRY(check_options(opt));
+  if (!bytes) return MOE_ERR_NULL;
+  if (T == 0) {
+    *bytes = 0;
+    return MOE_OK;
+  }
+  Plan p;
+  make_plan(T, d, ffn, E, top_k, opt, &p);
+  *bytes = p.total_bytes;
+  return MOE_OK;
+}
+
+int moe_workspace_size(int T, int d, int ffn, int E, int top_k, size_t* bytes) {
+  return moe_workspace_size_ex(T, d, ffn, E, top_k, nullptr, bytes);
+}
+
+int moe_plan(int T, int d, int ffn, int E, int top_k, const moe_options* opt, int* block_rows,
+             int* split_k) {
+  MOE_TRY(check_sizes(T, d, ffn, E, top_k, true));
+  MOE_TRY(check_options(opt));
+  Plan p;
+  make_plan(T, d, ffn, E, top_k, opt, &p);
+  if (block_rows) *block_rows = p.bm;
+  if (split_k) *split_k = p.split;
+  return MOE_OK;
+}
+
+int moe_route_workspace_size(int T, int E, int top_k, const moe_options* opt, size_t* bytes) {
+  MOE_TRY(check_sizes(T, 0, 0, E, top_k, false));
+  MOE_TRY(check_options(opt));
+  if (!bytes) return MOE_ERR_NULL;
+  if (T == 0) {
+    *bytes = 0;
+    return MOE_OK;
+  }
+  Plan p;
+  make_plan(T, 0, 0, E, top_k, opt, &p);
+  *bytes = p.route_bytes;
+  return MOE_OK;
+}
+
+int moe_forward_ex(const uint16_t* x, const float* router_logits, const uint16_t* W_gate_up,
+                   const uint16_t* W_down, int top_k, int renormalize, uint16_t* out, int T, int d,
+                   int ffn, int E, int score_func, const moe_options* opt, void* workspace,
+                   size_t workspace_bytes, void* hip_stream) {
+  MOE_TRY(check_sizes(T, d, ffn, E, top_k, true));
+  MOE_TRY(check_options(opt));
+  if (score_func != MOE_SCORE_SOFTMAX && score_func != MOE_SCORE_SIGMOID)
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !router_logits || !W_gate_up || !W_down || !out || !workspace) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(router_logits, 16) || !aligned(W_gate_up, 16) ||
+      !aligned(W_down, 16) || !aligned(out, 16) || !aligned(workspace, kAlign))
+    return MOE_ERR_ALIGN;
+  Plan p;
+  make_plan(T, d, ffn, E, top_k, opt, &p);
+  if (workspace_bytes < p.total_bytes) return MOE_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  (void)hipGetLastError();  // report only this call's launches
+  const int renorm = renormalize ? 1 : 0;
+  MOE_TRY(run_routing(router_logits, p, renorm, score_func, workspace, opt, s));
+  const int32_t* perm = at<int32_t>(workspace, p.o_perm);
+  const int32_t* blocks = at<int32_t>(workspace, p.o_blocks);
+  const int32_t* nb = at<int32_t>(workspace, p.o_nb);
+  const int32_t* offsets = at<int32_t>(workspace, p.o_offsets);
+  uint16_t* x_perm = at<uint16_t>(workspace, p.o_xperm);
+  uint16_t* h = at<uint16_t>(workspace, p.o_h);
+  float* y = at<float>(workspace, p.o_y);
+  MOE_TRY_HIP(launch_gather(x, perm, p.A, d, top_k, x_perm, s));
+  MOE_TRY(record(opt, 3, s));
+  MOE_TRY_HIP(launch_gate_up(p.bm, x_perm, W_gate_up, blocks, nb, offsets, h, p.A, d, ffn,
+                             p.nb_max, s));
+  MOE_TRY(record(opt, 4, s));
+  MOE_TRY_HIP(launch_down(p.bm, h, W_down, blocks, nb, offsets, y, p.A, d, ffn, p.split,
+                          p.ksplit, p.nb_max, s));
+  MOE_TRY(record(opt, 5, s));
+  MOE_TRY_HIP(launch_combine(y, p.split, p.A, d, at<int32_t>(workspace, p.o_inv),
+                             at<float>(workspace, p.o_w), top_k, T, out, s));
+  MOE_TRY(record(opt, 6, s));
+  return MOE_OK;
+}
+
+int moe_forward(const uint16_t* x, const float* router_logits, const uint16_t* W_gate_up,
+                const uint16_t* W_down, int top_k, int renormalize, uint16_t* out, int T, int d,
+                int ffn, int E, int score_func, void* workspace, size_t workspace_bytes,
+                void* hip_stream) {
+  return moe_forward_ex(x, router_logits, W_gate_up, W_down, top_k, renormalize, out, T, d, ffn,
+                        E, score_func, nullptr, workspace, workspace_bytes, hip_stream);
+}
+
+int moe_route(const float* router_logits, int T, int E, int top_k, int renormalize,
+              int score_func, const moe_options* opt, int32_t* topk_ids, float* topk_w,
+              int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* blocks,
+              int32_t* nb, const uint16_t* x, int d, uint16_t* x_perm, int* bm_used,
+              void* workspace, size_t workspace_bytes, void* hip_stream) {
+  MOE_TRY(check_sizes(T, 0, 0, E, top_k, false));
+  MOE_TRY(check_options(opt));
+  if (score_func != MOE_SCORE_SOFTMAX && score_func != MOE_SCORE_SIGMOID)
+    return MOE_ERR_UNSUPPORTED;
+  const bool gather = x && x_perm;
+  if (gather && (d < 1)) return MOE_ERR_SHAPE;
+  if (gather && d % 64 != 0) return MOE_ERR_ALIGN;
+  Plan p;
+  make_plan(T, 0, 0, E, top_k, opt, &p);
+  if (bm_used) *bm_used = p.bm;
+  if (T == 0) return MOE_OK;
+  if (!router_logits || !workspace) return MOE_ERR_NULL;
+  if (!aligned(router_logits, 16) || !aligned(workspace, kAlign)) return MOE_ERR_ALIGN;
+  if (gather && (!aligned(x, 16) || !aligned(x_perm, 16))) return MOE_ERR_ALIGN;
+  if (workspace_bytes < p.route_bytes) return MOE_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  (void)hipGetLastError();
+  MOE_TRY(run_routing(router_logits, p, renormalize ? 1 : 0, score_func, workspace, opt, s));
+  if (gather)
+    MOE_TRY_HIP(launch_gather(x, at<int32_t>(workspace, p.o_perm), p.A, d, top_k, x_perm, s));
+  MOE_TRY(record(opt, 3, s));
+  const hipMemcpyKind dd = hipMemcpyDeviceToDevice;
+  struct Copy {
+    void* dst;
+    size_t off, bytes;
+  } copies[] = {
+      {topk_ids, p.o_ids, (size_t)p.A * 4},          {topk_w, p.o_w, (size_t)p.A * 4},
+      {counts, p.o_counts, (size_t)E * 4},           {offsets, p.o_offsets, (size_t)(E + 1) * 4},
+      {perm, p.o_perm, (size_t)p.A * 4},             {inv, p.o_inv, (size_t)p.A * 4},
+      {blocks, p.o_blocks, (size_t)p.nb_max * 2 * 4}, {nb, p.o_nb, 4},
+  };
+  for (const Copy& c : copies)
+    if (c.dst) MOE_TRY_HIP(hipMemcpyAsync(c.dst, at<char>(workspace, c.off), c.bytes, dd, s));
+  return MOE_OK;
+}
+
+int moe_timer_create(void** event) {
+  if (!event) return MOE_ERR_NULL;
+  hipEvent_t ev = nullptr;
+  if (hipEventCreate(&ev) != hipSuccess) return MOE_ERR_HIP;
+  *event = ev;
+  return MOE_OK;
+}
+
+int moe_timer_destroy(void* event) {
+  if (!event) return MOE_ERR_NULL;
+  return hipEventDestroy(static_cast<hipEvent_t>(event)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+int moe_timer_elapsed_ms(void* start, void* stop, float* ms) {
+  if (!start || !stop || !ms) return MOE_ERR_NULL;
+  if (hipEventSynchronize(static_cast<hipEvent_t>(stop)) != hipSuccess) return MOE_ERR_HIP;
+  return hipEventElapsedTime(ms, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop)) ==
+                 hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// moe_internal.hpp -- shared definitions of the HIP library's translation
+// units (device types, workspace plan, kernel launchers).  Internal: not part
+// of the C ABI in include/moe.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Vector types of the gfx950 bf16 matrix instructions and 16-byte moves.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Flat routed rows handled by one reorder chunk; the histogram kernel keeps
+// one count per (chunk, expert) so the reorder can start every chunk at its
+// final position without a global sort.
+constexpr int kChunk = 1024;
+
+// Host-side plan of one call: sizes, tile choices and workspace carve-up.
+struct Plan {
+  int T, d, ffn, E, k;
+  int A;          // routed rows T*k
+  int bm;         // rows per schedule block (BLOCK_M)
+  int nb_max;     // upper bound of the block count: ceil(A/bm) + min(E, A)
+  int nchunks;    // ceil(A / kChunk)
+  int split;      // split of the down projection's reduction
+  int ksplit;     // reduction length of one split (multiple of 64)
+  // byte offsets into the workspace (256-byte aligned)
+  size_t o_ids, o_w, o_counts, o_offsets, o_ccnt, o_cbase, o_perm, o_inv, o_blocks, o_nb;
+  size_t route_bytes;  // end of the routing section
+  size_t o_xperm, o_h, o_y;
+  size_t total_bytes;
+};
+
+// ---- launchers (enqueue on `s`, return the launch status) ----------------
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, int score,
+                        int32_t* ids, float* w, hipStream_t s);
+
+hipError_t launch_hist_scan(const int32_t* ids, int A, int E, int bm, int nchunks,
+                            int32_t* counts, int32_t* offsets, int32_t* chunk_cnt,
+                            int32_t* chunk_base, int32_t* blocks, int32_t* nb, hipStream_t s);
+
+hipError_t launch_permute(const int32_t* ids, int A, int E, int nchunks, const int32_t* offsets,
+                          const int32_t* chunk_cnt, const int32_t* chunk_base, int32_t* perm,
+                          int32_t* inv, hipStream_t s);
+
+hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int A, int d, int k,
+                         uint16_t* x_perm, hipStream_t s);
+
+// Fused gate/up SwiGLU grouped GEMM: h[A, F] = silu(X Wg^T) * (X Wu^T) per block.
+hipError_t launch_gate_up(int bm, const uint16_t* x_perm, const uint16_t* w_gate_up,
+                          const int32_t* blocks, const int32_t* nb, const int32_t* offsets,
+                          uint16_t* h, int A, int d, int ffn, int nb_max, hipStream_t s);
+
+// Down grouped GEMM: y[split, A, d] = partial sums of h Wd^T per block.
+hipError_t launch_down(int bm, const uint16_t* h, const uint16_t* w_down, const int32_t* blocks,
+                       const int32_t* nb, const int32_t* offsets, float* y, int A, int d, int ffn,
+                       int split, int ksplit, int nb_max, hipStream_t s);
+
+// Weighted combination: out[t] = bf16(sum_j w[t,j] * sum_s y[s, inv[t*k+j]]).
+hipError_t launch_combine(const float* y, int split, int A, int d, const int32_t* inv,
+                          const float* w, int k, int T, uint16_t* out, hipStream_t s);
+
+// Column tile widths (output columns per workgroup) of the two GEMMs for a
+// block size; the planner uses them to size the grids.
+int gate_up_tile_cols(int bm);
+int down_tile_cols(int bm);
+
+}  // namespace moe

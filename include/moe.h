@@ -1,0 +1,194 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Mixture-of-Experts forward path.
+ *
+ * The library computes, for T tokens, the complete single-GPU MoE forward
+ * pass: score the tokens (router top-k), reorder them onto experts, run the
+ * variable-size per-expert SwiGLU GEMMs and combine the results back with
+ * the routing weights.
+ *
+ * Source of the operation.  [R] is the Pith review page of "Cross-Platform
+ * Fused MoE Dispatch in Triton: Portable Expert Routing Without CUDA"
+ * (arXiv 2605.23911), which also carries the paper's abstract:
+ *   - [R] "The reading": the four steps above.
+ *   - [R] "What carries the argument": gate and up projections computed from
+ *     one shared load of each input tile, SiLU applied in registers so the
+ *     two intermediates never reach global memory; a grouped GEMM whose
+ *     fixed-size blocks map to (expert, token-offset) pairs.
+ *   - [R] "Assumptions & free parameters": softmax or sigmoid router, top-k,
+ *     SwiGLU FFN (paper Eq. (1)-(4)); BLOCK_M fixed per launch.
+ *   - abstract: router scoring, token permutation, expert GEMMs, weighted
+ *     output combination.
+ *
+ * Conventions for every entry point
+ *   - bf16 tensors are passed as uint16_t bit patterns; all tensors are
+ *     dense row-major.
+ *   - Data pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates or frees device memory and never synchronises the
+ *     stream; every kernel is enqueued on `hip_stream` (a hipStream_t; NULL
+ *     means the default stream) and the call returns at once.
+ *   - All argument checks run on the host before any HIP call.  On failure
+ *     the entry point returns a negative moe_status, enqueues nothing and
+ *     leaves every output untouched.  A failed launch returns MOE_ERR_HIP;
+ *     faults inside a kernel surface at the caller's next synchronisation.
+ *   - Calls are re-entrant.  Concurrent calls are safe on distinct streams
+ *     with distinct workspaces; calls that share a workspace must be
+ *     ordered on one stream.
+ *   - The contents of the workspace after a call are unspecified.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Limits of this build (violations return MOE_ERR_UNSUPPORTED). */
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_ROWS (1 << 20)   /* T * top_k */
+
+enum moe_score {
+    MOE_SCORE_SOFTMAX = 0,  /* softmax over the logits                    */
+    MOE_SCORE_SIGMOID = 1   /* logistic sigmoid of each logit             */
+};
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL = -1,        /* a required pointer is NULL                 */
+    MOE_ERR_SHAPE = -2,       /* negative or zero size where one is needed  */
+    MOE_ERR_TOPK = -3,        /* top_k < 1 or top_k > E                     */
+    MOE_ERR_ALIGN = -4,       /* d or ffn not a multiple of 64, or a pointer
+                                 not 16-byte aligned (workspace: 256)       */
+    MOE_ERR_WORKSPACE = -5,   /* workspace smaller than the size query      */
+    MOE_ERR_UNSUPPORTED = -6, /* beyond this build's limits, bad option     */
+    MOE_ERR_HIP = -7          /* a HIP launch or record call failed         */
+};
+
+/* Optional knobs of moe_forward_ex / moe_route.  Zero-initialise for the
+ * automatic choices. */
+typedef struct moe_options {
+    /* Rows per schedule block (BLOCK_M, [R] "Assumptions & free
+     * parameters": fixed for one launch).  0 = chosen from T*top_k/E; else
+     * one of 16, 32, 64, 128, 192. */
+    int block_rows;
+    /* Split of the down projection's reduction (ffn) into this many parts
+     * whose partial sums the combination adds in a fixed order.  0 =
+     * automatic; else 1..8. */
+    int split_k;
+    /* NULL, or 7 hipEvent_t handles created by the caller (for instance
+     * with moe_timer_create).  events[0] is recorded on the stream before
+     * the first kernel and events[i] right after kernel i (1 route, 2
+     * histogram+scan+schedule, 3 reorder+gather, 4 fused gate/up SwiGLU
+     * GEMM, 5 down GEMM, 6 weighted combination).  moe_route records
+     * 0..3 only. */
+    void *const *stage_events;
+} moe_options;
+
+/* Returns MOE_ABI_VERSION. */
+int moe_abi_version(void);
+
+/* Static text for a moe_status value (never NULL). */
+const char *moe_status_string(int status);
+
+/* Host-only size query: bytes of workspace moe_forward needs for these
+ * sizes with the automatic options.  T = 0 gives 0.  Same checks and error
+ * codes as moe_forward (pointer checks aside). */
+int moe_workspace_size(int T, int d, int ffn, int E, int top_k, size_t *bytes);
+
+/* As moe_workspace_size for moe_forward_ex with options `opt` (NULL means
+ * automatic). */
+int moe_workspace_size_ex(int T, int d, int ffn, int E, int top_k, const moe_options *opt,
+                          size_t *bytes);
+
+/* Host-only: the block_rows (BLOCK_M) and split_k the library would use for
+ * these sizes and options.  Either output pointer may be NULL. */
+int moe_plan(int T, int d, int ffn, int E, int top_k, const moe_options *opt,
+             int *block_rows, int *split_k);
+
+/*
+ * The MoE forward pass ([R] "The reading"; abstract).
+ *
+ *   x             bf16 [T, d]           token activations
+ *   router_logits fp32 [T, E]           router logits (finite values)
+ *   W_gate_up     bf16 [E, 2*ffn, d]    per expert: gate rows [0, ffn),
+ *                                       then up rows [ffn, 2*ffn)
+ *   W_down        bf16 [E, d, ffn]      per expert down projection
+ *   top_k         experts per token, 1..min(E, 16)
+ *   renormalize   softmax: 1 = softmax over the top_k selected logits,
+ *                 0 = softmax over all E logits, then take the top_k;
+ *                 sigmoid: 1 = divide by the sum of the top_k sigmoids
+ *   out           bf16 [T, d]           written; must not alias an input
+ *   score_func    MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID
+ *   workspace     device buffer of at least moe_workspace_size bytes,
+ *                 256-byte aligned
+ *
+ * Computes, for each token t,
+ *   out[t] = bf16_rne( sum_j w[t,j] * Wd[e_j] (silu(Wg[e_j] x_t) * Wu[e_j] x_t) )
+ * where e_0..e_{k-1} are the top_k experts by logit (descending, equal
+ * logits to the lower expert index) and w[t,j] their routing weights.
+ * Constraints: T >= 0 (T = 0 is a no-op), 1 <= E <= 512, d and ffn
+ * positive multiples of 64, T*top_k <= 2^20, pointers 16-byte aligned.
+ * Deterministic: the same inputs give bitwise the same out.
+ */
+int moe_forward(const uint16_t *x, const float *router_logits, const uint16_t *W_gate_up,
+                const uint16_t *W_down, int top_k, int renormalize, uint16_t *out,
+                int T, int d, int ffn, int E, int score_func,
+                void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* moe_forward with options (NULL = automatic, identical to moe_forward).
+ * The workspace must hold moe_workspace_size_ex(..., opt, ...) bytes. */
+int moe_forward_ex(const uint16_t *x, const float *router_logits, const uint16_t *W_gate_up,
+                   const uint16_t *W_down, int top_k, int renormalize, uint16_t *out,
+                   int T, int d, int ffn, int E, int score_func, const moe_options *opt,
+                   void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Host-only size query for moe_route. */
+int moe_route_workspace_size(int T, int E, int top_k, const moe_options *opt, size_t *bytes);
+
+/*
+ * Routing only: the first three kernels of moe_forward, with their results
+ * copied to caller buffers ([R] "The reading": scoring and reordering;
+ * "What carries the argument": the (expert, token-offset) block table).
+ * A = T*top_k.  Every output may be NULL (not produced):
+ *   topk_ids int32 [T, top_k]   experts of each token, descending logit,
+ *                               equal logits to the lower index
+ *   topk_w   fp32  [T, top_k]   routing weights (as in moe_forward)
+ *   counts   int32 [E]          rows routed to each expert
+ *   offsets  int32 [E+1]        exclusive prefix sum of counts
+ *   perm     int32 [A]          sorted row p -> flat index t*top_k + j;
+ *                               rows of one expert keep ascending flat index
+ *   inv      int32 [A]          flat index -> sorted row
+ *   blocks   int32 [nb_max, 2]  (expert, first sorted row) of each block of
+ *                               up to block_rows rows of one expert, experts
+ *                               ascending; nb_max = ceil(A/BM) + min(E, A)
+ *   nb       int32 [1]          number of valid blocks (device)
+ *   x, x_perm  bf16 [T, d] and [A, d]: if both are non-NULL, x_perm[p] =
+ *                               x[perm[p] / top_k] is also written (d > 0,
+ *                               a multiple of 64)
+ *   bm_used  HOST int [1]       the block_rows used
+ * The workspace must hold moe_route_workspace_size bytes.
+ */
+int moe_route(const float *router_logits, int T, int E, int top_k, int renormalize, int score_func,
+              const moe_options *opt,
+              int32_t *topk_ids, float *topk_w, int32_t *counts, int32_t *offsets,
+              int32_t *perm, int32_t *inv, int32_t *blocks, int32_t *nb,
+              const uint16_t *x, int d, uint16_t *x_perm, int *bm_used,
+              void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Thin wrappers over HIP events for timing the stages of moe_forward_ex
+ * (moe_options.stage_events).  Each returns a moe_status. */
+int moe_timer_create(void **event);
+int moe_timer_destroy(void *event);
+/* Milliseconds between two recorded events; waits for `stop` to complete. */
+int moe_timer_elapsed_ms(void *start, void *stop, float *ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

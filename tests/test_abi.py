@@ -1,0 +1,176 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/moe.h declares, and rejects bad arguments on the host before any HIP
+call (so these calls never reach a kernel launch).
+
+Every call below is built to fail a host check; none of them passes a set of
+arguments that validation would accept, so nothing is ever launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import expert_dispatch_router_amd as moe
+from expert_dispatch_router_amd import _lib
+from expert_dispatch_router_amd.synth import CONFIGS
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe.h")
+
+OK, NULL, SHAPE, TOPK, ALIGN, WS, UNSUP = 0, -1, -2, -3, -4, -5, -6
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 12
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+        assert n in _lib.SIGNATURES, n
+    assert moe.moe_abi_version() == 1
+
+
+def test_status_strings():
+    for s in (OK, NULL, SHAPE, TOPK, ALIGN, WS, UNSUP, -7, 99):
+        assert isinstance(moe.status_string(s), str) and moe.status_string(s)
+
+
+def _ws(T, d, F, E, k, opt=None):
+    n = ctypes.c_size_t(0)
+    rc = moe.lib().moe_workspace_size_ex(T, d, F, E, k, opt, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size_checks():
+    assert _ws(-1, 64, 64, 4, 2)[0] == SHAPE
+    assert _ws(4, 0, 64, 4, 2)[0] == SHAPE
+    assert _ws(4, 64, 64, 0, 1)[0] == SHAPE
+    assert _ws(4, 64, 64, 4, 0)[0] == TOPK
+    assert _ws(4, 64, 64, 4, 5)[0] == TOPK
+    assert _ws(4, 64, 64, 513, 2)[0] == UNSUP
+    assert _ws(4, 64, 64, 64, 17)[0] == UNSUP
+    assert _ws(4, 96, 64, 4, 2)[0] == ALIGN
+    assert _ws(4, 64, 100, 4, 2)[0] == ALIGN
+    assert _ws(1 << 20, 64, 64, 8, 2)[0] == UNSUP
+    assert _ws(0, 64, 64, 4, 2) == (OK, 0)
+    rc, n = _ws(64, 256, 512, 8, 2)
+    assert rc == OK and n > 0 and n % 256 == 0
+    n = ctypes.c_size_t(0)
+    assert moe.lib().moe_workspace_size(4, 64, 64, 4, 2, None) == NULL
+
+
+def test_options_checks():
+    for bad in (_lib.MoeOptions(8, 0, None), _lib.MoeOptions(0, 9, None), _lib.MoeOptions(0, -1, None)):
+        assert _ws(64, 256, 512, 8, 2, ctypes.byref(bad))[0] == UNSUP
+    for bm in (16, 32, 64, 128, 192):
+        rc, n = _ws(64, 256, 512, 8, 2, ctypes.byref(_lib.MoeOptions(bm, 0, None)))
+        assert rc == OK and n > 0
+
+
+def test_plan_choices_for_the_workloads():
+    # near-uniform routing: one block per expert in the common case
+    assert moe.moe_plan(512, 4096, 14336, 8, 2)[0] == 192
+    assert moe.moe_plan(512, 7168, 2048, 256, 8)[0] == 32
+    for name, c in CONFIGS.items():
+        bm, split = moe.moe_plan(c.T, c.d, c.ffn, c.E, c.top_k)
+        assert bm in (16, 32, 64, 128, 192) and 1 <= split <= 8, name
+        assert moe.moe_plan(c.T, c.d, c.ffn, c.E, c.top_k, block_rows=16, split_k=3) == (16, 3)
+
+
+def test_workspace_grows_with_split_and_small_blocks():
+    a = moe.moe_workspace_size(512, 4096, 14336, 8, 2, block_rows=192, split_k=1)
+    b = moe.moe_workspace_size(512, 4096, 14336, 8, 2, block_rows=192, split_k=4)
+    c = moe.moe_workspace_size(512, 4096, 14336, 8, 2, block_rows=16, split_k=4)
+    assert a < b < c
+    # the fp32 split partials dominate: 3 more parts of [A, d] fp32
+    assert b - a == 3 * 1024 * 4096 * 4
+
+
+FAKE = 1 << 20  # a 256-aligned non-null address that is never dereferenced
+
+
+def _fwd(**kw):
+    a = dict(x=FAKE, logits=FAKE, wgu=FAKE, wd=FAKE, k=2, renorm=1, out=FAKE, T=4, d=64, F=64, E=4,
+             score=0, opt=None, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return moe.lib().moe_forward_ex(a["x"], a["logits"], a["wgu"], a["wd"], a["k"], a["renorm"],
+                                    a["out"], a["T"], a["d"], a["F"], a["E"], a["score"], a["opt"],
+                                    a["ws"], a["wsb"], a["stream"])
+
+
+def test_forward_rejects_before_any_launch():
+    # wsb=0 makes every otherwise-valid combination fail with MOE_ERR_WORKSPACE
+    assert _fwd() == WS
+    for name in ("x", "logits", "wgu", "wd", "out", "ws"):
+        assert _fwd(**{name: None}) == NULL, name
+    for name in ("x", "logits", "wgu", "wd", "out"):
+        assert _fwd(**{name: FAKE + 8}) == ALIGN, name
+    assert _fwd(ws=FAKE + 16) == ALIGN
+    assert _fwd(T=-1) == SHAPE
+    assert _fwd(k=0) == TOPK
+    assert _fwd(k=5) == TOPK
+    assert _fwd(d=100) == ALIGN
+    assert _fwd(F=32) == ALIGN
+    assert _fwd(score=2) == UNSUP
+    assert _fwd(E=600, k=2) == UNSUP
+    assert _fwd(opt=ctypes.byref(_lib.MoeOptions(48, 0, None))) == UNSUP
+    rc, need = _ws(4, 64, 64, 4, 2)
+    assert _fwd(wsb=need - 1) == WS
+    # T = 0 is a no-op that succeeds even with NULL buffers
+    assert _fwd(T=0, x=None, logits=None, wgu=None, wd=None, out=None, ws=None) == OK
+
+
+def test_plain_forward_entry_validates_the_same_way():
+    L = moe.lib()
+    assert L.moe_forward(FAKE, FAKE, FAKE, FAKE, 2, 1, FAKE, 4, 64, 64, 4, 0, FAKE, 0, None) == WS
+    assert L.moe_forward(None, FAKE, FAKE, FAKE, 2, 1, FAKE, 4, 64, 64, 4, 0, FAKE, 0, None) == NULL
+
+
+def _route(**kw):
+    a = dict(logits=FAKE, T=4, E=4, k=2, renorm=1, score=0, opt=None, x=None, d=0, xp=None,
+             ws=FAKE, wsb=0)
+    a.update(kw)
+    bm = ctypes.c_int(-1)
+    rc = moe.lib().moe_route(a["logits"], a["T"], a["E"], a["k"], a["renorm"], a["score"], a["opt"],
+                             FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["x"], a["d"], a["xp"],
+                             ctypes.byref(bm), a["ws"], a["wsb"], None)
+    return rc, bm.value
+
+
+def test_route_rejects_before_any_launch():
+    assert _route()[0] == WS
+    assert _route(logits=None)[0] == NULL
+    assert _route(ws=None)[0] == NULL
+    assert _route(logits=FAKE + 4)[0] == ALIGN
+    assert _route(k=7)[0] == TOPK
+    assert _route(score=5)[0] == UNSUP
+    assert _route(x=FAKE, xp=FAKE, d=96)[0] == ALIGN
+    assert _route(x=FAKE, xp=FAKE, d=0)[0] == SHAPE
+    assert _route(x=FAKE + 8, xp=FAKE, d=64)[0] == ALIGN
+    rc, bm = _route(T=0, logits=None, ws=None)
+    assert rc == OK and bm in (16, 32, 64, 128, 192)
+    n = ctypes.c_size_t(0)
+    assert moe.lib().moe_route_workspace_size(4, 4, 2, None, ctypes.byref(n)) == OK and n.value > 0
+
+
+def test_timer_argument_checks():
+    L = moe.lib()
+    assert L.moe_timer_create(None) == NULL
+    assert L.moe_timer_destroy(None) == NULL
+    assert L.moe_timer_elapsed_ms(None, None, None) == NULL
+
+
+def test_product_path_never_imports_the_oracle():
+    pkg = os.path.dirname(moe.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(root, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "moe_oracle" not in text and "liboracle" not in text, f

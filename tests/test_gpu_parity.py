@@ -1,0 +1,193 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Routing artefacts must match bit for bit at every size, including the full
+workload sizes.  The bf16 output must meet the tolerance of tests/parity.py:
+on every token for shapes the oracle finishes in seconds (several tiles and
+ragged tails in every dimension, every compiled block size and several
+splits of the down projection), and on sampled tokens at the full workload
+sizes in the launch configuration the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import expert_dispatch_router_amd as moe
+from expert_dispatch_router_amd import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+ALL_BM = (16, 32, 64, 128, 192)
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    _need_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- routing
+
+@pytest.mark.parametrize("name", sorted(synth.CONFIGS))
+def test_route_workloads_bit_exact(name):
+    cfg = synth.CONFIGS[name]
+    lg = synth.make_logits(cfg, 0, DEV)
+    x = synth.make_x(cfg, 0, DEV)
+    g = moe.moe_route(lg, cfg.top_k, cfg.renormalize, cfg.score, x=x)
+    ref = parity.oracle_routing(lg, cfg.top_k, cfg.score, cfg.renormalize, g["bm"])
+    parity.check_routing(g, ref)
+    # the gather: x_perm[p] = x[perm[p] / k], byte for byte
+    src = torch.from_numpy(ref["perm"] // cfg.top_k).long().to(DEV)
+    assert torch.equal(g["x_perm"].view(torch.int16), x[src].view(torch.int16))
+
+
+def _edge_logits():
+    gen = torch.Generator().manual_seed(11)
+    cases = []
+    cases.append(("ties_small", torch.randint(-1, 2, (300, 16), generator=gen).float(), 4, 0, True))
+    z = torch.zeros(200, 8)
+    z[::2] = -0.0
+    cases.append(("signed_zeros", z, 3, 0, True))
+    hot = torch.randn(500, 32, generator=gen)
+    hot[:, 5] += 40.0
+    cases.append(("one_hot_expert", hot, 2, 0, True))
+    cases.append(("single_token", torch.randn(1, 8, generator=gen), 2, 0, True))
+    cases.append(("k_equals_E", torch.randn(77, 8, generator=gen), 8, 0, False))
+    cases.append(("one_expert", torch.randn(33, 1, generator=gen), 1, 1, True))
+    cases.append(("max_experts_topk", torch.randn(300, 512, generator=gen), 16, 1, True))
+    cases.append(("empty_experts", torch.randn(4, 64, generator=gen), 2, 0, True))
+    cases.append(("ragged_chunks", torch.randn(700, 100, generator=gen), 3, 0, False))
+    sat = 20.0 + 30.0 * torch.rand(64, 24, generator=gen)
+    cases.append(("sigmoid_saturated", sat, 6, 1, False))
+    cases.append(("many_chunks", torch.randn(5000, 256, generator=gen), 8, 1, True))
+    return cases
+
+
+@pytest.mark.parametrize("case", _edge_logits(), ids=lambda c: c[0])
+def test_route_edge_cases_bit_exact(case):
+    _, lg, k, score, renorm = case
+    lg = lg.to(DEV)
+    g = moe.moe_route(lg, k, renorm, score)
+    parity.check_routing(g, parity.oracle_routing(lg, k, score, renorm, g["bm"]))
+
+
+@pytest.mark.parametrize("bm", ALL_BM)
+def test_route_every_block_size(bm):
+    gen = torch.Generator().manual_seed(bm)
+    lg = torch.randn(600, 20, generator=gen)
+    lg[:, 2] += 2.5  # one busy expert so it spans several blocks
+    lg = lg.to(DEV)
+    g = moe.moe_route(lg, 3, True, 0, block_rows=bm)
+    assert g["bm"] == bm
+    parity.check_routing(g, parity.oracle_routing(lg, 3, 0, True, bm))
+
+
+# ---------------------------------------------------------------- forward
+
+_REF_CACHE = {}
+
+
+def _mid_case():
+    """T=200, d=512, F=384, E=12, k=3: several column tiles with a ragged
+    last one, several K steps, experts of ~50 rows so blocks end mid-tile."""
+    if "mid" not in _REF_CACHE:
+        cfg, x, lg, wgu, wd = parity.make_case(200, 512, 384, 12, 3, seed=5)
+        ref = parity.oracle_out(x, lg, wgu, wd, 3, 0, True)
+        _REF_CACHE["mid"] = (cfg, x, lg, wgu, wd, ref)
+    return _REF_CACHE["mid"]
+
+
+def test_forward_tiny_all_tokens():
+    cfg = synth.CONFIGS["tiny"]
+    x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)
+    out = moe.moe_forward(x, lg, wgu, wd, cfg.top_k, cfg.renormalize, score=cfg.score)
+    ref = parity.oracle_out(x, lg, wgu, wd, cfg.top_k, cfg.score, cfg.renormalize)
+    parity.check_out(out, ref, "tiny")
+
+
+@pytest.mark.parametrize("bm", ALL_BM)
+@pytest.mark.parametrize("split", [1, 2, 3])
+def test_forward_every_block_size_and_split(bm, split):
+    cfg, x, lg, wgu, wd, ref = _mid_case()
+    out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm, split_k=split)
+    parity.check_out(out, ref, f"bm={bm} split={split}")
+
+
+@pytest.mark.parametrize("score,renorm", [(0, False), (1, True), (1, False)])
+def test_forward_score_functions(score, renorm):
+    cfg, x, lg, wgu, wd = parity.make_case(96, 256, 256, 16, 4, score=score, renorm=renorm, seed=9)
+    out = moe.moe_forward(x, lg, wgu, wd, 4, renorm, score=score)
+    parity.check_out(out, parity.oracle_out(x, lg, wgu, wd, 4, score, renorm), f"score={score}")
+
+
+@pytest.mark.parametrize("bm", [32, 192])
+def test_forward_partial_column_tiles(bm):
+    """d=320 and F=192: the last column tile of both GEMMs is partly empty."""
+    cfg, x, lg, wgu, wd = parity.make_case(70, 320, 192, 6, 2, seed=13)
+    out = moe.moe_forward(x, lg, wgu, wd, 2, True, block_rows=bm, split_k=2)
+    parity.check_out(out, parity.oracle_out(x, lg, wgu, wd, 2, 0, True), f"partial bm={bm}")
+
+
+def test_forward_hot_expert_many_blocks():
+    """All tokens pick expert 1 first: 300 rows of one expert, 10 blocks."""
+    gen = torch.Generator().manual_seed(3)
+    lg = torch.randn(300, 8, generator=gen)
+    lg[:, 1] += 30.0
+    cfg, x, lg, wgu, wd = parity.make_case(300, 256, 128, 8, 2, seed=3, logits=lg)
+    out = moe.moe_forward(x, lg, wgu, wd, 2, True, block_rows=32)
+    parity.check_out(out, parity.oracle_out(x, lg, wgu, wd, 2, 0, True), "hot expert")
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (17, 1, 1), (40, 6, 6), (5, 64, 2)])
+def test_forward_degenerate_shapes(T, E, k):
+    cfg, x, lg, wgu, wd = parity.make_case(T, 128, 64, E, k, seed=T + E)
+    out = moe.moe_forward(x, lg, wgu, wd, k, True)
+    parity.check_out(out, parity.oracle_out(x, lg, wgu, wd, k, 0, True), f"T={T} E={E} k={k}")
+
+
+def test_forward_zero_tokens_is_noop():
+    x = torch.empty(0, 128, dtype=torch.bfloat16, device=DEV)
+    lg = torch.empty(0, 4, device=DEV)
+    wgu = torch.zeros(4, 128, 128, dtype=torch.bfloat16, device=DEV)
+    wd = torch.zeros(4, 128, 64, dtype=torch.bfloat16, device=DEV)
+    out = torch.empty(0, 128, dtype=torch.bfloat16, device=DEV)
+    assert moe.moe_forward(x, lg, wgu, wd, 2, True, out=out) is out
+
+
+def test_forward_deterministic_and_stream():
+    cfg, x, lg, wgu, wd, ref = _mid_case()
+    a = moe.moe_forward(x, lg, wgu, wd, 3, True, split_k=3)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = moe.moe_forward(x, lg, wgu, wd, 3, True, split_k=3, stream=s)
+    s.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    c = moe.moe_forward(x, lg, wgu, wd, 3, True, split_k=3)
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
+FULL = ["mixtral_128", "mixtral_256", "mixtral_512", "qwen2_128", "qwen2_256", "qwen2_512",
+        "skewed_128", "skewed_256", "skewed_512", "dsv3_512", "dsv3_4096"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size_sampled(name):
+    """Full workload sizes, automatic options (what the benchmark runs);
+    the oracle evaluates a sample of tokens one by one."""
+    cfg = synth.CONFIGS[name]
+    x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)
+    out = moe.moe_forward(x, lg, wgu, wd, cfg.top_k, cfg.renormalize, score=cfg.score)
+    rng = np.random.default_rng(len(name))
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 6, replace=False)]))
+    ref = parity.oracle_out(x, lg, wgu, wd, cfg.top_k, cfg.score, cfg.renormalize, tokens=toks)
+    parity.check_out(out[torch.from_numpy(toks).long().to(DEV)], ref, name)
+    del x, lg, wgu, wd, out
+    torch.cuda.empty_cache()
