@@ -49,6 +49,7 @@ SIGNATURES = {
 class MoeOptions(ctypes.Structure):
     """struct moe_options of include/moe.h."""
     _fields_ = [("block_rows", ctypes.c_int), ("split_k", ctypes.c_int),
+                ("tile_variant", ctypes.c_int), ("rotate", ctypes.c_int),
                 ("stage_events", ctypes.c_void_p)]
 
 
@@ -93,10 +94,10 @@ def moe_abi_version() -> int:
     return int(lib().moe_abi_version())
 
 
-def _opts(block_rows=0, split_k=0, stage_events=None):
-    if not block_rows and not split_k and stage_events is None:
+def _opts(block_rows=0, split_k=0, stage_events=None, tile_variant=0, rotate=0):
+    if not block_rows and not split_k and stage_events is None and not tile_variant and not rotate:
         return None, None
-    o = MoeOptions(int(block_rows), int(split_k), None)
+    o = MoeOptions(int(block_rows), int(split_k), int(tile_variant), int(rotate), None)
     keep = None
     if stage_events is not None:
         keep = (ctypes.c_void_p * len(stage_events))(*stage_events)
@@ -104,17 +105,18 @@ def _opts(block_rows=0, split_k=0, stage_events=None):
     return o, keep
 
 
-def moe_workspace_size(T, d, ffn, E, top_k, block_rows=0, split_k=0) -> int:
-    o, _ = _opts(block_rows, split_k)
+def moe_workspace_size(T, d, ffn, E, top_k, block_rows=0, split_k=0, tile_variant=0,
+                       rotate=0) -> int:
+    o, _ = _opts(block_rows, split_k, None, tile_variant, rotate)
     n = _SZ(0)
     _check("moe_workspace_size_ex", lib().moe_workspace_size_ex(
         T, d, ffn, E, top_k, ctypes.byref(o) if o else None, ctypes.byref(n)))
     return int(n.value)
 
 
-def moe_plan(T, d, ffn, E, top_k, block_rows=0, split_k=0):
+def moe_plan(T, d, ffn, E, top_k, block_rows=0, split_k=0, tile_variant=0, rotate=0):
     """(block_rows, split_k) the library uses for these sizes and options."""
-    o, _ = _opts(block_rows, split_k)
+    o, _ = _opts(block_rows, split_k, None, tile_variant, rotate)
     bm, sk = _I(0), _I(0)
     _check("moe_plan", lib().moe_plan(T, d, ffn, E, top_k, ctypes.byref(o) if o else None,
                                        ctypes.byref(bm), ctypes.byref(sk)))
@@ -154,7 +156,7 @@ def _stream_ptr(stream, device):
 
 def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=None,
                 score="softmax", workspace=None, stream=None, block_rows=0, split_k=0,
-                stage_events=None):
+                stage_events=None, tile_variant=0, rotate=0):
     """out[T,d] (bf16) = the MoE forward pass, enqueued on ``stream``.
 
     x bf16 [T,d]; router_logits fp32 [T,E]; W_gate_up bf16 [E,2F,d];
@@ -168,10 +170,10 @@ def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=Non
         raise ValueError("inconsistent shapes")
     if out is None:
         out = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
-    ws_need = moe_workspace_size(T, d, F, E, top_k, block_rows, split_k)
+    ws_need = moe_workspace_size(T, d, F, E, top_k, block_rows, split_k, tile_variant, rotate)
     if workspace is None:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=x.device)
-    o, keep = _opts(block_rows, split_k, stage_events)
+    o, keep = _opts(block_rows, split_k, stage_events, tile_variant, rotate)
     rc = lib().moe_forward_ex(
         _dev_ptr(x, torch.bfloat16, "x"), _dev_ptr(router_logits, torch.float32, "router_logits"),
         _dev_ptr(W_gate_up, torch.bfloat16, "W_gate_up"), _dev_ptr(W_down, torch.bfloat16, "W_down"),

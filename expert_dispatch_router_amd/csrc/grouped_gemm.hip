@@ -64,6 +64,14 @@ struct Gemm {
   static_assert(BM % 16 == 0, "BM is a multiple of 16");
 };
 
+// 128-bit raw buffer load; offsets past the resource's byte range read 0.
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+
+// gfx9 raw-buffer descriptor word 3 (32-bit data format, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
+
 // X: activations [A, K] (sorted rows).  W: weights [E, NG*N, K].
 // out: K4 -> bf16 h [A, N];  K5 -> fp32 y [split, A, N].
 template <int BM, int NWT, int WAVES, int PF, bool SWIGLU>
@@ -71,9 +79,10 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
     const int32_t* __restrict__ offsets, void* __restrict__ out, int A, int N, int K, int ksplit,
-    int tiles_per_block) {
+    int tiles_per_block, int rotate) {
   using G = Gemm<BM, NWT, WAVES, PF, SWIGLU>;
   constexpr int MT = G::kMT, NG = G::kNG, XPT = G::kXPerThread;
+  static_assert(PF >= 2, "the activation stage is issued PF-1 steps ahead");
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kLdsStride];
 
   const int b = blockIdx.x / tiles_per_block;
@@ -97,39 +106,39 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
   const int lrow = lane & 15;
   const int lk = (lane >> 4) * 8;
 
-  // Every global load below is unconditional, with its address clamped into
-  // the operands, so the compiler can count outstanding loads exactly and
-  // wait only for the oldest ring stage.  Subtiles past the last column load
-  // the last valid rows and are never stored; K steps past the end reload
-  // the last step (an L2 hit).
-  const uint16_t* wrow[NG][NWT];
+  // Buffer resources: this expert's weights, and this block's rows of X.
+  // Rows past the block's end are outside the X range and load as zeros;
+  // column subtiles past N are never stored.  Every load below is
+  // unconditional (K steps past the end reload the last step, an L2 hit),
+  // so the compiler counts outstanding loads exactly and waits only for the
+  // oldest ring stage.
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (size_t)e * NG * N * K), (short)0, NG * N * K * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(X + (size_t)r0 * K), (short)0, rows * K * 2, kRsrcWord3);
+  int woff[NG][NWT];
   bool jok[NWT];
 #pragma unroll
   for (int j = 0; j < NWT; ++j) {
     jok[j] = n0 + 16 * j < N;
-    const int nr = (jok[j] ? n0 + 16 * j : N - 16) + lrow;
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
-      wrow[g][j] = W + ((size_t)e * NG * N + (size_t)g * N + nr) * K + kb + lk;
+    for (int g = 0; g < NG; ++g) woff[g][j] = ((g * N + n0 + 16 * j + lrow) * K + kb + lk) * 2;
   }
-
   // Activation chunks this thread stages: chunk c -> (row c/8, 16-byte
   // column chunk c%8).  When the tile has fewer chunks than threads, extra
-  // threads repeat a chunk (same data, same LDS slot).  Rows past the
-  // block's end read its last row and store zeros.
-  const uint16_t* xsrc[XPT];
+  // threads repeat a chunk (same data, same LDS slot).
+  int xoff[XPT];
   int xdst[XPT];
-  bool xreal[XPT];
 #pragma unroll
   for (int q = 0; q < XPT; ++q) {
     const int c = (tid + q * G::kThreads) % G::kXChunks;
-    const int row = c >> 3;
-    const int ch = c & 7;
-    xreal[q] = row < rows;
-    xsrc[q] = X + (size_t)(r0 + (xreal[q] ? row : rows - 1)) * K + kb + ch * 8;
-    xdst[q] = row * kLdsStride + ch * 8;
+    xoff[q] = ((c >> 3) * K + kb + (c & 7) * 8) * 2;
+    xdst[q] = (c >> 3) * kLdsStride + (c & 7) * 8;
   }
 
+  // Ring of PF slots.  Slot s = ks % PF carries the weights of step ks and
+  // the activation tile of step ks - 1 (activation tiles are issued one step
+  // later than weights, so only PF-1 of them are live at once).
   bf16x8 wr[PF][NG][NWT][2];
   u32x4 xr[PF][XPT];
   f32x4 acc[NG][MT][NWT];
@@ -140,36 +149,51 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < NWT; ++j) acc[g][mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // K-step order: with `rotate`, each workgroup starts its reduction at its
+  // own step and wraps around.  When every weight row is a power-of-two
+  // number of bytes long, workgroups walking K in lockstep all address the
+  // same memory channels at once; rotating the start spreads them.  The
+  // order is fixed per workgroup, so results stay deterministic.
+  const int shift = rotate ? (int)(((unsigned)blockIdx.x * 2654435761u) % (unsigned)max(nks, 1)) : 0;
+  auto step_of = [&](int ks) {
+    const int p = ks + shift;
+    return p >= nks ? p - nks : p;
+  };
   auto load_x = [&](u32x4(&dst)[XPT], int ks) {
+    const int soff = step_of(ks) * kBK * 2;
 #pragma unroll
-    for (int q = 0; q < XPT; ++q)
-      dst[q] = *reinterpret_cast<const u32x4*>(xsrc[q] + (size_t)ks * kBK);
+    for (int q = 0; q < XPT; ++q) dst[q] = buf_load16(xres, xoff[q], soff);
   };
   auto load_w = [&](bf16x8(&dst)[NG][NWT][2], int ks) {
+    const int soff = step_of(ks) * kBK * 2;
 #pragma unroll
     for (int j = 0; j < NWT; ++j)
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        const uint16_t* p = wrow[g][j] + (size_t)ks * kBK;
-        dst[g][j][0] = *reinterpret_cast<const bf16x8*>(p);
-        dst[g][j][1] = *reinterpret_cast<const bf16x8*>(p + 32);
+        dst[g][j][0] = __builtin_bit_cast(bf16x8, buf_load16(wres, woff[g][j], soff));
+        dst[g][j][1] = __builtin_bit_cast(bf16x8, buf_load16(wres, woff[g][j] + 64, soff));
       }
   };
   auto store_x = [&](int buf, const u32x4(&src)[XPT]) {
 #pragma unroll
-    for (int q = 0; q < XPT; ++q) {
-      const uint32_t keep = xreal[q] ? 0xffffffffu : 0u;
-      *reinterpret_cast<u32x4*>(&xs[buf][xdst[q]]) = src[q] & keep;
-    }
+    for (int q = 0; q < XPT; ++q) *reinterpret_cast<u32x4*>(&xs[buf][xdst[q]]) = src[q];
   };
+  // Multiply one K step.  Activation fragments are read from LDS one 16-row
+  // subtile ahead of their MFMAs (rows past the block's end hold zeros, so
+  // the read is always in bounds); the scheduling barriers keep the compiler
+  // from hoisting every fragment read of the unrolled loop to the top.
   auto compute = [&](int buf, const bf16x8(&wv)[NG][NWT][2]) {
-    const uint16_t* xb = &xs[buf][0];
+    const uint16_t* xb = &xs[buf][lrow * kLdsStride + lk];
+    bf16x8 xa0 = *reinterpret_cast<const bf16x8*>(xb);
+    bf16x8 xa1 = *reinterpret_cast<const bf16x8*>(xb + 32);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
+      bf16x8 xn0 = xa0, xn1 = xa1;
+      if (mt + 1 < MT) {
+        xn0 = *reinterpret_cast<const bf16x8*>(xb + (mt + 1) * 16 * kLdsStride);
+        xn1 = *reinterpret_cast<const bf16x8*>(xb + (mt + 1) * 16 * kLdsStride + 32);
+      }
       if (mt < mt_act) {
-        const uint16_t* xp = xb + (mt * 16 + lrow) * kLdsStride + lk;
-        const bf16x8 xa0 = *reinterpret_cast<const bf16x8*>(xp);
-        const bf16x8 xa1 = *reinterpret_cast<const bf16x8*>(xp + 32);
 #pragma unroll
         for (int j = 0; j < NWT; ++j)
 #pragma unroll
@@ -180,40 +204,54 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
                                                                     acc[g][mt][j], 0, 0, 0);
           }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      xa0 = xn0;
+      xa1 = xn1;
     }
   };
 
   if (nks > 0) {
-    // Prologue: stages 0..PF-1 in flight (activation, then weights, per stage).
+    const int last = nks - 1;
+    // Prologue, in steady-state issue order: W(0); then X(i-1), W(i).
+    // The barriers pin this order so the loop is entered with the same queue
+    // of outstanding loads as every later iteration.
+    load_w(wr[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < PF; ++s) {
-      load_x(xr[s], min(s, nks - 1));
-      load_w(wr[s], min(s, nks - 1));
+    for (int i = 1; i < PF; ++i) {
+      load_x(xr[i], min(i - 1, last));
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(wr[i], min(i, last));
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // Full groups of PF steps; ring slot s is a fixed register set.  Step
-    // ks: stage its activation tile in LDS, barrier, refill the slot's
-    // activation part, multiply, refill the slot's weight part.
+    // Step ks (slot s): stage X(ks) (slot s+1) in LDS, barrier, multiply with
+    // W(ks), then refill slot s with X(ks+PF-1) and W(ks+PF), in that order
+    // -- waiting for X(ks) never waits for W(ks+1..ks+PF-1).
     int ks0 = 0;
     for (; ks0 + PF <= nks; ks0 += PF) {
 #pragma unroll
       for (int s = 0; s < PF; ++s) {
         const int ks = ks0 + s;
-        const int nxt = min(ks + PF, nks - 1);
         const int buf = ks & 1;
-        store_x(buf, xr[s]);
+        store_x(buf, xr[(s + 1) % PF]);
         lds_barrier();
-        load_x(xr[s], nxt);
         compute(buf, wr[s]);
-        load_w(wr[s], nxt);
+        // Keep the refill after the multiplies: hoisting it would hold two
+        // weight stages of this slot in registers at once.
+        __builtin_amdgcn_sched_barrier(0);
+        load_x(xr[s], min(ks + PF - 1, last));
+        __builtin_amdgcn_sched_barrier(0);
+        load_w(wr[s], min(ks + PF, last));
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // Remaining (< PF) steps are already in flight: no further loads.
+    // Remaining (< PF) steps: their stages are already in flight.
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
       const int ks = ks0 + s;
       if (ks < nks) {
         const int buf = ks & 1;
-        store_x(buf, xr[s]);
+        store_x(buf, xr[(s + 1) % PF]);
         lds_barrier();
         compute(buf, wr[s]);
       }
@@ -253,47 +291,53 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
 template <int BM, int NWT, int WAVES, int PF, bool SWIGLU>
 hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, const int32_t* blocks,
                       const int32_t* nb, const int32_t* offsets, void* out, int A, int N, int K,
-                      int split, int ksplit, int nb_max, hipStream_t s) {
+                      int split, int ksplit, int nb_max, int rotate, hipStream_t s) {
   using G = Gemm<BM, NWT, WAVES, PF, SWIGLU>;
   const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
   const int tiles_per_block = n_tiles * split;
   const long long grid = (long long)tiles_per_block * nb_max;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   grouped_gemm_kernel<BM, NWT, WAVES, PF, SWIGLU><<<(unsigned)grid, G::kThreads, 0, s>>>(
-      X, W, blocks, nb, offsets, out, A, N, K, ksplit, tiles_per_block);
+      X, W, blocks, nb, offsets, out, A, N, K, ksplit, tiles_per_block, rotate);
   return hipGetLastError();
 }
 
-// Tile shapes per block size.  NWT*16 columns per wave (x2 for gate+up in
-// K4), 4 waves, PF K steps of prefetch; register budget ~ acc + PF stages.
-#define MOE_GU_CFGS(X) X(16, 4, 4, 2) X(32, 4, 4, 2) X(64, 4, 4, 2) X(128, 2, 4, 2) X(192, 2, 4, 2)
-#define MOE_DN_CFGS(X) X(16, 4, 4, 3) X(32, 4, 4, 3) X(64, 4, 4, 3) X(128, 4, 4, 2) X(192, 4, 4, 2)
+// Tile shapes: (variant, BM, NWT, waves, PF).  NWT*16 output columns per wave
+// (x2 rows for gate+up in K4), PF K steps of weight prefetch.  Chosen by
+// measurement on the MoE workload shapes; variant 1 of K4 at BM=64 is the
+// narrow tile for launches with few blocks.
+#define MOE_GU_CFGS(X) \
+  X(0, 16, 4, 4, 2) X(0, 32, 4, 4, 2) X(0, 64, 4, 4, 3) X(1, 64, 2, 4, 4) X(0, 128, 2, 4, 3) \
+  X(0, 192, 2, 4, 3)
+#define MOE_DN_CFGS(X) \
+  X(0, 16, 8, 4, 2) X(0, 32, 8, 4, 2) X(0, 64, 4, 4, 4) X(0, 128, 4, 4, 3) X(0, 192, 4, 4, 3)
 
 }  // namespace
 
-int gate_up_tile_cols(int bm) {
-#define X(BM, NWT, WV, PF) \
-  if (bm == BM) return Gemm<BM, NWT, WV, PF, true>::kTileCols;
+int gate_up_tile_cols(int bm, int variant) {
+#define X(V, BM, NWT, WV, PF) \
+  if (bm == BM && variant == V) return Gemm<BM, NWT, WV, PF, true>::kTileCols;
   MOE_GU_CFGS(X)
 #undef X
   return 0;
 }
 
 int down_tile_cols(int bm) {
-#define X(BM, NWT, WV, PF) \
-  if (bm == BM) return Gemm<BM, NWT, WV, PF, false>::kTileCols;
+#define X(V, BM, NWT, WV, PF) \
+  if (bm == BM && V == 0) return Gemm<BM, NWT, WV, PF, false>::kTileCols;
   MOE_DN_CFGS(X)
 #undef X
   return 0;
 }
 
-hipError_t launch_gate_up(int bm, const uint16_t* x_perm, const uint16_t* w_gate_up,
+hipError_t launch_gate_up(int bm, int variant, const uint16_t* x_perm, const uint16_t* w_gate_up,
                           const int32_t* blocks, const int32_t* nb, const int32_t* offsets,
-                          uint16_t* h, int A, int d, int ffn, int nb_max, hipStream_t s) {
-#define X(BM, NWT, WV, PF)                                                                   \
-  if (bm == BM)                                                                              \
-    return launch_cfg<BM, NWT, WV, PF, true>(x_perm, w_gate_up, blocks, nb, offsets, h, A,   \
-                                             ffn, d, 1, d, nb_max, s);
+                          uint16_t* h, int A, int d, int ffn, int nb_max, int rotate,
+                          hipStream_t s) {
+#define X(V, BM, NWT, WV, PF)                                                                  \
+  if (bm == BM && variant == V)                                                                \
+    return launch_cfg<BM, NWT, WV, PF, true>(x_perm, w_gate_up, blocks, nb, offsets, h, A, ffn, \
+                                             d, 1, d, nb_max, rotate, s);
   MOE_GU_CFGS(X)
 #undef X
   return hipErrorInvalidValue;
@@ -301,11 +345,11 @@ hipError_t launch_gate_up(int bm, const uint16_t* x_perm, const uint16_t* w_gate
 
 hipError_t launch_down(int bm, const uint16_t* h, const uint16_t* w_down, const int32_t* blocks,
                        const int32_t* nb, const int32_t* offsets, float* y, int A, int d, int ffn,
-                       int split, int ksplit, int nb_max, hipStream_t s) {
-#define X(BM, NWT, WV, PF)                                                                  \
-  if (bm == BM)                                                                             \
-    return launch_cfg<BM, NWT, WV, PF, false>(h, w_down, blocks, nb, offsets, y, A, d, ffn, \
-                                              split, ksplit, nb_max, s);
+                       int split, int ksplit, int nb_max, int rotate, hipStream_t s) {
+#define X(V, BM, NWT, WV, PF)                                                                  \
+  if (bm == BM && V == 0)                                                                      \
+    return launch_cfg<BM, NWT, WV, PF, false>(h, w_down, blocks, nb, offsets, y, A, d, ffn,    \
+                                              split, ksplit, nb_max, rotate, s);
   MOE_DN_CFGS(X)
 #undef X
   return hipErrorInvalidValue;

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "../../include/moe.h"
 #include "moe_internal.hpp"
 
@@ -33,6 +35,11 @@ int check_sizes(int T, int d, int ffn, int E, int k, bool dims) {
   if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
   if (dims && (d % 64 != 0 || ffn % 64 != 0)) return MOE_ERR_ALIGN;
   if ((long long)T * k > MOE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
+  // The GEMMs address one expert's weights with 32-bit buffer offsets
+  // (including the rows of a partly filled last column tile).
+  const long long lim = 1LL << 31;
+  if (dims && ((2LL * ffn + 256) * d * 2 >= lim || (d + 256LL) * ffn * 2 >= lim))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -40,6 +47,11 @@ int check_options(const moe_options* opt) {
   if (!opt) return MOE_OK;
   if (opt->block_rows != 0 && !is_block_rows(opt->block_rows)) return MOE_ERR_UNSUPPORTED;
   if (opt->split_k < 0 || opt->split_k > kMaxSplit) return MOE_ERR_UNSUPPORTED;
+  if (opt->tile_variant < 0 || opt->rotate < 0 || opt->rotate > 2) return MOE_ERR_UNSUPPORTED;
+  if (opt->tile_variant > 0) {
+    const int bm = opt->block_rows;
+    if (bm == 0 || gate_up_tile_cols(bm, opt->tile_variant - 1) == 0) return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
@@ -55,21 +67,37 @@ int auto_block_rows(int A, int E) {
   return kBlockRows[sizeof(kBlockRows) / sizeof(kBlockRows[0]) - 1];
 }
 
-// Split of the down projection's reduction: enough workgroups to fill the
-// chip when blocks x column tiles are few (few experts, wide d).
+// Workgroups of a GEMM launch when every expert is active: blocks x tiles.
+long long est_workgroups(int A, int E, int bm, int n_cols, int tile_cols) {
+  const long long blocks = std::max<long long>((A + bm - 1) / bm, std::min(E, A));
+  return std::max<long long>(blocks, 1) * ((n_cols + tile_cols - 1) / tile_cols);
+}
+
+// Split of the down projection's reduction.  Measured on the MoE workload
+// shapes: one round of long-running workgroups (~one per CU) beats many
+// short ones, so split only as far as needed to reach ~256 workgroups, and
+// use two parts when a launch is small (< 640 workgroups).
 int auto_split(int A, int E, int d, int ffn, int bm) {
-  const int tile_cols = down_tile_cols(bm);
-  const long long n_tiles = (d + tile_cols - 1) / tile_cols;
-  const long long blocks_est = (long long)((A + bm - 1) / bm) < (long long)(E < A ? E : A)
-                                   ? (long long)(E < A ? E : A)
-                                   : (long long)((A + bm - 1) / bm);
-  const long long wg = n_tiles * (blocks_est > 0 ? blocks_est : 1);
-  int s = (int)((kTargetDownWorkgroups + wg - 1) / wg);
+  const long long wg = est_workgroups(A, E, bm, d, down_tile_cols(bm));
+  int s = (int)((256 + wg - 1) / wg);
+  if (wg < 640 && s < 2) s = 2;
   const int max_by_k = ffn / (8 * 64);  // keep at least 8 K steps per part
   if (s > max_by_k) s = max_by_k;
   if (s > kMaxSplit) s = kMaxSplit;
   return s < 1 ? 1 : s;
 }
+
+// Tile variant of the fused gate/up GEMM: at BM = 64, the narrow variant when
+// the wide one would give at most ~1.5 workgroups per CU.
+int auto_gu_variant(int A, int E, int ffn, int bm) {
+  if (bm != 64) return 0;
+  return est_workgroups(A, E, bm, ffn, gate_up_tile_cols(64, 0)) <= 384 ? 1 : 0;
+}
+
+// Rotate the K start when weight rows are a power-of-two number of bytes
+// (>= 2 KiB): measured to relieve lockstep channel conflicts there, and to
+// be neutral or slightly slower otherwise.
+bool auto_rotate(int K) { return K >= 1024 && (K & (K - 1)) == 0; }
 
 void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan* p) {
   memset(p, 0, sizeof(*p));
@@ -89,6 +117,11 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     const int per = (ksteps + s - 1) / s;
     p->ksplit = per * 64;
     p->split = (ksteps + per - 1) / per;  // every part has at least one K step
+    p->gu_variant = (opt && opt->tile_variant) ? opt->tile_variant - 1
+                                               : auto_gu_variant(A, E, ffn, p->bm);
+    const int rot = opt ? opt->rotate : 0;
+    p->gu_rotate = rot == 0 ? auto_rotate(d) : rot == 2;
+    p->dn_rotate = rot == 0 ? auto_rotate(ffn) : rot == 2;
   }
   size_t o = 0;
   auto seg = [&](size_t bytes) {
@@ -254,11 +287,11 @@ int moe_forward_ex(const uint16_t* x, const float* router_logits, const uint16_t
   float* y = at<float>(workspace, p.o_y);
   MOE_TRY_HIP(launch_gather(x, perm, p.A, d, top_k, x_perm, s));
   MOE_TRY(record(opt, 3, s));
-  MOE_TRY_HIP(launch_gate_up(p.bm, x_perm, W_gate_up, blocks, nb, offsets, h, p.A, d, ffn,
-                             p.nb_max, s));
+  MOE_TRY_HIP(launch_gate_up(p.bm, p.gu_variant, x_perm, W_gate_up, blocks, nb, offsets, h, p.A,
+                             d, ffn, p.nb_max, p.gu_rotate, s));
   MOE_TRY(record(opt, 4, s));
   MOE_TRY_HIP(launch_down(p.bm, h, W_down, blocks, nb, offsets, y, p.A, d, ffn, p.split,
-                          p.ksplit, p.nb_max, s));
+                          p.ksplit, p.nb_max, p.dn_rotate, s));
   MOE_TRY(record(opt, 5, s));
   MOE_TRY_HIP(launch_combine(y, p.split, p.A, d, at<int32_t>(workspace, p.o_inv),
                              at<float>(workspace, p.o_w), top_k, T, out, s));

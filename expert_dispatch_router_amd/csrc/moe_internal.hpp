@@ -29,6 +29,9 @@ struct Plan {
   int nchunks;    // ceil(A / kChunk)
   int split;      // split of the down projection's reduction
   int ksplit;     // reduction length of one split (multiple of 64)
+  int gu_variant; // tile variant of the fused gate/up GEMM
+  int gu_rotate;  // rotate the K-step start per workgroup (fused gate/up GEMM)
+  int dn_rotate;  // same for the down GEMM
   // byte offsets into the workspace (256-byte aligned)
   size_t o_ids, o_w, o_counts, o_offsets, o_ccnt, o_cbase, o_perm, o_inv, o_blocks, o_nb;
   size_t route_bytes;  // end of the routing section
@@ -53,14 +56,15 @@ hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int A, int d, i
                          uint16_t* x_perm, hipStream_t s);
 
 // Fused gate/up SwiGLU grouped GEMM: h[A, F] = silu(X Wg^T) * (X Wu^T) per block.
-hipError_t launch_gate_up(int bm, const uint16_t* x_perm, const uint16_t* w_gate_up,
+hipError_t launch_gate_up(int bm, int variant, const uint16_t* x_perm, const uint16_t* w_gate_up,
                           const int32_t* blocks, const int32_t* nb, const int32_t* offsets,
-                          uint16_t* h, int A, int d, int ffn, int nb_max, hipStream_t s);
+                          uint16_t* h, int A, int d, int ffn, int nb_max, int rotate,
+                          hipStream_t s);
 
 // Down grouped GEMM: y[split, A, d] = partial sums of h Wd^T per block.
 hipError_t launch_down(int bm, const uint16_t* h, const uint16_t* w_down, const int32_t* blocks,
                        const int32_t* nb, const int32_t* offsets, float* y, int A, int d, int ffn,
-                       int split, int ksplit, int nb_max, hipStream_t s);
+                       int split, int ksplit, int nb_max, int rotate, hipStream_t s);
 
 // Weighted combination: out[t] = bf16(sum_j w[t,j] * sum_s y[s, inv[t*k+j]]).
 hipError_t launch_combine(const float* y, int split, int A, int d, const int32_t* inv,
@@ -68,7 +72,7 @@ hipError_t launch_combine(const float* y, int split, int A, int d, const int32_t
 
 // Column tile widths (output columns per workgroup) of the two GEMMs for a
 // block size; the planner uses them to size the grids.
-int gate_up_tile_cols(int bm);
+int gate_up_tile_cols(int bm, int variant);
 int down_tile_cols(int bm);
 
 }  // namespace moe

@@ -80,6 +80,15 @@ typedef struct moe_options {
      * whose partial sums the combination adds in a fixed order.  0 =
      * automatic; else 1..8. */
     int split_k;
+    /* Tile variant of the fused gate/up GEMM.  0 = automatic; k >= 1 selects
+     * compiled variant k-1 for the chosen block_rows (which must then be set
+     * explicitly).  BM = 64 has variants 0 (256 columns per workgroup) and 1
+     * (128 columns); every other BM has variant 0 only. */
+    int tile_variant;
+    /* K-start rotation of the GEMM workgroups.  0 = automatic (on when the
+     * reduction length is a power of two >= 1024), 1 = off, 2 = on.  Results
+     * are deterministic either way; rounding differs slightly between them. */
+    int rotate;
     /* NULL, or 7 hipEvent_t handles created by the caller (for instance
      * with moe_timer_create).  events[0] is recorded on the stream before
      * the first kernel and events[i] right after kernel i (1 route, 2

@@ -65,12 +65,21 @@ def test_workspace_size_checks():
     assert moe.lib().moe_workspace_size(4, 64, 64, 4, 2, None) == NULL
 
 
+def _o(bm=0, split=0, variant=0, rotate=0):
+    return ctypes.byref(_lib.MoeOptions(bm, split, variant, rotate, None))
+
+
 def test_options_checks():
-    for bad in (_lib.MoeOptions(8, 0, None), _lib.MoeOptions(0, 9, None), _lib.MoeOptions(0, -1, None)):
-        assert _ws(64, 256, 512, 8, 2, ctypes.byref(bad))[0] == UNSUP
+    for bad in (_o(8), _o(0, 9), _o(0, -1), _o(0, 0, 1), _o(32, 0, 2), _o(64, 0, 3), _o(0, 0, 0, 3),
+                _o(0, 0, -1), _o(0, 0, 0, -1)):
+        assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
     for bm in (16, 32, 64, 128, 192):
-        rc, n = _ws(64, 256, 512, 8, 2, ctypes.byref(_lib.MoeOptions(bm, 0, None)))
+        rc, n = _ws(64, 256, 512, 8, 2, _o(bm))
         assert rc == OK and n > 0
+        assert _ws(64, 256, 512, 8, 2, _o(bm, 0, 1))[0] == OK
+    assert _ws(64, 256, 512, 8, 2, _o(64, 0, 2))[0] == OK
+    for r in (1, 2):
+        assert _ws(64, 256, 512, 8, 2, _o(0, 0, 0, r))[0] == OK
 
 
 def test_plan_choices_for_the_workloads():
@@ -119,7 +128,7 @@ def test_forward_rejects_before_any_launch():
     assert _fwd(F=32) == ALIGN
     assert _fwd(score=2) == UNSUP
     assert _fwd(E=600, k=2) == UNSUP
-    assert _fwd(opt=ctypes.byref(_lib.MoeOptions(48, 0, None))) == UNSUP
+    assert _fwd(opt=_o(48)) == UNSUP
     rc, need = _ws(4, 64, 64, 4, 2)
     assert _fwd(wsb=need - 1) == WS
     # T = 0 is a no-op that succeeds even with NULL buffers

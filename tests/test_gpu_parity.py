@@ -121,6 +121,21 @@ def test_forward_every_block_size_and_split(bm, split):
     parity.check_out(out, ref, f"bm={bm} split={split}")
 
 
+@pytest.mark.parametrize("bm", ALL_BM)
+@pytest.mark.parametrize("rotate", [1, 2])
+def test_forward_rotation_on_and_off(bm, rotate):
+    cfg, x, lg, wgu, wd, ref = _mid_case()
+    out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm, split_k=2, rotate=rotate)
+    parity.check_out(out, ref, f"bm={bm} rotate={rotate}")
+
+
+@pytest.mark.parametrize("variant", [1, 2])
+def test_forward_tile_variants(variant):
+    cfg, x, lg, wgu, wd, ref = _mid_case()
+    out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=64, tile_variant=variant)
+    parity.check_out(out, ref, f"bm=64 variant={variant}")
+
+
 @pytest.mark.parametrize("score,renorm", [(0, False), (1, True), (1, False)])
 def test_forward_score_functions(score, renorm):
     cfg, x, lg, wgu, wd = parity.make_case(96, 256, 256, 16, 4, score=score, renorm=renorm, seed=9)
