@@ -229,19 +229,25 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes):
         v = [val for name, val in rows if pred(name)]
         return sum(v) / len(v), len(v)
 
-    is_k4 = lambda n: "grouped_gemm_kernel" in n and "Lb1E" in n
-    is_copy = lambda n: ("copy" in n.lower() or "elementwise" in n.lower()) and "grouped_gemm" not in n
+    is_k4 = lambda n: "grouped_gemm_kernel" in n and "true>" in n
+    is_copy = lambda n: "copyBuffer" in n
     f = load(fetch_dir, "FETCH_SIZE")
     w = load(write_dir, "WRITE_SIZE")
     fk4, nf = mean_of(f, is_k4)
     wk4, nw = mean_of(w, is_k4)
-    fcp, _ = mean_of(f, is_copy)
-    wcp, _ = mean_of(w, is_copy)
+    # the calibration copies are the copyBuffer dispatches of copy_bytes: the
+    # largest ones (other copies of a run move a few KiB)
+    def big_copies(rows):
+        vals = sorted((v for n, v in rows if is_copy(n)), reverse=True)
+        top = [v for v in vals if v >= 0.25 * vals[0]]
+        return sum(top) / len(top), len(top)
+    fcp, ncf = big_copies(f)
+    wcp, ncw = big_copies(w)
     f_scale = copy_bytes / (fcp * 1024.0)
     w_scale = copy_bytes / (wcp * 1024.0)
     out = {"kernel": "gate_up_swiglu", "workload": workload, "source_sha256_16": source_sha(),
            "fetch_kib_per_launch": fk4, "write_kib_per_launch": wk4, "launches": [nf, nw],
-           "copy_bytes": copy_bytes, "copy_fetch_kib": fcp, "copy_write_kib": wcp,
+           "copy_bytes": copy_bytes, "copy_fetch_kib": fcp, "copy_write_kib": wcp, "copies": [ncf, ncw],
            "fetch_scale": f_scale, "write_scale": w_scale,
            "bytes_per_launch": fk4 * 1024.0 * f_scale + wk4 * 1024.0 * w_scale}
     path = os.path.join(ROOT, "profiles", f"traffic_gate_up_swiglu_{workload}.json")

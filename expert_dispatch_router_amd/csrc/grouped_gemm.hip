@@ -149,12 +149,14 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < NWT; ++j) acc[g][mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K-step order: with `rotate`, each workgroup starts its reduction at its
-  // own step and wraps around.  When every weight row is a power-of-two
-  // number of bytes long, workgroups walking K in lockstep all address the
-  // same memory channels at once; rotating the start spreads them.  The
-  // order is fixed per workgroup, so results stay deterministic.
-  const int shift = rotate ? (int)(((unsigned)blockIdx.x * 2654435761u) % (unsigned)max(nks, 1)) : 0;
+  // K-step order: with `rotate`, every workgroup of schedule block b starts
+  // its reduction at a step derived from b and wraps around.  Workgroups
+  // walking K in lockstep all address the same memory channels at once;
+  // starting different blocks at different steps spreads them, while the
+  // column tiles of one block still read the same activation K-slice (so it
+  // stays shared in L2).  The order is fixed per block: results stay
+  // deterministic.
+  const int shift = rotate ? (int)(((unsigned)b * 2654435761u) % (unsigned)max(nks, 1)) : 0;
   auto step_of = [&](int ks) {
     const int p = ks + shift;
     return p >= nks ? p - nks : p;

@@ -94,10 +94,10 @@ int auto_gu_variant(int A, int E, int ffn, int bm) {
   return est_workgroups(A, E, bm, ffn, gate_up_tile_cols(64, 0)) <= 384 ? 1 : 0;
 }
 
-// Rotate the K start when weight rows are a power-of-two number of bytes
-// (>= 2 KiB): measured to relieve lockstep channel conflicts there, and to
-// be neutral or slightly slower otherwise.
-bool auto_rotate(int K) { return K >= 1024 && (K & (K - 1)) == 0; }
+// Rotating each block's K start (see the GEMM kernel) was measured faster or
+// equal on every MoE workload shape, so it is on unless the caller turns it
+// off.
+bool auto_rotate(int) { return true; }
 
 void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan* p) {
   memset(p, 0, sizeof(*p));

@@ -85,9 +85,9 @@ typedef struct moe_options {
      * explicitly).  BM = 64 has variants 0 (256 columns per workgroup) and 1
      * (128 columns); every other BM has variant 0 only. */
     int tile_variant;
-    /* K-start rotation of the GEMM workgroups.  0 = automatic (on when the
-     * reduction length is a power of two >= 1024), 1 = off, 2 = on.  Results
-     * are deterministic either way; rounding differs slightly between them. */
+    /* K-start rotation of the GEMMs: each schedule block starts its
+     * reduction at its own step.  0 = automatic (on), 1 = off, 2 = on.
+     * Results are deterministic either way; rounding differs slightly. */
     int rotate;
     /* NULL, or 7 hipEvent_t handles created by the caller (for instance
      * with moe_timer_create).  events[0] is recorded on the stream before
