@@ -1,7 +1,7 @@
 """Helpers of the GPU parity tests: seeded inputs, the oracle on the same
 bytes, and the acceptance checks.
 
-Acceptance (spec tolerance of the MoE output): relative Frobenius error
+Acceptance (the required tolerance of the MoE output): relative Frobenius error
 <= 1e-2 and max-abs error <= 2e-2 * RMS(reference), both against the
 oracle's fp32 result before rounding, computed in float64.  Routing
 artefacts (ids, counts, offsets, perm, inv, blocks, nb) must match bit for
