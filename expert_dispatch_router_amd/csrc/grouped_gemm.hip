@@ -306,13 +306,18 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, const int32_t* block
 
 // Tile shapes: (variant, BM, NWT, waves, PF).  NWT*16 output columns per wave
 // (x2 rows for gate+up in K4), PF K steps of weight prefetch.  Chosen by
-// measurement on the MoE workload shapes; variant 1 of K4 at BM=64 is the
-// narrow tile for launches with few blocks.
+// measurement on the MoE workload shapes.  Variant 1 of K4 at BM=64 is the
+// narrow tile for launches with few blocks; variant 1 of K4 at BM=192 is a
+// 7-wave, 112-column tile (two waves on three SIMDs) whose tile count
+// divides evenly over the CUs where 128-column tiles leave a half-empty last
+// round; variant 1 of K5 at BM=192 runs two waves per SIMD for launches of
+// at most two rounds.
 #define MOE_GU_CFGS(X) \
   X(0, 16, 4, 4, 2) X(0, 32, 4, 4, 2) X(0, 64, 4, 4, 3) X(1, 64, 2, 4, 4) X(0, 128, 2, 4, 3) \
-  X(0, 192, 2, 4, 3)
+  X(0, 192, 2, 4, 3) X(1, 192, 1, 7, 3)
 #define MOE_DN_CFGS(X) \
-  X(0, 16, 8, 4, 2) X(0, 32, 8, 4, 2) X(0, 64, 4, 4, 4) X(0, 128, 4, 4, 3) X(0, 192, 4, 4, 3)
+  X(0, 16, 8, 4, 2) X(0, 32, 8, 4, 2) X(0, 64, 4, 4, 4) X(0, 128, 4, 4, 3) X(0, 192, 4, 4, 3) \
+  X(1, 192, 2, 8, 4)
 
 }  // namespace
 
@@ -324,9 +329,9 @@ int gate_up_tile_cols(int bm, int variant) {
   return 0;
 }
 
-int down_tile_cols(int bm) {
+int down_tile_cols(int bm, int variant) {
 #define X(V, BM, NWT, WV, PF) \
-  if (bm == BM && V == 0) return Gemm<BM, NWT, WV, PF, false>::kTileCols;
+  if (bm == BM && V == variant) return Gemm<BM, NWT, WV, PF, false>::kTileCols;
   MOE_DN_CFGS(X)
 #undef X
   return 0;
@@ -345,11 +350,12 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x_perm, const uin
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_down(int bm, const uint16_t* h, const uint16_t* w_down, const int32_t* blocks,
-                       const int32_t* nb, const int32_t* offsets, float* y, int A, int d, int ffn,
-                       int split, int ksplit, int nb_max, int rotate, hipStream_t s) {
+hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w_down,
+                       const int32_t* blocks, const int32_t* nb, const int32_t* offsets, float* y,
+                       int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
+                       hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                  \
-  if (bm == BM && V == 0)                                                                      \
+  if (bm == BM && V == variant)                                                                      \
     return launch_cfg<BM, NWT, WV, PF, false>(h, w_down, blocks, nb, offsets, y, A, d, ffn,    \
                                               split, ksplit, nb_max, rotate, s);
   MOE_DN_CFGS(X)

@@ -78,7 +78,7 @@ long long est_workgroups(int A, int E, int bm, int n_cols, int tile_cols) {
 // short ones, so split only as far as needed to reach ~256 workgroups, and
 // use two parts when a launch is small (< 640 workgroups).
 int auto_split(int A, int E, int d, int ffn, int bm) {
-  const long long wg = est_workgroups(A, E, bm, d, down_tile_cols(bm));
+  const long long wg = est_workgroups(A, E, bm, d, down_tile_cols(bm, 0));
   int s = (int)((256 + wg - 1) / wg);
   if (wg < 640 && s < 2) s = 2;
   const int max_by_k = ffn / (8 * 64);  // keep at least 8 K steps per part
@@ -87,11 +87,33 @@ int auto_split(int A, int E, int d, int ffn, int bm) {
   return s < 1 ? 1 : s;
 }
 
-// Tile variant of the fused gate/up GEMM: at BM = 64, the narrow variant when
-// the wide one would give at most ~1.5 workgroups per CU.
+// Fraction of a launch's workgroup slots doing work when `wg` workgroups run
+// in rounds of `slots` (one resident workgroup per CU).
+double round_balance(long long wg, long long slots) {
+  const long long rounds = (wg + slots - 1) / slots;
+  return rounds > 0 ? (double)wg / (double)(rounds * slots) : 1.0;
+}
+
+// Tile variant of the fused gate/up GEMM.  BM = 64: the narrow variant when
+// the wide one would give at most ~1.5 workgroups per CU.  BM = 192: the
+// 112-column variant when its tiles fill the rounds better than 128-column
+// tiles do (both hold one workgroup per CU).
 int auto_gu_variant(int A, int E, int ffn, int bm) {
-  if (bm != 64) return 0;
-  return est_workgroups(A, E, bm, ffn, gate_up_tile_cols(64, 0)) <= 384 ? 1 : 0;
+  if (bm == 64) return est_workgroups(A, E, bm, ffn, gate_up_tile_cols(64, 0)) <= 384 ? 1 : 0;
+  if (bm == 192) {
+    const double b0 = round_balance(est_workgroups(A, E, bm, ffn, gate_up_tile_cols(192, 0)), 256);
+    const double b1 = round_balance(est_workgroups(A, E, bm, ffn, gate_up_tile_cols(192, 1)), 256);
+    const bool exact1 = ffn % gate_up_tile_cols(192, 1) == 0;  // no partial last tile
+    return (exact1 && b1 > b0 + 0.05) ? 1 : 0;
+  }
+  return 0;
+}
+
+// Tile variant of the down GEMM: at BM = 192, two waves per SIMD when the
+// launch is at most two rounds of workgroups.
+int auto_dn_variant(int A, int E, int d, int bm, int split) {
+  if (bm != 192) return 0;
+  return est_workgroups(A, E, bm, d, down_tile_cols(192, 1)) * split <= 512 ? 1 : 0;
 }
 
 // Rotating each block's K start (see the GEMM kernel) was measured faster or
@@ -119,6 +141,7 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     p->split = (ksteps + per - 1) / per;  // every part has at least one K step
     p->gu_variant = (opt && opt->tile_variant) ? opt->tile_variant - 1
                                                : auto_gu_variant(A, E, ffn, p->bm);
+    p->dn_variant = auto_dn_variant(A, E, d, p->bm, p->split);
     const int rot = opt ? opt->rotate : 0;
     p->gu_rotate = rot == 0 ? auto_rotate(d) : rot == 2;
     p->dn_rotate = rot == 0 ? auto_rotate(ffn) : rot == 2;
@@ -290,8 +313,8 @@ int moe_forward_ex(const uint16_t* x, const float* router_logits, const uint16_t
   MOE_TRY_HIP(launch_gate_up(p.bm, p.gu_variant, x_perm, W_gate_up, blocks, nb, offsets, h, p.A,
                              d, ffn, p.nb_max, p.gu_rotate, s));
   MOE_TRY(record(opt, 4, s));
-  MOE_TRY_HIP(launch_down(p.bm, h, W_down, blocks, nb, offsets, y, p.A, d, ffn, p.split,
-                          p.ksplit, p.nb_max, p.dn_rotate, s));
+  MOE_TRY_HIP(launch_down(p.bm, p.dn_variant, h, W_down, blocks, nb, offsets, y, p.A, d, ffn,
+                          p.split, p.ksplit, p.nb_max, p.dn_rotate, s));
   MOE_TRY(record(opt, 5, s));
   MOE_TRY_HIP(launch_combine(y, p.split, p.A, d, at<int32_t>(workspace, p.o_inv),
                              at<float>(workspace, p.o_w), top_k, T, out, s));

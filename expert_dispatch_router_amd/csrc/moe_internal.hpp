@@ -30,6 +30,7 @@ struct Plan {
   int split;      // split of the down projection's reduction
   int ksplit;     // reduction length of one split (multiple of 64)
   int gu_variant; // tile variant of the fused gate/up GEMM
+  int dn_variant; // tile variant of the down GEMM
   int gu_rotate;  // rotate the K-step start per workgroup (fused gate/up GEMM)
   int dn_rotate;  // same for the down GEMM
   // byte offsets into the workspace (256-byte aligned)
@@ -62,9 +63,10 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x_perm, const uin
                           hipStream_t s);
 
 // Down grouped GEMM: y[split, A, d] = partial sums of h Wd^T per block.
-hipError_t launch_down(int bm, const uint16_t* h, const uint16_t* w_down, const int32_t* blocks,
-                       const int32_t* nb, const int32_t* offsets, float* y, int A, int d, int ffn,
-                       int split, int ksplit, int nb_max, int rotate, hipStream_t s);
+hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w_down,
+                       const int32_t* blocks, const int32_t* nb, const int32_t* offsets, float* y,
+                       int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
+                       hipStream_t s);
 
 // Weighted combination: out[t] = bf16(sum_j w[t,j] * sum_s y[s, inv[t*k+j]]).
 hipError_t launch_combine(const float* y, int split, int A, int d, const int32_t* inv,
@@ -73,6 +75,6 @@ hipError_t launch_combine(const float* y, int split, int A, int d, const int32_t
 // Column tile widths (output columns per workgroup) of the two GEMMs for a
 // block size; the planner uses them to size the grids.
 int gate_up_tile_cols(int bm, int variant);
-int down_tile_cols(int bm);
+int down_tile_cols(int bm, int variant);
 
 }  // namespace moe

@@ -83,7 +83,8 @@ typedef struct moe_options {
     /* Tile variant of the fused gate/up GEMM.  0 = automatic; k >= 1 selects
      * compiled variant k-1 for the chosen block_rows (which must then be set
      * explicitly).  BM = 64 has variants 0 (256 columns per workgroup) and 1
-     * (128 columns); every other BM has variant 0 only. */
+     * (128 columns); BM = 192 has variants 0 (128 columns) and 1 (112
+     * columns); every other BM has variant 0 only. */
     int tile_variant;
     /* K-start rotation of the GEMMs: each schedule block starts its
      * reduction at its own step.  0 = automatic (on), 1 = off, 2 = on.

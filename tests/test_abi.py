@@ -70,7 +70,7 @@ def _o(bm=0, split=0, variant=0, rotate=0):
 
 
 def test_options_checks():
-    for bad in (_o(8), _o(0, 9), _o(0, -1), _o(0, 0, 1), _o(32, 0, 2), _o(64, 0, 3), _o(0, 0, 0, 3),
+    for bad in (_o(8), _o(0, 9), _o(0, -1), _o(0, 0, 1), _o(32, 0, 2), _o(64, 0, 3), _o(192, 0, 3), _o(0, 0, 0, 3),
                 _o(0, 0, -1), _o(0, 0, 0, -1)):
         assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
     for bm in (16, 32, 64, 128, 192):
@@ -78,6 +78,8 @@ def test_options_checks():
         assert rc == OK and n > 0
         assert _ws(64, 256, 512, 8, 2, _o(bm, 0, 1))[0] == OK
     assert _ws(64, 256, 512, 8, 2, _o(64, 0, 2))[0] == OK
+    assert _ws(64, 256, 512, 8, 2, _o(192, 0, 2))[0] == OK
+    assert _ws(64, 256, 512, 8, 2, _o(128, 0, 2))[0] == UNSUP
     for r in (1, 2):
         assert _ws(64, 256, 512, 8, 2, _o(0, 0, 0, r))[0] == OK
 

@@ -129,11 +129,18 @@ def test_forward_rotation_on_and_off(bm, rotate):
     parity.check_out(out, ref, f"bm={bm} rotate={rotate}")
 
 
-@pytest.mark.parametrize("variant", [1, 2])
-def test_forward_tile_variants(variant):
+@pytest.mark.parametrize("bm,variant", [(64, 1), (64, 2), (192, 1), (192, 2)])
+def test_forward_tile_variants(bm, variant):
     cfg, x, lg, wgu, wd, ref = _mid_case()
-    out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=64, tile_variant=variant)
-    parity.check_out(out, ref, f"bm=64 variant={variant}")
+    out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm, tile_variant=variant)
+    parity.check_out(out, ref, f"bm={bm} variant={variant}")
+
+
+def test_forward_down_variant_two_waves_per_simd():
+    """BM=192 with a small split picks the 8-wave down GEMM (few workgroups)."""
+    cfg, x, lg, wgu, wd, ref = _mid_case()
+    out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=192, split_k=1)
+    parity.check_out(out, ref, "bm=192 down variant 1")
 
 
 @pytest.mark.parametrize("score,renorm", [(0, False), (1, True), (1, False)])
