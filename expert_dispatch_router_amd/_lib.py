@@ -50,6 +50,7 @@ class MoeOptions(ctypes.Structure):
     """struct moe_options of include/moe.h."""
     _fields_ = [("block_rows", ctypes.c_int), ("split_k", ctypes.c_int),
                 ("tile_variant", ctypes.c_int), ("rotate", ctypes.c_int),
+                ("routing_kernels", ctypes.c_int), ("gather_mode", ctypes.c_int),
                 ("stage_events", ctypes.c_void_p)]
 
 
@@ -94,10 +95,13 @@ def moe_abi_version() -> int:
     return int(lib().moe_abi_version())
 
 
-def _opts(block_rows=0, split_k=0, stage_events=None, tile_variant=0, rotate=0):
-    if not block_rows and not split_k and stage_events is None and not tile_variant and not rotate:
+def _opts(block_rows=0, split_k=0, stage_events=None, tile_variant=0, rotate=0,
+          routing_kernels=0, gather_mode=0):
+    if not any((block_rows, split_k, tile_variant, rotate, routing_kernels, gather_mode)) and \
+            stage_events is None:
         return None, None
-    o = MoeOptions(int(block_rows), int(split_k), int(tile_variant), int(rotate), None)
+    o = MoeOptions(int(block_rows), int(split_k), int(tile_variant), int(rotate),
+                   int(routing_kernels), int(gather_mode), None)
     keep = None
     if stage_events is not None:
         keep = (ctypes.c_void_p * len(stage_events))(*stage_events)
@@ -106,8 +110,8 @@ def _opts(block_rows=0, split_k=0, stage_events=None, tile_variant=0, rotate=0):
 
 
 def moe_workspace_size(T, d, ffn, E, top_k, block_rows=0, split_k=0, tile_variant=0,
-                       rotate=0) -> int:
-    o, _ = _opts(block_rows, split_k, None, tile_variant, rotate)
+                       rotate=0, routing_kernels=0, gather_mode=0) -> int:
+    o, _ = _opts(block_rows, split_k, None, tile_variant, rotate, routing_kernels, gather_mode)
     n = _SZ(0)
     _check("moe_workspace_size_ex", lib().moe_workspace_size_ex(
         T, d, ffn, E, top_k, ctypes.byref(o) if o else None, ctypes.byref(n)))
@@ -123,8 +127,8 @@ def moe_plan(T, d, ffn, E, top_k, block_rows=0, split_k=0, tile_variant=0, rotat
     return int(bm.value), int(sk.value)
 
 
-def moe_route_workspace_size(T, E, top_k, block_rows=0) -> int:
-    o, _ = _opts(block_rows)
+def moe_route_workspace_size(T, E, top_k, block_rows=0, routing_kernels=0) -> int:
+    o, _ = _opts(block_rows, routing_kernels=routing_kernels)
     n = _SZ(0)
     _check("moe_route_workspace_size", lib().moe_route_workspace_size(
         T, E, top_k, ctypes.byref(o) if o else None, ctypes.byref(n)))
@@ -156,7 +160,7 @@ def _stream_ptr(stream, device):
 
 def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=None,
                 score="softmax", workspace=None, stream=None, block_rows=0, split_k=0,
-                stage_events=None, tile_variant=0, rotate=0):
+                stage_events=None, tile_variant=0, rotate=0, routing_kernels=0, gather_mode=0):
     """out[T,d] (bf16) = the MoE forward pass, enqueued on ``stream``.
 
     x bf16 [T,d]; router_logits fp32 [T,E]; W_gate_up bf16 [E,2F,d];
@@ -170,10 +174,12 @@ def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=Non
         raise ValueError("inconsistent shapes")
     if out is None:
         out = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
-    ws_need = moe_workspace_size(T, d, F, E, top_k, block_rows, split_k, tile_variant, rotate)
+    ws_need = moe_workspace_size(T, d, F, E, top_k, block_rows, split_k, tile_variant, rotate,
+                                 routing_kernels, gather_mode)
     if workspace is None:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=x.device)
-    o, keep = _opts(block_rows, split_k, stage_events, tile_variant, rotate)
+    o, keep = _opts(block_rows, split_k, stage_events, tile_variant, rotate, routing_kernels,
+                    gather_mode)
     rc = lib().moe_forward_ex(
         _dev_ptr(x, torch.bfloat16, "x"), _dev_ptr(router_logits, torch.float32, "router_logits"),
         _dev_ptr(W_gate_up, torch.bfloat16, "W_gate_up"), _dev_ptr(W_down, torch.bfloat16, "W_down"),
@@ -187,7 +193,7 @@ def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=Non
 
 
 def moe_route(router_logits, top_k, renormalize, score="softmax", x=None, block_rows=0,
-              workspace=None, stream=None):
+              workspace=None, stream=None, routing_kernels=0):
     """Runs the routing kernels and returns a dict of GPU tensors: ids, w,
     counts, offsets, perm, inv, blocks [nb_max,2], nb [1], x_perm (if x is
     given) and the host int bm."""
@@ -199,8 +205,8 @@ def moe_route(router_logits, top_k, renormalize, score="softmax", x=None, block_
                w=torch.empty(T, top_k, dtype=torch.float32, device=dev),
                counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
                perm=torch.empty(A, **i32), inv=torch.empty(A, **i32))
-    o, _ = _opts(block_rows)
-    ws_need = moe_route_workspace_size(T, E, top_k, block_rows)
+    o, _ = _opts(block_rows, routing_kernels=routing_kernels)
+    ws_need = moe_route_workspace_size(T, E, top_k, block_rows, routing_kernels)
     if workspace is None:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
     bm, _ = moe_plan(T, 64, 64, E, top_k, block_rows)

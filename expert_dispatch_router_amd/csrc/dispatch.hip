@@ -15,6 +15,7 @@
 // experts; an expert with no rows gets no block; the token-offset of a block
 // is its first sorted row.
 #include "moe_internal.hpp"
+#include "route_core.hpp"
 #include "../../include/moe.h"
 
 namespace moe {
@@ -128,6 +129,148 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict_
   for (int c = threadIdx.x; c < d / 8; c += 256) o[c] = s[c];
 }
 
+// Small problems (T <= 1024 tokens, E <= 32 experts): the whole routing in
+// one workgroup of 1024 threads, thread t = token t.  Three launches (route,
+// histogram+scan+schedule, reorder) cost more than this work.
+//   1. route: the token's E logits in registers, k rounds of "best live
+//      candidate" in ascending expert order under the same rank rule as the
+//      lane-group route (so the same experts, in the same order);
+//   2. count: per expert, a ballot over each wave of "my token chose e"; the
+//      masks and their popcounts go to LDS;
+//   3. one exclusive scan over the (expert, wave) counts in expert-major
+//      order gives, for every wave, where its rows of expert e start; a
+//      token has at most one row per expert, so ascending token order within
+//      an expert is ascending flat index i = t*k + j, and a row's position is
+//      that start plus the rank of its lane in the wave's ballot;
+//   4. counts, offsets, the block table and the block count.
+// Identical results to the general path.
+constexpr int kSmallWaves = kScanThreads / 64;
+
+template <int EMAX>
+__global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int renorm, int score, int bm,
+    int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    int32_t* __restrict__ blocks, int32_t* __restrict__ nb) {
+  static_assert(EMAX <= 32 && EMAX * kSmallWaves <= kScanThreads, "one thread per (e, wave)");
+  __shared__ unsigned long long wmask[EMAX * kSmallWaves];  // [e][wave] ballot of expert e
+  __shared__ int start[EMAX * kSmallWaves];                 // [e][wave] first sorted position
+  __shared__ int wave_sum[kSmallWaves];
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  const bool ok = t < T;
+
+  // 1. route
+  float v[EMAX];
+#pragma unroll
+  for (int e = 0; e < EMAX; ++e) v[e] = (ok && e < E) ? logits[(size_t)t * E + e] : 0.0f;
+  const unsigned valid = ok ? (E >= 32 ? 0xffffffffu : (1u << E) - 1u) : 0u;
+  unsigned live = valid;
+  float sel_v[MOE_MAX_TOPK];
+  int sel_e[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    float bv = 0.0f;
+    int be = -1;
+    if (j < k) {
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e)
+        if (((live >> e) & 1u) && ranks_before(v[e], e, bv, be)) {
+          bv = v[e];
+          be = e;
+        }
+      if (be >= 0) live &= ~(1u << be);
+    }
+    sel_v[j] = bv;
+    sel_e[j] = be;
+  }
+  float z_all = 0.0f;
+  if (score == MOE_SCORE_SOFTMAX && !renorm) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e)
+      if ((valid >> e) & 1u) z_all += expf(v[e] - sel_v[0]);
+  }
+  float wt[MOE_MAX_TOPK];
+  topk_weights(sel_v, k, renorm, score, z_all, wt);
+  if (ok) {
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j < k) {
+        ids[(size_t)t * k + j] = sel_e[j];
+        w[(size_t)t * k + j] = wt[j];
+      }
+  }
+
+  // 2. count
+  const unsigned chosen = valid & ~live;
+  for (int e = 0; e < E; ++e) {
+    const unsigned long long m = __ballot((chosen >> e) & 1u);
+    if (lane == 0) wmask[e * kSmallWaves + wave] = m;
+  }
+  __syncthreads();
+
+  // 3. exclusive scan over (e, wave), e-major: a wave-level scan, then the
+  // totals of the earlier waves.
+  const int n = E * kSmallWaves;
+  const int c = t < n ? __popcll(wmask[t]) : 0;
+  int incl = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wave_sum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int q = 0; q < wave; ++q) before += wave_sum[q];
+  if (t < n) start[t] = before + incl - c;
+  __syncthreads();
+
+  // positions of this token's rows
+  if (ok) {
+    const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j < k) {
+        const int q = sel_e[j] * kSmallWaves + wave;
+        const int p = start[q] + __popcll(wmask[q] & below);
+        perm[p] = t * k + j;
+        inv[t * k + j] = p;
+      }
+  }
+
+  // 4. expert totals, offsets and the block table (wave 0, lane e)
+  if (wave == 0) {
+    int cnt = 0, first = 0;
+    if (lane < E) {
+      first = start[lane * kSmallWaves];
+      const int last = lane * kSmallWaves + kSmallWaves - 1;
+      cnt = start[last] + __popcll(wmask[last]) - first;
+    }
+    const int nbk = (cnt + bm - 1) / bm;
+    int bincl = nbk;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(bincl, off, 64);
+      if (lane >= off) bincl += o;
+    }
+    if (lane < E) {
+      counts[lane] = cnt;
+      offsets[lane] = first;
+      if (lane == E - 1) {
+        offsets[E] = first + cnt;
+        nb[0] = bincl;
+      }
+      const int b0 = bincl - nbk;
+      for (int r = 0; r < nbk; ++r) {
+        blocks[2 * (b0 + r)] = lane;
+        blocks[2 * (b0 + r) + 1] = first + r * bm;
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_hist_scan(const int32_t* ids, int A, int E, int bm, int nchunks, int32_t* counts,
@@ -150,6 +293,34 @@ hipError_t launch_permute(const int32_t* ids, int A, int E, int nchunks, const i
 hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int A, int d, int k,
                          uint16_t* x_perm, hipStream_t s) {
   gather_kernel<<<A, 256, 0, s>>>(x, perm, d, k, x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+bool small_routing_fits(int T, int E, int k) {
+  (void)k;
+  return T <= kSmallRoutingMaxTokens && E <= kSmallRoutingMaxExperts;
+}
+
+hipError_t launch_route_dispatch_small(const float* logits, int T, int E, int k, int renorm,
+                                       int score, int bm, int32_t* ids, float* w,
+                                       int32_t* counts, int32_t* offsets, int32_t* perm,
+                                       int32_t* inv, int32_t* blocks, int32_t* nb,
+                                       hipStream_t s) {
+  if (!small_routing_fits(T, E, k)) return hipErrorInvalidValue;
+#define MOE_LAUNCH_SMALL(EMAX)                                                               \
+  route_dispatch_small_kernel<EMAX><<<1, kScanThreads, 0, s>>>(                              \
+      logits, T, E, k, renorm, score, bm, ids, w, counts, offsets, perm, inv, blocks, nb)
+  if (E <= 8)
+    MOE_LAUNCH_SMALL(8);
+  else if (E <= 16)
+    MOE_LAUNCH_SMALL(16);
+  else
+    MOE_LAUNCH_SMALL(32);
+#undef MOE_LAUNCH_SMALL
   return hipGetLastError();
 }
 

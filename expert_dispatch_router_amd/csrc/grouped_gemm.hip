@@ -79,7 +79,8 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
     const int32_t* __restrict__ offsets, void* __restrict__ out, int A, int N, int K, int ksplit,
-    int tiles_per_block, int rotate) {
+    int tiles_per_block, int rotate, const int32_t* __restrict__ gather_perm, int gather_k,
+    int x_rows) {
   using G = Gemm<BM, NWT, WAVES, PF, SWIGLU>;
   constexpr int MT = G::kMT, NG = G::kNG, XPT = G::kXPerThread;
   static_assert(PF >= 2, "the activation stage is issued PF-1 steps ahead");
@@ -114,8 +115,14 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
   // oldest ring stage.
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(W + (size_t)e * NG * N * K), (short)0, NG * N * K * 2, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(X + (size_t)r0 * K), (short)0, rows * K * 2, kRsrcWord3);
+  // X rows: sorted rows r0 .. r0+rows-1 of X, or -- with gather_perm -- the
+  // token rows x[perm[r0 + row] / gather_k] of the unsorted activations (the
+  // reorder's row gather folded into this load).  Rows past the block's end
+  // get an offset outside the descriptor's range and load as zeros.
+  const __amdgpu_buffer_rsrc_t xres =
+      gather_perm ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, x_rows * K * 2, kRsrcWord3)
+                  : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (size_t)r0 * K), (short)0,
+                                                      rows * K * 2, kRsrcWord3);
   int woff[NG][NWT];
   bool jok[NWT];
 #pragma unroll
@@ -132,8 +139,11 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
 #pragma unroll
   for (int q = 0; q < XPT; ++q) {
     const int c = (tid + q * G::kThreads) % G::kXChunks;
-    xoff[q] = ((c >> 3) * K + kb + (c & 7) * 8) * 2;
-    xdst[q] = (c >> 3) * kLdsStride + (c & 7) * 8;
+    const int row = c >> 3;
+    int src_row = row;
+    if (gather_perm) src_row = row < rows ? gather_perm[r0 + row] / gather_k : x_rows;
+    xoff[q] = (src_row * K + kb + (c & 7) * 8) * 2;
+    xdst[q] = row * kLdsStride + (c & 7) * 8;
   }
 
   // Ring of PF slots.  Slot s = ks % PF carries the weights of step ks and
@@ -293,14 +303,16 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
 template <int BM, int NWT, int WAVES, int PF, bool SWIGLU>
 hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, const int32_t* blocks,
                       const int32_t* nb, const int32_t* offsets, void* out, int A, int N, int K,
-                      int split, int ksplit, int nb_max, int rotate, hipStream_t s) {
+                      int split, int ksplit, int nb_max, int rotate, const int32_t* gather_perm,
+                      int gather_k, int x_rows, hipStream_t s) {
   using G = Gemm<BM, NWT, WAVES, PF, SWIGLU>;
   const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
   const int tiles_per_block = n_tiles * split;
   const long long grid = (long long)tiles_per_block * nb_max;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   grouped_gemm_kernel<BM, NWT, WAVES, PF, SWIGLU><<<(unsigned)grid, G::kThreads, 0, s>>>(
-      X, W, blocks, nb, offsets, out, A, N, K, ksplit, tiles_per_block, rotate);
+      X, W, blocks, nb, offsets, out, A, N, K, ksplit, tiles_per_block, rotate, gather_perm,
+      gather_k, x_rows);
   return hipGetLastError();
 }
 
@@ -337,14 +349,14 @@ int down_tile_cols(int bm, int variant) {
   return 0;
 }
 
-hipError_t launch_gate_up(int bm, int variant, const uint16_t* x_perm, const uint16_t* w_gate_up,
-                          const int32_t* blocks, const int32_t* nb, const int32_t* offsets,
-                          uint16_t* h, int A, int d, int ffn, int nb_max, int rotate,
-                          hipStream_t s) {
+hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t* gather_perm,
+                          int k, int T, const uint16_t* w_gate_up, const int32_t* blocks,
+                          const int32_t* nb, const int32_t* offsets, uint16_t* h, int A, int d,
+                          int ffn, int nb_max, int rotate, hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && variant == V)                                                                \
-    return launch_cfg<BM, NWT, WV, PF, true>(x_perm, w_gate_up, blocks, nb, offsets, h, A, ffn, \
-                                             d, 1, d, nb_max, rotate, s);
+    return launch_cfg<BM, NWT, WV, PF, true>(x, w_gate_up, blocks, nb, offsets, h, A, ffn, d, 1, \
+                                             d, nb_max, rotate, gather_perm, k, T, s);
   MOE_GU_CFGS(X)
 #undef X
   return hipErrorInvalidValue;
@@ -357,7 +369,7 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && V == variant)                                                                      \
     return launch_cfg<BM, NWT, WV, PF, false>(h, w_down, blocks, nb, offsets, y, A, d, ffn,    \
-                                              split, ksplit, nb_max, rotate, s);
+                                              split, ksplit, nb_max, rotate, nullptr, 1, A, s);
   MOE_DN_CFGS(X)
 #undef X
   return hipErrorInvalidValue;

@@ -43,11 +43,22 @@ int check_sizes(int T, int d, int ffn, int E, int k, bool dims) {
   return MOE_OK;
 }
 
+// Forced paths must fit their limits.
+int check_paths(int T, int d, int E, int k, const moe_options* opt) {
+  if (!opt) return MOE_OK;
+  if (opt->routing_kernels == 1 && !small_routing_fits(T, E, k)) return MOE_ERR_UNSUPPORTED;
+  if (opt->gather_mode == 1 && (long long)T * d * 2 + 2LL * d >= (1LL << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 int check_options(const moe_options* opt) {
   if (!opt) return MOE_OK;
   if (opt->block_rows != 0 && !is_block_rows(opt->block_rows)) return MOE_ERR_UNSUPPORTED;
   if (opt->split_k < 0 || opt->split_k > kMaxSplit) return MOE_ERR_UNSUPPORTED;
   if (opt->tile_variant < 0 || opt->rotate < 0 || opt->rotate > 2) return MOE_ERR_UNSUPPORTED;
+  if (opt->routing_kernels < 0 || opt->routing_kernels > 2) return MOE_ERR_UNSUPPORTED;
+  if (opt->gather_mode < 0 || opt->gather_mode > 2) return MOE_ERR_UNSUPPORTED;
   if (opt->tile_variant > 0) {
     const int bm = opt->block_rows;
     if (bm == 0 || gate_up_tile_cols(bm, opt->tile_variant - 1) == 0) return MOE_ERR_UNSUPPORTED;
@@ -133,6 +144,12 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->bm = (opt && opt->block_rows) ? opt->block_rows : auto_block_rows(A > 0 ? A : 1, E);
   p->nb_max = (A + p->bm - 1) / p->bm + (E < A ? E : A);
   p->nchunks = (A + kChunk - 1) / kChunk;
+  const int rk = opt ? opt->routing_kernels : 0;
+  p->small_routing = rk == 1 || (rk == 0 && small_routing_fits(T, E, k));
+  // The fused gate/up GEMM addresses x [T, d] with 32-bit buffer offsets.
+  const int gm = opt ? opt->gather_mode : 0;
+  const bool x_fits = (long long)T * d * 2 + 2LL * d < (1LL << 31);
+  p->gather_in_gemm = gm == 1 || (gm == 0 && x_fits);
   if (ffn > 0) {
     int s = (opt && opt->split_k) ? opt->split_k : auto_split(A, E, d, ffn, p->bm);
     const int ksteps = ffn / 64;
@@ -164,7 +181,7 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->o_blocks = seg((size_t)p->nb_max * 2 * 4);
   p->o_nb = seg(4);
   p->route_bytes = o;
-  p->o_xperm = seg((size_t)A * d * 2);
+  p->o_xperm = seg(p->gather_in_gemm ? 0 : (size_t)A * d * 2);
   p->o_h = seg((size_t)A * ffn * 2);
   p->o_y = seg((size_t)p->split * A * d * 4);
   p->total_bytes = o;
@@ -194,13 +211,24 @@ int record(const moe_options* opt, int i, hipStream_t s) {
     if (rc_ != MOE_OK) return rc_; \
   } while (0)
 
-// K1..K3 into the workspace's routing section.
+// K1..K3 into the workspace's routing section: one workgroup for small
+// problems, else three launches.
 int run_routing(const float* logits, const Plan& p, int renorm, int score, void* ws,
                 const moe_options* opt, hipStream_t s) {
   int32_t* ids = at<int32_t>(ws, p.o_ids);
   float* w = at<float>(ws, p.o_w);
   int32_t* offsets = at<int32_t>(ws, p.o_offsets);
   MOE_TRY(record(opt, 0, s));
+  if (p.small_routing) {
+    MOE_TRY_HIP(launch_route_dispatch_small(logits, p.T, p.E, p.k, renorm, score, p.bm, ids, w,
+                                            at<int32_t>(ws, p.o_counts), offsets,
+                                            at<int32_t>(ws, p.o_perm), at<int32_t>(ws, p.o_inv),
+                                            at<int32_t>(ws, p.o_blocks), at<int32_t>(ws, p.o_nb),
+                                            s));
+    MOE_TRY(record(opt, 1, s));
+    MOE_TRY(record(opt, 2, s));
+    return MOE_OK;
+  }
   MOE_TRY_HIP(launch_route(logits, p.T, p.E, p.k, renorm, score, ids, w, s));
   MOE_TRY(record(opt, 1, s));
   MOE_TRY_HIP(launch_hist_scan(ids, p.A, p.E, p.bm, p.nchunks, at<int32_t>(ws, p.o_counts),
@@ -240,6 +268,7 @@ int moe_workspace_size_ex(int T, int d, int ffn, int E, int top_k, const moe_opt
                           size_t* bytes) {
   MOE_TRY(check_sizes(T, d, ffn, E, top_k, true));
   MOE_TRY(check_options(opt));
+  MOE_TRY(check_paths(T, d, E, top_k, opt));
   if (!bytes) return MOE_ERR_NULL;
   if (T == 0) {
     *bytes = 0;
@@ -259,6 +288,7 @@ int moe_plan(int T, int d, int ffn, int E, int top_k, const moe_options* opt, in
              int* split_k) {
   MOE_TRY(check_sizes(T, d, ffn, E, top_k, true));
   MOE_TRY(check_options(opt));
+  MOE_TRY(check_paths(T, d, E, top_k, opt));
   Plan p;
   make_plan(T, d, ffn, E, top_k, opt, &p);
   if (block_rows) *block_rows = p.bm;
@@ -269,6 +299,7 @@ int moe_plan(int T, int d, int ffn, int E, int top_k, const moe_options* opt, in
 int moe_route_workspace_size(int T, int E, int top_k, const moe_options* opt, size_t* bytes) {
   MOE_TRY(check_sizes(T, 0, 0, E, top_k, false));
   MOE_TRY(check_options(opt));
+  MOE_TRY(check_paths(T, 0, E, top_k, opt));
   if (!bytes) return MOE_ERR_NULL;
   if (T == 0) {
     *bytes = 0;
@@ -286,6 +317,7 @@ int moe_forward_ex(const uint16_t* x, const float* router_logits, const uint16_t
                    size_t workspace_bytes, void* hip_stream) {
   MOE_TRY(check_sizes(T, d, ffn, E, top_k, true));
   MOE_TRY(check_options(opt));
+  MOE_TRY(check_paths(T, d, E, top_k, opt));
   if (score_func != MOE_SCORE_SOFTMAX && score_func != MOE_SCORE_SIGMOID)
     return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
@@ -308,10 +340,11 @@ int moe_forward_ex(const uint16_t* x, const float* router_logits, const uint16_t
   uint16_t* x_perm = at<uint16_t>(workspace, p.o_xperm);
   uint16_t* h = at<uint16_t>(workspace, p.o_h);
   float* y = at<float>(workspace, p.o_y);
-  MOE_TRY_HIP(launch_gather(x, perm, p.A, d, top_k, x_perm, s));
+  if (!p.gather_in_gemm) MOE_TRY_HIP(launch_gather(x, perm, p.A, d, top_k, x_perm, s));
   MOE_TRY(record(opt, 3, s));
-  MOE_TRY_HIP(launch_gate_up(p.bm, p.gu_variant, x_perm, W_gate_up, blocks, nb, offsets, h, p.A,
-                             d, ffn, p.nb_max, p.gu_rotate, s));
+  MOE_TRY_HIP(launch_gate_up(p.bm, p.gu_variant, p.gather_in_gemm ? x : x_perm,
+                             p.gather_in_gemm ? perm : nullptr, top_k, T, W_gate_up, blocks, nb,
+                             offsets, h, p.A, d, ffn, p.nb_max, p.gu_rotate, s));
   MOE_TRY(record(opt, 4, s));
   MOE_TRY_HIP(launch_down(p.bm, p.dn_variant, h, W_down, blocks, nb, offsets, y, p.A, d, ffn,
                           p.split, p.ksplit, p.nb_max, p.dn_rotate, s));
@@ -337,6 +370,7 @@ int moe_route(const float* router_logits, int T, int E, int top_k, int renormali
               void* workspace, size_t workspace_bytes, void* hip_stream) {
   MOE_TRY(check_sizes(T, 0, 0, E, top_k, false));
   MOE_TRY(check_options(opt));
+  MOE_TRY(check_paths(T, 0, E, top_k, opt));
   if (score_func != MOE_SCORE_SOFTMAX && score_func != MOE_SCORE_SIGMOID)
     return MOE_ERR_UNSUPPORTED;
   const bool gather = x && x_perm;
@@ -375,7 +409,8 @@ int moe_route(const float* router_logits, int T, int E, int top_k, int renormali
 int moe_timer_create(void** event) {
   if (!event) return MOE_ERR_NULL;
   hipEvent_t ev = nullptr;
-  if (hipEventCreate(&ev) != hipSuccess) return MOE_ERR_HIP;
+  // Timing only: no system-scope fence (no L2 write-back) when recorded.
+  if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) return MOE_ERR_HIP;
   *event = ev;
   return MOE_OK;
 }

@@ -33,6 +33,8 @@ struct Plan {
   int dn_variant; // tile variant of the down GEMM
   int gu_rotate;  // rotate the K-step start per workgroup (fused gate/up GEMM)
   int dn_rotate;  // same for the down GEMM
+  int small_routing;  // one-workgroup routing kernel instead of three launches
+  int gather_in_gemm; // the fused gate/up GEMM reads token rows through perm
   // byte offsets into the workspace (256-byte aligned)
   size_t o_ids, o_w, o_counts, o_offsets, o_ccnt, o_cbase, o_perm, o_inv, o_blocks, o_nb;
   size_t route_bytes;  // end of the routing section
@@ -53,14 +55,26 @@ hipError_t launch_permute(const int32_t* ids, int A, int E, int nchunks, const i
                           const int32_t* chunk_cnt, const int32_t* chunk_base, int32_t* perm,
                           int32_t* inv, hipStream_t s);
 
+// Whole routing (route + histogram/scan/schedule + reorder) in one
+// workgroup of 1024 threads, one token per thread.
+constexpr int kSmallRoutingMaxTokens = 1024;
+constexpr int kSmallRoutingMaxExperts = 32;
+bool small_routing_fits(int T, int E, int k);
+hipError_t launch_route_dispatch_small(const float* logits, int T, int E, int k, int renorm,
+                                       int score, int bm, int32_t* ids, float* w,
+                                       int32_t* counts, int32_t* offsets, int32_t* perm,
+                                       int32_t* inv, int32_t* blocks, int32_t* nb, hipStream_t s);
+
 hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int A, int d, int k,
                          uint16_t* x_perm, hipStream_t s);
 
-// Fused gate/up SwiGLU grouped GEMM: h[A, F] = silu(X Wg^T) * (X Wu^T) per block.
-hipError_t launch_gate_up(int bm, int variant, const uint16_t* x_perm, const uint16_t* w_gate_up,
-                          const int32_t* blocks, const int32_t* nb, const int32_t* offsets,
-                          uint16_t* h, int A, int d, int ffn, int nb_max, int rotate,
-                          hipStream_t s);
+// Fused gate/up SwiGLU grouped GEMM: h[A, F] = silu(X Wg^T) * (X Wu^T) per
+// block.  X is x_perm [A, d] when gather_perm is null, else the token rows
+// x [T, d] read through gather_perm (row p is x[gather_perm[p] / k]).
+hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t* gather_perm,
+                          int k, int T, const uint16_t* w_gate_up, const int32_t* blocks,
+                          const int32_t* nb, const int32_t* offsets, uint16_t* h, int A, int d,
+                          int ffn, int nb_max, int rotate, hipStream_t s);
 
 // Down grouped GEMM: y[split, A, d] = partial sums of h Wd^T per block.
 hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w_down,

@@ -1,0 +1,164 @@
+// route_core.hpp -- the per-token router top-k and weights, shared by the
+// routing kernels: the rank order of candidates, the weights of a selection,
+// and one token routed by a group of LPT lanes.
+//
+// [R] = the Pith review of "Cross-Platform Fused MoE Dispatch in Triton".
+// Tokens are scored and their top-k experts chosen ("The reading"); the
+// score is a softmax or a sigmoid of the router logits ("Assumptions & free
+// parameters", paper Eq. (1)-(4)).
+//
+// Selection key: the raw fp32 logit (softmax and sigmoid are increasing, so
+// the chosen set is the same; comparing logits keeps equal-score cases that
+// rounding would create, e.g. saturated sigmoids, ordered).  Equal logits --
+// IEEE equality, so -0 == +0 -- rank the lower expert first.  The order of
+// the k results is descending key.
+//
+// Mapping: a group of LPT lanes (a power of two, LPT = min(64, E rounded up))
+// owns one token; lane `sub` of the group holds experts sub, sub+LPT, ...
+// (EPL of them).  Each of the k rounds takes each lane's best unselected
+// candidate and reduces it over the group with xor-butterfly shuffles; the
+// group agrees on the winner because the rank order is total.
+#pragma once
+
+#include "moe_internal.hpp"
+#include "../../include/moe.h"
+
+namespace moe {
+
+// a ranks before b; an index < 0 means "no candidate" and ranks last.
+__device__ __forceinline__ bool ranks_before(float va, int ea, float vb, int eb) {
+  if (ea < 0) return false;
+  if (eb < 0) return true;
+  return va > vb || (va == vb && ea < eb);
+}
+
+// Weights of the k selected logits sel_v (descending): softmax over the
+// selection (renorm), softmax over all experts with denominator z_all
+// (computed by the caller as the sum of exp(logit - sel_v[0])), or sigmoid,
+// optionally divided by the sum of the k sigmoids.
+__device__ __forceinline__ void topk_weights(const float* sel_v, int k, int renorm, int score,
+                                             float z_all, float* wt) {
+  if (score == MOE_SCORE_SOFTMAX) {
+    const float m = sel_v[0];  // the largest logit of the token
+    float z = z_all;
+    if (renorm) {
+      z = 0.0f;
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_TOPK; ++j)
+        if (j < k) z += expf(sel_v[j] - m);
+    }
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) wt[j] = (j < k) ? expf(sel_v[j] - m) / z : 0.0f;
+  } else {
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      wt[j] = (j < k) ? 1.0f / (1.0f + expf(-sel_v[j])) : 0.0f;
+      s += wt[j];
+    }
+    if (renorm) {
+#pragma unroll
+      for (int j = 0; j < MOE_MAX_TOPK; ++j) wt[j] = wt[j] / s;
+    }
+  }
+}
+
+// Routes token t (all LPT lanes of its group call this; tok_ok is false for
+// padding groups past the last token).  Lane j of the group writes entry j:
+// ids[t*k + j] and w[t*k + j].
+template <int LPT, int EPL>
+__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, bool tok_ok,
+                                            int sub, int E, int k, int renorm, int score,
+                                            int32_t* __restrict__ ids, float* __restrict__ w) {
+  float v[EPL];
+  unsigned live = 0;  // bit i set: expert sub + i*LPT exists and is not yet chosen
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = sub + i * LPT;
+    const bool ok = tok_ok && e < E;
+    v[i] = ok ? logits[(size_t)t * E + e] : 0.0f;
+    live |= ok ? (1u << i) : 0u;
+  }
+
+  float sel_v[MOE_MAX_TOPK];
+  int sel_e[MOE_MAX_TOPK];
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+    sel_v[j] = 0.0f;
+    sel_e[j] = -1;
+    if (j < k) {
+      float bv = 0.0f;
+      int be = -1;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = sub + i * LPT;
+        if (((live >> i) & 1u) && ranks_before(v[i], e, bv, be)) {
+          bv = v[i];
+          be = e;
+        }
+      }
+#pragma unroll
+      for (int off = LPT / 2; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, 64);
+        const int oe = __shfl_xor(be, off, 64);
+        if (ranks_before(ov, oe, bv, be)) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      sel_v[j] = bv;
+      sel_e[j] = be;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (sub + i * LPT == be) live &= ~(1u << i);
+    }
+  }
+
+  // Routing weights of the selected experts (fp32).
+  float z_all = 0.0f;  // full softmax denominator, only without renormalisation
+  if (score == MOE_SCORE_SOFTMAX && !renorm) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = sub + i * LPT;
+      if (tok_ok && e < E) z_all += expf(v[i] - sel_v[0]);
+    }
+#pragma unroll
+    for (int off = LPT / 2; off >= 1; off >>= 1) z_all += __shfl_xor(z_all, off, 64);
+  }
+  float wt[MOE_MAX_TOPK];
+  topk_weights(sel_v, k, renorm, score, z_all, wt);
+
+  if (tok_ok) {
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      if (j < k && sub == j) {
+        ids[(size_t)t * k + j] = sel_e[j];
+        w[(size_t)t * k + j] = wt[j];
+      }
+    }
+  }
+}
+
+// Expands CALL(LPT, EPL) for the lane-group shape of E experts: every lane of
+// a group must hold at least one candidate whenever k <= E (k <= 16 <= LPT
+// for E > 16, and k <= E <= LPT otherwise).
+#define MOE_ROUTE_SHAPES(E, CALL) \
+  do {                            \
+    if ((E) <= 8) {               \
+      CALL(8, 1);                 \
+    } else if ((E) <= 16) {       \
+      CALL(16, 1);                \
+    } else if ((E) <= 32) {       \
+      CALL(32, 1);                \
+    } else if ((E) <= 64) {       \
+      CALL(64, 1);                \
+    } else if ((E) <= 128) {      \
+      CALL(64, 2);                \
+    } else if ((E) <= 256) {      \
+      CALL(64, 4);                \
+    } else {                      \
+      CALL(64, 8);                \
+    }                             \
+  } while (0)
+
+}  // namespace moe

@@ -90,12 +90,25 @@ typedef struct moe_options {
      * reduction at its own step.  0 = automatic (on), 1 = off, 2 = on.
      * Results are deterministic either way; rounding differs slightly. */
     int rotate;
+    /* Routing kernels.  0 = automatic: one workgroup does the route,
+     * histogram, scan, schedule and reorder when T <= 1024 and E <= 32,
+     * else three launches; 1 = the one-workgroup kernel
+     * (MOE_ERR_UNSUPPORTED beyond those limits); 2 = three launches.  Same
+     * results either way. */
+    int routing_kernels;
+    /* Row gather of moe_forward.  0 = automatic (1 when 2*T*d < 2^31);
+     * 1 = the fused gate/up GEMM reads each sorted row straight from x
+     * through perm (no x_perm buffer); 2 = a gather kernel writes x_perm to
+     * the workspace first.  Same results either way. */
+    int gather_mode;
     /* NULL, or 7 hipEvent_t handles created by the caller (for instance
      * with moe_timer_create).  events[0] is recorded on the stream before
      * the first kernel and events[i] right after kernel i (1 route, 2
      * histogram+scan+schedule, 3 reorder+gather, 4 fused gate/up SwiGLU
-     * GEMM, 5 down GEMM, 6 weighted combination).  moe_route records
-     * 0..3 only. */
+     * GEMM, 5 down GEMM, 6 weighted combination).  With the one-workgroup
+     * routing kernel, events 1 and 2 are both recorded after it; with the
+     * gather inside the GEMM, event 3 follows the routing directly.
+     * NULL entries are skipped.  moe_route records 0..3 only. */
     void *const *stage_events;
 } moe_options;
 
@@ -191,7 +204,9 @@ int moe_route(const float *router_logits, int T, int E, int top_k, int renormali
               void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /* Thin wrappers over HIP events for timing the stages of moe_forward_ex
- * (moe_options.stage_events).  Each returns a moe_status. */
+ * (moe_options.stage_events).  The events are created without a
+ * system-scope fence on record: they time work, they do not make its results
+ * visible to the host.  Each returns a moe_status. */
 int moe_timer_create(void **event);
 int moe_timer_destroy(void *event);
 /* Milliseconds between two recorded events; waits for `stop` to complete. */

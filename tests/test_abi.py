@@ -65,8 +65,8 @@ def test_workspace_size_checks():
     assert moe.lib().moe_workspace_size(4, 64, 64, 4, 2, None) == NULL
 
 
-def _o(bm=0, split=0, variant=0, rotate=0):
-    return ctypes.byref(_lib.MoeOptions(bm, split, variant, rotate, None))
+def _o(bm=0, split=0, variant=0, rotate=0, routing=0, gather=0):
+    return ctypes.byref(_lib.MoeOptions(bm, split, variant, rotate, routing, gather, None))
 
 
 def test_options_checks():
@@ -82,6 +82,29 @@ def test_options_checks():
     assert _ws(64, 256, 512, 8, 2, _o(128, 0, 2))[0] == UNSUP
     for r in (1, 2):
         assert _ws(64, 256, 512, 8, 2, _o(0, 0, 0, r))[0] == OK
+
+
+def test_routing_and_gather_options():
+    for bad in (_o(routing=3), _o(routing=-1), _o(gather=3), _o(gather=-1)):
+        assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
+    for r in (0, 1, 2):
+        for g in (0, 1, 2):
+            assert _ws(64, 256, 512, 8, 2, _o(routing=r, gather=g))[0] == OK
+    # the one-workgroup routing kernel: one token per thread, at most 32 experts
+    assert _ws(1024, 256, 512, 32, 16, _o(routing=1))[0] == OK
+    assert _ws(1025, 256, 512, 8, 2, _o(routing=1))[0] == UNSUP
+    assert _ws(512, 256, 512, 33, 2, _o(routing=1))[0] == UNSUP
+    assert _ws(1025, 256, 512, 8, 2, _o(routing=2))[0] == OK
+    r = ctypes.c_size_t(0)
+    assert moe.lib().moe_route_workspace_size(1025, 8, 2, _o(routing=1), ctypes.byref(r)) == UNSUP
+    # gather inside the GEMM addresses x with 32-bit byte offsets
+    assert _ws(65536, 16384, 512, 8, 1, _o(gather=1))[0] == UNSUP
+    assert _ws(65536, 16384, 512, 8, 1, _o(gather=2))[0] == OK
+    # no x_perm buffer when the GEMM gathers: the workspace shrinks by A*d*2 (256-aligned)
+    g1 = moe.moe_workspace_size(512, 4096, 14336, 8, 2, gather_mode=1)
+    g2 = moe.moe_workspace_size(512, 4096, 14336, 8, 2, gather_mode=2)
+    assert g2 - g1 == 1024 * 4096 * 2
+    assert moe.moe_workspace_size(512, 4096, 14336, 8, 2) == g1
 
 
 def test_plan_choices_for_the_workloads():

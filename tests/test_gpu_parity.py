@@ -36,12 +36,18 @@ def _gpu():
 
 # ---------------------------------------------------------------- routing
 
+def _small_routing_fits(T, E, k):
+    # limits of the one-workgroup routing kernel (include/moe.h, routing_kernels)
+    return T <= 1024 and E <= 32
+
+
+@pytest.mark.parametrize("routing", [0, 2])
 @pytest.mark.parametrize("name", sorted(synth.CONFIGS))
-def test_route_workloads_bit_exact(name):
+def test_route_workloads_bit_exact(name, routing):
     cfg = synth.CONFIGS[name]
     lg = synth.make_logits(cfg, 0, DEV)
     x = synth.make_x(cfg, 0, DEV)
-    g = moe.moe_route(lg, cfg.top_k, cfg.renormalize, cfg.score, x=x)
+    g = moe.moe_route(lg, cfg.top_k, cfg.renormalize, cfg.score, x=x, routing_kernels=routing)
     ref = parity.oracle_routing(lg, cfg.top_k, cfg.score, cfg.renormalize, g["bm"])
     parity.check_routing(g, ref)
     # the gather: x_perm[p] = x[perm[p] / k], byte for byte
@@ -71,23 +77,42 @@ def _edge_logits():
     return cases
 
 
+@pytest.mark.parametrize("routing", [1, 2])
 @pytest.mark.parametrize("case", _edge_logits(), ids=lambda c: c[0])
-def test_route_edge_cases_bit_exact(case):
+def test_route_edge_cases_bit_exact(case, routing):
     _, lg, k, score, renorm = case
+    if routing == 1 and not _small_routing_fits(lg.shape[0], lg.shape[1], k):
+        pytest.skip("beyond the one-workgroup routing kernel's limits")
     lg = lg.to(DEV)
-    g = moe.moe_route(lg, k, renorm, score)
+    g = moe.moe_route(lg, k, renorm, score, routing_kernels=routing)
     parity.check_routing(g, parity.oracle_routing(lg, k, score, renorm, g["bm"]))
 
 
+@pytest.mark.parametrize("routing", [1, 2])
 @pytest.mark.parametrize("bm", ALL_BM)
-def test_route_every_block_size(bm):
+def test_route_every_block_size(bm, routing):
     gen = torch.Generator().manual_seed(bm)
     lg = torch.randn(600, 20, generator=gen)
     lg[:, 2] += 2.5  # one busy expert so it spans several blocks
     lg = lg.to(DEV)
-    g = moe.moe_route(lg, 3, True, 0, block_rows=bm)
+    g = moe.moe_route(lg, 3, True, 0, block_rows=bm, routing_kernels=routing)
     assert g["bm"] == bm
     parity.check_routing(g, parity.oracle_routing(lg, 3, 0, True, bm))
+
+
+def test_route_small_kernel_at_its_limits():
+    """The one-workgroup kernel at its limits (1024 tokens, 32 experts, top-16)
+    and at E=k: both routing paths give the oracle's artefacts."""
+    gen = torch.Generator().manual_seed(21)
+    for T, E, k in ((1024, 32, 16), (1024, 8, 2), (1000, 17, 5), (3, 4, 4), (1024, 1, 1)):
+        assert _small_routing_fits(T, E, k)
+        lg = torch.randn(T, E, generator=gen).to(DEV)
+        ref = None
+        for routing in (1, 2):
+            g = moe.moe_route(lg, k, True, 0, routing_kernels=routing)
+            if ref is None:
+                ref = parity.oracle_routing(lg, k, 0, True, g["bm"])
+            parity.check_routing(g, ref)
 
 
 # ---------------------------------------------------------------- forward
@@ -156,6 +181,22 @@ def test_forward_partial_column_tiles(bm):
     cfg, x, lg, wgu, wd = parity.make_case(70, 320, 192, 6, 2, seed=13)
     out = moe.moe_forward(x, lg, wgu, wd, 2, True, block_rows=bm, split_k=2)
     parity.check_out(out, parity.oracle_out(x, lg, wgu, wd, 2, 0, True), f"partial bm={bm}")
+
+
+@pytest.mark.parametrize("gather", [1, 2])
+@pytest.mark.parametrize("routing", [1, 2])
+@pytest.mark.parametrize("bm", [16, 64, 192])
+def test_forward_routing_and_gather_paths(bm, routing, gather):
+    """Every combination of routing kernels (one workgroup / three launches)
+    and row gather (inside the gate/up GEMM / separate kernel) meets the
+    tolerance, and all four give the same bytes."""
+    cfg, x, lg, wgu, wd, ref = _mid_case()
+    out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm,
+                          routing_kernels=routing, gather_mode=gather)
+    parity.check_out(out, ref, f"bm={bm} routing={routing} gather={gather}")
+    base = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm,
+                           routing_kernels=2, gather_mode=2)
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
 
 
 def test_forward_hot_expert_many_blocks():
