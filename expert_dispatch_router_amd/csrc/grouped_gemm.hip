@@ -325,8 +325,8 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, const int32_t* block
 // round; variant 1 of K5 at BM=192 runs two waves per SIMD for launches of
 // at most two rounds.
 #define MOE_GU_CFGS(X) \
-  X(0, 16, 4, 4, 2) X(0, 32, 4, 4, 2) X(0, 64, 4, 4, 3) X(1, 64, 2, 4, 4) X(0, 128, 2, 4, 3) \
-  X(0, 192, 2, 4, 3) X(1, 192, 1, 7, 3)
+  X(0, 16, 4, 4, 2) X(0, 32, 4, 4, 2) X(0, 64, 4, 4, 3) X(1, 64, 2, 4, 4) X(0, 128, 1, 8, 3) \
+  X(1, 128, 1, 4, 4) X(0, 192, 2, 4, 3) X(1, 192, 1, 7, 3)
 #define MOE_DN_CFGS(X) \
   X(0, 16, 8, 4, 2) X(0, 32, 8, 4, 2) X(0, 64, 4, 4, 4) X(0, 128, 4, 4, 3) X(0, 192, 4, 4, 3) \
   X(1, 192, 2, 8, 4)

@@ -73,8 +73,11 @@ enum moe_status {
  * automatic choices. */
 typedef struct moe_options {
     /* Rows per schedule block (BLOCK_M, [R] "Assumptions & free
-     * parameters": fixed for one launch).  0 = chosen from T*top_k/E; else
-     * one of 16, 32, 64, 128, 192. */
+     * parameters": fixed for one launch).  0 = automatic: the smallest size
+     * >= 128 that holds the mean rows per expert plus three standard
+     * deviations of a uniform router; else one of 16, 32, 64, 128, 192.
+     * Blocks hold up to block_rows rows; the GEMMs skip 16-row subtiles past
+     * a block's last row. */
     int block_rows;
     /* Split of the down projection's reduction (ffn) into this many parts
      * whose partial sums the combination adds in a fixed order.  0 =
@@ -83,7 +86,8 @@ typedef struct moe_options {
     /* Tile variant of the fused gate/up GEMM.  0 = automatic; k >= 1 selects
      * compiled variant k-1 for the chosen block_rows (which must then be set
      * explicitly).  BM = 64 has variants 0 (256 columns per workgroup) and 1
-     * (128 columns); BM = 192 has variants 0 (128 columns) and 1 (112
+     * (128 columns); BM = 128 has variants 0 (128 columns, 8 waves) and 1
+     * (64 columns); BM = 192 has variants 0 (128 columns) and 1 (112
      * columns); every other BM has variant 0 only. */
     int tile_variant;
     /* K-start rotation of the GEMMs: each schedule block starts its

@@ -79,7 +79,8 @@ def test_options_checks():
         assert _ws(64, 256, 512, 8, 2, _o(bm, 0, 1))[0] == OK
     assert _ws(64, 256, 512, 8, 2, _o(64, 0, 2))[0] == OK
     assert _ws(64, 256, 512, 8, 2, _o(192, 0, 2))[0] == OK
-    assert _ws(64, 256, 512, 8, 2, _o(128, 0, 2))[0] == UNSUP
+    assert _ws(64, 256, 512, 8, 2, _o(128, 0, 2))[0] == OK
+    assert _ws(64, 256, 512, 8, 2, _o(128, 0, 3))[0] == UNSUP
     for r in (1, 2):
         assert _ws(64, 256, 512, 8, 2, _o(0, 0, 0, r))[0] == OK
 
@@ -108,9 +109,12 @@ def test_routing_and_gather_options():
 
 
 def test_plan_choices_for_the_workloads():
-    # near-uniform routing: one block per expert in the common case
+    # near-uniform routing: one block per expert in the common case; never
+    # fewer than 128 rows per block (robust to skewed routing)
     assert moe.moe_plan(512, 4096, 14336, 8, 2)[0] == 192
-    assert moe.moe_plan(512, 7168, 2048, 256, 8)[0] == 32
+    assert moe.moe_plan(512, 7168, 2048, 256, 8)[0] == 128
+    assert moe.moe_plan(64, 256, 512, 8, 2)[0] == 128
+    assert moe.moe_plan(4096, 7168, 2048, 256, 8)[0] == 192
     for name, c in CONFIGS.items():
         bm, split = moe.moe_plan(c.T, c.d, c.ffn, c.E, c.top_k)
         assert bm in (16, 32, 64, 128, 192) and 1 <= split <= 8, name

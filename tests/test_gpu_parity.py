@@ -154,7 +154,7 @@ def test_forward_rotation_on_and_off(bm, rotate):
     parity.check_out(out, ref, f"bm={bm} rotate={rotate}")
 
 
-@pytest.mark.parametrize("bm,variant", [(64, 1), (64, 2), (192, 1), (192, 2)])
+@pytest.mark.parametrize("bm,variant", [(64, 1), (64, 2), (128, 1), (128, 2), (192, 1), (192, 2)])
 def test_forward_tile_variants(bm, variant):
     cfg, x, lg, wgu, wd, ref = _mid_case()
     out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm, tile_variant=variant)
