@@ -158,7 +158,8 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->nb_max = (A + p->bm - 1) / p->bm + (E < A ? E : A);
   p->nchunks = (A + kChunk - 1) / kChunk;
   const int rk = opt ? opt->routing_kernels : 0;
-  p->small_routing = rk == 1 || (rk == 0 && small_routing_fits(T, E, k));
+  p->small_routing = rk == 1 || (rk == 0 && small_routing_fits(T, E, k) &&
+                                  (long long)T * E * k <= kSmallRoutingAutoWork);
   // The fused gate/up GEMM addresses x [T, d] with 32-bit buffer offsets.
   const int gm = opt ? opt->gather_mode : 0;
   const bool x_fits = (long long)T * d * 2 + 2LL * d < (1LL << 31);

@@ -59,6 +59,9 @@ hipError_t launch_permute(const int32_t* ids, int A, int E, int nchunks, const i
 // workgroup of 1024 threads, one token per thread.
 constexpr int kSmallRoutingMaxTokens = 1024;
 constexpr int kSmallRoutingMaxExperts = 32;
+// The automatic choice also bounds T*E*k: the kernel's top-k runs on one CU
+// (measured faster than the three launches at E = 8, slower at E = 64).
+constexpr long long kSmallRoutingAutoWork = 1 << 15;
 bool small_routing_fits(int T, int E, int k);
 hipError_t launch_route_dispatch_small(const float* logits, int T, int E, int k, int renorm,
                                        int score, int bm, int32_t* ids, float* w,
