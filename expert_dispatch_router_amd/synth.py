@@ -115,6 +115,14 @@ def make_weights(cfg: MoEConfig, seed: int = 0, device="cpu"):
     return wgu, wd
 
 
+def make_router_weight(cfg: MoEConfig, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Router matrix W_r bf16 [E, d] ~ N(0, 1/d), drawn on the CPU, so that
+    x . W_r^T has unit-variance scores for x ~ N(0, 1)."""
+    g = _gen(seed + 5, "cpu")
+    w = torch.randn(cfg.E, cfg.d, generator=g, dtype=torch.float32) / math.sqrt(cfg.d)
+    return w.to(torch.bfloat16).to(device)
+
+
 def make_inputs(cfg: MoEConfig, seed: int = 0, device="cpu", weight_device=None):
     """All four inputs.  x and logits are drawn on the CPU and moved;
     weights are drawn on ``weight_device`` (default: ``device``)."""

@@ -4,8 +4,8 @@ Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
 its Python binding) never imports it and shares no code with it.
 
-The arithmetic lives in ``moe_oracle.c`` (plain C, fp32 accumulation, one
-token at a time, OpenMP over tokens only).  This module compiles it with gcc
+The arithmetic lives in ``moe_oracle.c`` (plain C, fp32 accumulation -- fp64
+for the router scores -- one token at a time, OpenMP over tokens only).  This module compiles it with gcc
 and marshals numpy arrays to it; it holds no arithmetic of its own except the
 composition of the steps in their documented order.
 
@@ -14,6 +14,7 @@ bf16 tensors are passed as ``numpy.uint16`` bit patterns.
 Steps (named after the page they follow, [R] = the Pith review of
 "Cross-Platform Fused MoE Dispatch in Triton: Portable Expert Routing Without
 CUDA"):
+  router_logits   O0 router scores x.W_r^T   [R] "The reading", Eq. (1)-(4)
   route           O1 top-k + O2 weights      [R] "The reading", Eq. (1)-(4)
   counts_offsets  O3 histogram + scan        [R] "What carries the argument"
   permute         O4 stable reorder          [R] "The reading"; abstract
@@ -72,8 +73,9 @@ def _load():
         lib.orc_block_table.argtypes = [P, P, I, I, P, I, P]
         lib.orc_ffn_tokens.argtypes = [P, P, P, P, P, I, I, I, I, I, P, I, P]
         lib.orc_round_bf16.argtypes = [P, P, ctypes.c_long]
+        lib.orc_router_logits.argtypes = [P, P, I, I, I, P]
         for f in ("orc_select_topk", "orc_weights", "orc_counts_offsets", "orc_permute",
-                  "orc_block_table", "orc_ffn_tokens", "orc_round_bf16"):
+                  "orc_block_table", "orc_ffn_tokens", "orc_round_bf16", "orc_router_logits"):
             getattr(lib, f).restype = I
         _lib = lib
         return lib
@@ -181,6 +183,20 @@ def ffn(x: np.ndarray, ids: np.ndarray, w: np.ndarray, w_gate_up, w_down, ffn_di
     _check(_load().orc_ffn_tokens(_ptr(x), _ptr(ids), _ptr(w), gu, dn, T, d, int(ffn_dim), E, k,
                                   _ptr(tokens), tokens.size, _ptr(out)), "ffn")
     del keep1, keep2
+    return out
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """O0: fp32 [T, E] router scores x . W_r^T of bf16 bits x [T, d] and
+    W_r [E, d] (fp64 sums, one rounding to fp32)."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    wr = np.ascontiguousarray(w_router, dtype=np.uint16)
+    T, d = x.shape
+    E, d2 = wr.shape
+    if d2 != d:
+        raise ValueError("x and W_r disagree on d")
+    out = np.empty((T, E), dtype=np.float32)
+    _check(_load().orc_router_logits(_ptr(x), _ptr(wr), T, d, E, _ptr(out)), "router_logits")
     return out
 
 

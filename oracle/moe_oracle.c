@@ -275,6 +275,32 @@ int orc_ffn_tokens(const uint16_t *x, const int32_t *ids, const float *w,
     return ORC_OK;
 }
 
+/* O0 -- router scores ([R] "The reading": tokens are scored before they are
+ * routed; "Assumptions & free parameters", Eq. (1)-(4): the standard router,
+ * a linear map of the token's hidden state to one score per expert):
+ *   logits[t][e] = sum_c x[t][c] * W_r[e][c].
+ * Reading: W_r is [E, d] with each expert's row contiguous, like the expert
+ * weights; x and W_r are bf16.  The precision is not fixed by the page:
+ * here the products are summed in fp64 in ascending c and the sum is
+ * rounded once to fp32, i.e. the exact dot product to within d * 2^-53 of
+ * sum_c |x[t][c] * W_r[e][c]| before that one rounding. */
+int orc_router_logits(const uint16_t *x, const uint16_t *wr, int T, int d, int E, float *logits)
+{
+    if ((!x || !wr || !logits) && T > 0) return ORC_EARG;
+    if (T < 0 || d < 1 || E < 1) return ORC_EARG;
+#pragma omp parallel for schedule(static)
+    for (int t = 0; t < T; ++t) {
+        for (int e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int c = 0; c < d; ++c)
+                s += (double)orc_bf16_to_f32(x[(size_t)t * d + c]) *
+                     (double)orc_bf16_to_f32(wr[(size_t)e * d + c]);
+            logits[(size_t)t * E + e] = (float)s;
+        }
+    }
+    return ORC_OK;
+}
+
 /* O7 -- the bf16 output: round-to-nearest-even of the fp32 result. */
 int orc_round_bf16(const float *in, uint16_t *out, long n)
 {
