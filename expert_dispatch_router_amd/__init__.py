@@ -1,8 +1,8 @@
 """MI355X (gfx950) Mixture-of-Experts forward path.
 
-The computation -- router top-k, reorder onto experts, fused gate/up SwiGLU
-grouped GEMM, down grouped GEMM, weighted combination -- runs in the HIP
-kernels of ``libmoe.so`` behind the C ABI of include/moe.h.  This package is
+The computation -- router scores (optional), router top-k, reorder onto
+experts, fused gate/up SwiGLU grouped GEMM, down grouped GEMM, weighted
+combination -- runs in the HIP kernels of ``libmoe.so`` behind the C ABI of include/moe.h.  This package is
 a thin ctypes binding over it plus the seeded synthetic-input generators
 (``expert_dispatch_router_amd.synth``).
 """
@@ -17,9 +17,11 @@ from ._lib import (  # noqa: F401
     lib,
     moe_abi_version,
     moe_forward,
+    moe_forward_router,
     moe_plan,
     moe_route,
     moe_route_workspace_size,
+    moe_router_logits,
     moe_workspace_size,
     status_string,
 )

@@ -37,6 +37,9 @@ SIGNATURES = {
     "moe_plan": (_I, [_I, _I, _I, _I, _I, _P, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "moe_forward": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "moe_forward_ex": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "moe_router_logits": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "moe_forward_router": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ,
+                                _P]),
     "moe_route_workspace_size": (_I, [_I, _I, _I, _P, ctypes.POINTER(_SZ)]),
     "moe_route": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
                        ctypes.POINTER(_I), _P, _SZ, _P]),
@@ -189,6 +192,60 @@ def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=Non
         _stream_ptr(stream, x.device))
     del keep
     _check("moe_forward_ex", rc)
+    return out
+
+
+def moe_router_logits(x, W_router, out=None, stream=None):
+    """logits fp32 [T,E] = x . W_router^T for x bf16 [T,d], W_router bf16
+    [E,d], enqueued on ``stream``."""
+    T, d = x.shape
+    E = W_router.shape[0]
+    if tuple(W_router.shape) != (E, d):
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        out = torch.empty(T, E, dtype=torch.float32, device=x.device)
+    if tuple(out.shape) != (T, E):
+        raise ValueError("out must be [T, E]")
+    rc = lib().moe_router_logits(_dev_ptr(x, torch.bfloat16, "x"),
+                                 _dev_ptr(W_router, torch.bfloat16, "W_router"),
+                                 _dev_ptr(out, torch.float32, "logits"), T, d, E,
+                                 _stream_ptr(stream, x.device))
+    _check("moe_router_logits", rc)
+    return out
+
+
+def moe_forward_router(x, W_router, W_gate_up, W_down, top_k, renormalize, out=None,
+                       logits_out=None, score="softmax", workspace=None, stream=None,
+                       block_rows=0, split_k=0, stage_events=None, tile_variant=0, rotate=0,
+                       routing_kernels=0, gather_mode=0):
+    """moe_forward from the hidden states: router scores x . W_router^T
+    (written to ``logits_out`` when given), then the forward pass."""
+    T, d = x.shape
+    E = W_router.shape[0]
+    F = W_down.shape[2]
+    if tuple(W_router.shape) != (E, d) or tuple(W_gate_up.shape) != (E, 2 * F, d) or \
+            tuple(W_down.shape) != (E, d, F):
+        raise ValueError("inconsistent shapes")
+    if logits_out is not None and tuple(logits_out.shape) != (T, E):
+        raise ValueError("logits_out must be [T, E]")
+    if out is None:
+        out = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
+    ws_need = moe_workspace_size(T, d, F, E, top_k, block_rows, split_k, tile_variant, rotate,
+                                 routing_kernels, gather_mode)
+    if workspace is None:
+        workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=x.device)
+    o, keep = _opts(block_rows, split_k, stage_events, tile_variant, rotate, routing_kernels,
+                    gather_mode)
+    rc = lib().moe_forward_router(
+        _dev_ptr(x, torch.bfloat16, "x"), _dev_ptr(W_router, torch.bfloat16, "W_router"),
+        _dev_ptr(W_gate_up, torch.bfloat16, "W_gate_up"), _dev_ptr(W_down, torch.bfloat16, "W_down"),
+        int(top_k), int(bool(renormalize)), _dev_ptr(out, torch.bfloat16, "out"),
+        None if logits_out is None else _dev_ptr(logits_out, torch.float32, "logits_out"),
+        T, d, F, E, _score_code(score), ctypes.byref(o) if o else None,
+        _dev_ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream_ptr(stream, x.device))
+    del keep
+    _check("moe_forward_router", rc)
     return out
 
 

@@ -22,7 +22,8 @@ LIB = os.path.join(PKG, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "dispatch.hip", "grouped_gemm.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["router.hip", "route.hip", "dispatch.hip", "grouped_gemm.hip", "combine.hip",
+           "moe_api.cpp"]
 
 # -packed-fp32-ops: no packed fp32 VALU ops in device code (the host pass
 # warns that it does not know the feature; that is harmless).

@@ -35,6 +35,7 @@
 //     past the last column are skipped whole (N % 16 == 0).
 //   * K5 may split its reduction into `split` contiguous parts, each written
 //     as its own fp32 partial; the combination kernel adds them in order.
+#include "buffer_load.hpp"
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -63,14 +64,6 @@ struct Gemm {
   static constexpr int kXPerThread = (kXChunks + kThreads - 1) / kThreads;
   static_assert(BM % 16 == 0, "BM is a multiple of 16");
 };
-
-// 128-bit raw buffer load; offsets past the resource's byte range read 0.
-__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-}
-
-// gfx9 raw-buffer descriptor word 3 (32-bit data format, no swizzle).
-constexpr int kRsrcWord3 = 0x00020000;
 
 // X: activations [A, K] (sorted rows).  W: weights [E, NG*N, K].
 // out: K4 -> bf16 h [A, N];  K5 -> fp32 y [split, A, N].

@@ -198,6 +198,7 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->o_xperm = seg(p->gather_in_gemm ? 0 : (size_t)A * d * 2);
   p->o_h = seg((size_t)A * ffn * 2);
   p->o_y = seg((size_t)p->split * A * d * 4);
+  p->o_logits = seg((size_t)T * E * 4);
   p->total_bytes = o;
 }
 
@@ -252,6 +253,44 @@ int run_routing(const float* logits, const Plan& p, int renorm, int score, void*
   MOE_TRY_HIP(launch_permute(ids, p.A, p.E, p.nchunks, offsets, at<int32_t>(ws, p.o_ccnt),
                              at<int32_t>(ws, p.o_cbase), at<int32_t>(ws, p.o_perm),
                              at<int32_t>(ws, p.o_inv), s));
+  return MOE_OK;
+}
+
+// The forward pass from router scores already on the device (steps K1..K6).
+int forward_from_logits(const uint16_t* x, const float* router_logits, const uint16_t* W_gate_up,
+                        const uint16_t* W_down, int top_k, int renorm, uint16_t* out, int score,
+                        const Plan& p, const moe_options* opt, void* workspace, hipStream_t s) {
+  const int T = p.T, d = p.d, ffn = p.ffn;
+  MOE_TRY(run_routing(router_logits, p, renorm, score, workspace, opt, s));
+  const int32_t* perm = at<int32_t>(workspace, p.o_perm);
+  const int32_t* blocks = at<int32_t>(workspace, p.o_blocks);
+  const int32_t* nb = at<int32_t>(workspace, p.o_nb);
+  const int32_t* offsets = at<int32_t>(workspace, p.o_offsets);
+  uint16_t* x_perm = at<uint16_t>(workspace, p.o_xperm);
+  uint16_t* h = at<uint16_t>(workspace, p.o_h);
+  float* y = at<float>(workspace, p.o_y);
+  if (!p.gather_in_gemm) MOE_TRY_HIP(launch_gather(x, perm, p.A, d, top_k, x_perm, s));
+  MOE_TRY(record(opt, 3, s));
+  MOE_TRY_HIP(launch_gate_up(p.bm, p.gu_variant, p.gather_in_gemm ? x : x_perm,
+                             p.gather_in_gemm ? perm : nullptr, top_k, T, W_gate_up, blocks, nb,
+                             offsets, h, p.A, d, ffn, p.nb_max, p.gu_rotate, s));
+  MOE_TRY(record(opt, 4, s));
+  MOE_TRY_HIP(launch_down(p.bm, p.dn_variant, h, W_down, blocks, nb, offsets, y, p.A, d, ffn,
+                          p.split, p.ksplit, p.nb_max, p.dn_rotate, s));
+  MOE_TRY(record(opt, 5, s));
+  MOE_TRY_HIP(launch_combine(y, p.split, p.A, d, at<int32_t>(workspace, p.o_inv),
+                             at<float>(workspace, p.o_w), top_k, T, out, s));
+  MOE_TRY(record(opt, 6, s));
+  return MOE_OK;
+}
+
+// Size checks of the router scores alone (x [T, d], W_r [E, d]).
+int check_router_sizes(int T, int d, int E) {
+  if (T < 0 || d < 1 || E < 1) return MOE_ERR_SHAPE;
+  if (E > MOE_MAX_EXPERTS || T > MOE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
+  if (d % 64 != 0) return MOE_ERR_ALIGN;
+  // one 16-row tile of x or W_r is addressed with 32-bit buffer offsets
+  if (16LL * d * 2 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -345,28 +384,49 @@ int moe_forward_ex(const uint16_t* x, const float* router_logits, const uint16_t
 
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();  // report only this call's launches
-  const int renorm = renormalize ? 1 : 0;
-  MOE_TRY(run_routing(router_logits, p, renorm, score_func, workspace, opt, s));
-  const int32_t* perm = at<int32_t>(workspace, p.o_perm);
-  const int32_t* blocks = at<int32_t>(workspace, p.o_blocks);
-  const int32_t* nb = at<int32_t>(workspace, p.o_nb);
-  const int32_t* offsets = at<int32_t>(workspace, p.o_offsets);
-  uint16_t* x_perm = at<uint16_t>(workspace, p.o_xperm);
-  uint16_t* h = at<uint16_t>(workspace, p.o_h);
-  float* y = at<float>(workspace, p.o_y);
-  if (!p.gather_in_gemm) MOE_TRY_HIP(launch_gather(x, perm, p.A, d, top_k, x_perm, s));
-  MOE_TRY(record(opt, 3, s));
-  MOE_TRY_HIP(launch_gate_up(p.bm, p.gu_variant, p.gather_in_gemm ? x : x_perm,
-                             p.gather_in_gemm ? perm : nullptr, top_k, T, W_gate_up, blocks, nb,
-                             offsets, h, p.A, d, ffn, p.nb_max, p.gu_rotate, s));
-  MOE_TRY(record(opt, 4, s));
-  MOE_TRY_HIP(launch_down(p.bm, p.dn_variant, h, W_down, blocks, nb, offsets, y, p.A, d, ffn,
-                          p.split, p.ksplit, p.nb_max, p.dn_rotate, s));
-  MOE_TRY(record(opt, 5, s));
-  MOE_TRY_HIP(launch_combine(y, p.split, p.A, d, at<int32_t>(workspace, p.o_inv),
-                             at<float>(workspace, p.o_w), top_k, T, out, s));
-  MOE_TRY(record(opt, 6, s));
+  return forward_from_logits(x, router_logits, W_gate_up, W_down, top_k, renormalize ? 1 : 0, out,
+                             score_func, p, opt, workspace, s);
+}
+
+int moe_router_logits(const uint16_t* x, const uint16_t* W_router, float* logits, int T, int d,
+                      int E, void* hip_stream) {
+  MOE_TRY(check_router_sizes(T, d, E));
+  if (T == 0) return MOE_OK;
+  if (!x || !W_router || !logits) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(W_router, 16) || !aligned(logits, 16)) return MOE_ERR_ALIGN;
+  (void)hipGetLastError();
+  MOE_TRY_HIP(launch_router_logits(x, W_router, T, d, E, logits,
+                                   static_cast<hipStream_t>(hip_stream)));
   return MOE_OK;
+}
+
+int moe_forward_router(const uint16_t* x, const uint16_t* W_router, const uint16_t* W_gate_up,
+                       const uint16_t* W_down, int top_k, int renormalize, uint16_t* out,
+                       float* logits_out, int T, int d, int ffn, int E, int score_func,
+                       const moe_options* opt, void* workspace, size_t workspace_bytes,
+                       void* hip_stream) {
+  MOE_TRY(check_sizes(T, d, ffn, E, top_k, true));
+  MOE_TRY(check_router_sizes(T, d, E));
+  MOE_TRY(check_options(opt));
+  MOE_TRY(check_paths(T, d, E, top_k, opt));
+  if (score_func != MOE_SCORE_SOFTMAX && score_func != MOE_SCORE_SIGMOID)
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !W_router || !W_gate_up || !W_down || !out || !workspace) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(W_router, 16) || !aligned(W_gate_up, 16) ||
+      !aligned(W_down, 16) || !aligned(out, 16) || !aligned(workspace, kAlign) ||
+      (logits_out && !aligned(logits_out, 16)))
+    return MOE_ERR_ALIGN;
+  Plan p;
+  make_plan(T, d, ffn, E, top_k, opt, &p);
+  if (workspace_bytes < p.total_bytes) return MOE_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  (void)hipGetLastError();
+  float* logits = logits_out ? logits_out : at<float>(workspace, p.o_logits);
+  MOE_TRY_HIP(launch_router_logits(x, W_router, T, d, E, logits, s));
+  return forward_from_logits(x, logits, W_gate_up, W_down, top_k, renormalize ? 1 : 0, out,
+                             score_func, p, opt, workspace, s);
 }
 
 int moe_forward(const uint16_t* x, const float* router_logits, const uint16_t* W_gate_up,

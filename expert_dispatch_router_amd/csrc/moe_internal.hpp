@@ -39,10 +39,15 @@ struct Plan {
   size_t o_ids, o_w, o_counts, o_offsets, o_ccnt, o_cbase, o_perm, o_inv, o_blocks, o_nb;
   size_t route_bytes;  // end of the routing section
   size_t o_xperm, o_h, o_y;
+  size_t o_logits;  // router scores [T, E] fp32 (moe_forward_router)
   size_t total_bytes;
 };
 
 // ---- launchers (enqueue on `s`, return the launch status) ----------------
+
+// Router scores logits[T, E] = x . W_r^T (bf16 in, fp32 out).
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
+                                float* logits, hipStream_t s);
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, int score,
                         int32_t* ids, float* w, hipStream_t s);

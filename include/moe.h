@@ -174,6 +174,37 @@ int moe_forward_ex(const uint16_t *x, const float *router_logits, const uint16_t
                    int T, int d, int ffn, int E, int score_func, const moe_options *opt,
                    void *workspace, size_t workspace_bytes, void *hip_stream);
 
+/*
+ * Router scores ([R] "The reading": tokens are scored before they are
+ * routed; "Assumptions & free parameters", Eq. (1)-(4): the standard router,
+ * a linear map of each token's hidden state to one score per expert):
+ *
+ *   logits[t][e] = sum_c x[t][c] * W_router[e][c]
+ *
+ *   x         bf16 [T, d]   token activations
+ *   W_router  bf16 [E, d]   one row per expert (K-contiguous, like the
+ *                           expert weights)
+ *   logits    fp32 [T, E]   written (fp32 accumulation; deterministic)
+ *
+ * Constraints: T >= 0 (T = 0 is a no-op), 1 <= E <= 512, d a positive
+ * multiple of 64 with 32*d < 2^31, T <= 2^20, pointers 16-byte aligned.
+ * No workspace; enqueued on hip_stream.
+ */
+int moe_router_logits(const uint16_t *x, const uint16_t *W_router, float *logits, int T, int d,
+                      int E, void *hip_stream);
+
+/* moe_forward_ex from the hidden states: the router scores of
+ * moe_router_logits, then the forward pass on them.  logits_out (fp32
+ * [T, E], 16-byte aligned) receives the scores, or may be NULL (they are
+ * kept in the workspace).  Same workspace size as moe_forward_ex; the
+ * constraints of both calls apply.  The stage events (opt) time the forward
+ * pass after the scores: events[0] is recorded after the router GEMM. */
+int moe_forward_router(const uint16_t *x, const uint16_t *W_router, const uint16_t *W_gate_up,
+                       const uint16_t *W_down, int top_k, int renormalize, uint16_t *out,
+                       float *logits_out, int T, int d, int ffn, int E, int score_func,
+                       const moe_options *opt, void *workspace, size_t workspace_bytes,
+                       void *hip_stream);
+
 /* Host-only size query for moe_route. */
 int moe_route_workspace_size(int T, int E, int top_k, const moe_options *opt, size_t *bytes);
 

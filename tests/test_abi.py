@@ -197,6 +197,49 @@ def test_route_rejects_before_any_launch():
     assert moe.lib().moe_route_workspace_size(4, 4, 2, None, ctypes.byref(n)) == OK and n.value > 0
 
 
+def _rl(**kw):
+    a = dict(x=FAKE, w=FAKE, out=FAKE, T=4, d=64, E=4)
+    a.update(kw)
+    return moe.lib().moe_router_logits(a["x"], a["w"], a["out"], a["T"], a["d"], a["E"], None)
+
+
+def test_router_logits_rejects_before_any_launch():
+    # every call below fails a host check (a valid one would launch)
+    assert _rl(T=-1) == SHAPE
+    assert _rl(E=0) == SHAPE
+    assert _rl(d=0) == SHAPE
+    assert _rl(E=513) == UNSUP
+    assert _rl(T=(1 << 20) + 1) == UNSUP
+    assert _rl(d=100) == ALIGN
+    assert _rl(d=1 << 26) == UNSUP
+    for name in ("x", "w", "out"):
+        assert _rl(**{name: None}) == NULL, name
+        assert _rl(**{name: FAKE + 4}) == ALIGN, name
+    assert _rl(T=0, x=None, w=None, out=None) == OK
+
+
+def _fr(**kw):
+    a = dict(x=FAKE, wr=FAKE, wgu=FAKE, wd=FAKE, k=2, renorm=1, out=FAKE, lo=None, T=4, d=64, F=64,
+             E=4, score=0, opt=None, ws=FAKE, wsb=0, stream=None)
+    a.update(kw)
+    return moe.lib().moe_forward_router(a["x"], a["wr"], a["wgu"], a["wd"], a["k"], a["renorm"],
+                                        a["out"], a["lo"], a["T"], a["d"], a["F"], a["E"],
+                                        a["score"], a["opt"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_forward_router_rejects_before_any_launch():
+    assert _fr() == WS  # wsb = 0
+    for name in ("x", "wr", "wgu", "wd", "out", "ws"):
+        assert _fr(**{name: None}) == NULL, name
+    assert _fr(lo=FAKE + 4) == ALIGN
+    assert _fr(wr=FAKE + 8) == ALIGN
+    assert _fr(k=0) == TOPK
+    assert _fr(d=96) == ALIGN
+    assert _fr(E=513) == UNSUP
+    assert _fr(score=2, wsb=1 << 30) == UNSUP
+    assert _fr(T=0, x=None, wr=None) == OK
+
+
 def test_timer_argument_checks():
     L = moe.lib()
     assert L.moe_timer_create(None) == NULL
