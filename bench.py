@@ -69,6 +69,35 @@ def algorithmic(cfg, counts):
     return dict(A=A, e_act=e_act, flop=flop, bytes=bytes_all, bytes_k4=bytes_k4, flop_k4=flop_k4)
 
 
+def router_gemm(cfg, x, seed, steps, stream):
+    """The router scores x . W_r^T (moe_router_logits), the step upstream of
+    the timed path, timed on its own: mean kernel time over ``steps`` calls
+    bracketed by events on the launch stream, against its algorithmic bytes
+    (x, W_r and the scores, each moved once)."""
+    import torch
+
+    import expert_dispatch_router_amd as moe
+    from expert_dispatch_router_amd import synth
+
+    wr = synth.make_router_weight(cfg, seed, x.device)
+    lg = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=x.device)
+    for _ in range(3):
+        moe.moe_router_logits(x, wr, out=lg, stream=stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        moe.moe_router_logits(x, wr, out=lg, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    nbytes = 2.0 * cfg.T * cfg.d + 2.0 * cfg.E * cfg.d + 4.0 * cfg.T * cfg.E
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"kernel": "router_logits (moe_router_logits, upstream of the timed step)",
+            "mean_launch_ms": ms, "alg_bytes_per_launch": nbytes, "achieved": gbs,
+            "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
+
+
 def traffic_for(cfg_name):
     """Counter-derived HBM bytes per launch of the fused kernel, if the
     stored measurement was taken on the current kernel source."""
@@ -133,7 +162,9 @@ def run(args):
     x, logits, wgu, wd = synth.make_inputs(cfg, args.seed, dev)
     bm, split = moe.moe_plan(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k)
     out = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(moe.moe_workspace_size(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k),
+    unfused = 1 if args.unfused else 0
+    ws = torch.empty(moe.moe_workspace_size(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k,
+                                            unfused_swiglu=unfused),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     copy_src = copy_dst = None
@@ -147,7 +178,7 @@ def run(args):
 
     def step(events=None):
         moe.moe_forward(x, logits, wgu, wd, cfg.top_k, cfg.renormalize, out=out, score=cfg.score,
-                        workspace=ws, stream=stream, stage_events=events)
+                        workspace=ws, stream=stream, stage_events=events, unfused_swiglu=unfused)
         if copy_src is not None:
             copy_dst.copy_(copy_src)
 
@@ -201,28 +232,37 @@ def run(args):
                                f"{' renormalised' if cfg.renormalize else ''}",
                    "tokens": cfg.T, "hidden": cfg.d, "ffn": cfg.ffn, "experts": cfg.E,
                    "top_k": cfg.top_k, "block_rows": bm, "split_k": split,
-                   "active_experts": alg["e_act"], "seed": args.seed},
+                   "active_experts": alg["e_act"], "seed": args.seed,
+                   "swiglu": "unfused ablation" if unfused else "fused"},
         "tflops": alg["flop"] / t_step / 1e12,
         "hbm_gbs": alg["bytes"] / t_step / 1e9,
         "roofline_frac_step": t_roof / t_step,
         "stage_ms": {n: round(float(v), 5) for n, v in zip(STAGES, stage_ms)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_for(cfg.name),
-                     "kernel": "gate_up_swiglu (fused gate/up SwiGLU grouped GEMM)",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None if unfused else traffic_for(cfg.name),
+                     "kernel": ("gate/up stage of the unfused ablation (gate GEMM + up GEMM + "
+                                "activation)") if unfused else
+                               "gate_up_swiglu (fused gate/up SwiGLU grouped GEMM)",
                      "alg_bytes_per_launch": alg["bytes_k4"],
                      "mean_launch_ms": float(k4_ms)},
         "cpu_baseline": None,
     }
+    res["router_gemm"] = router_gemm(cfg, x, args.seed, args.steps, stream)
     if not args.profile and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, x, logits, wgu, wd, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 
 def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the fused kernel, scaled
-    by what the same counters read for the plain copy of copy_bytes bytes
-    (reads copy_bytes, writes copy_bytes)."""
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the GEMM-stage kernels,
+    scaled by what the same counters read for the plain copy of copy_bytes
+    bytes (reads copy_bytes, writes copy_bytes).  Writes
+    profiles/traffic_gate_up_swiglu_<workload>.json for the fused kernel, or
+    profiles/traffic_unfused_swiglu_<workload>.json when the run used the
+    unfused ablation (gate GEMM, up GEMM, activation kernel)."""
     import csv
+    import re
 
     def load(d, counter):
         rows = []
@@ -235,16 +275,20 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes):
             raise SystemExit(f"no {counter} rows under {d}")
         return rows
 
-    def mean_of(rows, pred):
-        v = [val for name, val in rows if pred(name)]
-        return sum(v) / len(v), len(v)
+    def mode(name):  # output mode of a grouped GEMM instantiation
+        m = re.search(r"grouped_gemm_kernel<\d+, \d+, \d+, \d+, (\d)>", name)
+        return int(m.group(1)) if m else None
 
-    is_k4 = lambda n: "grouped_gemm_kernel" in n and "true>" in n
+    classes = {
+        "gate_up_swiglu": lambda n: mode(n) == 0,
+        "down": lambda n: mode(n) == 1,
+        "proj_bf16": lambda n: mode(n) == 2,
+        "swiglu_act": lambda n: "swiglu_act_kernel" in n,
+    }
     is_copy = lambda n: "copyBuffer" in n
     f = load(fetch_dir, "FETCH_SIZE")
     w = load(write_dir, "WRITE_SIZE")
-    fk4, nf = mean_of(f, is_k4)
-    wk4, nw = mean_of(w, is_k4)
+
     # the calibration copies are the copyBuffer dispatches of copy_bytes: the
     # largest ones (other copies of a run move a few KiB)
     def big_copies(rows):
@@ -255,12 +299,30 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes):
     wcp, ncw = big_copies(w)
     f_scale = copy_bytes / (fcp * 1024.0)
     w_scale = copy_bytes / (wcp * 1024.0)
-    out = {"kernel": "gate_up_swiglu", "workload": workload, "source_sha256_16": source_sha(),
-           "fetch_kib_per_launch": fk4, "write_kib_per_launch": wk4, "launches": [nf, nw],
-           "copy_bytes": copy_bytes, "copy_fetch_kib": fcp, "copy_write_kib": wcp, "copies": [ncf, ncw],
-           "fetch_scale": f_scale, "write_scale": w_scale,
-           "bytes_per_launch": fk4 * 1024.0 * f_scale + wk4 * 1024.0 * w_scale}
-    path = os.path.join(ROOT, "profiles", f"traffic_gate_up_swiglu_{workload}.json")
+    per = {}
+    for cname, pred in classes.items():
+        fv = [v for n, v in f if pred(n)]
+        wv = [v for n, v in w if pred(n)]
+        if not fv or not wv:
+            continue
+        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        per[cname] = {"fetch_kib_per_launch": fk, "write_kib_per_launch": wk,
+                      "launches": [len(fv), len(wv)],
+                      "bytes_per_launch": fk * 1024.0 * f_scale + wk * 1024.0 * w_scale}
+    unfused = "proj_bf16" in per
+    out = {"workload": workload, "source_sha256_16": source_sha(), "copy_bytes": copy_bytes,
+           "copy_fetch_kib": fcp, "copy_write_kib": wcp, "copies": [ncf, ncw],
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": per}
+    if unfused:
+        # per forward pass: two projections and one activation kernel
+        out["kernel"] = "unfused_swiglu (gate GEMM + up GEMM + activation)"
+        out["bytes_per_forward"] = 2 * per["proj_bf16"]["bytes_per_launch"] + \
+            per["swiglu_act"]["bytes_per_launch"]
+        path = os.path.join(ROOT, "profiles", f"traffic_unfused_swiglu_{workload}.json")
+    else:
+        out["kernel"] = "gate_up_swiglu"
+        out["bytes_per_launch"] = per["gate_up_swiglu"]["bytes_per_launch"]
+        path = os.path.join(ROOT, "profiles", f"traffic_gate_up_swiglu_{workload}.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
@@ -278,6 +340,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--unfused", action="store_true",
+                    help="SwiGLU ablation: gate GEMM, up GEMM and activation kernel")
     args = ap.parse_args()
     if args.traffic:
         summarize_traffic(args.traffic[0], args.traffic[1], args.workload,

@@ -54,10 +54,15 @@ __device__ __forceinline__ void lds_barrier() {
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
-template <int BM, int NWT, int WAVES, int PF, bool SWIGLU>
+// Output of a launch: the fused SwiGLU h (bf16, gate and up rows from one
+// activation tile), fp32 partial sums of one part of a split reduction, or
+// the plain product in bf16 (one projection of the unfused SwiGLU).
+enum { kOutSwiGLU = 0, kOutF32Parts = 1, kOutBF16 = 2 };
+
+template <int BM, int NWT, int WAVES, int PF, int MODE>
 struct Gemm {
   static constexpr int kMT = BM / 16;                        // 16-row subtiles
-  static constexpr int kNG = SWIGLU ? 2 : 1;                 // weight groups (gate, up)
+  static constexpr int kNG = MODE == kOutSwiGLU ? 2 : 1;     // weight groups (gate, up)
   static constexpr int kThreads = WAVES * 64;
   static constexpr int kTileCols = WAVES * NWT * 16;         // output columns per workgroup
   static constexpr int kXChunks = BM * (kBK / 8);            // 16-byte chunks per activation tile
@@ -67,14 +72,14 @@ struct Gemm {
 
 // X: activations [A, K] (sorted rows).  W: weights [E, NG*N, K].
 // out: K4 -> bf16 h [A, N];  K5 -> fp32 y [split, A, N].
-template <int BM, int NWT, int WAVES, int PF, bool SWIGLU>
+template <int BM, int NWT, int WAVES, int PF, int MODE>
 __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
     const int32_t* __restrict__ offsets, void* __restrict__ out, int A, int N, int K, int ksplit,
     int tiles_per_block, int rotate, const int32_t* __restrict__ gather_perm, int gather_k,
     int x_rows) {
-  using G = Gemm<BM, NWT, WAVES, PF, SWIGLU>;
+  using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   constexpr int MT = G::kMT, NG = G::kNG, XPT = G::kXPerThread;
   static_assert(PF >= 2, "the activation stage is issued PF-1 steps ahead");
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kLdsStride];
@@ -107,7 +112,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
   // so the compiler counts outstanding loads exactly and waits only for the
   // oldest ring stage.
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (size_t)e * NG * N * K), (short)0, NG * N * K * 2, kRsrcWord3);
+      (void*)(W + (size_t)e * w_estride), (short)0, NG * N * K * 2, kRsrcWord3);
   // X rows: sorted rows r0 .. r0+rows-1 of X, or -- with gather_perm -- the
   // token rows x[perm[r0 + row] / gather_k] of the unsorted activations (the
   // reorder's row gather folded into this load).  Rows past the block's end
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
         for (int j = 0; j < NWT; ++j) {
           if (!jok[j]) continue;
           const int n = n0 + 16 * j + 4 * (lane >> 4);
-          if constexpr (SWIGLU) {
+          if constexpr (MODE == kOutSwiGLU) {
             const f32x4 gv = acc[0][mt][j];
             const f32x4 uv = acc[NG - 1][mt][j];
             bf16x4 hv;
@@ -283,9 +288,17 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
             hv[2] = (__bf16)(silu_f32(gv[2]) * uv[2]);
             hv[3] = (__bf16)(silu_f32(gv[3]) * uv[3]);
             *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(out) + orow * N + n) = hv;
-          } else {
+          } else if constexpr (MODE == kOutF32Parts) {
             float* y = static_cast<float*>(out) + ((size_t)part * A + orow) * N + n;
             *reinterpret_cast<f32x4*>(y) = acc[0][mt][j];
+          } else {
+            const f32x4 v = acc[0][mt][j];
+            bf16x4 o;
+            o[0] = (__bf16)v[0];
+            o[1] = (__bf16)v[1];
+            o[2] = (__bf16)v[2];
+            o[3] = (__bf16)v[3];
+            *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(out) + orow * N + n) = o;
           }
         }
       }
@@ -293,19 +306,19 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
   }
 }
 
-template <int BM, int NWT, int WAVES, int PF, bool SWIGLU>
-hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, const int32_t* blocks,
+template <int BM, int NWT, int WAVES, int PF, int MODE>
+hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride, const int32_t* blocks,
                       const int32_t* nb, const int32_t* offsets, void* out, int A, int N, int K,
                       int split, int ksplit, int nb_max, int rotate, const int32_t* gather_perm,
                       int gather_k, int x_rows, hipStream_t s) {
-  using G = Gemm<BM, NWT, WAVES, PF, SWIGLU>;
+  using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
   const int tiles_per_block = n_tiles * split;
   const long long grid = (long long)tiles_per_block * nb_max;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  grouped_gemm_kernel<BM, NWT, WAVES, PF, SWIGLU><<<(unsigned)grid, G::kThreads, 0, s>>>(
-      X, W, blocks, nb, offsets, out, A, N, K, ksplit, tiles_per_block, rotate, gather_perm,
-      gather_k, x_rows);
+  grouped_gemm_kernel<BM, NWT, WAVES, PF, MODE><<<(unsigned)grid, G::kThreads, 0, s>>>(
+      X, W, w_estride, blocks, nb, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
+      gather_perm, gather_k, x_rows);
   return hipGetLastError();
 }
 
@@ -328,7 +341,7 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, const int32_t* block
 
 int gate_up_tile_cols(int bm, int variant) {
 #define X(V, BM, NWT, WV, PF) \
-  if (bm == BM && variant == V) return Gemm<BM, NWT, WV, PF, true>::kTileCols;
+  if (bm == BM && variant == V) return Gemm<BM, NWT, WV, PF, kOutSwiGLU>::kTileCols;
   MOE_GU_CFGS(X)
 #undef X
   return 0;
@@ -336,7 +349,7 @@ int gate_up_tile_cols(int bm, int variant) {
 
 int down_tile_cols(int bm, int variant) {
 #define X(V, BM, NWT, WV, PF) \
-  if (bm == BM && V == variant) return Gemm<BM, NWT, WV, PF, false>::kTileCols;
+  if (bm == BM && V == variant) return Gemm<BM, NWT, WV, PF, kOutF32Parts>::kTileCols;
   MOE_DN_CFGS(X)
 #undef X
   return 0;
@@ -348,8 +361,9 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
                           int ffn, int nb_max, int rotate, hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && variant == V)                                                                \
-    return launch_cfg<BM, NWT, WV, PF, true>(x, w_gate_up, blocks, nb, offsets, h, A, ffn, d, 1, \
-                                             d, nb_max, rotate, gather_perm, k, T, s);
+    return launch_cfg<BM, NWT, WV, PF, kOutSwiGLU>(x, w_gate_up, 2LL * ffn * d, blocks, nb,      \
+                                                   offsets, h, A, ffn, d, 1, d, nb_max, rotate,  \
+                                                   gather_perm, k, T, s);
   MOE_GU_CFGS(X)
 #undef X
   return hipErrorInvalidValue;
@@ -361,11 +375,57 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
                        hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && V == variant)                                                                      \
-    return launch_cfg<BM, NWT, WV, PF, false>(h, w_down, blocks, nb, offsets, y, A, d, ffn,    \
-                                              split, ksplit, nb_max, rotate, nullptr, 1, A, s);
+    return launch_cfg<BM, NWT, WV, PF, kOutF32Parts>(h, w_down, (long long)d * ffn, blocks, nb,  \
+                                                     offsets, y, A, d, ffn, split, ksplit,       \
+                                                     nb_max, rotate, nullptr, 1, A, s);
   MOE_DN_CFGS(X)
 #undef X
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_proj_bf16(int bm, const uint16_t* x, const int32_t* gather_perm, int k, int T,
+                            const uint16_t* w, long long w_estride, const int32_t* blocks,
+                            const int32_t* nb, const int32_t* offsets, uint16_t* out, int A, int d,
+                            int ffn, int nb_max, int rotate, hipStream_t s) {
+#define X(V, BM, NWT, WV, PF)                                                                   \
+  if constexpr (V == 0) {                                                                       \
+    if (bm == BM)                                                                               \
+      return launch_cfg<BM, NWT, WV, PF, kOutBF16>(x, w, w_estride, blocks, nb, offsets, out, A, \
+                                                   ffn, d, 1, d, nb_max, rotate, gather_perm, k, \
+                                                   T, s);                                       \
+  }
+  MOE_GU_CFGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+namespace {
+
+// h = bf16(silu(g) * u) elementwise from the bf16 gate and up products, 8
+// values per thread.
+__global__ __launch_bounds__(256) void swiglu_act_kernel(const uint16_t* __restrict__ g,
+                                                         const uint16_t* __restrict__ u,
+                                                         uint16_t* __restrict__ h, long long n8) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const bf16x8 gv = reinterpret_cast<const bf16x8*>(g)[i];
+  const bf16x8 uv = reinterpret_cast<const bf16x8*>(u)[i];
+  bf16x8 hv;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) hv[q] = (__bf16)(silu_f32((float)gv[q]) * (float)uv[q]);
+  reinterpret_cast<bf16x8*>(h)[i] = hv;
+}
+
+}  // namespace
+
+hipError_t launch_swiglu_act(const uint16_t* g, const uint16_t* u, uint16_t* h, long long n,
+                             hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const long long n8 = n / 8;
+  const long long grid = (n8 + 255) / 256;
+  if (n % 8 != 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  swiglu_act_kernel<<<(unsigned)grid, 256, 0, s>>>(g, u, h, n8);
+  return hipGetLastError();
 }
 
 }  // namespace moe

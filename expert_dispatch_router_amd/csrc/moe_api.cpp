@@ -59,6 +59,7 @@ int check_options(const moe_options* opt) {
   if (opt->tile_variant < 0 || opt->rotate < 0 || opt->rotate > 2) return MOE_ERR_UNSUPPORTED;
   if (opt->routing_kernels < 0 || opt->routing_kernels > 2) return MOE_ERR_UNSUPPORTED;
   if (opt->gather_mode < 0 || opt->gather_mode > 2) return MOE_ERR_UNSUPPORTED;
+  if (opt->unfused_swiglu < 0 || opt->unfused_swiglu > 1) return MOE_ERR_UNSUPPORTED;
   if (opt->tile_variant > 0) {
     const int bm = opt->block_rows;
     if (bm == 0 || gate_up_tile_cols(bm, opt->tile_variant - 1) == 0) return MOE_ERR_UNSUPPORTED;
@@ -164,6 +165,7 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   const int gm = opt ? opt->gather_mode : 0;
   const bool x_fits = (long long)T * d * 2 + 2LL * d < (1LL << 31);
   p->gather_in_gemm = gm == 1 || (gm == 0 && x_fits);
+  p->unfused = opt ? opt->unfused_swiglu : 0;
   if (ffn > 0) {
     int s = (opt && opt->split_k) ? opt->split_k : auto_split(A, E, d, ffn, p->bm);
     const int ksteps = ffn / 64;
@@ -197,6 +199,8 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->route_bytes = o;
   p->o_xperm = seg(p->gather_in_gemm ? 0 : (size_t)A * d * 2);
   p->o_h = seg((size_t)A * ffn * 2);
+  p->o_g = seg(p->unfused ? (size_t)A * ffn * 2 : 0);
+  p->o_u = seg(p->unfused ? (size_t)A * ffn * 2 : 0);
   p->o_y = seg((size_t)p->split * A * d * 4);
   p->o_logits = seg((size_t)T * E * 4);
   p->total_bytes = o;
@@ -271,9 +275,23 @@ int forward_from_logits(const uint16_t* x, const float* router_logits, const uin
   float* y = at<float>(workspace, p.o_y);
   if (!p.gather_in_gemm) MOE_TRY_HIP(launch_gather(x, perm, p.A, d, top_k, x_perm, s));
   MOE_TRY(record(opt, 3, s));
-  MOE_TRY_HIP(launch_gate_up(p.bm, p.gu_variant, p.gather_in_gemm ? x : x_perm,
-                             p.gather_in_gemm ? perm : nullptr, top_k, T, W_gate_up, blocks, nb,
-                             offsets, h, p.A, d, ffn, p.nb_max, p.gu_rotate, s));
+  const uint16_t* X = p.gather_in_gemm ? x : x_perm;
+  const int32_t* gperm = p.gather_in_gemm ? perm : nullptr;
+  if (p.unfused) {
+    // Ablation: the two projections each read the activation rows and write
+    // a bf16 product; a third kernel applies SiLU and the product.
+    uint16_t* g = at<uint16_t>(workspace, p.o_g);
+    uint16_t* u = at<uint16_t>(workspace, p.o_u);
+    const long long estride = 2LL * ffn * d;
+    MOE_TRY_HIP(launch_proj_bf16(p.bm, X, gperm, top_k, T, W_gate_up, estride, blocks, nb,
+                                 offsets, g, p.A, d, ffn, p.nb_max, p.gu_rotate, s));
+    MOE_TRY_HIP(launch_proj_bf16(p.bm, X, gperm, top_k, T, W_gate_up + (size_t)ffn * d, estride,
+                                 blocks, nb, offsets, u, p.A, d, ffn, p.nb_max, p.gu_rotate, s));
+    MOE_TRY_HIP(launch_swiglu_act(g, u, h, (long long)p.A * ffn, s));
+  } else {
+    MOE_TRY_HIP(launch_gate_up(p.bm, p.gu_variant, X, gperm, top_k, T, W_gate_up, blocks, nb,
+                               offsets, h, p.A, d, ffn, p.nb_max, p.gu_rotate, s));
+  }
   MOE_TRY(record(opt, 4, s));
   MOE_TRY_HIP(launch_down(p.bm, p.dn_variant, h, W_down, blocks, nb, offsets, y, p.A, d, ffn,
                           p.split, p.ksplit, p.nb_max, p.dn_rotate, s));

@@ -35,10 +35,12 @@ struct Plan {
   int dn_rotate;  // same for the down GEMM
   int small_routing;  // one-workgroup routing kernel instead of three launches
   int gather_in_gemm; // the fused gate/up GEMM reads token rows through perm
+  int unfused;        // SwiGLU as gate GEMM, up GEMM and activation (ablation)
   // byte offsets into the workspace (256-byte aligned)
   size_t o_ids, o_w, o_counts, o_offsets, o_ccnt, o_cbase, o_perm, o_inv, o_blocks, o_nb;
   size_t route_bytes;  // end of the routing section
   size_t o_xperm, o_h, o_y;
+  size_t o_g, o_u;  // unfused gate and up products [A, ffn] bf16
   size_t o_logits;  // router scores [T, E] fp32 (moe_forward_router)
   size_t total_bytes;
 };
@@ -83,6 +85,18 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
                           int k, int T, const uint16_t* w_gate_up, const int32_t* blocks,
                           const int32_t* nb, const int32_t* offsets, uint16_t* h, int A, int d,
                           int ffn, int nb_max, int rotate, hipStream_t s);
+
+// One projection of the unfused SwiGLU: out[A, ffn] = bf16(X w[e]^T) per
+// block, w[e] = w + e * w_estride elements (ffn rows of d); X as for
+// launch_gate_up.
+hipError_t launch_proj_bf16(int bm, const uint16_t* x, const int32_t* gather_perm, int k, int T,
+                            const uint16_t* w, long long w_estride, const int32_t* blocks,
+                            const int32_t* nb, const int32_t* offsets, uint16_t* out, int A, int d,
+                            int ffn, int nb_max, int rotate, hipStream_t s);
+
+// h = bf16(silu(g) * u) over n elements (n % 8 == 0).
+hipError_t launch_swiglu_act(const uint16_t* g, const uint16_t* u, uint16_t* h, long long n,
+                             hipStream_t s);
 
 // Down grouped GEMM: y[split, A, d] = partial sums of h Wd^T per block.
 hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w_down,

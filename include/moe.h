@@ -105,11 +105,20 @@ typedef struct moe_options {
      * through perm (no x_perm buffer); 2 = a gather kernel writes x_perm to
      * the workspace first.  Same results either way. */
     int gather_mode;
+    /* SwiGLU ablation.  0 = fused (default): gate and up products from one
+     * shared activation tile, SiLU and the product in registers, h written
+     * once.  1 = unfused: a gate GEMM and an up GEMM each read the
+     * activation rows and write a bf16 product [A, ffn] to the workspace,
+     * and a third kernel forms h = bf16(silu(g) * u).  The workspace grows
+     * by 4*A*ffn bytes; results differ from the fused path by the two extra
+     * bf16 roundings. */
+    int unfused_swiglu;
     /* NULL, or 7 hipEvent_t handles created by the caller (for instance
      * with moe_timer_create).  events[0] is recorded on the stream before
      * the first kernel and events[i] right after kernel i (1 route, 2
      * histogram+scan+schedule, 3 reorder+gather, 4 fused gate/up SwiGLU
-     * GEMM, 5 down GEMM, 6 weighted combination).  With the one-workgroup
+     * GEMM (or the three unfused kernels), 5 down GEMM, 6 weighted
+     * combination).  With the one-workgroup
      * routing kernel, events 1 and 2 are both recorded after it; with the
      * gather inside the GEMM, event 3 follows the routing directly.
      * NULL entries are skipped.  moe_route records 0..3 only. */

@@ -18,6 +18,11 @@ from expert_dispatch_router_amd import synth
 REL_FRO_TOL = 1e-2
 MAX_ABS_TOL = 2e-2
 W_RTOL = 4e-6
+# The unfused SwiGLU ablation stores the gate and up products in bf16 before
+# SiLU and the product (the activation dtype of an unfused pipeline), so each
+# h element carries three independent bf16 roundings instead of one: its
+# rounding noise is ~sqrt(3) times the fused path's, and so are its bounds.
+UNFUSED_SCALE = 3.0 ** 0.5
 
 
 def to_np_u16(t: torch.Tensor) -> np.ndarray:
@@ -82,9 +87,11 @@ def errors(out_bf16_rows: torch.Tensor, ref32: np.ndarray):
     return rel_fro, max_abs
 
 
-def check_out(out_bf16_rows, ref32, what=""):
+def check_out(out_bf16_rows, ref32, what="", scale=1.0):
+    """Asserts the output tolerance; ``scale`` widens both bounds (only the
+    unfused ablation passes UNFUSED_SCALE)."""
     rel_fro, max_abs = errors(out_bf16_rows, ref32)
     assert np.all(np.isfinite(out_bf16_rows.float().cpu().numpy())), f"{what}: non-finite output"
-    assert rel_fro <= REL_FRO_TOL, f"{what}: rel-Frobenius {rel_fro:.3e}"
-    assert max_abs <= MAX_ABS_TOL, f"{what}: max-abs/RMS {max_abs:.3e}"
+    assert rel_fro <= REL_FRO_TOL * scale, f"{what}: rel-Frobenius {rel_fro:.3e}"
+    assert max_abs <= MAX_ABS_TOL * scale, f"{what}: max-abs/RMS {max_abs:.3e}"
     return rel_fro, max_abs

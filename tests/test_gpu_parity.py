@@ -199,6 +199,17 @@ def test_forward_routing_and_gather_paths(bm, routing, gather):
     assert torch.equal(out.view(torch.int16), base.view(torch.int16))
 
 
+@pytest.mark.parametrize("gather", [1, 2])
+@pytest.mark.parametrize("bm", [16, 64, 128, 192])
+def test_forward_unfused_swiglu_ablation(bm, gather):
+    """The unfused SwiGLU (gate GEMM, up GEMM, activation kernel) against the
+    oracle, within the ablation's bound (bf16 gate and up products)."""
+    cfg, x, lg, wgu, wd, ref = _mid_case()
+    out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm, gather_mode=gather,
+                          unfused_swiglu=1)
+    parity.check_out(out, ref, f"unfused bm={bm} gather={gather}", scale=parity.UNFUSED_SCALE)
+
+
 def test_forward_hot_expert_many_blocks():
     """All tokens pick expert 1 first: 300 rows of one expert, 10 blocks."""
     gen = torch.Generator().manual_seed(3)
@@ -239,6 +250,22 @@ def test_forward_deterministic_and_stream():
 
 FULL = ["mixtral_128", "mixtral_256", "mixtral_512", "qwen2_128", "qwen2_256", "qwen2_512",
         "skewed_128", "skewed_256", "skewed_512", "dsv3_512", "dsv3_4096"]
+
+
+@pytest.mark.parametrize("name", ["mixtral_512", "dsv3_512", "qwen2_128"])
+def test_forward_unfused_full_size_sampled(name):
+    """The unfused ablation at full workload sizes, as the benchmark runs it."""
+    cfg = synth.CONFIGS[name]
+    x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)
+    out = moe.moe_forward(x, lg, wgu, wd, cfg.top_k, cfg.renormalize, score=cfg.score,
+                          unfused_swiglu=1)
+    rng = np.random.default_rng(len(name) + 1)
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 4, replace=False)]))
+    ref = parity.oracle_out(x, lg, wgu, wd, cfg.top_k, cfg.score, cfg.renormalize, tokens=toks)
+    parity.check_out(out[torch.from_numpy(toks).long().to(DEV)], ref, name + " unfused",
+                     scale=parity.UNFUSED_SCALE)
+    del x, lg, wgu, wd, out
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name", FULL)
