@@ -331,8 +331,9 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU's clocks settle within ~20 forward passes of sustained load
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="mixtral_512")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--profile", action="store_true")

@@ -42,6 +42,7 @@ namespace moe {
 namespace {
 
 constexpr int kBK = 64;               // K per pipeline step (two 32-wide MFMA chunks)
+constexpr int kXcds = 8;              // accelerator complex dies of an MI355X
 constexpr int kLdsStride = kBK + 8;   // bf16 per LDS row: 144 bytes, conflict-free reads
 
 // Wait for this wave's LDS traffic, then a workgroup barrier.  Unlike
@@ -78,15 +79,27 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
     const int32_t* __restrict__ offsets, void* __restrict__ out, int A, int N, int K, int ksplit,
     int tiles_per_block, int rotate, const int32_t* __restrict__ gather_perm, int gather_k,
-    int x_rows) {
+    int x_rows, int xcd_group) {
   using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   constexpr int MT = G::kMT, NG = G::kNG, XPT = G::kXPerThread;
   static_assert(PF >= 2, "the activation stage is issued PF-1 steps ahead");
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kLdsStride];
 
-  const int b = blockIdx.x / tiles_per_block;
+  // Workgroup -> (block, tile).  Workgroups are dispatched to the XCDs
+  // round-robin (workgroup i to XCD i % kXcds).  With xcd_group, the real
+  // workgroups (nb * tiles_per_block of the device-built schedule, rounded
+  // up to kXcds) are renumbered so that each XCD runs one contiguous range
+  // of (block, tile) ids: the tiles of a block then share that XCD's L2 for
+  // the block's activation rows instead of fetching them once per XCD.
+  int wg = blockIdx.x;
+  if (xcd_group) {
+    const int r8 = (nb_dev[0] * tiles_per_block + kXcds - 1) / kXcds * kXcds;
+    if (wg >= r8) return;
+    wg = (wg % kXcds) * (r8 / kXcds) + wg / kXcds;
+  }
+  const int b = wg / tiles_per_block;
   if (b >= nb_dev[0]) return;  // beyond the schedule built on the device
-  const int rem = blockIdx.x - b * tiles_per_block;
+  const int rem = wg - b * tiles_per_block;
   const int e = blocks[2 * b];
   const int r0 = blocks[2 * b + 1];
   const int rows = min(BM, offsets[e + 1] - r0);
@@ -310,7 +323,7 @@ template <int BM, int NWT, int WAVES, int PF, int MODE>
 hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride, const int32_t* blocks,
                       const int32_t* nb, const int32_t* offsets, void* out, int A, int N, int K,
                       int split, int ksplit, int nb_max, int rotate, const int32_t* gather_perm,
-                      int gather_k, int x_rows, hipStream_t s) {
+                      int gather_k, int x_rows, int xcd_group, hipStream_t s) {
   using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
   const int tiles_per_block = n_tiles * split;
@@ -318,7 +331,7 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   grouped_gemm_kernel<BM, NWT, WAVES, PF, MODE><<<(unsigned)grid, G::kThreads, 0, s>>>(
       X, W, w_estride, blocks, nb, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
-      gather_perm, gather_k, x_rows);
+      gather_perm, gather_k, x_rows, xcd_group);
   return hipGetLastError();
 }
 
@@ -358,12 +371,12 @@ int down_tile_cols(int bm, int variant) {
 hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t* gather_perm,
                           int k, int T, const uint16_t* w_gate_up, const int32_t* blocks,
                           const int32_t* nb, const int32_t* offsets, uint16_t* h, int A, int d,
-                          int ffn, int nb_max, int rotate, hipStream_t s) {
+                          int ffn, int nb_max, int rotate, int xcd_group, hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && variant == V)                                                                \
     return launch_cfg<BM, NWT, WV, PF, kOutSwiGLU>(x, w_gate_up, 2LL * ffn * d, blocks, nb,      \
                                                    offsets, h, A, ffn, d, 1, d, nb_max, rotate,  \
-                                                   gather_perm, k, T, s);
+                                                   gather_perm, k, T, xcd_group, s);
   MOE_GU_CFGS(X)
 #undef X
   return hipErrorInvalidValue;
@@ -372,12 +385,13 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
 hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w_down,
                        const int32_t* blocks, const int32_t* nb, const int32_t* offsets, float* y,
                        int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
-                       hipStream_t s) {
+                       int xcd_group, hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && V == variant)                                                                      \
     return launch_cfg<BM, NWT, WV, PF, kOutF32Parts>(h, w_down, (long long)d * ffn, blocks, nb,  \
                                                      offsets, y, A, d, ffn, split, ksplit,       \
-                                                     nb_max, rotate, nullptr, 1, A, s);
+                                                     nb_max, rotate, nullptr, 1, A, xcd_group,   \
+                                                     s);
   MOE_DN_CFGS(X)
 #undef X
   return hipErrorInvalidValue;
@@ -386,13 +400,13 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
 hipError_t launch_proj_bf16(int bm, const uint16_t* x, const int32_t* gather_perm, int k, int T,
                             const uint16_t* w, long long w_estride, const int32_t* blocks,
                             const int32_t* nb, const int32_t* offsets, uint16_t* out, int A, int d,
-                            int ffn, int nb_max, int rotate, hipStream_t s) {
+                            int ffn, int nb_max, int rotate, int xcd_group, hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                   \
   if constexpr (V == 0) {                                                                       \
     if (bm == BM)                                                                               \
       return launch_cfg<BM, NWT, WV, PF, kOutBF16>(x, w, w_estride, blocks, nb, offsets, out, A, \
                                                    ffn, d, 1, d, nb_max, rotate, gather_perm, k, \
-                                                   T, s);                                       \
+                                                   T, xcd_group, s);                            \
   }
   MOE_GU_CFGS(X)
 #undef X

@@ -32,6 +32,7 @@ struct Plan {
   int gu_variant; // tile variant of the fused gate/up GEMM
   int dn_variant; // tile variant of the down GEMM
   int gu_rotate;  // rotate the K-step start per workgroup (fused gate/up GEMM)
+  int gu_xcd, dn_xcd;  // group each block's workgroups on one XCD (see the GEMM kernel)
   int dn_rotate;  // same for the down GEMM
   int small_routing;  // one-workgroup routing kernel instead of three launches
   int gather_in_gemm; // the fused gate/up GEMM reads token rows through perm
@@ -84,7 +85,7 @@ hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int A, int d, i
 hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t* gather_perm,
                           int k, int T, const uint16_t* w_gate_up, const int32_t* blocks,
                           const int32_t* nb, const int32_t* offsets, uint16_t* h, int A, int d,
-                          int ffn, int nb_max, int rotate, hipStream_t s);
+                          int ffn, int nb_max, int rotate, int xcd_group, hipStream_t s);
 
 // One projection of the unfused SwiGLU: out[A, ffn] = bf16(X w[e]^T) per
 // block, w[e] = w + e * w_estride elements (ffn rows of d); X as for
@@ -92,7 +93,7 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
 hipError_t launch_proj_bf16(int bm, const uint16_t* x, const int32_t* gather_perm, int k, int T,
                             const uint16_t* w, long long w_estride, const int32_t* blocks,
                             const int32_t* nb, const int32_t* offsets, uint16_t* out, int A, int d,
-                            int ffn, int nb_max, int rotate, hipStream_t s);
+                            int ffn, int nb_max, int rotate, int xcd_group, hipStream_t s);
 
 // h = bf16(silu(g) * u) over n elements (n % 8 == 0).
 hipError_t launch_swiglu_act(const uint16_t* g, const uint16_t* u, uint16_t* h, long long n,
@@ -102,7 +103,7 @@ hipError_t launch_swiglu_act(const uint16_t* g, const uint16_t* u, uint16_t* h, 
 hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w_down,
                        const int32_t* blocks, const int32_t* nb, const int32_t* offsets, float* y,
                        int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
-                       hipStream_t s);
+                       int xcd_group, hipStream_t s);
 
 // Weighted combination: out[t] = bf16(sum_j w[t,j] * sum_s y[s, inv[t*k+j]]).
 hipError_t launch_combine(const float* y, int split, int A, int d, const int32_t* inv,

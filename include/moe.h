@@ -113,6 +113,12 @@ typedef struct moe_options {
      * by 4*A*ffn bytes; results differ from the fused path by the two extra
      * bf16 roundings. */
     int unfused_swiglu;
+    /* Workgroup order of the GEMMs.  0 = automatic (grouped when about 128
+     * or more schedule blocks are expected), 1 = plain (workgroup i
+     * takes block i / tiles, tile i % tiles), 2 = grouped by XCD: each of
+     * the 8 XCDs runs a contiguous range of (block, tile) ids, so a block's
+     * rows are fetched into one L2.  Same results either way. */
+    int xcd_order;
     /* NULL, or 7 hipEvent_t handles created by the caller (for instance
      * with moe_timer_create).  events[0] is recorded on the stream before
      * the first kernel and events[i] right after kernel i (1 route, 2

@@ -65,8 +65,9 @@ def test_workspace_size_checks():
     assert moe.lib().moe_workspace_size(4, 64, 64, 4, 2, None) == NULL
 
 
-def _o(bm=0, split=0, variant=0, rotate=0, routing=0, gather=0, unfused=0):
-    return ctypes.byref(_lib.MoeOptions(bm, split, variant, rotate, routing, gather, unfused, None))
+def _o(bm=0, split=0, variant=0, rotate=0, routing=0, gather=0, unfused=0, xcd=0):
+    return ctypes.byref(_lib.MoeOptions(bm, split, variant, rotate, routing, gather, unfused, xcd,
+                                        None))
 
 
 def test_options_checks():
@@ -102,7 +103,7 @@ def test_routing_and_gather_options():
     assert _ws(65536, 16384, 512, 8, 1, _o(gather=1))[0] == UNSUP
     assert _ws(65536, 16384, 512, 8, 1, _o(gather=2))[0] == OK
     # the unfused SwiGLU ablation keeps gate and up products: 2 * A*ffn*2 bytes more
-    for bad in (_o(unfused=2), _o(unfused=-1)):
+    for bad in (_o(unfused=2), _o(unfused=-1), _o(xcd=3), _o(xcd=-1)):
         assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
     u0 = moe.moe_workspace_size(512, 4096, 14336, 8, 2)
     u1 = moe.moe_workspace_size(512, 4096, 14336, 8, 2, unfused_swiglu=1)

@@ -210,6 +210,19 @@ def test_forward_unfused_swiglu_ablation(bm, gather):
     parity.check_out(out, ref, f"unfused bm={bm} gather={gather}", scale=parity.UNFUSED_SCALE)
 
 
+@pytest.mark.parametrize("xcd", [1, 2])
+@pytest.mark.parametrize("bm,split", [(16, 2), (64, 1), (192, 3)])
+def test_forward_xcd_order(bm, split, xcd):
+    """Both workgroup orders give the oracle's result, and the same bytes."""
+    cfg, x, lg, wgu, wd, ref = _mid_case()
+    out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm, split_k=split,
+                          xcd_order=xcd)
+    parity.check_out(out, ref, f"xcd={xcd} bm={bm}")
+    base = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm, split_k=split,
+                           xcd_order=1)
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+
+
 def test_forward_hot_expert_many_blocks():
     """All tokens pick expert 1 first: 300 rows of one expert, 10 blocks."""
     gen = torch.Generator().manual_seed(3)
