@@ -83,14 +83,13 @@ def router_gemm(cfg, x, seed, steps, stream):
     lg = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=x.device)
     for _ in range(3):
         moe.moe_router_logits(x, wr, out=lg, stream=stream)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    ev = [(moe.Timer(), moe.Timer()) for _ in range(steps)]
     for a, b in ev:
         a.record(stream)
         moe.moe_router_logits(x, wr, out=lg, stream=stream)
         b.record(stream)
     torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    ms = sum(a.elapsed_ms(b) for a, b in ev) / steps
     nbytes = 2.0 * cfg.T * cfg.d + 2.0 * cfg.E * cfg.d + 4.0 * cfg.T * cfg.E
     gbs = nbytes / (ms * 1e-3) / 1e9
     return {"kernel": "router_logits (moe_router_logits, upstream of the timed step)",

@@ -45,6 +45,7 @@ SIGNATURES = {
                        ctypes.POINTER(_I), _P, _SZ, _P]),
     "moe_timer_create": (_I, [ctypes.POINTER(_P)]),
     "moe_timer_destroy": (_I, [_P]),
+    "moe_timer_record": (_I, [_P, _P]),
     "moe_timer_elapsed_ms": (_I, [_P, _P, ctypes.POINTER(ctypes.c_float)]),
 }
 
@@ -302,6 +303,11 @@ class Timer:
         h = _P(None)
         _check("moe_timer_create", lib().moe_timer_create(ctypes.byref(h)))
         self.handle = h.value
+
+    def record(self, stream=None):
+        """Records the event on ``stream`` (torch's current stream if None)."""
+        s = torch.cuda.current_stream() if stream is None else stream
+        _check("moe_timer_record", lib().moe_timer_record(self.handle, s.cuda_stream))
 
     def elapsed_ms(self, stop: "Timer") -> float:
         ms = ctypes.c_float(0.0)

@@ -520,6 +520,14 @@ int moe_timer_create(void** event) {
   return MOE_OK;
 }
 
+int moe_timer_record(void* event, void* hip_stream) {
+  if (!event) return MOE_ERR_NULL;
+  return hipEventRecord(static_cast<hipEvent_t>(event), static_cast<hipStream_t>(hip_stream)) ==
+                 hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
 int moe_timer_destroy(void* event) {
   if (!event) return MOE_ERR_NULL;
   return hipEventDestroy(static_cast<hipEvent_t>(event)) == hipSuccess ? MOE_OK : MOE_ERR_HIP;

@@ -259,6 +259,9 @@ int moe_route(const float *router_logits, int T, int E, int top_k, int renormali
  * visible to the host.  Each returns a moe_status. */
 int moe_timer_create(void **event);
 int moe_timer_destroy(void *event);
+/* Records `event` on hip_stream (NULL = the default stream), for timing a
+ * call that takes no stage events (e.g. moe_router_logits). */
+int moe_timer_record(void *event, void *hip_stream);
 /* Milliseconds between two recorded events; waits for `stop` to complete. */
 int moe_timer_elapsed_ms(void *start, void *stop, float *ms);
 

@@ -252,6 +252,7 @@ def test_timer_argument_checks():
     assert L.moe_timer_create(None) == NULL
     assert L.moe_timer_destroy(None) == NULL
     assert L.moe_timer_elapsed_ms(None, None, None) == NULL
+    assert L.moe_timer_record(None, None) == NULL
 
 
 def test_product_path_never_imports_the_oracle():
