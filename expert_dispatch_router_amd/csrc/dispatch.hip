@@ -129,6 +129,25 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict_
   for (int c = threadIdx.x; c < d / 8; c += 256) o[c] = s[c];
 }
 
+// Tiled gather for the GEMM's activation loads: sorted row p of x_perm is
+// x[perm[p] / k], stored in K-step tiles -- the 64 columns [64 s, 64 s + 64)
+// of the 16 rows of group G = p / 16 are 2 KiB at (G * d/64 + s) * 2048,
+// row p % 16 at +128 * (p % 16).  One step of a block then reads whole
+// 2 KiB pieces instead of 128 bytes from rows 2*d bytes apart (which, for
+// power-of-two d, all fall on the same memory channel).
+__global__ __launch_bounds__(256) void gather_tiled_kernel(const uint16_t* __restrict__ x,
+                                                           const int32_t* __restrict__ perm, int d,
+                                                           int k, uint16_t* __restrict__ x_t) {
+  const int p = blockIdx.x;
+  const int src = perm[p] / k;
+  const uint4* s = reinterpret_cast<const uint4*>(x + (size_t)src * d);
+  const size_t g0 = (size_t)(p >> 4) * (d / 64) * 1024 + (p & 15) * 64;  // elements
+  for (int c = threadIdx.x; c < d / 8; c += 256) {
+    const int col = c * 8;
+    *reinterpret_cast<uint4*>(x_t + g0 + (size_t)(col >> 6) * 1024 + (col & 63)) = s[c];
+  }
+}
+
 // Small problems (T <= 1024 tokens, E <= 32 experts): the whole routing in
 // one workgroup of 1024 threads, thread t = token t.  Three launches (route,
 // histogram+scan+schedule, reorder) cost more than this work.
@@ -293,6 +312,13 @@ hipError_t launch_permute(const int32_t* ids, int A, int E, int nchunks, const i
 hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int A, int d, int k,
                          uint16_t* x_perm, hipStream_t s) {
   gather_kernel<<<A, 256, 0, s>>>(x, perm, d, k, x_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_tiled(const uint16_t* x, const int32_t* perm, int A, int d, int k,
+                               uint16_t* x_t, hipStream_t s) {
+  if (A <= 0) return hipSuccess;
+  gather_tiled_kernel<<<A, 256, 0, s>>>(x, perm, d, k, x_t);
   return hipGetLastError();
 }
 

@@ -68,18 +68,21 @@ struct Gemm {
   static constexpr int kTileCols = WAVES * NWT * 16;         // output columns per workgroup
   static constexpr int kXChunks = BM * (kBK / 8);            // 16-byte chunks per activation tile
   static constexpr int kXPerThread = (kXChunks + kThreads - 1) / kThreads;
+  // 4-wave, one-subtile tiles are sized for two workgroups per CU.
+  static constexpr int kMinBlocks = (WAVES == 4 && NWT == 1) ? 2 : 1;
   static_assert(BM % 16 == 0, "BM is a multiple of 16");
 };
 
 // X: activations [A, K] (sorted rows).  W: weights [E, NG*N, K].
 // out: K4 -> bf16 h [A, N];  K5 -> fp32 y [split, A, N].
 template <int BM, int NWT, int WAVES, int PF, int MODE>
-__global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
+__global__ __launch_bounds__(WAVES * 64, (Gemm<BM, NWT, WAVES, PF, MODE>::kMinBlocks))
+void grouped_gemm_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
     const int32_t* __restrict__ offsets, void* __restrict__ out, int A, int N, int K, int ksplit,
     int tiles_per_block, int rotate, const int32_t* __restrict__ gather_perm, int gather_k,
-    int x_rows, int xcd_group) {
+    int x_rows, int xcd_group, int x_tiled) {
   using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   constexpr int MT = G::kMT, NG = G::kNG, XPT = G::kXPerThread;
   static_assert(PF >= 2, "the activation stage is issued PF-1 steps ahead");
@@ -128,12 +131,17 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
       (void*)(W + (size_t)e * w_estride), (short)0, NG * N * K * 2, kRsrcWord3);
   // X rows: sorted rows r0 .. r0+rows-1 of X, or -- with gather_perm -- the
   // token rows x[perm[r0 + row] / gather_k] of the unsorted activations (the
-  // reorder's row gather folded into this load).  Rows past the block's end
-  // get an offset outside the descriptor's range and load as zeros.
+  // reorder's row gather folded into this load), or -- with x_tiled -- the
+  // sorted rows of X stored in K-step tiles: the 64-wide K step s of the
+  // 16-row group G is 2 KiB at ((G * K/64) + s) * 2048, row p % 16 at
+  // +128 * (p % 16).  Rows past the block's end get an offset outside the
+  // descriptor's range and load as zeros.
   const __amdgpu_buffer_rsrc_t xres =
-      gather_perm ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, x_rows * K * 2, kRsrcWord3)
-                  : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (size_t)r0 * K), (short)0,
-                                                      rows * K * 2, kRsrcWord3);
+      (gather_perm || x_tiled)
+          ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, x_rows * K * 2, kRsrcWord3)
+          : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (size_t)r0 * K), (short)0,
+                                              rows * K * 2, kRsrcWord3);
+  const int xstep = x_tiled ? 16 * kBK * 2 : kBK * 2;  // bytes between K steps of one row
   int woff[NG][NWT];
   bool jok[NWT];
 #pragma unroll
@@ -151,9 +159,16 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
   for (int q = 0; q < XPT; ++q) {
     const int c = (tid + q * G::kThreads) % G::kXChunks;
     const int row = c >> 3;
-    int src_row = row;
-    if (gather_perm) src_row = row < rows ? gather_perm[r0 + row] / gather_k : x_rows;
-    xoff[q] = (src_row * K + kb + (c & 7) * 8) * 2;
+    if (x_tiled) {
+      const int p = r0 + row;
+      xoff[q] = row < rows ? ((p >> 4) * (K / kBK) + kb / kBK) * (16 * kBK * 2) + (p & 15) * kBK * 2 +
+                                 (c & 7) * 16
+                           : x_rows * K * 2;
+    } else {
+      int src_row = row;
+      if (gather_perm) src_row = row < rows ? gather_perm[r0 + row] / gather_k : x_rows;
+      xoff[q] = (src_row * K + kb + (c & 7) * 8) * 2;
+    }
     xdst[q] = row * kLdsStride + (c & 7) * 8;
   }
 
@@ -170,20 +185,22 @@ __global__ __launch_bounds__(WAVES * 64) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < NWT; ++j) acc[g][mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K-step order: with `rotate`, every workgroup of schedule block b starts
-  // its reduction at a step derived from b and wraps around.  Workgroups
-  // walking K in lockstep all address the same memory channels at once;
-  // starting different blocks at different steps spreads them, while the
-  // column tiles of one block still read the same activation K-slice (so it
-  // stays shared in L2).  The order is fixed per block: results stay
-  // deterministic.
-  const int shift = rotate ? (int)(((unsigned)b * 2654435761u) % (unsigned)max(nks, 1)) : 0;
+  // K-step order: with `rotate` (1: per block, 2: per workgroup), a
+  // workgroup starts its reduction at a step derived from its block b (or
+  // its own id) and wraps around.  Workgroups walking K in lockstep address
+  // the same memory channels at once -- weight rows 2^n bytes apart share
+  // their low address bits -- and different starting steps spread them.
+  // Per block, the column tiles of one block still read the same activation
+  // K-slice at the same time (shared in L2); per workgroup spreads further.
+  // The order is fixed by (block, tile): results stay deterministic.
+  const unsigned rkey = rotate == 2 ? (unsigned)wg : (unsigned)b;
+  const int shift = rotate ? (int)((rkey * 2654435761u) % (unsigned)max(nks, 1)) : 0;
   auto step_of = [&](int ks) {
     const int p = ks + shift;
     return p >= nks ? p - nks : p;
   };
   auto load_x = [&](u32x4(&dst)[XPT], int ks) {
-    const int soff = step_of(ks) * kBK * 2;
+    const int soff = step_of(ks) * xstep;
 #pragma unroll
     for (int q = 0; q < XPT; ++q) dst[q] = buf_load16(xres, xoff[q], soff);
   };
@@ -323,7 +340,7 @@ template <int BM, int NWT, int WAVES, int PF, int MODE>
 hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride, const int32_t* blocks,
                       const int32_t* nb, const int32_t* offsets, void* out, int A, int N, int K,
                       int split, int ksplit, int nb_max, int rotate, const int32_t* gather_perm,
-                      int gather_k, int x_rows, int xcd_group, hipStream_t s) {
+                      int gather_k, int x_rows, int xcd_group, int x_tiled, hipStream_t s) {
   using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
   const int tiles_per_block = n_tiles * split;
@@ -331,24 +348,23 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   grouped_gemm_kernel<BM, NWT, WAVES, PF, MODE><<<(unsigned)grid, G::kThreads, 0, s>>>(
       X, W, w_estride, blocks, nb, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
-      gather_perm, gather_k, x_rows, xcd_group);
+      gather_perm, gather_k, x_rows, xcd_group, x_tiled);
   return hipGetLastError();
 }
 
 // Tile shapes: (variant, BM, NWT, waves, PF).  NWT*16 output columns per wave
 // (x2 rows for gate+up in K4), PF K steps of weight prefetch.  Chosen by
-// measurement on the MoE workload shapes.  Variant 1 of K4 at BM=64 is the
-// narrow tile for launches with few blocks; variant 1 of K4 at BM=192 is a
+// measurement on the MoE workload shapes.  K4 variant 1 at BM=64 and 128 is
+// the narrow tile for launches with few blocks; K4 variant 1 at BM=192 is a
 // 7-wave, 112-column tile (two waves on three SIMDs) whose tile count
 // divides evenly over the CUs where 128-column tiles leave a half-empty last
-// round; variant 1 of K5 at BM=192 runs two waves per SIMD for launches of
-// at most two rounds.
+// round.
 #define MOE_GU_CFGS(X) \
   X(0, 16, 4, 4, 2) X(0, 32, 4, 4, 2) X(0, 64, 4, 4, 3) X(1, 64, 2, 4, 4) X(0, 128, 1, 8, 3) \
-  X(1, 128, 1, 4, 4) X(0, 192, 2, 4, 3) X(1, 192, 1, 7, 3)
+  X(1, 128, 1, 4, 4) X(0, 192, 1, 8, 3) X(1, 192, 1, 7, 3)
 #define MOE_DN_CFGS(X) \
-  X(0, 16, 8, 4, 2) X(0, 32, 8, 4, 2) X(0, 64, 4, 4, 4) X(0, 128, 4, 4, 3) X(0, 192, 4, 4, 3) \
-  X(1, 192, 2, 8, 4)
+  X(0, 16, 8, 4, 2) X(0, 32, 8, 4, 2) X(0, 64, 4, 4, 4) X(0, 128, 4, 4, 3) X(1, 128, 2, 8, 3) \
+  X(0, 192, 2, 8, 3) X(1, 192, 4, 4, 3)
 
 }  // namespace
 
@@ -371,12 +387,14 @@ int down_tile_cols(int bm, int variant) {
 hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t* gather_perm,
                           int k, int T, const uint16_t* w_gate_up, const int32_t* blocks,
                           const int32_t* nb, const int32_t* offsets, uint16_t* h, int A, int d,
-                          int ffn, int nb_max, int rotate, int xcd_group, hipStream_t s) {
+                          int ffn, int nb_max, int rotate, int xcd_group, int x_tiled,
+                          hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && variant == V)                                                                \
     return launch_cfg<BM, NWT, WV, PF, kOutSwiGLU>(x, w_gate_up, 2LL * ffn * d, blocks, nb,      \
                                                    offsets, h, A, ffn, d, 1, d, nb_max, rotate,  \
-                                                   gather_perm, k, T, xcd_group, s);
+                                                   gather_perm, k, x_tiled ? (A + 15) / 16 * 16 : T, \
+                                                   xcd_group, x_tiled, s);
   MOE_GU_CFGS(X)
 #undef X
   return hipErrorInvalidValue;
@@ -390,7 +408,7 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
   if (bm == BM && V == variant)                                                                      \
     return launch_cfg<BM, NWT, WV, PF, kOutF32Parts>(h, w_down, (long long)d * ffn, blocks, nb,  \
                                                      offsets, y, A, d, ffn, split, ksplit,       \
-                                                     nb_max, rotate, nullptr, 1, A, xcd_group,   \
+                                                     nb_max, rotate, nullptr, 1, A, xcd_group, 0,\
                                                      s);
   MOE_DN_CFGS(X)
 #undef X
@@ -400,13 +418,15 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
 hipError_t launch_proj_bf16(int bm, const uint16_t* x, const int32_t* gather_perm, int k, int T,
                             const uint16_t* w, long long w_estride, const int32_t* blocks,
                             const int32_t* nb, const int32_t* offsets, uint16_t* out, int A, int d,
-                            int ffn, int nb_max, int rotate, int xcd_group, hipStream_t s) {
+                            int ffn, int nb_max, int rotate, int xcd_group, int x_tiled,
+                            hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                   \
   if constexpr (V == 0) {                                                                       \
     if (bm == BM)                                                                               \
       return launch_cfg<BM, NWT, WV, PF, kOutBF16>(x, w, w_estride, blocks, nb, offsets, out, A, \
                                                    ffn, d, 1, d, nb_max, rotate, gather_perm, k, \
-                                                   T, xcd_group, s);                            \
+                                                   x_tiled ? (A + 15) / 16 * 16 : T, xcd_group,  \
+                                                   x_tiled, s);                                 \
   }
   MOE_GU_CFGS(X)
 #undef X

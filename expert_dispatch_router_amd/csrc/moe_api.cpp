@@ -49,6 +49,8 @@ int check_paths(int T, int d, int E, int k, const moe_options* opt) {
   if (opt->routing_kernels == 1 && !small_routing_fits(T, E, k)) return MOE_ERR_UNSUPPORTED;
   if (opt->gather_mode == 1 && (long long)T * d * 2 + 2LL * d >= (1LL << 31))
     return MOE_ERR_UNSUPPORTED;
+  if (opt->gather_mode == 3 && ((long long)T * k + 16) * d * 2 >= (1LL << 31))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -56,11 +58,16 @@ int check_options(const moe_options* opt) {
   if (!opt) return MOE_OK;
   if (opt->block_rows != 0 && !is_block_rows(opt->block_rows)) return MOE_ERR_UNSUPPORTED;
   if (opt->split_k < 0 || opt->split_k > kMaxSplit) return MOE_ERR_UNSUPPORTED;
-  if (opt->tile_variant < 0 || opt->rotate < 0 || opt->rotate > 2) return MOE_ERR_UNSUPPORTED;
+  if (opt->tile_variant < 0 || opt->rotate < 0 || opt->rotate > 3) return MOE_ERR_UNSUPPORTED;
   if (opt->routing_kernels < 0 || opt->routing_kernels > 2) return MOE_ERR_UNSUPPORTED;
-  if (opt->gather_mode < 0 || opt->gather_mode > 2) return MOE_ERR_UNSUPPORTED;
+  if (opt->gather_mode < 0 || opt->gather_mode > 3) return MOE_ERR_UNSUPPORTED;
   if (opt->unfused_swiglu < 0 || opt->unfused_swiglu > 1) return MOE_ERR_UNSUPPORTED;
   if (opt->xcd_order < 0 || opt->xcd_order > 2) return MOE_ERR_UNSUPPORTED;
+  if (opt->down_variant < 0) return MOE_ERR_UNSUPPORTED;
+  if (opt->down_variant > 0) {
+    const int bm = opt->block_rows;
+    if (bm == 0 || down_tile_cols(bm, opt->down_variant - 1) == 0) return MOE_ERR_UNSUPPORTED;
+  }
   if (opt->tile_variant > 0) {
     const int bm = opt->block_rows;
     if (bm == 0 || gate_up_tile_cols(bm, opt->tile_variant - 1) == 0) return MOE_ERR_UNSUPPORTED;
@@ -135,13 +142,6 @@ int auto_gu_variant(int A, int E, int ffn, int bm) {
   return 0;
 }
 
-// Tile variant of the down GEMM: at BM = 192, two waves per SIMD when the
-// launch is at most two rounds of workgroups.
-int auto_dn_variant(int A, int E, int d, int bm, int split) {
-  if (bm != 192) return 0;
-  return est_workgroups(A, E, bm, d, down_tile_cols(192, 1)) * split <= 512 ? 1 : 0;
-}
-
 // XCD-grouped workgroup order: measured 1-2% faster when a launch has many
 // schedule blocks (each XCD then streams its own range of experts and keeps
 // their activation rows in its L2), and neutral to a few percent slower with
@@ -154,7 +154,7 @@ bool auto_xcd_order(int A, int E, int bm) {
 // Rotating each block's K start (see the GEMM kernel) was measured faster or
 // equal on every MoE workload shape, so it is on unless the caller turns it
 // off.
-bool auto_rotate(int) { return true; }
+int auto_rotate(int) { return 1; }
 
 void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan* p) {
   memset(p, 0, sizeof(*p));
@@ -175,6 +175,7 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   const int gm = opt ? opt->gather_mode : 0;
   const bool x_fits = (long long)T * d * 2 + 2LL * d < (1LL << 31);
   p->gather_in_gemm = gm == 1 || (gm == 0 && x_fits);
+  p->x_tiled = gm == 3;
   p->unfused = opt ? opt->unfused_swiglu : 0;
   if (ffn > 0) {
     int s = (opt && opt->split_k) ? opt->split_k : auto_split(A, E, d, ffn, p->bm);
@@ -184,10 +185,11 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     p->split = (ksteps + per - 1) / per;  // every part has at least one K step
     p->gu_variant = (opt && opt->tile_variant) ? opt->tile_variant - 1
                                                : auto_gu_variant(A, E, ffn, p->bm);
-    p->dn_variant = auto_dn_variant(A, E, d, p->bm, p->split);
+    p->dn_variant = (opt && opt->down_variant) ? opt->down_variant - 1 : 0;
     const int rot = opt ? opt->rotate : 0;
-    p->gu_rotate = rot == 0 ? auto_rotate(d) : rot == 2;
-    p->dn_rotate = rot == 0 ? auto_rotate(ffn) : rot == 2;
+    // kernel values: 0 off, 1 per block, 2 per workgroup
+    p->gu_rotate = rot == 0 ? auto_rotate(d) : rot - 1;
+    p->dn_rotate = rot == 0 ? auto_rotate(ffn) : rot - 1;
     const int xo = opt ? opt->xcd_order : 0;
     p->gu_xcd = p->dn_xcd = xo == 0 ? auto_xcd_order(A, E, p->bm) : xo == 2;
   }
@@ -209,7 +211,7 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->o_blocks = seg((size_t)p->nb_max * 2 * 4);
   p->o_nb = seg(4);
   p->route_bytes = o;
-  p->o_xperm = seg(p->gather_in_gemm ? 0 : (size_t)A * d * 2);
+  p->o_xperm = seg(p->gather_in_gemm ? 0 : (size_t)(A + 15) / 16 * 16 * d * 2);
   p->o_h = seg((size_t)A * ffn * 2);
   p->o_g = seg(p->unfused ? (size_t)A * ffn * 2 : 0);
   p->o_u = seg(p->unfused ? (size_t)A * ffn * 2 : 0);
@@ -285,7 +287,10 @@ int forward_from_logits(const uint16_t* x, const float* router_logits, const uin
   uint16_t* x_perm = at<uint16_t>(workspace, p.o_xperm);
   uint16_t* h = at<uint16_t>(workspace, p.o_h);
   float* y = at<float>(workspace, p.o_y);
-  if (!p.gather_in_gemm) MOE_TRY_HIP(launch_gather(x, perm, p.A, d, top_k, x_perm, s));
+  if (p.x_tiled)
+    MOE_TRY_HIP(launch_gather_tiled(x, perm, p.A, d, top_k, x_perm, s));
+  else if (!p.gather_in_gemm)
+    MOE_TRY_HIP(launch_gather(x, perm, p.A, d, top_k, x_perm, s));
   MOE_TRY(record(opt, 3, s));
   const uint16_t* X = p.gather_in_gemm ? x : x_perm;
   const int32_t* gperm = p.gather_in_gemm ? perm : nullptr;
@@ -296,14 +301,16 @@ int forward_from_logits(const uint16_t* x, const float* router_logits, const uin
     uint16_t* u = at<uint16_t>(workspace, p.o_u);
     const long long estride = 2LL * ffn * d;
     MOE_TRY_HIP(launch_proj_bf16(p.bm, X, gperm, top_k, T, W_gate_up, estride, blocks, nb,
-                                 offsets, g, p.A, d, ffn, p.nb_max, p.gu_rotate, p.gu_xcd, s));
+                                 offsets, g, p.A, d, ffn, p.nb_max, p.gu_rotate, p.gu_xcd,
+                                 p.x_tiled, s));
     MOE_TRY_HIP(launch_proj_bf16(p.bm, X, gperm, top_k, T, W_gate_up + (size_t)ffn * d, estride,
                                  blocks, nb, offsets, u, p.A, d, ffn, p.nb_max, p.gu_rotate,
-                                 p.gu_xcd, s));
+                                 p.gu_xcd, p.x_tiled, s));
     MOE_TRY_HIP(launch_swiglu_act(g, u, h, (long long)p.A * ffn, s));
   } else {
     MOE_TRY_HIP(launch_gate_up(p.bm, p.gu_variant, X, gperm, top_k, T, W_gate_up, blocks, nb,
-                               offsets, h, p.A, d, ffn, p.nb_max, p.gu_rotate, p.gu_xcd, s));
+                               offsets, h, p.A, d, ffn, p.nb_max, p.gu_rotate, p.gu_xcd,
+                               p.x_tiled, s));
   }
   MOE_TRY(record(opt, 4, s));
   MOE_TRY_HIP(launch_down(p.bm, p.dn_variant, h, W_down, blocks, nb, offsets, y, p.A, d, ffn,

@@ -36,6 +36,7 @@ struct Plan {
   int dn_rotate;  // same for the down GEMM
   int small_routing;  // one-workgroup routing kernel instead of three launches
   int gather_in_gemm; // the fused gate/up GEMM reads token rows through perm
+  int x_tiled;        // else x_perm is written in K-step tiles (gather mode 3)
   int unfused;        // SwiGLU as gate GEMM, up GEMM and activation (ablation)
   // byte offsets into the workspace (256-byte aligned)
   size_t o_ids, o_w, o_counts, o_offsets, o_ccnt, o_cbase, o_perm, o_inv, o_blocks, o_nb;
@@ -79,13 +80,19 @@ hipError_t launch_route_dispatch_small(const float* logits, int T, int E, int k,
 hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int A, int d, int k,
                          uint16_t* x_perm, hipStream_t s);
 
+// x_perm in K-step tiles ([ceil(A/16)] groups x [d/64] steps x 16 rows x 64
+// columns), the layout the GEMM reads with x_tiled.
+hipError_t launch_gather_tiled(const uint16_t* x, const int32_t* perm, int A, int d, int k,
+                               uint16_t* x_t, hipStream_t s);
+
 // Fused gate/up SwiGLU grouped GEMM: h[A, F] = silu(X Wg^T) * (X Wu^T) per
 // block.  X is x_perm [A, d] when gather_perm is null, else the token rows
 // x [T, d] read through gather_perm (row p is x[gather_perm[p] / k]).
 hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t* gather_perm,
                           int k, int T, const uint16_t* w_gate_up, const int32_t* blocks,
                           const int32_t* nb, const int32_t* offsets, uint16_t* h, int A, int d,
-                          int ffn, int nb_max, int rotate, int xcd_group, hipStream_t s);
+                          int ffn, int nb_max, int rotate, int xcd_group, int x_tiled,
+                          hipStream_t s);
 
 // One projection of the unfused SwiGLU: out[A, ffn] = bf16(X w[e]^T) per
 // block, w[e] = w + e * w_estride elements (ffn rows of d); X as for
@@ -93,7 +100,8 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
 hipError_t launch_proj_bf16(int bm, const uint16_t* x, const int32_t* gather_perm, int k, int T,
                             const uint16_t* w, long long w_estride, const int32_t* blocks,
                             const int32_t* nb, const int32_t* offsets, uint16_t* out, int A, int d,
-                            int ffn, int nb_max, int rotate, int xcd_group, hipStream_t s);
+                            int ffn, int nb_max, int rotate, int xcd_group, int x_tiled,
+                            hipStream_t s);
 
 // h = bf16(silu(g) * u) over n elements (n % 8 == 0).
 hipError_t launch_swiglu_act(const uint16_t* g, const uint16_t* u, uint16_t* h, long long n,

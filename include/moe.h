@@ -87,12 +87,18 @@ typedef struct moe_options {
      * compiled variant k-1 for the chosen block_rows (which must then be set
      * explicitly).  BM = 64 has variants 0 (256 columns per workgroup) and 1
      * (128 columns); BM = 128 has variants 0 (128 columns, 8 waves) and 1
-     * (64 columns); BM = 192 has variants 0 (128 columns) and 1 (112
-     * columns); every other BM has variant 0 only. */
+     * (64 columns); BM = 192 has variants 0 (128 columns, 8 waves) and 1
+     * (112 columns, 7 waves); every other BM has variant 0 only. */
     int tile_variant;
-    /* K-start rotation of the GEMMs: each schedule block starts its
-     * reduction at its own step.  0 = automatic (on), 1 = off, 2 = on.
-     * Results are deterministic either way; rounding differs slightly. */
+    /* Tile variant of the down GEMM, like tile_variant (block_rows must be
+     * set).  BM = 128 and 192 have variants 0 and 1 (256 columns per
+     * workgroup: 4 waves of 64 and 8 waves of 32 at BM = 128, the reverse
+     * at BM = 192); every other BM has variant 0 only.  0 = automatic. */
+    int down_variant;
+    /* K-start rotation of the GEMMs: a workgroup starts its reduction at a
+     * step derived from its schedule block (2) or from its own id (3), and
+     * wraps around.  0 = automatic (per block), 1 = off.  Results are
+     * deterministic either way; rounding differs slightly. */
     int rotate;
     /* Routing kernels.  0 = automatic: one workgroup does the route,
      * histogram, scan, schedule and reorder when T <= 1024, E <= 32 and
@@ -103,7 +109,10 @@ typedef struct moe_options {
     /* Row gather of moe_forward.  0 = automatic (1 when 2*T*d < 2^31);
      * 1 = the fused gate/up GEMM reads each sorted row straight from x
      * through perm (no x_perm buffer); 2 = a gather kernel writes x_perm to
-     * the workspace first.  Same results either way. */
+     * the workspace first; 3 = as 2, with x_perm stored in K-step tiles
+     * (for each group of 16 sorted rows, each 64-column step is 2 KiB
+     * contiguous), so the GEMM's per-step activation reads are contiguous.
+     * Same results either way. */
     int gather_mode;
     /* SwiGLU ablation.  0 = fused (default): gate and up products from one
      * shared activation tile, SiLU and the product in registers, h written

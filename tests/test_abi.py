@@ -65,13 +65,13 @@ def test_workspace_size_checks():
     assert moe.lib().moe_workspace_size(4, 64, 64, 4, 2, None) == NULL
 
 
-def _o(bm=0, split=0, variant=0, rotate=0, routing=0, gather=0, unfused=0, xcd=0):
-    return ctypes.byref(_lib.MoeOptions(bm, split, variant, rotate, routing, gather, unfused, xcd,
-                                        None))
+def _o(bm=0, split=0, variant=0, rotate=0, routing=0, gather=0, unfused=0, xcd=0, dvar=0):
+    return ctypes.byref(_lib.MoeOptions(bm, split, variant, dvar, rotate, routing, gather, unfused,
+                                        xcd, None))
 
 
 def test_options_checks():
-    for bad in (_o(8), _o(0, 9), _o(0, -1), _o(0, 0, 1), _o(32, 0, 2), _o(64, 0, 3), _o(192, 0, 3), _o(0, 0, 0, 3),
+    for bad in (_o(8), _o(0, 9), _o(0, -1), _o(0, 0, 1), _o(32, 0, 2), _o(64, 0, 3), _o(192, 0, 3), _o(0, 0, 0, 4),
                 _o(0, 0, -1), _o(0, 0, 0, -1)):
         assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
     for bm in (16, 32, 64, 128, 192):
@@ -82,15 +82,15 @@ def test_options_checks():
     assert _ws(64, 256, 512, 8, 2, _o(192, 0, 2))[0] == OK
     assert _ws(64, 256, 512, 8, 2, _o(128, 0, 2))[0] == OK
     assert _ws(64, 256, 512, 8, 2, _o(128, 0, 3))[0] == UNSUP
-    for r in (1, 2):
+    for r in (1, 2, 3):
         assert _ws(64, 256, 512, 8, 2, _o(0, 0, 0, r))[0] == OK
 
 
 def test_routing_and_gather_options():
-    for bad in (_o(routing=3), _o(routing=-1), _o(gather=3), _o(gather=-1)):
+    for bad in (_o(routing=3), _o(routing=-1), _o(gather=4), _o(gather=-1)):
         assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
     for r in (0, 1, 2):
-        for g in (0, 1, 2):
+        for g in (0, 1, 2, 3):
             assert _ws(64, 256, 512, 8, 2, _o(routing=r, gather=g))[0] == OK
     # the one-workgroup routing kernel: one token per thread, at most 32 experts
     assert _ws(1024, 256, 512, 32, 16, _o(routing=1))[0] == OK
@@ -102,8 +102,11 @@ def test_routing_and_gather_options():
     # gather inside the GEMM addresses x with 32-bit byte offsets
     assert _ws(65536, 16384, 512, 8, 1, _o(gather=1))[0] == UNSUP
     assert _ws(65536, 16384, 512, 8, 1, _o(gather=2))[0] == OK
+    assert _ws(64, 256, 512, 8, 2, _o(192, dvar=2))[0] == OK
+    assert _ws(64, 256, 512, 8, 2, _o(64, dvar=1))[0] == OK
     # the unfused SwiGLU ablation keeps gate and up products: 2 * A*ffn*2 bytes more
-    for bad in (_o(unfused=2), _o(unfused=-1), _o(xcd=3), _o(xcd=-1)):
+    for bad in (_o(unfused=2), _o(unfused=-1), _o(xcd=3), _o(xcd=-1), _o(dvar=1), _o(dvar=-1),
+                _o(64, dvar=2), _o(192, dvar=3)):
         assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
     u0 = moe.moe_workspace_size(512, 4096, 14336, 8, 2)
     u1 = moe.moe_workspace_size(512, 4096, 14336, 8, 2, unfused_swiglu=1)

@@ -147,7 +147,7 @@ def test_forward_every_block_size_and_split(bm, split):
 
 
 @pytest.mark.parametrize("bm", ALL_BM)
-@pytest.mark.parametrize("rotate", [1, 2])
+@pytest.mark.parametrize("rotate", [1, 2, 3])
 def test_forward_rotation_on_and_off(bm, rotate):
     cfg, x, lg, wgu, wd, ref = _mid_case()
     out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm, split_k=2, rotate=rotate)
@@ -183,7 +183,7 @@ def test_forward_partial_column_tiles(bm):
     parity.check_out(out, parity.oracle_out(x, lg, wgu, wd, 2, 0, True), f"partial bm={bm}")
 
 
-@pytest.mark.parametrize("gather", [1, 2])
+@pytest.mark.parametrize("gather", [1, 2, 3])
 @pytest.mark.parametrize("routing", [1, 2])
 @pytest.mark.parametrize("bm", [16, 64, 192])
 def test_forward_routing_and_gather_paths(bm, routing, gather):
@@ -199,7 +199,7 @@ def test_forward_routing_and_gather_paths(bm, routing, gather):
     assert torch.equal(out.view(torch.int16), base.view(torch.int16))
 
 
-@pytest.mark.parametrize("gather", [1, 2])
+@pytest.mark.parametrize("gather", [1, 2, 3])
 @pytest.mark.parametrize("bm", [16, 64, 128, 192])
 def test_forward_unfused_swiglu_ablation(bm, gather):
     """The unfused SwiGLU (gate GEMM, up GEMM, activation kernel) against the
