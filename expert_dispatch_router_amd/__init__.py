@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     moe_route,
     moe_route_workspace_size,
     moe_router_logits,
+    moe_router_workspace_size,
     moe_workspace_size,
     status_string,
 )

@@ -37,7 +37,8 @@ SIGNATURES = {
     "moe_plan": (_I, [_I, _I, _I, _I, _I, _P, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "moe_forward": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "moe_forward_ex": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
-    "moe_router_logits": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "moe_router_logits": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
+    "moe_router_workspace_size": (_I, [_I, _I, _I, ctypes.POINTER(_SZ)]),
     "moe_forward_router": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ,
                                 _P]),
     "moe_route_workspace_size": (_I, [_I, _I, _I, _P, ctypes.POINTER(_SZ)]),
@@ -203,7 +204,13 @@ def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=Non
     return out
 
 
-def moe_router_logits(x, W_router, out=None, stream=None):
+def moe_router_workspace_size(T, d, E) -> int:
+    n = _SZ(0)
+    _check("moe_router_workspace_size", lib().moe_router_workspace_size(T, d, E, ctypes.byref(n)))
+    return int(n.value)
+
+
+def moe_router_logits(x, W_router, out=None, workspace=None, stream=None):
     """logits fp32 [T,E] = x . W_router^T for x bf16 [T,d], W_router bf16
     [E,d], enqueued on ``stream``."""
     T, d = x.shape
@@ -214,9 +221,14 @@ def moe_router_logits(x, W_router, out=None, stream=None):
         out = torch.empty(T, E, dtype=torch.float32, device=x.device)
     if tuple(out.shape) != (T, E):
         raise ValueError("out must be [T, E]")
+    need = moe_router_workspace_size(T, d, E)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     rc = lib().moe_router_logits(_dev_ptr(x, torch.bfloat16, "x"),
                                  _dev_ptr(W_router, torch.bfloat16, "W_router"),
                                  _dev_ptr(out, torch.float32, "logits"), T, d, E,
+                                 _dev_ptr(workspace, torch.uint8, "workspace"),
+                                 0 if workspace is None else workspace.numel(),
                                  _stream_ptr(stream, x.device))
     _check("moe_router_logits", rc)
     return out

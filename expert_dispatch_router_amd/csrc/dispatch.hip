@@ -167,7 +167,7 @@ constexpr int kSmallWaves = kScanThreads / 64;
 
 template <int EMAX>
 __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int renorm, int score, int bm,
+    const LogitSrc logits, int T, int E, int k, int renorm, int score, int bm,
     int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
     int32_t* __restrict__ blocks, int32_t* __restrict__ nb) {
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
   // 1. route
   float v[EMAX];
 #pragma unroll
-  for (int e = 0; e < EMAX; ++e) v[e] = (ok && e < E) ? logits[(size_t)t * E + e] : 0.0f;
+  for (int e = 0; e < EMAX; ++e) v[e] = (ok && e < E) ? load_logit(logits, (size_t)t * E + e) : 0.0f;
   const unsigned valid = ok ? (E >= 32 ? 0xffffffffu : (1u << E) - 1u) : 0u;
   unsigned live = valid;
   float sel_v[MOE_MAX_TOPK];
@@ -331,7 +331,7 @@ bool small_routing_fits(int T, int E, int k) {
   return T <= kSmallRoutingMaxTokens && E <= kSmallRoutingMaxExperts;
 }
 
-hipError_t launch_route_dispatch_small(const float* logits, int T, int E, int k, int renorm,
+hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int k, int renorm,
                                        int score, int bm, int32_t* ids, float* w,
                                        int32_t* counts, int32_t* offsets, int32_t* perm,
                                        int32_t* inv, int32_t* blocks, int32_t* nb,

@@ -217,6 +217,8 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->o_u = seg(p->unfused ? (size_t)A * ffn * 2 : 0);
   p->o_y = seg((size_t)p->split * A * d * 4);
   p->o_logits = seg((size_t)T * E * 4);
+  p->router = plan_router(T, d > 0 ? d : 64, E);
+  p->o_rparts = seg(p->router.parts > 1 ? (size_t)p->router.parts * T * E * 4 : 0);
   p->total_bytes = o;
 }
 
@@ -246,7 +248,7 @@ int record(const moe_options* opt, int i, hipStream_t s) {
 
 // K1..K3 into the workspace's routing section: one workgroup for small
 // problems, else three launches.
-int run_routing(const float* logits, const Plan& p, int renorm, int score, void* ws,
+int run_routing(const LogitSrc& logits, const Plan& p, int renorm, int score, void* ws,
                 const moe_options* opt, hipStream_t s) {
   int32_t* ids = at<int32_t>(ws, p.o_ids);
   float* w = at<float>(ws, p.o_w);
@@ -275,7 +277,7 @@ int run_routing(const float* logits, const Plan& p, int renorm, int score, void*
 }
 
 // The forward pass from router scores already on the device (steps K1..K6).
-int forward_from_logits(const uint16_t* x, const float* router_logits, const uint16_t* W_gate_up,
+int forward_from_logits(const uint16_t* x, const LogitSrc& router_logits, const uint16_t* W_gate_up,
                         const uint16_t* W_down, int top_k, int renorm, uint16_t* out, int score,
                         const Plan& p, const moe_options* opt, void* workspace, hipStream_t s) {
   const int T = p.T, d = p.d, ffn = p.ffn;
@@ -327,8 +329,8 @@ int check_router_sizes(int T, int d, int E) {
   if (T < 0 || d < 1 || E < 1) return MOE_ERR_SHAPE;
   if (E > MOE_MAX_EXPERTS || T > MOE_MAX_ROWS) return MOE_ERR_UNSUPPORTED;
   if (d % 64 != 0) return MOE_ERR_ALIGN;
-  // one 16-row tile of x or W_r is addressed with 32-bit buffer offsets
-  if (16LL * d * 2 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  // one 32-row tile of x or W_r is addressed with 32-bit buffer offsets
+  if (32LL * d * 2 >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -422,19 +424,39 @@ int moe_forward_ex(const uint16_t* x, const float* router_logits, const uint16_t
 
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();  // report only this call's launches
-  return forward_from_logits(x, router_logits, W_gate_up, W_down, top_k, renormalize ? 1 : 0, out,
-                             score_func, p, opt, workspace, s);
+  return forward_from_logits(x, LogitSrc{router_logits, 1, 0, nullptr}, W_gate_up, W_down, top_k,
+                             renormalize ? 1 : 0, out, score_func, p, opt, workspace, s);
+}
+
+int moe_router_workspace_size(int T, int d, int E, size_t* bytes) {
+  MOE_TRY(check_router_sizes(T, d, E));
+  if (!bytes) return MOE_ERR_NULL;
+  const RouterPlan rp = plan_router(T, d, E);
+  *bytes = (T > 0 && rp.parts > 1) ? align_up((size_t)rp.parts * T * E * 4) : 0;
+  return MOE_OK;
 }
 
 int moe_router_logits(const uint16_t* x, const uint16_t* W_router, float* logits, int T, int d,
-                      int E, void* hip_stream) {
+                      int E, void* workspace, size_t workspace_bytes, void* hip_stream) {
   MOE_TRY(check_router_sizes(T, d, E));
   if (T == 0) return MOE_OK;
   if (!x || !W_router || !logits) return MOE_ERR_NULL;
   if (!aligned(x, 16) || !aligned(W_router, 16) || !aligned(logits, 16)) return MOE_ERR_ALIGN;
+  const RouterPlan rp = plan_router(T, d, E);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (rp.parts > 1) {
+    if (!workspace) return MOE_ERR_NULL;
+    if (!aligned(workspace, kAlign)) return MOE_ERR_ALIGN;
+    if (workspace_bytes < (size_t)rp.parts * T * E * 4) return MOE_ERR_WORKSPACE;
+  }
   (void)hipGetLastError();
-  MOE_TRY_HIP(launch_router_logits(x, W_router, T, d, E, logits,
-                                   static_cast<hipStream_t>(hip_stream)));
+  if (rp.parts == 1) {
+    MOE_TRY_HIP(launch_router(x, W_router, T, d, E, rp, logits, s));
+  } else {
+    float* parts = static_cast<float*>(workspace);
+    MOE_TRY_HIP(launch_router(x, W_router, T, d, E, rp, parts, s));
+    MOE_TRY_HIP(launch_router_reduce(parts, rp.parts, (long long)T * E, logits, s));
+  }
   return MOE_OK;
 }
 
@@ -461,9 +483,20 @@ int moe_forward_router(const uint16_t* x, const uint16_t* W_router, const uint16
 
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();
-  float* logits = logits_out ? logits_out : at<float>(workspace, p.o_logits);
-  MOE_TRY_HIP(launch_router_logits(x, W_router, T, d, E, logits, s));
-  return forward_from_logits(x, logits, W_gate_up, W_down, top_k, renormalize ? 1 : 0, out,
+  // One part: the router kernel writes the logits and routing reads them.
+  // Several: it writes partial sums, which the routing kernel adds in part
+  // order as it loads them (writing the sums to logits_out when given).
+  LogitSrc src;
+  if (p.router.parts == 1) {
+    float* logits = logits_out ? logits_out : at<float>(workspace, p.o_logits);
+    MOE_TRY_HIP(launch_router(x, W_router, T, d, E, p.router, logits, s));
+    src = LogitSrc{logits, 1, 0, nullptr};
+  } else {
+    float* parts = at<float>(workspace, p.o_rparts);
+    MOE_TRY_HIP(launch_router(x, W_router, T, d, E, p.router, parts, s));
+    src = LogitSrc{parts, p.router.parts, (long long)T * E, logits_out};
+  }
+  return forward_from_logits(x, src, W_gate_up, W_down, top_k, renormalize ? 1 : 0, out,
                              score_func, p, opt, workspace, s);
 }
 
@@ -499,7 +532,8 @@ int moe_route(const float* router_logits, int T, int E, int top_k, int renormali
 
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();
-  MOE_TRY(run_routing(router_logits, p, renormalize ? 1 : 0, score_func, workspace, opt, s));
+  MOE_TRY(run_routing(LogitSrc{router_logits, 1, 0, nullptr}, p, renormalize ? 1 : 0, score_func,
+                      workspace, opt, s));
   if (gather)
     MOE_TRY_HIP(launch_gather(x, at<int32_t>(workspace, p.o_perm), p.A, d, top_k, x_perm, s));
   MOE_TRY(record(opt, 3, s));

@@ -15,13 +15,40 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Router scores as the routing kernels read them: `nparts` fp32 partial
+// sums [nparts][T][E], `part_stride` elements apart, added in part order
+// (one part: the logits themselves).  When `out` is not null the summed
+// logits are also written there ([T][E]).
+struct LogitSrc {
+  const float* p;
+  int nparts;
+  long long part_stride;
+  float* out;
+};
+
+__device__ __forceinline__ float load_logit(const LogitSrc& s, size_t idx) {
+  float v = s.p[idx];
+  for (int q = 1; q < s.nparts; ++q) v += s.p[(size_t)q * s.part_stride + idx];
+  if (s.out) s.out[idx] = v;
+  return v;
+}
+
 // Flat routed rows handled by one reorder chunk; the histogram kernel keeps
 // one count per (chunk, expert) so the reorder can start every chunk at its
 // final position without a global sort.
 constexpr int kChunk = 1024;
 
+// Launch shape of the router scores kernel (see router.hip).
+struct RouterPlan {
+  int ts;     // 16-token subtiles per wave (1 or 2)
+  int nsub;   // 16-expert subtiles per wave (1, 2 or 4)
+  int parts;  // split of the reduction over d (partial sums added in order)
+};
+RouterPlan plan_router(int T, int d, int E);
+
 // Host-side plan of one call: sizes, tile choices and workspace carve-up.
 struct Plan {
+  RouterPlan router;
   int T, d, ffn, E, k;
   int A;          // routed rows T*k
   int bm;         // rows per schedule block (BLOCK_M)
@@ -44,16 +71,21 @@ struct Plan {
   size_t o_xperm, o_h, o_y;
   size_t o_g, o_u;  // unfused gate and up products [A, ffn] bf16
   size_t o_logits;  // router scores [T, E] fp32 (moe_forward_router)
+  size_t o_rparts;  // router partial sums [router.parts, T, E] fp32
   size_t total_bytes;
 };
 
 // ---- launchers (enqueue on `s`, return the launch status) ----------------
 
-// Router scores logits[T, E] = x . W_r^T (bf16 in, fp32 out).
-hipError_t launch_router_logits(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
-                                float* logits, hipStream_t s);
+// Router scores x . W_r^T (bf16 in, fp32 out): with rp.parts == 1 the
+// logits [T, E] into `out`, else rp.parts partial sums [parts, T, E].
+hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
+                         const RouterPlan& rp, float* out, hipStream_t s);
+// logits = the partial sums added in part order.
+hipError_t launch_router_reduce(const float* parts, int nparts, long long n, float* logits,
+                                hipStream_t s);
 
-hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, int score,
+hipError_t launch_route(const LogitSrc& logits, int T, int E, int k, int renorm, int score,
                         int32_t* ids, float* w, hipStream_t s);
 
 hipError_t launch_hist_scan(const int32_t* ids, int A, int E, int bm, int nchunks,
@@ -72,7 +104,7 @@ constexpr int kSmallRoutingMaxExperts = 32;
 // (measured faster than the three launches at E = 8, slower at E = 64).
 constexpr long long kSmallRoutingAutoWork = 1 << 15;
 bool small_routing_fits(int T, int E, int k);
-hipError_t launch_route_dispatch_small(const float* logits, int T, int E, int k, int renorm,
+hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int k, int renorm,
                                        int score, int bm, int32_t* ids, float* w,
                                        int32_t* counts, int32_t* offsets, int32_t* perm,
                                        int32_t* inv, int32_t* blocks, int32_t* nb, hipStream_t s);

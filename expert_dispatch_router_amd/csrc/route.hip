@@ -8,7 +8,7 @@ namespace {
 constexpr int kRouteThreads = 256;
 
 template <int LPT, int EPL>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const LogitSrc logits,
                                                               int T, int E, int k, int renorm,
                                                               int score, int32_t* __restrict__ ids,
                                                               float* __restrict__ w) {
@@ -19,7 +19,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float* __res
 
 }  // namespace
 
-hipError_t launch_route(const float* logits, int T, int E, int k, int renorm, int score,
+hipError_t launch_route(const LogitSrc& logits, int T, int E, int k, int renorm, int score,
                         int32_t* ids, float* w, hipStream_t s) {
 #define MOE_LAUNCH_ROUTE(LPT, EPL)                                                        \
   {                                                                                       \

@@ -67,7 +67,7 @@ __device__ __forceinline__ void topk_weights(const float* sel_v, int k, int reno
 // padding groups past the last token).  Lane j of the group writes entry j:
 // ids[t*k + j] and w[t*k + j].
 template <int LPT, int EPL>
-__device__ __forceinline__ void route_token(const float* __restrict__ logits, int t, bool tok_ok,
+__device__ __forceinline__ void route_token(const LogitSrc& logits, int t, bool tok_ok,
                                             int sub, int E, int k, int renorm, int score,
                                             int32_t* __restrict__ ids, float* __restrict__ w) {
   float v[EPL];
@@ -76,7 +76,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ logits, in
   for (int i = 0; i < EPL; ++i) {
     const int e = sub + i * LPT;
     const bool ok = tok_ok && e < E;
-    v[i] = ok ? logits[(size_t)t * E + e] : 0.0f;
+    v[i] = ok ? load_logit(logits, (size_t)t * E + e) : 0.0f;
     live |= ok ? (1u << i) : 0u;
   }
 

@@ -208,21 +208,30 @@ int moe_forward_ex(const uint16_t *x, const float *router_logits, const uint16_t
  *   x         bf16 [T, d]   token activations
  *   W_router  bf16 [E, d]   one row per expert (K-contiguous, like the
  *                           expert weights)
- *   logits    fp32 [T, E]   written (fp32 accumulation; deterministic)
+ *   logits    fp32 [T, E]   written (fp32 accumulation; deterministic: the
+ *                           reduction over d is split into a fixed number
+ *                           of parts for these sizes, added in part order)
+ *   workspace device buffer of moe_router_workspace_size bytes (256-byte
+ *             aligned; may be NULL when that size is 0) for the partial sums
  *
  * Constraints: T >= 0 (T = 0 is a no-op), 1 <= E <= 512, d a positive
- * multiple of 64 with 32*d < 2^31, T <= 2^20, pointers 16-byte aligned.
- * No workspace; enqueued on hip_stream.
+ * multiple of 64 with 64*d < 2^31, T <= 2^20, pointers 16-byte aligned.
+ * Enqueued on hip_stream.
  */
 int moe_router_logits(const uint16_t *x, const uint16_t *W_router, float *logits, int T, int d,
-                      int E, void *hip_stream);
+                      int E, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* Host-only size query for moe_router_logits. */
+int moe_router_workspace_size(int T, int d, int E, size_t *bytes);
 
 /* moe_forward_ex from the hidden states: the router scores of
- * moe_router_logits, then the forward pass on them.  logits_out (fp32
- * [T, E], 16-byte aligned) receives the scores, or may be NULL (they are
- * kept in the workspace).  Same workspace size as moe_forward_ex; the
- * constraints of both calls apply.  The stage events (opt) time the forward
- * pass after the scores: events[0] is recorded after the router GEMM. */
+ * moe_router_logits, then the forward pass on them; when the scores are
+ * computed in several partial sums, the routing kernel adds them (in the
+ * same order) as it reads them.  logits_out (fp32 [T, E], 16-byte aligned)
+ * receives the scores (bitwise those of moe_router_logits), or may be NULL.
+ * Same workspace size as moe_forward_ex; the constraints of both calls
+ * apply.  The stage events (opt) time the forward pass after the router
+ * GEMM: events[0] is recorded after it. */
 int moe_forward_router(const uint16_t *x, const uint16_t *W_router, const uint16_t *W_gate_up,
                        const uint16_t *W_down, int top_k, int renormalize, uint16_t *out,
                        float *logits_out, int T, int d, int ffn, int E, int score_func,

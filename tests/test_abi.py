@@ -208,9 +208,10 @@ def test_route_rejects_before_any_launch():
 
 
 def _rl(**kw):
-    a = dict(x=FAKE, w=FAKE, out=FAKE, T=4, d=64, E=4)
+    a = dict(x=FAKE, w=FAKE, out=FAKE, T=4, d=64, E=4, ws=None, wsb=0)
     a.update(kw)
-    return moe.lib().moe_router_logits(a["x"], a["w"], a["out"], a["T"], a["d"], a["E"], None)
+    return moe.lib().moe_router_logits(a["x"], a["w"], a["out"], a["T"], a["d"], a["E"], a["ws"],
+                                       a["wsb"], None)
 
 
 def test_router_logits_rejects_before_any_launch():
@@ -221,11 +222,20 @@ def test_router_logits_rejects_before_any_launch():
     assert _rl(E=513) == UNSUP
     assert _rl(T=(1 << 20) + 1) == UNSUP
     assert _rl(d=100) == ALIGN
-    assert _rl(d=1 << 26) == UNSUP
+    assert _rl(d=1 << 25) == UNSUP
     for name in ("x", "w", "out"):
         assert _rl(**{name: None}) == NULL, name
         assert _rl(**{name: FAKE + 4}) == ALIGN, name
     assert _rl(T=0, x=None, w=None, out=None) == OK
+    # sizes that split the reduction need the workspace for partial sums
+    need = moe.moe_router_workspace_size(512, 4096, 8)
+    assert need >= 2 * 512 * 8 * 4 and need % 256 == 0
+    assert _rl(T=512, d=4096, E=8) == NULL
+    assert _rl(T=512, d=4096, E=8, ws=FAKE, wsb=need - 1) == WS
+    assert _rl(T=512, d=4096, E=8, ws=FAKE + 16, wsb=need) == ALIGN
+    assert moe.moe_router_workspace_size(8192, 64, 512) == 0  # one part: no workspace
+    n = ctypes.c_size_t(0)
+    assert moe.lib().moe_router_workspace_size(4, 100, 4, ctypes.byref(n)) == ALIGN
 
 
 def _fr(**kw):

@@ -57,8 +57,11 @@ def _check_scores(got, x, wr):
 
 
 @pytest.mark.parametrize("T,d,E", [(1, 64, 1), (17, 128, 6), (100, 512, 60), (33, 1024, 256),
-                                   (40, 7168, 256), (5, 64, 512), (300, 256, 16)])
+                                   (40, 7168, 256), (5, 64, 512), (300, 256, 16), (64, 4096, 8),
+                                   (130, 2048, 33), (513, 1024, 17), (97, 3584, 64)])
 def test_router_scores_within_the_summation_bound(T, d, E):
+    """Shapes with one part and with the reduction split in several (the
+    partial sums added in order), ragged in tokens and experts."""
     x, wr = _router_case(T, d, E, seed=T + d + E)
     got = moe.moe_router_logits(x, wr)
     _check_scores(got, x, wr)
