@@ -348,7 +348,7 @@ def main():
                           args.copy_bytes or (1 << 30))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         raise SystemExit(2)
     if os.environ.get("WORLD_SIZE", "1") not in ("1", ""):

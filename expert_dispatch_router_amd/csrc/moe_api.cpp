@@ -351,7 +351,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_TOPK: return "top_k must be in [1, E]";
     case MOE_ERR_ALIGN: return "d and ffn must be multiples of 64; pointers 16-byte aligned, workspace 256";
     case MOE_ERR_WORKSPACE: return "workspace too small";
-    case MOE_ERR_UNSUPPORTED: return "outside this build's limits or an unsupported option";
+    case MOE_ERR_UNSUPPORTED: return "outside the library's limits or an unsupported option";
     case MOE_ERR_HIP: return "a HIP call failed";
     default: return "unknown status";
   }

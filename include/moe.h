@@ -47,7 +47,7 @@ extern "C" {
 
 #define MOE_ABI_VERSION 1
 
-/* Limits of this build (violations return MOE_ERR_UNSUPPORTED). */
+/* Limits of the library (violations return MOE_ERR_UNSUPPORTED). */
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_ROWS (1 << 20)   /* T * top_k */
@@ -65,7 +65,7 @@ enum moe_status {
     MOE_ERR_ALIGN = -4,       /* d or ffn not a multiple of 64, or a pointer
                                  not 16-byte aligned (workspace: 256)       */
     MOE_ERR_WORKSPACE = -5,   /* workspace smaller than the size query      */
-    MOE_ERR_UNSUPPORTED = -6, /* beyond this build's limits, bad option     */
+    MOE_ERR_UNSUPPORTED = -6, /* beyond the library limits, bad option      */
     MOE_ERR_HIP = -7          /* a HIP launch or record call failed         */
 };
 
