@@ -195,7 +195,8 @@ def run(args):
     t1 = time.perf_counter()
     elapsed = t1 - t0
     ms_step = elapsed * 1e3 / args.steps
-    k4_ms = sum(a.elapsed_ms(b) for a, b in k4_timers) / args.steps
+    k4_each = np.array([a.elapsed_ms(b) for a, b in k4_timers])
+    k4_ms = float(k4_each.mean())
     # Stage breakdown: a second, separately run set of steps with all seven
     # stage events (each event adds a little time of its own).
     timers = [[moe.Timer() for _ in range(7)] for _ in range(args.steps)]
@@ -207,6 +208,9 @@ def run(args):
         for s in range(6):
             stage_ms[s] += timers[i][s].elapsed_ms(timers[i][s + 1])
     stage_ms /= args.steps
+    pass_each = np.array([timers[i][0].elapsed_ms(timers[i][6]) for i in range(args.steps)])
+    pct = lambda v: {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
+                     "p90": float(np.percentile(v, 90))}
 
     t_step = elapsed / args.steps
     t_roof = max(alg["bytes"] / (HBM_PEAK_GBS * 1e9), alg["flop"] / (BF16_PEAK_TFLOPS * 1e12))
@@ -237,6 +241,10 @@ def run(args):
         "hbm_gbs": alg["bytes"] / t_step / 1e9,
         "roofline_frac_step": t_roof / t_step,
         "stage_ms": {n: round(float(v), 5) for n, v in zip(STAGES, stage_ms)},
+        # distributions: the fused kernel over the timed steps; the whole
+        # pass (first to last stage event) over the stage-breakdown steps
+        "k4_ms_pct": pct(k4_each),
+        "pass_ms_pct": pct(pass_each),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": None if unfused else traffic_for(cfg.name),
@@ -253,7 +261,8 @@ def run(args):
     print(json.dumps(res), flush=True)
 
 
-def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes):
+def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes,
+                      out_dir=os.path.join(ROOT, "profiles")):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the GEMM-stage kernels,
     scaled by what the same counters read for the plain copy of copy_bytes
     bytes (reads copy_bytes, writes copy_bytes).  Writes
@@ -317,14 +326,15 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes):
         out["kernel"] = "unfused_swiglu (gate GEMM + up GEMM + activation)"
         out["bytes_per_forward"] = 2 * per["proj_bf16"]["bytes_per_launch"] + \
             per["swiglu_act"]["bytes_per_launch"]
-        path = os.path.join(ROOT, "profiles", f"traffic_unfused_swiglu_{workload}.json")
+        path = os.path.join(out_dir, f"traffic_unfused_swiglu_{workload}.json")
     else:
         out["kernel"] = "gate_up_swiglu"
         out["bytes_per_launch"] = per["gate_up_swiglu"]["bytes_per_launch"]
-        path = os.path.join(ROOT, "profiles", f"traffic_gate_up_swiglu_{workload}.json")
+        path = os.path.join(out_dir, f"traffic_gate_up_swiglu_{workload}.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
+    return out
 
 
 def main():
