@@ -97,6 +97,30 @@ def router_gemm(cfg, x, seed, steps, stream):
             "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS}
 
 
+def graph_replay(step, steps, T):
+    """The same pass captured once in a HIP graph and replayed `steps`
+    times (no host launch work per pass): ms per pass and tokens/s."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(strm=side)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(strm=torch.cuda.current_stream())
+    for _ in range(5):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3)}
+
+
 def traffic_for(cfg_name):
     """Counter-derived HBM bytes per launch of the fused kernel, if the
     stored measurement was taken on the current kernel source."""
@@ -175,9 +199,10 @@ def run(args):
     counts = routing["counts"].cpu().numpy()
     alg = algorithmic(cfg, counts)
 
-    def step(events=None):
+    def step(events=None, strm=None):
         moe.moe_forward(x, logits, wgu, wd, cfg.top_k, cfg.renormalize, out=out, score=cfg.score,
-                        workspace=ws, stream=stream, stage_events=events, unfused_swiglu=unfused)
+                        workspace=ws, stream=strm or stream, stage_events=events,
+                        unfused_swiglu=unfused)
         if copy_src is not None:
             copy_dst.copy_(copy_src)
 
@@ -256,6 +281,8 @@ def run(args):
         "cpu_baseline": None,
     }
     res["router_gemm"] = router_gemm(cfg, x, args.seed, args.steps, stream)
+    if args.graph:
+        res["graph"] = graph_replay(step, args.steps, cfg.T)
     if not args.profile and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, x, logits, wgu, wd, args.cpu_seconds)
     print(json.dumps(res), flush=True)
@@ -350,6 +377,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-bytes", type=int, default=0)
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the pass captured in a HIP graph and replayed")
     ap.add_argument("--unfused", action="store_true",
                     help="SwiGLU ablation: gate GEMM, up GEMM and activation kernel")
     args = ap.parse_args()

@@ -78,19 +78,40 @@ def oracle_out(x, logits, wgu, wd, k, score, renorm, tokens=None):
     return oracle.ffn(to_np_u16(x), ids, w, gu, dn, F, tokens=toks)
 
 
-def errors(out_bf16_rows: torch.Tensor, ref32: np.ndarray):
+def bf16_half_ulp(ref: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp at each value: the error of rounding it to bf16 is at
+    most this (8 significand bits: ulp = 2^(floor(log2|v|) - 7))."""
+    a = np.abs(ref.astype(np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(e - 8.0), 0.0)
+
+
+def errors(out_bf16_rows: torch.Tensor, ref32: np.ndarray, beyond_format=False):
+    """(rel-Frobenius, max-abs / RMS).  With ``beyond_format`` the max-abs
+    term counts only the error in excess of each element's own bf16 rounding
+    (|got - ref| - half_ulp(ref), floored at 0)."""
     got = out_bf16_rows.detach().float().cpu().numpy().astype(np.float64)
     ref = ref32.astype(np.float64)
     rms = np.sqrt(np.mean(ref * ref))
     rel_fro = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
-    max_abs = np.max(np.abs(got - ref)) / max(rms, 1e-300)
+    diff = np.abs(got - ref)
+    if beyond_format:
+        diff = np.maximum(diff - bf16_half_ulp(ref), 0.0)
+    max_abs = np.max(diff) / max(rms, 1e-300)
     return rel_fro, max_abs
 
 
-def check_out(out_bf16_rows, ref32, what="", scale=1.0):
+def check_out(out_bf16_rows, ref32, what="", scale=1.0, beyond_format=False):
     """Asserts the output tolerance; ``scale`` widens both bounds (only the
-    unfused ablation passes UNFUSED_SCALE)."""
-    rel_fro, max_abs = errors(out_bf16_rows, ref32)
+    unfused ablation passes UNFUSED_SCALE).
+
+    ``beyond_format`` is for inputs whose exact output has elements far above
+    its RMS (rows with very different routing-weight sums, as unrenormalised
+    softmax over many experts gives): bf16 itself cannot hold an element
+    |y| > 5.12 * RMS to within 2e-2 * RMS (its rounding error reaches
+    2^-8 * |y|), so the max-abs bound is applied to the error beyond that
+    rounding.  The rel-Frobenius bound is unchanged."""
+    rel_fro, max_abs = errors(out_bf16_rows, ref32, beyond_format)
     assert np.all(np.isfinite(out_bf16_rows.float().cpu().numpy())), f"{what}: non-finite output"
     assert rel_fro <= REL_FRO_TOL * scale, f"{what}: rel-Frobenius {rel_fro:.3e}"
     assert max_abs <= MAX_ABS_TOL * scale, f"{what}: max-abs/RMS {max_abs:.3e}"
