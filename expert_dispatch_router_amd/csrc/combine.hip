@@ -8,9 +8,11 @@
 //
 // Deterministic by construction: each output element is owned by one thread
 // that adds the split partials of a routed row in split order and the k
-// routed rows in j order -- no atomics, so repeated runs are bitwise equal.
-// Workgroups cover 1024 columns of one token, 4 consecutive columns per thread.
-#include "moe_internal.hpp"
+// routed rows in j order (combine_quad) -- no atomics, so repeated runs are
+// bitwise equal.  Workgroups cover 1024 columns of one token, 4 consecutive
+// columns per thread.  The down GEMM can do the same work in its epilogue
+// instead (moe_options.fold_combine).
+#include "combine_core.hpp"
 
 namespace moe {
 namespace {
@@ -24,21 +26,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int cb = blockIdx.x - t * col_blocks;
   const int c = (cb * 256 + threadIdx.x) * 4;
   if (c >= d) return;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const size_t row = (size_t)inv[(size_t)t * k + j];
-    const float wj = w[(size_t)t * k + j];
-    f32x4 v = *reinterpret_cast<const f32x4*>(y + row * d + c);
-    for (int s = 1; s < split; ++s)
-      v += *reinterpret_cast<const f32x4*>(y + ((size_t)s * A + row) * d + c);
-    acc += wj * v;
-  }
-  bf16x4 o;
-  o[0] = (__bf16)acc[0];
-  o[1] = (__bf16)acc[1];
-  o[2] = (__bf16)acc[2];
-  o[3] = (__bf16)acc[3];
-  *reinterpret_cast<bf16x4*>(out + (size_t)t * d + c) = o;
+  combine_quad(y, split, A, d, inv, w, k, t, c, out, PlainLoad{});
 }
 
 }  // namespace

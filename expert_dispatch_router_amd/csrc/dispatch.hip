@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
     const LogitSrc logits, int T, int E, int k, int renorm, int score, int bm,
     int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    int32_t* __restrict__ blocks, int32_t* __restrict__ nb) {
+    int32_t* __restrict__ blocks, int32_t* __restrict__ nb, ZeroRange zero) {
   static_assert(EMAX <= 32 && EMAX * kSmallWaves <= kScanThreads, "one thread per (e, wave)");
   __shared__ unsigned long long wmask[EMAX * kSmallWaves];  // [e][wave] ballot of expert e
   __shared__ int start[EMAX * kSmallWaves];                 // [e][wave] first sorted position
@@ -179,6 +179,7 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
   const int wave = t >> 6;
   const int lane = t & 63;
   const bool ok = t < T;
+  for (int i = t; i < zero.n; i += kScanThreads) zero.p[i] = 0;
 
   // 1. route
   float v[EMAX];
@@ -335,11 +336,11 @@ hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int
                                        int score, int bm, int32_t* ids, float* w,
                                        int32_t* counts, int32_t* offsets, int32_t* perm,
                                        int32_t* inv, int32_t* blocks, int32_t* nb,
-                                       hipStream_t s) {
+                                       ZeroRange zero, hipStream_t s) {
   if (!small_routing_fits(T, E, k)) return hipErrorInvalidValue;
 #define MOE_LAUNCH_SMALL(EMAX)                                                               \
   route_dispatch_small_kernel<EMAX><<<1, kScanThreads, 0, s>>>(                              \
-      logits, T, E, k, renorm, score, bm, ids, w, counts, offsets, perm, inv, blocks, nb)
+      logits, T, E, k, renorm, score, bm, ids, w, counts, offsets, perm, inv, blocks, nb, zero)
   if (E <= 8)
     MOE_LAUNCH_SMALL(8);
   else if (E <= 16)

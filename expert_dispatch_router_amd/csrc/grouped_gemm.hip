@@ -35,8 +35,13 @@
 //     past the last column are skipped whole (N % 16 == 0).
 //   * K5 may split its reduction into `split` contiguous parts, each written
 //     as its own fp32 partial; the combination kernel adds them in order.
+//   * K5 can also do the weighted combination itself (FoldCombine): after
+//     writing its partials a workgroup counts them per (token, column tile);
+//     the workgroup that writes the last of a token's k * split partials of
+//     a tile computes that token's output columns there, in the same fixed
+//     order as the combination kernel.  No waiting: every workgroup ends.
 #include "buffer_load.hpp"
-#include "moe_internal.hpp"
+#include "combine_core.hpp"
 
 namespace moe {
 namespace {
@@ -82,7 +87,7 @@ void grouped_gemm_kernel(
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
     const int32_t* __restrict__ offsets, void* __restrict__ out, int A, int N, int K, int ksplit,
     int tiles_per_block, int rotate, const int32_t* __restrict__ gather_perm, int gather_k,
-    int x_rows, int xcd_group, int x_tiled) {
+    int x_rows, int xcd_group, int x_tiled, FoldCombine fold) {
   using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   constexpr int MT = G::kMT, NG = G::kNG, XPT = G::kXPerThread;
   static_assert(PF >= 2, "the activation stage is issued PF-1 steps ahead");
@@ -320,7 +325,16 @@ void grouped_gemm_kernel(
             *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(out) + orow * N + n) = hv;
           } else if constexpr (MODE == kOutF32Parts) {
             float* y = static_cast<float*>(out) + ((size_t)part * A + orow) * N + n;
-            *reinterpret_cast<f32x4*>(y) = acc[0][mt][j];
+            if (fold.cnt) {
+              // read by another workgroup of this launch: agent-scope stores
+              // (written through to the device-coherent level)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                __hip_atomic_store(y + i, acc[0][mt][j][i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+              *reinterpret_cast<f32x4*>(y) = acc[0][mt][j];
+            }
           } else {
             const f32x4 v = acc[0][mt][j];
             bf16x4 o;
@@ -334,13 +348,47 @@ void grouped_gemm_kernel(
       }
     }
   }
+
+  if constexpr (MODE == kOutF32Parts) {
+    if (fold.cnt) {
+      // The partials went out as agent-scope stores; once every thread's
+      // stores have completed (the wait below, then the barrier), one thread
+      // per row counts the row's token for this column tile.  Whoever
+      // completes a count owns that token's combination for the tile and
+      // reads the partials with agent-scope loads.  No L2 writeback or
+      // invalidation is needed on either side.
+      __shared__ int n_last;
+      __shared__ int last_tok[BM];
+      if (tid == 0) n_last = 0;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      const int nsplit = tiles_per_block / n_tiles;
+      const int need = fold.k * nsplit;  // k routed rows x split parts
+      for (int m = tid; m < rows; m += G::kThreads) {
+        const int t = fold.perm[r0 + m] / fold.k;
+        if (atomicAdd(&fold.cnt[(size_t)t * n_tiles + tile], 1) == need - 1)
+          last_tok[atomicAdd(&n_last, 1)] = t;
+      }
+      __syncthreads();
+      const int nl = n_last;
+      if (nl > 0) {
+        const int c0 = tile * G::kTileCols;
+        const int nq = min(G::kTileCols, N - c0) / 4;
+        const float* y = static_cast<const float*>(out);
+        for (int i = tid; i < nl * nq; i += G::kThreads)
+          combine_quad(y, nsplit, A, N, fold.inv, fold.w, fold.k, last_tok[i / nq],
+                       c0 + (i % nq) * 4, fold.out, AgentLoad{});
+      }
+    }
+  }
 }
 
 template <int BM, int NWT, int WAVES, int PF, int MODE>
 hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride, const int32_t* blocks,
                       const int32_t* nb, const int32_t* offsets, void* out, int A, int N, int K,
                       int split, int ksplit, int nb_max, int rotate, const int32_t* gather_perm,
-                      int gather_k, int x_rows, int xcd_group, int x_tiled, hipStream_t s) {
+                      int gather_k, int x_rows, int xcd_group, int x_tiled,
+                      const FoldCombine& fold, hipStream_t s) {
   using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
   const int tiles_per_block = n_tiles * split;
@@ -348,7 +396,7 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   grouped_gemm_kernel<BM, NWT, WAVES, PF, MODE><<<(unsigned)grid, G::kThreads, 0, s>>>(
       X, W, w_estride, blocks, nb, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
-      gather_perm, gather_k, x_rows, xcd_group, x_tiled);
+      gather_perm, gather_k, x_rows, xcd_group, x_tiled, fold);
   return hipGetLastError();
 }
 
@@ -394,7 +442,7 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
     return launch_cfg<BM, NWT, WV, PF, kOutSwiGLU>(x, w_gate_up, 2LL * ffn * d, blocks, nb,      \
                                                    offsets, h, A, ffn, d, 1, d, nb_max, rotate,  \
                                                    gather_perm, k, x_tiled ? (A + 15) / 16 * 16 : T, \
-                                                   xcd_group, x_tiled, s);
+                                                   xcd_group, x_tiled, FoldCombine{}, s);
   MOE_GU_CFGS(X)
 #undef X
   return hipErrorInvalidValue;
@@ -403,13 +451,13 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
 hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w_down,
                        const int32_t* blocks, const int32_t* nb, const int32_t* offsets, float* y,
                        int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
-                       int xcd_group, hipStream_t s) {
+                       int xcd_group, const FoldCombine& fold, hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && V == variant)                                                                      \
     return launch_cfg<BM, NWT, WV, PF, kOutF32Parts>(h, w_down, (long long)d * ffn, blocks, nb,  \
                                                      offsets, y, A, d, ffn, split, ksplit,       \
                                                      nb_max, rotate, nullptr, 1, A, xcd_group, 0,\
-                                                     s);
+                                                     fold, s);
   MOE_DN_CFGS(X)
 #undef X
   return hipErrorInvalidValue;
@@ -426,7 +474,7 @@ hipError_t launch_proj_bf16(int bm, const uint16_t* x, const int32_t* gather_per
       return launch_cfg<BM, NWT, WV, PF, kOutBF16>(x, w, w_estride, blocks, nb, offsets, out, A, \
                                                    ffn, d, 1, d, nb_max, rotate, gather_perm, k, \
                                                    x_tiled ? (A + 15) / 16 * 16 : T, xcd_group,  \
-                                                   x_tiled, s);                                 \
+                                                   x_tiled, FoldCombine{}, s);                  \
   }
   MOE_GU_CFGS(X)
 #undef X

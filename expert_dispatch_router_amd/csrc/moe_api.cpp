@@ -63,6 +63,7 @@ int check_options(const moe_options* opt) {
   if (opt->gather_mode < 0 || opt->gather_mode > 3) return MOE_ERR_UNSUPPORTED;
   if (opt->unfused_swiglu < 0 || opt->unfused_swiglu > 1) return MOE_ERR_UNSUPPORTED;
   if (opt->xcd_order < 0 || opt->xcd_order > 2) return MOE_ERR_UNSUPPORTED;
+  if (opt->fold_combine < 0 || opt->fold_combine > 2) return MOE_ERR_UNSUPPORTED;
   if (opt->down_variant < 0) return MOE_ERR_UNSUPPORTED;
   if (opt->down_variant > 0) {
     const int bm = opt->block_rows;
@@ -156,6 +157,15 @@ bool auto_xcd_order(int A, int E, int bm) {
 // off.
 int auto_rotate(int) { return 1; }
 
+// The weighted combination as its own kernel, or folded into the down GEMM.
+// The separate kernel measured faster on every MoE workload shape (tiny to
+// DeepSeek-V3): folded, the workgroups that finish last do the whole
+// combination serially, and the partials go out as write-through stores.
+int auto_fold(int T, int d, int E, int k) {
+  (void)T, (void)d, (void)E, (void)k;
+  return 0;
+}
+
 void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan* p) {
   memset(p, 0, sizeof(*p));
   p->T = T;
@@ -192,6 +202,10 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     p->dn_rotate = rot == 0 ? auto_rotate(ffn) : rot - 1;
     const int xo = opt ? opt->xcd_order : 0;
     p->gu_xcd = p->dn_xcd = xo == 0 ? auto_xcd_order(A, E, p->bm) : xo == 2;
+    const int fc = opt ? opt->fold_combine : 0;
+    p->fold = fc == 0 ? auto_fold(T, d, E, k) : fc == 2;
+    const int dcols = down_tile_cols(p->bm, p->dn_variant);
+    p->dn_tiles = dcols > 0 ? (d + dcols - 1) / dcols : 0;
   }
   size_t o = 0;
   auto seg = [&](size_t bytes) {
@@ -219,6 +233,7 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->o_logits = seg((size_t)T * E * 4);
   p->router = plan_router(T, d > 0 ? d : 64, E);
   p->o_rparts = seg(p->router.parts > 1 ? (size_t)p->router.parts * T * E * 4 : 0);
+  p->o_fold = seg(p->fold ? (size_t)T * p->dn_tiles * 4 : 0);
   p->total_bytes = o;
 }
 
@@ -249,7 +264,7 @@ int record(const moe_options* opt, int i, hipStream_t s) {
 // K1..K3 into the workspace's routing section: one workgroup for small
 // problems, else three launches.
 int run_routing(const LogitSrc& logits, const Plan& p, int renorm, int score, void* ws,
-                const moe_options* opt, hipStream_t s) {
+                const moe_options* opt, ZeroRange zero, hipStream_t s) {
   int32_t* ids = at<int32_t>(ws, p.o_ids);
   float* w = at<float>(ws, p.o_w);
   int32_t* offsets = at<int32_t>(ws, p.o_offsets);
@@ -259,12 +274,12 @@ int run_routing(const LogitSrc& logits, const Plan& p, int renorm, int score, vo
                                             at<int32_t>(ws, p.o_counts), offsets,
                                             at<int32_t>(ws, p.o_perm), at<int32_t>(ws, p.o_inv),
                                             at<int32_t>(ws, p.o_blocks), at<int32_t>(ws, p.o_nb),
-                                            s));
+                                            zero, s));
     MOE_TRY(record(opt, 1, s));
     MOE_TRY(record(opt, 2, s));
     return MOE_OK;
   }
-  MOE_TRY_HIP(launch_route(logits, p.T, p.E, p.k, renorm, score, ids, w, s));
+  MOE_TRY_HIP(launch_route(logits, p.T, p.E, p.k, renorm, score, ids, w, zero, s));
   MOE_TRY(record(opt, 1, s));
   MOE_TRY_HIP(launch_hist_scan(ids, p.A, p.E, p.bm, p.nchunks, at<int32_t>(ws, p.o_counts),
                                offsets, at<int32_t>(ws, p.o_ccnt), at<int32_t>(ws, p.o_cbase),
@@ -281,7 +296,11 @@ int forward_from_logits(const uint16_t* x, const LogitSrc& router_logits, const 
                         const uint16_t* W_down, int top_k, int renorm, uint16_t* out, int score,
                         const Plan& p, const moe_options* opt, void* workspace, hipStream_t s) {
   const int T = p.T, d = p.d, ffn = p.ffn;
-  MOE_TRY(run_routing(router_logits, p, renorm, score, workspace, opt, s));
+  // With the combination folded into the down GEMM, the routing kernels
+  // clear its arrival counters.
+  int32_t* fold_cnt = p.fold ? at<int32_t>(workspace, p.o_fold) : nullptr;
+  MOE_TRY(run_routing(router_logits, p, renorm, score, workspace, opt,
+                      ZeroRange{fold_cnt, p.fold ? T * p.dn_tiles : 0}, s));
   const int32_t* perm = at<int32_t>(workspace, p.o_perm);
   const int32_t* blocks = at<int32_t>(workspace, p.o_blocks);
   const int32_t* nb = at<int32_t>(workspace, p.o_nb);
@@ -315,11 +334,15 @@ int forward_from_logits(const uint16_t* x, const LogitSrc& router_logits, const 
                                p.x_tiled, s));
   }
   MOE_TRY(record(opt, 4, s));
+  const int32_t* inv = at<int32_t>(workspace, p.o_inv);
+  const float* wts = at<float>(workspace, p.o_w);
+  const FoldCombine fold{perm, inv, wts, top_k, fold_cnt, out};
   MOE_TRY_HIP(launch_down(p.bm, p.dn_variant, h, W_down, blocks, nb, offsets, y, p.A, d, ffn,
-                          p.split, p.ksplit, p.nb_max, p.dn_rotate, p.dn_xcd, s));
+                          p.split, p.ksplit, p.nb_max, p.dn_rotate, p.dn_xcd,
+                          p.fold ? fold : FoldCombine{}, s));
   MOE_TRY(record(opt, 5, s));
-  MOE_TRY_HIP(launch_combine(y, p.split, p.A, d, at<int32_t>(workspace, p.o_inv),
-                             at<float>(workspace, p.o_w), top_k, T, out, s));
+  if (!p.fold)
+    MOE_TRY_HIP(launch_combine(y, p.split, p.A, d, inv, wts, top_k, T, out, s));
   MOE_TRY(record(opt, 6, s));
   return MOE_OK;
 }
@@ -533,7 +556,7 @@ int moe_route(const float* router_logits, int T, int E, int top_k, int renormali
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();
   MOE_TRY(run_routing(LogitSrc{router_logits, 1, 0, nullptr}, p, renormalize ? 1 : 0, score_func,
-                      workspace, opt, s));
+                      workspace, opt, ZeroRange{nullptr, 0}, s));
   if (gather)
     MOE_TRY_HIP(launch_gather(x, at<int32_t>(workspace, p.o_perm), p.A, d, top_k, x_perm, s));
   MOE_TRY(record(opt, 3, s));

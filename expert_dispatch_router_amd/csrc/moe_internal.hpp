@@ -65,6 +65,8 @@ struct Plan {
   int gather_in_gemm; // the fused gate/up GEMM reads token rows through perm
   int x_tiled;        // else x_perm is written in K-step tiles (gather mode 3)
   int unfused;        // SwiGLU as gate GEMM, up GEMM and activation (ablation)
+  int fold;           // weighted combination in the down GEMM's epilogue
+  int dn_tiles;       // column tiles of the down GEMM (d / its tile width)
   // byte offsets into the workspace (256-byte aligned)
   size_t o_ids, o_w, o_counts, o_offsets, o_ccnt, o_cbase, o_perm, o_inv, o_blocks, o_nb;
   size_t route_bytes;  // end of the routing section
@@ -72,6 +74,7 @@ struct Plan {
   size_t o_g, o_u;  // unfused gate and up products [A, ffn] bf16
   size_t o_logits;  // router scores [T, E] fp32 (moe_forward_router)
   size_t o_rparts;  // router partial sums [router.parts, T, E] fp32
+  size_t o_fold;    // arrival counters of the folded combination [T, dn_tiles] int32
   size_t total_bytes;
 };
 
@@ -85,8 +88,15 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, int T, int
 hipError_t launch_router_reduce(const float* parts, int nparts, long long n, float* logits,
                                 hipStream_t s);
 
+// An int32 range the routing kernels set to zero (p may be null): the
+// arrival counters of the folded combination, cleared before the GEMMs run.
+struct ZeroRange {
+  int32_t* p;
+  int n;
+};
+
 hipError_t launch_route(const LogitSrc& logits, int T, int E, int k, int renorm, int score,
-                        int32_t* ids, float* w, hipStream_t s);
+                        int32_t* ids, float* w, ZeroRange zero, hipStream_t s);
 
 hipError_t launch_hist_scan(const int32_t* ids, int A, int E, int bm, int nchunks,
                             int32_t* counts, int32_t* offsets, int32_t* chunk_cnt,
@@ -107,7 +117,8 @@ bool small_routing_fits(int T, int E, int k);
 hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int k, int renorm,
                                        int score, int bm, int32_t* ids, float* w,
                                        int32_t* counts, int32_t* offsets, int32_t* perm,
-                                       int32_t* inv, int32_t* blocks, int32_t* nb, hipStream_t s);
+                                       int32_t* inv, int32_t* blocks, int32_t* nb,
+                                       ZeroRange zero, hipStream_t s);
 
 hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int A, int d, int k,
                          uint16_t* x_perm, hipStream_t s);
@@ -139,11 +150,26 @@ hipError_t launch_proj_bf16(int bm, const uint16_t* x, const int32_t* gather_per
 hipError_t launch_swiglu_act(const uint16_t* g, const uint16_t* u, uint16_t* h, long long n,
                              hipStream_t s);
 
-// Down grouped GEMM: y[split, A, d] = partial sums of h Wd^T per block.
+// The weighted combination folded into the down GEMM (cnt null: not
+// folded).  cnt [T, tiles] counts the partials written for each (token,
+// column tile) and must be zero when the GEMM starts; the workgroup that
+// writes the last of a token's k * split partials of a tile writes that
+// token's output columns of the tile.
+struct FoldCombine {
+  const int32_t* perm;
+  const int32_t* inv;
+  const float* w;
+  int k;
+  int32_t* cnt;
+  uint16_t* out;
+};
+
+// Down grouped GEMM: y[split, A, d] = partial sums of h Wd^T per block, and
+// with fold.cnt the weighted combination into fold.out.
 hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w_down,
                        const int32_t* blocks, const int32_t* nb, const int32_t* offsets, float* y,
                        int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
-                       int xcd_group, hipStream_t s);
+                       int xcd_group, const FoldCombine& fold, hipStream_t s);
 
 // Weighted combination: out[t] = bf16(sum_j w[t,j] * sum_s y[s, inv[t*k+j]]).
 hipError_t launch_combine(const float* y, int split, int A, int d, const int32_t* inv,

@@ -128,6 +128,18 @@ typedef struct moe_options {
      * the 8 XCDs runs a contiguous range of (block, tile) ids, so a block's
      * rows are fetched into one L2.  Same results either way. */
     int xcd_order;
+    /* Weighted combination.  The number of launches is a free choice of the
+     * method, fusion depth against launch overhead ([R] "Assumptions & free
+     * parameters").  0 = automatic (the separate kernel, measured faster on
+     * every workload shape), 1 = its own kernel after the down GEMM, 2 = folded
+     * into the down GEMM: each of its workgroups counts the partial rows it
+     * wrote per (token, column tile), and the workgroup that writes the last
+     * of a token's top_k * split partials of a tile also writes that token's
+     * output columns of the tile -- the same sums in the same fixed order as
+     * the separate kernel, so the output bytes are the same either way.  The
+     * routing kernels clear the counters (4*T*ceil(d/256) bytes or fewer of
+     * workspace) on every call. */
+    int fold_combine;
     /* NULL, or 7 hipEvent_t handles created by the caller (for instance
      * with moe_timer_create).  events[0] is recorded on the stream before
      * the first kernel and events[i] right after kernel i (1 route, 2
@@ -135,7 +147,8 @@ typedef struct moe_options {
      * GEMM (or the three unfused kernels), 5 down GEMM, 6 weighted
      * combination).  With the one-workgroup
      * routing kernel, events 1 and 2 are both recorded after it; with the
-     * gather inside the GEMM, event 3 follows the routing directly.
+     * gather inside the GEMM, event 3 follows the routing directly; with
+     * the combination folded, events 5 and 6 both follow the down GEMM.
      * NULL entries are skipped.  moe_route records 0..3 only. */
     void *const *stage_events;
 } moe_options;

@@ -65,9 +65,10 @@ def test_workspace_size_checks():
     assert moe.lib().moe_workspace_size(4, 64, 64, 4, 2, None) == NULL
 
 
-def _o(bm=0, split=0, variant=0, rotate=0, routing=0, gather=0, unfused=0, xcd=0, dvar=0):
+def _o(bm=0, split=0, variant=0, rotate=0, routing=0, gather=0, unfused=0, xcd=0, dvar=0,
+       fold=0):
     return ctypes.byref(_lib.MoeOptions(bm, split, variant, dvar, rotate, routing, gather, unfused,
-                                        xcd, None))
+                                        xcd, fold, None))
 
 
 def test_options_checks():
@@ -116,6 +117,22 @@ def test_routing_and_gather_options():
     g2 = moe.moe_workspace_size(512, 4096, 14336, 8, 2, gather_mode=2)
     assert g2 - g1 == 1024 * 4096 * 2
     assert moe.moe_workspace_size(512, 4096, 14336, 8, 2) == g1
+
+
+def test_fold_combine_option():
+    for bad in (_o(fold=3), _o(fold=-1)):
+        assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
+    for f in (0, 1, 2):
+        assert _ws(64, 256, 512, 8, 2, _o(fold=f))[0] == OK
+    # folded: one int32 arrival counter per (token, down-GEMM column tile);
+    # Mixtral T=512 at BM=192 has 256-column down tiles -> 512 * 16 counters
+    f1 = moe.moe_workspace_size(512, 4096, 14336, 8, 2, fold_combine=1)
+    f2 = moe.moe_workspace_size(512, 4096, 14336, 8, 2, fold_combine=2)
+    assert f2 - f1 == 512 * 16 * 4
+    # the 16-row tiles of the down GEMM are 512 columns wide
+    g1 = moe.moe_workspace_size(64, 1024, 512, 8, 2, block_rows=16, fold_combine=1)
+    g2 = moe.moe_workspace_size(64, 1024, 512, 8, 2, block_rows=16, fold_combine=2)
+    assert g2 - g1 == 64 * 2 * 4
 
 
 def test_plan_choices_for_the_workloads():
