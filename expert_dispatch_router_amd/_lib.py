@@ -42,8 +42,8 @@ SIGNATURES = {
     "moe_forward_router": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ,
                                 _P]),
     "moe_route_workspace_size": (_I, [_I, _I, _I, _P, ctypes.POINTER(_SZ)]),
-    "moe_route": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P,
-                       ctypes.POINTER(_I), _P, _SZ, _P]),
+    "moe_route": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I,
+                       _P, ctypes.POINTER(_I), _P, _SZ, _P]),
     "moe_timer_create": (_I, [ctypes.POINTER(_P)]),
     "moe_timer_destroy": (_I, [_P]),
     "moe_timer_record": (_I, [_P, _P]),
@@ -275,8 +275,8 @@ def moe_forward_router(x, W_router, W_gate_up, W_down, top_k, renormalize, out=N
 def moe_route(router_logits, top_k, renormalize, score="softmax", x=None, block_rows=0,
               workspace=None, stream=None, routing_kernels=0):
     """Runs the routing kernels and returns a dict of GPU tensors: ids, w,
-    counts, offsets, perm, inv, blocks [nb_max,2], nb [1], x_perm (if x is
-    given) and the host int bm."""
+    counts, offsets, perm, inv, blocks [nb_max,2], nb [1], order [nb_max]
+    (the blocks longest first), x_perm (if x is given) and the host int bm."""
     T, E = router_logits.shape
     dev = router_logits.device
     A = T * top_k
@@ -293,6 +293,7 @@ def moe_route(router_logits, top_k, renormalize, score="softmax", x=None, block_
     nb_max = (A + bm - 1) // bm + min(E, A) if A > 0 else 0
     res["blocks"] = torch.zeros(max(nb_max, 1), 2, **i32)
     res["nb"] = torch.zeros(1, **i32)
+    res["order"] = torch.zeros(max(nb_max, 1), **i32)
     d = 0
     if x is not None:
         d = x.shape[1]
@@ -303,7 +304,7 @@ def moe_route(router_logits, top_k, renormalize, score="softmax", x=None, block_
         int(bool(renormalize)), _score_code(score), ctypes.byref(o) if o else None,
         res["ids"].data_ptr(), res["w"].data_ptr(), res["counts"].data_ptr(),
         res["offsets"].data_ptr(), res["perm"].data_ptr(), res["inv"].data_ptr(),
-        res["blocks"].data_ptr(), res["nb"].data_ptr(),
+        res["blocks"].data_ptr(), res["nb"].data_ptr(), res["order"].data_ptr(),
         _dev_ptr(x, torch.bfloat16, "x") if x is not None else None, d,
         res["x_perm"].data_ptr() if x is not None else None, ctypes.byref(bm_used),
         _dev_ptr(workspace, torch.uint8, "workspace"), workspace.numel(),

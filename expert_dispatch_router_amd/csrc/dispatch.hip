@@ -44,11 +44,15 @@ __device__ int block_inclusive_scan(int v, int* sh) {
 // One workgroup.  Per chunk c of kChunk flat rows: count each expert in LDS,
 // record the count and the number of earlier rows of that expert.  Then the
 // expert totals, their exclusive prefix (offsets), the number of blocks of
-// each expert, their prefix, and the block table.
+// each expert, their prefix, and the block table.  With `order`, also the
+// longest-first launch order of the blocks: the full blocks in block order,
+// then each expert's partial last block by rows descending, ties to the
+// lower expert -- a stable sort of the blocks by decreasing row count.
 __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
     const int32_t* __restrict__ ids, int A, int E, int bm, int nchunks,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ chunk_cnt,
-    int32_t* __restrict__ chunk_base, int32_t* __restrict__ blocks, int32_t* __restrict__ nb) {
+    int32_t* __restrict__ chunk_base, int32_t* __restrict__ blocks, int32_t* __restrict__ nb,
+    int32_t* __restrict__ order) {
   __shared__ int hist[MOE_MAX_EXPERTS];
   __shared__ int run[MOE_MAX_EXPERTS];
   __shared__ int sh[MOE_MAX_EXPERTS];
@@ -85,6 +89,26 @@ __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
     }
   }
   if (tid == E - 1) nb[0] = bincl;
+  if (order) {  // uniform
+    const int nfull = cnt / bm;
+    const int rem = cnt - nfull * bm;
+    const int fincl = block_inclusive_scan(nfull, sh);
+    const int ftotal = sh[MOE_MAX_EXPERTS - 1];
+    if (tid < E) {
+      const int b0 = bincl - nbk;
+      for (int r = 0; r < nfull; ++r) order[fincl - nfull + r] = b0 + r;
+      hist[tid] = rem;
+    }
+    __syncthreads();
+    if (tid < E && rem > 0) {
+      int rank = 0;
+      for (int e = 0; e < E; ++e) {
+        const int q = hist[e];
+        rank += (q > rem) || (q == rem && e < tid);
+      }
+      order[ftotal + rank] = bincl - 1;
+    }
+  }
 }
 
 // One wave per (chunk, expert).  The wave walks its chunk in order, 64 rows
@@ -170,7 +194,8 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
     const LogitSrc logits, int T, int E, int k, int renorm, int score, int bm,
     int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
-    int32_t* __restrict__ blocks, int32_t* __restrict__ nb, ZeroRange zero) {
+    int32_t* __restrict__ blocks, int32_t* __restrict__ nb, int32_t* __restrict__ order,
+    ZeroRange zero) {
   static_assert(EMAX <= 32 && EMAX * kSmallWaves <= kScanThreads, "one thread per (e, wave)");
   __shared__ unsigned long long wmask[EMAX * kSmallWaves];  // [e][wave] ballot of expert e
   __shared__ int start[EMAX * kSmallWaves];                 // [e][wave] first sorted position
@@ -288,6 +313,28 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
         blocks[2 * (b0 + r) + 1] = first + r * bm;
       }
     }
+    // longest-first launch order, as in hist_scan_kernel (lanes >= E have
+    // no rows and take no part)
+    if (order) {
+      const int nfull = cnt / bm;
+      const int rem = cnt - nfull * bm;
+      int fincl = nfull;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(fincl, off, 64);
+        if (lane >= off) fincl += o;
+      }
+      const int ftotal = __shfl(fincl, 63, 64);
+      if (lane < E)
+        for (int r = 0; r < nfull; ++r) order[fincl - nfull + r] = bincl - nbk + r;
+      int rank = 0;
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) {
+        const int q = __shfl(rem, e, 64);
+        rank += (q > rem) || (q == rem && e < lane);
+      }
+      if (lane < E && rem > 0) order[ftotal + rank] = bincl - 1;
+    }
   }
 }
 
@@ -295,9 +342,9 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
 
 hipError_t launch_hist_scan(const int32_t* ids, int A, int E, int bm, int nchunks, int32_t* counts,
                             int32_t* offsets, int32_t* chunk_cnt, int32_t* chunk_base,
-                            int32_t* blocks, int32_t* nb, hipStream_t s) {
+                            int32_t* blocks, int32_t* nb, int32_t* order, hipStream_t s) {
   hist_scan_kernel<<<1, kScanThreads, 0, s>>>(ids, A, E, bm, nchunks, counts, offsets, chunk_cnt,
-                                              chunk_base, blocks, nb);
+                                              chunk_base, blocks, nb, order);
   return hipGetLastError();
 }
 
@@ -336,11 +383,12 @@ hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int
                                        int score, int bm, int32_t* ids, float* w,
                                        int32_t* counts, int32_t* offsets, int32_t* perm,
                                        int32_t* inv, int32_t* blocks, int32_t* nb,
-                                       ZeroRange zero, hipStream_t s) {
+                                       int32_t* order, ZeroRange zero, hipStream_t s) {
   if (!small_routing_fits(T, E, k)) return hipErrorInvalidValue;
 #define MOE_LAUNCH_SMALL(EMAX)                                                               \
   route_dispatch_small_kernel<EMAX><<<1, kScanThreads, 0, s>>>(                              \
-      logits, T, E, k, renorm, score, bm, ids, w, counts, offsets, perm, inv, blocks, nb, zero)
+      logits, T, E, k, renorm, score, bm, ids, w, counts, offsets, perm, inv, blocks, nb, order, \
+      zero)
   if (E <= 8)
     MOE_LAUNCH_SMALL(8);
   else if (E <= 16)

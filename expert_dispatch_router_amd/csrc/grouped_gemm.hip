@@ -85,7 +85,8 @@ __global__ __launch_bounds__(WAVES * 64, (Gemm<BM, NWT, WAVES, PF, MODE>::kMinBl
 void grouped_gemm_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
-    const int32_t* __restrict__ offsets, void* __restrict__ out, int A, int N, int K, int ksplit,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ offsets,
+    void* __restrict__ out, int A, int N, int K, int ksplit,
     int tiles_per_block, int rotate, const int32_t* __restrict__ gather_perm, int gather_k,
     int x_rows, int xcd_group, int x_tiled, FoldCombine fold) {
   using G = Gemm<BM, NWT, WAVES, PF, MODE>;
@@ -105,9 +106,13 @@ void grouped_gemm_kernel(
     if (wg >= r8) return;
     wg = (wg % kXcds) * (r8 / kXcds) + wg / kXcds;
   }
-  const int b = wg / tiles_per_block;
-  if (b >= nb_dev[0]) return;  // beyond the schedule built on the device
-  const int rem = wg - b * tiles_per_block;
+  // Without XCD grouping the blocks may be taken longest first (`order`,
+  // built on the device): the heavy blocks start in the first round and the
+  // light ones fill the tail.  Results do not depend on the order.
+  const int bi = wg / tiles_per_block;
+  if (bi >= nb_dev[0]) return;  // beyond the schedule built on the device
+  const int b = order ? order[bi] : bi;
+  const int rem = wg - bi * tiles_per_block;
   const int e = blocks[2 * b];
   const int r0 = blocks[2 * b + 1];
   const int rows = min(BM, offsets[e + 1] - r0);
@@ -385,7 +390,8 @@ void grouped_gemm_kernel(
 
 template <int BM, int NWT, int WAVES, int PF, int MODE>
 hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride, const int32_t* blocks,
-                      const int32_t* nb, const int32_t* offsets, void* out, int A, int N, int K,
+                      const int32_t* nb, const int32_t* order, const int32_t* offsets, void* out,
+                      int A, int N, int K,
                       int split, int ksplit, int nb_max, int rotate, const int32_t* gather_perm,
                       int gather_k, int x_rows, int xcd_group, int x_tiled,
                       const FoldCombine& fold, hipStream_t s) {
@@ -395,7 +401,7 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
   const long long grid = (long long)tiles_per_block * nb_max;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   grouped_gemm_kernel<BM, NWT, WAVES, PF, MODE><<<(unsigned)grid, G::kThreads, 0, s>>>(
-      X, W, w_estride, blocks, nb, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
+      X, W, w_estride, blocks, nb, order, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
       gather_perm, gather_k, x_rows, xcd_group, x_tiled, fold);
   return hipGetLastError();
 }
@@ -434,13 +440,14 @@ int down_tile_cols(int bm, int variant) {
 
 hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t* gather_perm,
                           int k, int T, const uint16_t* w_gate_up, const int32_t* blocks,
-                          const int32_t* nb, const int32_t* offsets, uint16_t* h, int A, int d,
+                          const int32_t* nb, const int32_t* order, const int32_t* offsets,
+                          uint16_t* h, int A, int d,
                           int ffn, int nb_max, int rotate, int xcd_group, int x_tiled,
                           hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && variant == V)                                                                \
     return launch_cfg<BM, NWT, WV, PF, kOutSwiGLU>(x, w_gate_up, 2LL * ffn * d, blocks, nb,      \
-                                                   offsets, h, A, ffn, d, 1, d, nb_max, rotate,  \
+                                                   order, offsets, h, A, ffn, d, 1, d, nb_max, rotate,  \
                                                    gather_perm, k, x_tiled ? (A + 15) / 16 * 16 : T, \
                                                    xcd_group, x_tiled, FoldCombine{}, s);
   MOE_GU_CFGS(X)
@@ -449,13 +456,14 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
 }
 
 hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w_down,
-                       const int32_t* blocks, const int32_t* nb, const int32_t* offsets, float* y,
+                       const int32_t* blocks, const int32_t* nb, const int32_t* order,
+                       const int32_t* offsets, float* y,
                        int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
                        int xcd_group, const FoldCombine& fold, hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && V == variant)                                                                      \
     return launch_cfg<BM, NWT, WV, PF, kOutF32Parts>(h, w_down, (long long)d * ffn, blocks, nb,  \
-                                                     offsets, y, A, d, ffn, split, ksplit,       \
+                                                     order, offsets, y, A, d, ffn, split, ksplit,       \
                                                      nb_max, rotate, nullptr, 1, A, xcd_group, 0,\
                                                      fold, s);
   MOE_DN_CFGS(X)
@@ -465,13 +473,15 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
 
 hipError_t launch_proj_bf16(int bm, const uint16_t* x, const int32_t* gather_perm, int k, int T,
                             const uint16_t* w, long long w_estride, const int32_t* blocks,
-                            const int32_t* nb, const int32_t* offsets, uint16_t* out, int A, int d,
+                            const int32_t* nb, const int32_t* order, const int32_t* offsets,
+                            uint16_t* out, int A, int d,
                             int ffn, int nb_max, int rotate, int xcd_group, int x_tiled,
                             hipStream_t s) {
 #define X(V, BM, NWT, WV, PF)                                                                   \
   if constexpr (V == 0) {                                                                       \
     if (bm == BM)                                                                               \
-      return launch_cfg<BM, NWT, WV, PF, kOutBF16>(x, w, w_estride, blocks, nb, offsets, out, A, \
+      return launch_cfg<BM, NWT, WV, PF, kOutBF16>(x, w, w_estride, blocks, nb, order, offsets,   \
+                                                   out, A,                                     \
                                                    ffn, d, 1, d, nb_max, rotate, gather_perm, k, \
                                                    x_tiled ? (A + 15) / 16 * 16 : T, xcd_group,  \
                                                    x_tiled, FoldCombine{}, s);                  \

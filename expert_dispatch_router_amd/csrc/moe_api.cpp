@@ -62,7 +62,7 @@ int check_options(const moe_options* opt) {
   if (opt->routing_kernels < 0 || opt->routing_kernels > 2) return MOE_ERR_UNSUPPORTED;
   if (opt->gather_mode < 0 || opt->gather_mode > 3) return MOE_ERR_UNSUPPORTED;
   if (opt->unfused_swiglu < 0 || opt->unfused_swiglu > 1) return MOE_ERR_UNSUPPORTED;
-  if (opt->xcd_order < 0 || opt->xcd_order > 2) return MOE_ERR_UNSUPPORTED;
+  if (opt->xcd_order < 0 || opt->xcd_order > 3) return MOE_ERR_UNSUPPORTED;
   if (opt->fold_combine < 0 || opt->fold_combine > 2) return MOE_ERR_UNSUPPORTED;
   if (opt->down_variant < 0) return MOE_ERR_UNSUPPORTED;
   if (opt->down_variant > 0) {
@@ -147,6 +147,15 @@ int auto_gu_variant(int A, int E, int ffn, int bm) {
 // schedule blocks (each XCD then streams its own range of experts and keeps
 // their activation rows in its L2), and neutral to a few percent slower with
 // few blocks (a few experts' weights then stream through one XCD each).
+// Launching the blocks longest first when they are not grouped by XCD:
+// measured no faster on the skewed workloads (the tail round of a launch is
+// bound by each workgroup's own stream, not by which blocks run in it) and
+// slower on some uniform ones, so automatic is off.
+bool auto_longest_first(int A, int E, int bm) {
+  (void)A, (void)E, (void)bm;
+  return false;
+}
+
 bool auto_xcd_order(int A, int E, int bm) {
   const long long blocks = std::max<long long>((A + bm - 1) / bm, std::min(E, A));
   return blocks >= 128;
@@ -202,6 +211,7 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     p->dn_rotate = rot == 0 ? auto_rotate(ffn) : rot - 1;
     const int xo = opt ? opt->xcd_order : 0;
     p->gu_xcd = p->dn_xcd = xo == 0 ? auto_xcd_order(A, E, p->bm) : xo == 2;
+    p->longest_first = xo == 3 || (xo == 0 && !p->gu_xcd && auto_longest_first(A, E, p->bm));
     const int fc = opt ? opt->fold_combine : 0;
     p->fold = fc == 0 ? auto_fold(T, d, E, k) : fc == 2;
     const int dcols = down_tile_cols(p->bm, p->dn_variant);
@@ -224,6 +234,7 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->o_inv = seg((size_t)A * 4);
   p->o_blocks = seg((size_t)p->nb_max * 2 * 4);
   p->o_nb = seg(4);
+  p->o_order = seg((size_t)p->nb_max * 4);
   p->route_bytes = o;
   p->o_xperm = seg(p->gather_in_gemm ? 0 : (size_t)(A + 15) / 16 * 16 * d * 2);
   p->o_h = seg((size_t)A * ffn * 2);
@@ -264,7 +275,7 @@ int record(const moe_options* opt, int i, hipStream_t s) {
 // K1..K3 into the workspace's routing section: one workgroup for small
 // problems, else three launches.
 int run_routing(const LogitSrc& logits, const Plan& p, int renorm, int score, void* ws,
-                const moe_options* opt, ZeroRange zero, hipStream_t s) {
+                const moe_options* opt, int32_t* order, ZeroRange zero, hipStream_t s) {
   int32_t* ids = at<int32_t>(ws, p.o_ids);
   float* w = at<float>(ws, p.o_w);
   int32_t* offsets = at<int32_t>(ws, p.o_offsets);
@@ -274,7 +285,7 @@ int run_routing(const LogitSrc& logits, const Plan& p, int renorm, int score, vo
                                             at<int32_t>(ws, p.o_counts), offsets,
                                             at<int32_t>(ws, p.o_perm), at<int32_t>(ws, p.o_inv),
                                             at<int32_t>(ws, p.o_blocks), at<int32_t>(ws, p.o_nb),
-                                            zero, s));
+                                            order, zero, s));
     MOE_TRY(record(opt, 1, s));
     MOE_TRY(record(opt, 2, s));
     return MOE_OK;
@@ -283,7 +294,7 @@ int run_routing(const LogitSrc& logits, const Plan& p, int renorm, int score, vo
   MOE_TRY(record(opt, 1, s));
   MOE_TRY_HIP(launch_hist_scan(ids, p.A, p.E, p.bm, p.nchunks, at<int32_t>(ws, p.o_counts),
                                offsets, at<int32_t>(ws, p.o_ccnt), at<int32_t>(ws, p.o_cbase),
-                               at<int32_t>(ws, p.o_blocks), at<int32_t>(ws, p.o_nb), s));
+                               at<int32_t>(ws, p.o_blocks), at<int32_t>(ws, p.o_nb), order, s));
   MOE_TRY(record(opt, 2, s));
   MOE_TRY_HIP(launch_permute(ids, p.A, p.E, p.nchunks, offsets, at<int32_t>(ws, p.o_ccnt),
                              at<int32_t>(ws, p.o_cbase), at<int32_t>(ws, p.o_perm),
@@ -299,7 +310,8 @@ int forward_from_logits(const uint16_t* x, const LogitSrc& router_logits, const 
   // With the combination folded into the down GEMM, the routing kernels
   // clear its arrival counters.
   int32_t* fold_cnt = p.fold ? at<int32_t>(workspace, p.o_fold) : nullptr;
-  MOE_TRY(run_routing(router_logits, p, renorm, score, workspace, opt,
+  int32_t* order = p.longest_first ? at<int32_t>(workspace, p.o_order) : nullptr;
+  MOE_TRY(run_routing(router_logits, p, renorm, score, workspace, opt, order,
                       ZeroRange{fold_cnt, p.fold ? T * p.dn_tiles : 0}, s));
   const int32_t* perm = at<int32_t>(workspace, p.o_perm);
   const int32_t* blocks = at<int32_t>(workspace, p.o_blocks);
@@ -322,22 +334,22 @@ int forward_from_logits(const uint16_t* x, const LogitSrc& router_logits, const 
     uint16_t* u = at<uint16_t>(workspace, p.o_u);
     const long long estride = 2LL * ffn * d;
     MOE_TRY_HIP(launch_proj_bf16(p.bm, X, gperm, top_k, T, W_gate_up, estride, blocks, nb,
-                                 offsets, g, p.A, d, ffn, p.nb_max, p.gu_rotate, p.gu_xcd,
+                                 order, offsets, g, p.A, d, ffn, p.nb_max, p.gu_rotate, p.gu_xcd,
                                  p.x_tiled, s));
     MOE_TRY_HIP(launch_proj_bf16(p.bm, X, gperm, top_k, T, W_gate_up + (size_t)ffn * d, estride,
-                                 blocks, nb, offsets, u, p.A, d, ffn, p.nb_max, p.gu_rotate,
+                                 blocks, nb, order, offsets, u, p.A, d, ffn, p.nb_max, p.gu_rotate,
                                  p.gu_xcd, p.x_tiled, s));
     MOE_TRY_HIP(launch_swiglu_act(g, u, h, (long long)p.A * ffn, s));
   } else {
     MOE_TRY_HIP(launch_gate_up(p.bm, p.gu_variant, X, gperm, top_k, T, W_gate_up, blocks, nb,
-                               offsets, h, p.A, d, ffn, p.nb_max, p.gu_rotate, p.gu_xcd,
+                               order, offsets, h, p.A, d, ffn, p.nb_max, p.gu_rotate, p.gu_xcd,
                                p.x_tiled, s));
   }
   MOE_TRY(record(opt, 4, s));
   const int32_t* inv = at<int32_t>(workspace, p.o_inv);
   const float* wts = at<float>(workspace, p.o_w);
   const FoldCombine fold{perm, inv, wts, top_k, fold_cnt, out};
-  MOE_TRY_HIP(launch_down(p.bm, p.dn_variant, h, W_down, blocks, nb, offsets, y, p.A, d, ffn,
+  MOE_TRY_HIP(launch_down(p.bm, p.dn_variant, h, W_down, blocks, nb, order, offsets, y, p.A, d, ffn,
                           p.split, p.ksplit, p.nb_max, p.dn_rotate, p.dn_xcd,
                           p.fold ? fold : FoldCombine{}, s));
   MOE_TRY(record(opt, 5, s));
@@ -534,8 +546,8 @@ int moe_forward(const uint16_t* x, const float* router_logits, const uint16_t* W
 int moe_route(const float* router_logits, int T, int E, int top_k, int renormalize,
               int score_func, const moe_options* opt, int32_t* topk_ids, float* topk_w,
               int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, int32_t* blocks,
-              int32_t* nb, const uint16_t* x, int d, uint16_t* x_perm, int* bm_used,
-              void* workspace, size_t workspace_bytes, void* hip_stream) {
+              int32_t* nb, int32_t* block_order, const uint16_t* x, int d, uint16_t* x_perm,
+              int* bm_used, void* workspace, size_t workspace_bytes, void* hip_stream) {
   MOE_TRY(check_sizes(T, 0, 0, E, top_k, false));
   MOE_TRY(check_options(opt));
   MOE_TRY(check_paths(T, 0, E, top_k, opt));
@@ -556,7 +568,8 @@ int moe_route(const float* router_logits, int T, int E, int top_k, int renormali
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   (void)hipGetLastError();
   MOE_TRY(run_routing(LogitSrc{router_logits, 1, 0, nullptr}, p, renormalize ? 1 : 0, score_func,
-                      workspace, opt, ZeroRange{nullptr, 0}, s));
+                      workspace, opt, block_order ? at<int32_t>(workspace, p.o_order) : nullptr,
+                      ZeroRange{nullptr, 0}, s));
   if (gather)
     MOE_TRY_HIP(launch_gather(x, at<int32_t>(workspace, p.o_perm), p.A, d, top_k, x_perm, s));
   MOE_TRY(record(opt, 3, s));
@@ -569,6 +582,7 @@ int moe_route(const float* router_logits, int T, int E, int top_k, int renormali
       {counts, p.o_counts, (size_t)E * 4},           {offsets, p.o_offsets, (size_t)(E + 1) * 4},
       {perm, p.o_perm, (size_t)p.A * 4},             {inv, p.o_inv, (size_t)p.A * 4},
       {blocks, p.o_blocks, (size_t)p.nb_max * 2 * 4}, {nb, p.o_nb, 4},
+      {block_order, p.o_order, (size_t)p.nb_max * 4},
   };
   for (const Copy& c : copies)
     if (c.dst) MOE_TRY_HIP(hipMemcpyAsync(c.dst, at<char>(workspace, c.off), c.bytes, dd, s));

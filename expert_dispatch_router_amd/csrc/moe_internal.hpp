@@ -60,6 +60,7 @@ struct Plan {
   int dn_variant; // tile variant of the down GEMM
   int gu_rotate;  // rotate the K-step start per workgroup (fused gate/up GEMM)
   int gu_xcd, dn_xcd;  // group each block's workgroups on one XCD (see the GEMM kernel)
+  int longest_first;   // else launch the blocks longest first (device-built order)
   int dn_rotate;  // same for the down GEMM
   int small_routing;  // one-workgroup routing kernel instead of three launches
   int gather_in_gemm; // the fused gate/up GEMM reads token rows through perm
@@ -69,6 +70,7 @@ struct Plan {
   int dn_tiles;       // column tiles of the down GEMM (d / its tile width)
   // byte offsets into the workspace (256-byte aligned)
   size_t o_ids, o_w, o_counts, o_offsets, o_ccnt, o_cbase, o_perm, o_inv, o_blocks, o_nb;
+  size_t o_order;  // longest-first launch order of the blocks [nb_max]
   size_t route_bytes;  // end of the routing section
   size_t o_xperm, o_h, o_y;
   size_t o_g, o_u;  // unfused gate and up products [A, ffn] bf16
@@ -98,9 +100,13 @@ struct ZeroRange {
 hipError_t launch_route(const LogitSrc& logits, int T, int E, int k, int renorm, int score,
                         int32_t* ids, float* w, ZeroRange zero, hipStream_t s);
 
+// Histogram, offsets and the block table; with `order` (may be null) also
+// the longest-first launch order of the blocks (a stable sort by decreasing
+// rows: the full blocks in block order, then the partial last blocks).
 hipError_t launch_hist_scan(const int32_t* ids, int A, int E, int bm, int nchunks,
                             int32_t* counts, int32_t* offsets, int32_t* chunk_cnt,
-                            int32_t* chunk_base, int32_t* blocks, int32_t* nb, hipStream_t s);
+                            int32_t* chunk_base, int32_t* blocks, int32_t* nb, int32_t* order,
+                            hipStream_t s);
 
 hipError_t launch_permute(const int32_t* ids, int A, int E, int nchunks, const int32_t* offsets,
                           const int32_t* chunk_cnt, const int32_t* chunk_base, int32_t* perm,
@@ -118,7 +124,7 @@ hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int
                                        int score, int bm, int32_t* ids, float* w,
                                        int32_t* counts, int32_t* offsets, int32_t* perm,
                                        int32_t* inv, int32_t* blocks, int32_t* nb,
-                                       ZeroRange zero, hipStream_t s);
+                                       int32_t* order, ZeroRange zero, hipStream_t s);
 
 hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int A, int d, int k,
                          uint16_t* x_perm, hipStream_t s);
@@ -131,9 +137,13 @@ hipError_t launch_gather_tiled(const uint16_t* x, const int32_t* perm, int A, in
 // Fused gate/up SwiGLU grouped GEMM: h[A, F] = silu(X Wg^T) * (X Wu^T) per
 // block.  X is x_perm [A, d] when gather_perm is null, else the token rows
 // x [T, d] read through gather_perm (row p is x[gather_perm[p] / k]).
+//
+// Every GEMM launcher takes `order`: null = workgroups take the blocks in
+// block order, else in the order listed there (longest first).
 hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t* gather_perm,
                           int k, int T, const uint16_t* w_gate_up, const int32_t* blocks,
-                          const int32_t* nb, const int32_t* offsets, uint16_t* h, int A, int d,
+                          const int32_t* nb, const int32_t* order, const int32_t* offsets,
+                          uint16_t* h, int A, int d,
                           int ffn, int nb_max, int rotate, int xcd_group, int x_tiled,
                           hipStream_t s);
 
@@ -142,7 +152,8 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
 // launch_gate_up.
 hipError_t launch_proj_bf16(int bm, const uint16_t* x, const int32_t* gather_perm, int k, int T,
                             const uint16_t* w, long long w_estride, const int32_t* blocks,
-                            const int32_t* nb, const int32_t* offsets, uint16_t* out, int A, int d,
+                            const int32_t* nb, const int32_t* order, const int32_t* offsets,
+                            uint16_t* out, int A, int d,
                             int ffn, int nb_max, int rotate, int xcd_group, int x_tiled,
                             hipStream_t s);
 
@@ -167,7 +178,8 @@ struct FoldCombine {
 // Down grouped GEMM: y[split, A, d] = partial sums of h Wd^T per block, and
 // with fold.cnt the weighted combination into fold.out.
 hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w_down,
-                       const int32_t* blocks, const int32_t* nb, const int32_t* offsets, float* y,
+                       const int32_t* blocks, const int32_t* nb, const int32_t* order,
+                       const int32_t* offsets, float* y,
                        int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
                        int xcd_group, const FoldCombine& fold, hipStream_t s);
 

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Limits of the library (violations return MOE_ERR_UNSUPPORTED). */
 #define MOE_MAX_EXPERTS 512
@@ -126,7 +126,11 @@ typedef struct moe_options {
      * or more schedule blocks are expected), 1 = plain (workgroup i
      * takes block i / tiles, tile i % tiles), 2 = grouped by XCD: each of
      * the 8 XCDs runs a contiguous range of (block, tile) ids, so a block's
-     * rows are fetched into one L2.  Same results either way. */
+     * rows are fetched into one L2; 3 = longest first: as plain, but over
+     * the blocks in decreasing row count (an order the routing kernels
+     * build on the device; moe_route's block_order), so that under skewed
+     * routing the heavy blocks start first and light ones fill the tail.
+     * Same results either way (with rotate = 3, rounding differs). */
     int xcd_order;
     /* Weighted combination.  The number of launches is a free choice of the
      * method, fusion depth against launch overhead ([R] "Assumptions & free
@@ -271,6 +275,12 @@ int moe_route_workspace_size(int T, int E, int top_k, const moe_options *opt, si
  *                               up to block_rows rows of one expert, experts
  *                               ascending; nb_max = ceil(A/BM) + min(E, A)
  *   nb       int32 [1]          number of valid blocks (device)
+ *   block_order int32 [nb_max]  the blocks longest first (the launch order
+ *                               of xcd_order = 3): a stable sort of the
+ *                               block indices by decreasing row count --
+ *                               the full blocks in block order, then each
+ *                               expert's partial last block by rows
+ *                               descending, equal rows to the lower expert
  *   x, x_perm  bf16 [T, d] and [A, d]: if both are non-NULL, x_perm[p] =
  *                               x[perm[p] / top_k] is also written (d > 0,
  *                               a multiple of 64)
@@ -280,7 +290,7 @@ int moe_route_workspace_size(int T, int E, int top_k, const moe_options *opt, si
 int moe_route(const float *router_logits, int T, int E, int top_k, int renormalize, int score_func,
               const moe_options *opt,
               int32_t *topk_ids, float *topk_w, int32_t *counts, int32_t *offsets,
-              int32_t *perm, int32_t *inv, int32_t *blocks, int32_t *nb,
+              int32_t *perm, int32_t *inv, int32_t *blocks, int32_t *nb, int32_t *block_order,
               const uint16_t *x, int d, uint16_t *x_perm, int *bm_used,
               void *workspace, size_t workspace_bytes, void *hip_stream);
 

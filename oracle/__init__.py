@@ -19,6 +19,7 @@ CUDA"):
   counts_offsets  O3 histogram + scan        [R] "What carries the argument"
   permute         O4 stable reorder          [R] "The reading"; abstract
   block_table     O5 (expert, offset) blocks [R] "What carries the argument"
+  block_order     O5b blocks longest first   [R] "Assumptions & free parameters"
   ffn             O6 SwiGLU FFN + combine    [R] "What carries the argument"
   round_bf16      O7 RNE to bf16
 """
@@ -71,6 +72,7 @@ def _load():
         lib.orc_counts_offsets.argtypes = [P, I, I, P, P]
         lib.orc_permute.argtypes = [P, I, I, P, P, P]
         lib.orc_block_table.argtypes = [P, P, I, I, P, I, P]
+        lib.orc_block_order.argtypes = [P, I, P, I, P]
         lib.orc_ffn_tokens.argtypes = [P, P, P, P, P, I, I, I, I, I, P, I, P]
         lib.orc_round_bf16.argtypes = [P, P, ctypes.c_long]
         lib.orc_router_logits.argtypes = [P, P, I, I, I, P]
@@ -148,6 +150,17 @@ def block_table(counts: np.ndarray, offsets: np.ndarray, BM: int):
     _check(_load().orc_block_table(_ptr(counts), _ptr(offsets), E, BM, _ptr(blocks), max_blocks,
                                    _ptr(nb)), "block_table")
     return blocks[: int(nb[0])].copy(), int(nb[0])
+
+
+def block_order(blocks: np.ndarray, offsets: np.ndarray, BM: int):
+    """O5b: the blocks longest first (stable by block index)."""
+    blocks = np.ascontiguousarray(blocks, dtype=np.int32).reshape(-1, 2)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    nb = blocks.shape[0]
+    order = np.zeros(max(nb, 1), dtype=np.int32)
+    _check(_load().orc_block_order(_ptr(blocks), nb, _ptr(offsets), BM, _ptr(order)),
+           "block_order")
+    return order[:nb].copy()
 
 
 def _expert_ptrs(w, E: int):

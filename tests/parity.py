@@ -4,8 +4,9 @@ bytes, and the acceptance checks.
 Acceptance (the required tolerance of the MoE output): relative Frobenius error
 <= 1e-2 and max-abs error <= 2e-2 * RMS(reference), both against the
 oracle's fp32 result before rounding, computed in float64.  Routing
-artefacts (ids, counts, offsets, perm, inv, blocks, nb) must match bit for
-bit; routing weights to a few fp32 ulps (device and libm expf differ).
+artefacts (ids, counts, offsets, perm, inv, blocks, nb, the longest-first
+block order) must match bit for bit; routing weights to a few fp32 ulps
+(device and libm expf differ).
 """
 from __future__ import annotations
 
@@ -44,7 +45,9 @@ def oracle_routing(logits: torch.Tensor, k: int, score: int, renorm: bool, bm: i
     counts, offsets = oracle.counts_offsets(ids, E)
     perm, inv = oracle.permute(ids, E, offsets)
     blocks, nb = oracle.block_table(counts, offsets, bm)
-    return dict(ids=ids, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, blocks=blocks, nb=nb)
+    order = oracle.block_order(blocks, offsets, bm)
+    return dict(ids=ids, w=w, counts=counts, offsets=offsets, perm=perm, inv=inv, blocks=blocks, nb=nb,
+                order=order)
 
 
 def check_routing(gpu: dict, ref: dict):
@@ -56,6 +59,8 @@ def check_routing(gpu: dict, ref: dict):
     nb = int(gpu["nb"].cpu().item())
     assert nb == ref["nb"], "nb"
     assert np.array_equal(gpu["blocks"].cpu().numpy()[:nb], ref["blocks"]), "blocks"
+    if "order" in gpu:
+        assert np.array_equal(gpu["order"].cpu().numpy()[:nb], ref["order"]), "block order"
     w = gpu["w"].cpu().numpy().astype(np.float64)
     rw = ref["w"].astype(np.float64)
     assert np.all(np.abs(w - rw) <= W_RTOL * np.abs(rw) + 1e-30), "weights"

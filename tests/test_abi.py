@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
         assert n in _lib.SIGNATURES, n
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
 
 
 def test_status_strings():
@@ -106,7 +106,9 @@ def test_routing_and_gather_options():
     assert _ws(64, 256, 512, 8, 2, _o(192, dvar=2))[0] == OK
     assert _ws(64, 256, 512, 8, 2, _o(64, dvar=1))[0] == OK
     # the unfused SwiGLU ablation keeps gate and up products: 2 * A*ffn*2 bytes more
-    for bad in (_o(unfused=2), _o(unfused=-1), _o(xcd=3), _o(xcd=-1), _o(dvar=1), _o(dvar=-1),
+    for x in (0, 1, 2, 3):
+        assert _ws(64, 256, 512, 8, 2, _o(xcd=x))[0] == OK
+    for bad in (_o(unfused=2), _o(unfused=-1), _o(xcd=4), _o(xcd=-1), _o(dvar=1), _o(dvar=-1),
                 _o(64, dvar=2), _o(192, dvar=3)):
         assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
     u0 = moe.moe_workspace_size(512, 4096, 14336, 8, 2)
@@ -203,7 +205,8 @@ def _route(**kw):
     a.update(kw)
     bm = ctypes.c_int(-1)
     rc = moe.lib().moe_route(a["logits"], a["T"], a["E"], a["k"], a["renorm"], a["score"], a["opt"],
-                             FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["x"], a["d"], a["xp"],
+                             FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["x"], a["d"],
+                             a["xp"],
                              ctypes.byref(bm), a["ws"], a["wsb"], None)
     return rc, bm.value
 

@@ -210,10 +210,11 @@ def test_forward_unfused_swiglu_ablation(bm, gather):
     parity.check_out(out, ref, f"unfused bm={bm} gather={gather}", scale=parity.UNFUSED_SCALE)
 
 
-@pytest.mark.parametrize("xcd", [1, 2])
+@pytest.mark.parametrize("xcd", [1, 2, 3])
 @pytest.mark.parametrize("bm,split", [(16, 2), (64, 1), (192, 3)])
 def test_forward_xcd_order(bm, split, xcd):
-    """Both workgroup orders give the oracle's result, and the same bytes."""
+    """Every workgroup order (plain, XCD-grouped, longest block first) gives
+    the oracle's result, and the same bytes."""
     cfg, x, lg, wgu, wd, ref = _mid_case()
     out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm, split_k=split,
                           xcd_order=xcd)
@@ -223,13 +224,15 @@ def test_forward_xcd_order(bm, split, xcd):
     assert torch.equal(out.view(torch.int16), base.view(torch.int16))
 
 
-def test_forward_hot_expert_many_blocks():
-    """All tokens pick expert 1 first: 300 rows of one expert, 10 blocks."""
+@pytest.mark.parametrize("xcd", [1, 3])
+def test_forward_hot_expert_many_blocks(xcd):
+    """All tokens pick expert 1 first: 300 rows of one expert, 10 blocks
+    (in block order, and longest first)."""
     gen = torch.Generator().manual_seed(3)
     lg = torch.randn(300, 8, generator=gen)
     lg[:, 1] += 30.0
     cfg, x, lg, wgu, wd = parity.make_case(300, 256, 128, 8, 2, seed=3, logits=lg)
-    out = moe.moe_forward(x, lg, wgu, wd, 2, True, block_rows=32)
+    out = moe.moe_forward(x, lg, wgu, wd, 2, True, block_rows=32, xcd_order=xcd)
     parity.check_out(out, parity.oracle_out(x, lg, wgu, wd, 2, 0, True), "hot expert")
 
 

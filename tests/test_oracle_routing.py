@@ -158,3 +158,35 @@ def test_sigmoid_saturation_keeps_logit_order():
     ids, w = oracle.route(l, 3, 1, False)
     assert ids.tolist() == [[1, 2, 0]]
     assert np.all(w == 1.0)
+
+
+def test_block_order_hand_worked():
+    """Blocks (BM=2) of the hand-worked case above hold 2, 1, 2, 1 rows:
+    longest first, equal counts in block order -> 0, 2, 1, 3."""
+    ids = np.array([[2, 0], [0, 2], [2, 1]], dtype=np.int32)
+    counts, offsets = oracle.counts_offsets(ids, 3)
+    blocks, nb = oracle.block_table(counts, offsets, 2)
+    assert oracle.block_order(blocks, offsets, 2).tolist() == [0, 2, 1, 3]
+
+
+def test_block_order_is_the_stable_sort_by_rows():
+    """Against numpy's stable argsort of the negated row counts, and the
+    pairwise definition (a permutation; rows non-increasing; equal rows in
+    ascending block index), on skewed random routings."""
+    rng = np.random.default_rng(21)
+    for trial in range(40):
+        E = int(rng.integers(1, 40))
+        k = int(rng.integers(1, min(E, 6) + 1))
+        T = int(rng.integers(0, 300))
+        BM = int(rng.choice([1, 2, 3, 16, 32, 64, 128, 192]))
+        bias = -2.0 * np.log(rng.permutation(E) + 1.0)
+        lg = (rng.standard_normal((T, E)) + bias).astype(np.float32)
+        ids, _ = oracle.route(lg, k, 0, True)
+        counts, offsets = oracle.counts_offsets(ids, E)
+        blocks, nb = oracle.block_table(counts, offsets, BM)
+        order = oracle.block_order(blocks, offsets, BM)
+        rows = np.array([min(BM, offsets[e + 1] - r0) for e, r0 in blocks], dtype=np.int64)
+        assert order.tolist() == np.argsort(-rows, kind="stable").tolist(), trial
+        assert sorted(order.tolist()) == list(range(nb))
+        for a, b in zip(order[:-1], order[1:]):
+            assert rows[a] > rows[b] or (rows[a] == rows[b] and a < b)
