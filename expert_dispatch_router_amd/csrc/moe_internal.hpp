@@ -40,7 +40,7 @@ constexpr int kChunk = 1024;
 
 // Launch shape of the router scores kernel (see router.hip).
 struct RouterPlan {
-  int ts;     // 16-token subtiles per wave (1 or 2)
+  int ts;     // 16-token subtiles per wave (1, 2 or 4)
   int nsub;   // 16-expert subtiles per wave (1, 2 or 4)
   int parts;  // split of the reduction over d (partial sums added in order)
 };

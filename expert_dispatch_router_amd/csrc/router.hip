@@ -13,8 +13,11 @@
 // One wave computes a tile of 16*TS tokens x 16*NSUB experts over one range
 // with v_mfma_f32_16x16x32_bf16 (W_r as the A operand, x as B: lane l holds
 // experts e0 + 4*(l/16) + r of token t0 + l%16 in each 16x16 subtile),
-// streaming its range through a ring of kRouterRing chunks; each x fragment
-// serves NSUB MFMAs and each W_r fragment TS.  A workgroup's 4 waves are 2
+// streaming its range through a ring of RING chunks; each x fragment serves
+// NSUB MFMAs and each W_r fragment TS.  The reads of x and W_r beyond the
+// first come from L2 (x once per expert tile, W_r once per token tile), so
+// large problems take the 64 x 64 tile (4 x 4 subtiles, a 2-deep ring to
+// stay within two waves per SIMD).  A workgroup's 4 waves are 2
 // token tiles x 2 expert tiles (4 token tiles when E fits one expert tile),
 // so waves sharing rows read them together.  With one part the wave writes
 // the logits; otherwise it writes its partial sums [part][T][E], which the
@@ -28,10 +31,9 @@ namespace moe {
 namespace {
 
 constexpr int kRouterWaves = 4;      // waves per workgroup: 2 token tiles x 2 expert tiles
-constexpr int kRouterRing = 4;       // 64-wide K chunks in flight per wave
 constexpr int kRouterTargetWaves = 1024;
 
-template <int TS, int NSUB>
+template <int TS, int NSUB, int RING>  // RING: 64-wide K chunks in flight per wave
 __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E,
     int parts, int wg_e, float* __restrict__ out) {
@@ -62,10 +64,10 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
   for (int i = 0; i < TS; ++i)
 #pragma unroll
     for (int j = 0; j < NSUB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Ring of kRouterRing chunks; chunk c lives in slot (c - c0) % ring.
+  // Ring of RING chunks; chunk c lives in slot (c - c0) % RING.
   // Every reload is unconditional (clamped to the last chunk), so the
   // compiler's wait before a slot's MFMAs covers exactly that slot.
-  bf16x8 rb[kRouterRing][TS][2], ra[kRouterRing][NSUB][2];
+  bf16x8 rb[RING][TS][2], ra[RING][NSUB][2];
   auto load = [&](int u, int c) {
     const int soff = min(c, c1 - 1) * 128;
 #pragma unroll
@@ -80,10 +82,10 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
     }
   };
 #pragma unroll
-  for (int u = 0; u < kRouterRing; ++u) load(u, c0 + u);
-  for (int cb = c0; cb < c1; cb += kRouterRing) {
+  for (int u = 0; u < RING; ++u) load(u, c0 + u);
+  for (int cb = c0; cb < c1; cb += RING) {
 #pragma unroll
-    for (int u = 0; u < kRouterRing; ++u) {
+    for (int u = 0; u < RING; ++u) {
       if (cb + u < c1) {  // wave-uniform
 #pragma unroll
         for (int i = 0; i < TS; ++i)
@@ -96,7 +98,7 @@ __global__ __launch_bounds__(kRouterWaves * 64) void router_kernel(
           }
       }
       __builtin_amdgcn_sched_barrier(0);
-      load(u, cb + u + kRouterRing);
+      load(u, cb + u + RING);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -130,8 +132,10 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restr
 
 RouterPlan plan_router(int T, int d, int E) {
   RouterPlan rp;
-  rp.ts = T >= 64 ? 2 : 1;
-  rp.nsub = E <= 16 ? 1 : 2;
+  // 64-row tiles of x and W_r need 64*d*2 bytes within a 32-bit buffer range
+  const bool wide_ok = 128LL * d < (1LL << 31);
+  rp.ts = (T >= 1024 && wide_ok) ? 4 : T >= 64 ? 2 : 1;
+  rp.nsub = (E >= 128 && rp.ts == 4) ? 4 : E <= 16 ? 1 : 2;
   const long long tiles = (long long)((T + 16 * rp.ts - 1) / (16 * rp.ts)) *
                           ((E + 16 * rp.nsub - 1) / (16 * rp.nsub));
   const int nch = d / 64;
@@ -152,13 +156,14 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, int T, int
   const int wg_t = kRouterWaves / wg_e;
   const int t_tiles = (T + 16 * rp.ts - 1) / (16 * rp.ts);
   const dim3 grid((t_tiles + wg_t - 1) / wg_t, (e_tiles + wg_e - 1) / wg_e, rp.parts);
-#define MOE_ROUTER(TS, NSUB)                                                                   \
+#define MOE_ROUTER(TS, NSUB, RING)                                                             \
   if (rp.ts == TS && rp.nsub == NSUB) {                                                        \
-    router_kernel<TS, NSUB><<<grid, kRouterWaves * 64, 0, s>>>(x, w_router, T, d, E, rp.parts,  \
-                                                               wg_e, out);                     \
+    router_kernel<TS, NSUB, RING><<<grid, kRouterWaves * 64, 0, s>>>(x, w_router, T, d, E,      \
+                                                                     rp.parts, wg_e, out);     \
     return hipGetLastError();                                                                  \
   }
-  MOE_ROUTER(1, 1) MOE_ROUTER(1, 2) MOE_ROUTER(2, 1) MOE_ROUTER(2, 2)
+  MOE_ROUTER(1, 1, 4) MOE_ROUTER(1, 2, 4) MOE_ROUTER(2, 1, 4) MOE_ROUTER(2, 2, 4)
+  MOE_ROUTER(4, 1, 2) MOE_ROUTER(4, 2, 2) MOE_ROUTER(4, 4, 2)
 #undef MOE_ROUTER
   return hipErrorInvalidValue;
 }

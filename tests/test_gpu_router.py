@@ -58,16 +58,19 @@ def _check_scores(got, x, wr):
 
 @pytest.mark.parametrize("T,d,E", [(1, 64, 1), (17, 128, 6), (100, 512, 60), (33, 1024, 256),
                                    (40, 7168, 256), (5, 64, 512), (300, 256, 16), (64, 4096, 8),
-                                   (130, 2048, 33), (513, 1024, 17), (97, 3584, 64)])
+                                   (130, 2048, 33), (513, 1024, 17), (97, 3584, 64),
+                                   (1030, 192, 130), (1024, 64, 16), (2000, 320, 40),
+                                   (1100, 7168, 256)])
 def test_router_scores_within_the_summation_bound(T, d, E):
     """Shapes with one part and with the reduction split in several (the
-    partial sums added in order), ragged in tokens and experts."""
+    partial sums added in order), ragged in tokens and experts, for every
+    wave tile (16..64 tokens x 16..64 experts)."""
     x, wr = _router_case(T, d, E, seed=T + d + E)
     got = moe.moe_router_logits(x, wr)
     _check_scores(got, x, wr)
 
 
-@pytest.mark.parametrize("name", ["mixtral_512", "dsv3_512"])
+@pytest.mark.parametrize("name", ["mixtral_512", "dsv3_512", "dsv3_4096"])
 def test_router_scores_full_size(name):
     cfg = synth.CONFIGS[name]
     x = synth.make_x(cfg, 0, DEV)
