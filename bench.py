@@ -183,9 +183,10 @@ def run(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x, logits, wgu, wd = synth.make_inputs(cfg, args.seed, dev)
-    bm, split = moe.moe_plan(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k)
-    out = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
     unfused = 1 if args.unfused else 0
+    bm, split, fused_down = moe.moe_plan(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k,
+                                         unfused_swiglu=unfused, with_fusion=True)
+    out = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(moe.moe_workspace_size(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k,
                                             unfused_swiglu=unfused),
                      dtype=torch.uint8, device=dev)
@@ -198,6 +199,9 @@ def run(args):
     routing = moe.moe_route(logits, cfg.top_k, cfg.renormalize, cfg.score)
     counts = routing["counts"].cpu().numpy()
     alg = algorithmic(cfg, counts)
+    if fused_down:
+        # one kernel streams the gate/up and the down weights
+        alg["bytes_k4"] = alg["e_act"] * 6.0 * cfg.ffn * cfg.d + 2.0 * alg["A"] * cfg.d
 
     def step(events=None, strm=None):
         moe.moe_forward(x, logits, wgu, wd, cfg.top_k, cfg.renormalize, out=out, score=cfg.score,
@@ -261,7 +265,8 @@ def run(args):
                    "tokens": cfg.T, "hidden": cfg.d, "ffn": cfg.ffn, "experts": cfg.E,
                    "top_k": cfg.top_k, "block_rows": bm, "split_k": split,
                    "active_experts": alg["e_act"], "seed": args.seed,
-                   "swiglu": "unfused ablation" if unfused else "fused"},
+                   "swiglu": "unfused ablation" if unfused else "fused",
+                   "down_projection": "in the gate/up GEMM" if fused_down else "own GEMM"},
         "tflops": alg["flop"] / t_step / 1e12,
         "hbm_gbs": alg["bytes"] / t_step / 1e9,
         "roofline_frac_step": t_roof / t_step,
@@ -272,9 +277,11 @@ def run(args):
         "pass_ms_pct": pct(pass_each),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if unfused else traffic_for(cfg.name),
+                     "traffic": None if (unfused or fused_down) else traffic_for(cfg.name),
                      "kernel": ("gate/up stage of the unfused ablation (gate GEMM + up GEMM + "
                                 "activation)") if unfused else
+                               ("gate_up_swiglu_down (fused gate/up SwiGLU grouped GEMM with "
+                                "the down projection in its epilogue)") if fused_down else
                                "gate_up_swiglu (fused gate/up SwiGLU grouped GEMM)",
                      "alg_bytes_per_launch": alg["bytes_k4"],
                      "mean_launch_ms": float(k4_ms)},

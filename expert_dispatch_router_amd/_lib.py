@@ -34,7 +34,8 @@ SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [_I]),
     "moe_workspace_size": (_I, [_I, _I, _I, _I, _I, ctypes.POINTER(_SZ)]),
     "moe_workspace_size_ex": (_I, [_I, _I, _I, _I, _I, _P, ctypes.POINTER(_SZ)]),
-    "moe_plan": (_I, [_I, _I, _I, _I, _I, _P, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "moe_plan": (_I, [_I, _I, _I, _I, _I, _P, ctypes.POINTER(_I), ctypes.POINTER(_I),
+                      ctypes.POINTER(_I)]),
     "moe_forward": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "moe_forward_ex": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
     "moe_router_logits": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
@@ -58,7 +59,8 @@ class MoeOptions(ctypes.Structure):
                 ("rotate", ctypes.c_int),
                 ("routing_kernels", ctypes.c_int), ("gather_mode", ctypes.c_int),
                 ("unfused_swiglu", ctypes.c_int), ("xcd_order", ctypes.c_int),
-                ("fold_combine", ctypes.c_int), ("stage_events", ctypes.c_void_p)]
+                ("fold_combine", ctypes.c_int), ("fuse_down", ctypes.c_int),
+                ("stage_events", ctypes.c_void_p)]
 
 
 class MoeError(RuntimeError):
@@ -104,13 +106,14 @@ def moe_abi_version() -> int:
 
 def _opts(block_rows=0, split_k=0, stage_events=None, tile_variant=0, rotate=0,
           routing_kernels=0, gather_mode=0, unfused_swiglu=0, xcd_order=0, down_variant=0,
-          fold_combine=0):
+          fold_combine=0, fuse_down=0):
     if not any((block_rows, split_k, tile_variant, rotate, routing_kernels, gather_mode,
-                unfused_swiglu, xcd_order, down_variant, fold_combine)) and stage_events is None:
+                unfused_swiglu, xcd_order, down_variant, fold_combine,
+                fuse_down)) and stage_events is None:
         return None, None
     o = MoeOptions(int(block_rows), int(split_k), int(tile_variant), int(down_variant),
                    int(rotate), int(routing_kernels), int(gather_mode), int(unfused_swiglu),
-                   int(xcd_order), int(fold_combine), None)
+                   int(xcd_order), int(fold_combine), int(fuse_down), None)
     keep = None
     if stage_events is not None:
         keep = (ctypes.c_void_p * len(stage_events))(*stage_events)
@@ -120,21 +123,27 @@ def _opts(block_rows=0, split_k=0, stage_events=None, tile_variant=0, rotate=0,
 
 def moe_workspace_size(T, d, ffn, E, top_k, block_rows=0, split_k=0, tile_variant=0,
                        rotate=0, routing_kernels=0, gather_mode=0, unfused_swiglu=0,
-                       xcd_order=0, down_variant=0, fold_combine=0) -> int:
+                       xcd_order=0, down_variant=0, fold_combine=0, fuse_down=0) -> int:
     o, _ = _opts(block_rows, split_k, None, tile_variant, rotate, routing_kernels, gather_mode,
-                 unfused_swiglu, xcd_order, down_variant, fold_combine)
+                 unfused_swiglu, xcd_order, down_variant, fold_combine, fuse_down)
     n = _SZ(0)
     _check("moe_workspace_size_ex", lib().moe_workspace_size_ex(
         T, d, ffn, E, top_k, ctypes.byref(o) if o else None, ctypes.byref(n)))
     return int(n.value)
 
 
-def moe_plan(T, d, ffn, E, top_k, block_rows=0, split_k=0, tile_variant=0, rotate=0):
-    """(block_rows, split_k) the library uses for these sizes and options."""
-    o, _ = _opts(block_rows, split_k, None, tile_variant, rotate)
-    bm, sk = _I(0), _I(0)
+def moe_plan(T, d, ffn, E, top_k, block_rows=0, split_k=0, tile_variant=0, rotate=0,
+             fuse_down=0, with_fusion=False, unfused_swiglu=0):
+    """(block_rows, split_k) the library uses for these sizes and options;
+    with ``with_fusion`` also whether the down projection is fused into the
+    gate/up GEMM."""
+    o, _ = _opts(block_rows, split_k, None, tile_variant, rotate, unfused_swiglu=unfused_swiglu,
+                 fuse_down=fuse_down)
+    bm, sk, fd = _I(0), _I(0), _I(0)
     _check("moe_plan", lib().moe_plan(T, d, ffn, E, top_k, ctypes.byref(o) if o else None,
-                                       ctypes.byref(bm), ctypes.byref(sk)))
+                                       ctypes.byref(bm), ctypes.byref(sk), ctypes.byref(fd)))
+    if with_fusion:
+        return int(bm.value), int(sk.value), bool(fd.value)
     return int(bm.value), int(sk.value)
 
 
@@ -172,7 +181,7 @@ def _stream_ptr(stream, device):
 def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=None,
                 score="softmax", workspace=None, stream=None, block_rows=0, split_k=0,
                 stage_events=None, tile_variant=0, rotate=0, routing_kernels=0, gather_mode=0,
-                unfused_swiglu=0, xcd_order=0, down_variant=0, fold_combine=0):
+                unfused_swiglu=0, xcd_order=0, down_variant=0, fold_combine=0, fuse_down=0):
     """out[T,d] (bf16) = the MoE forward pass, enqueued on ``stream``.
 
     x bf16 [T,d]; router_logits fp32 [T,E]; W_gate_up bf16 [E,2F,d];
@@ -188,11 +197,11 @@ def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=Non
         out = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
     ws_need = moe_workspace_size(T, d, F, E, top_k, block_rows, split_k, tile_variant, rotate,
                                  routing_kernels, gather_mode, unfused_swiglu, xcd_order,
-                                 down_variant, fold_combine)
+                                 down_variant, fold_combine, fuse_down)
     if workspace is None:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=x.device)
     o, keep = _opts(block_rows, split_k, stage_events, tile_variant, rotate, routing_kernels,
-                    gather_mode, unfused_swiglu, xcd_order, down_variant, fold_combine)
+                    gather_mode, unfused_swiglu, xcd_order, down_variant, fold_combine, fuse_down)
     rc = lib().moe_forward_ex(
         _dev_ptr(x, torch.bfloat16, "x"), _dev_ptr(router_logits, torch.float32, "router_logits"),
         _dev_ptr(W_gate_up, torch.bfloat16, "W_gate_up"), _dev_ptr(W_down, torch.bfloat16, "W_down"),
@@ -239,7 +248,7 @@ def moe_forward_router(x, W_router, W_gate_up, W_down, top_k, renormalize, out=N
                        logits_out=None, score="softmax", workspace=None, stream=None,
                        block_rows=0, split_k=0, stage_events=None, tile_variant=0, rotate=0,
                        routing_kernels=0, gather_mode=0, unfused_swiglu=0, xcd_order=0,
-                       down_variant=0, fold_combine=0):
+                       down_variant=0, fold_combine=0, fuse_down=0):
     """moe_forward from the hidden states: router scores x . W_router^T
     (written to ``logits_out`` when given), then the forward pass."""
     T, d = x.shape
@@ -254,11 +263,11 @@ def moe_forward_router(x, W_router, W_gate_up, W_down, top_k, renormalize, out=N
         out = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
     ws_need = moe_workspace_size(T, d, F, E, top_k, block_rows, split_k, tile_variant, rotate,
                                  routing_kernels, gather_mode, unfused_swiglu, xcd_order,
-                                 down_variant, fold_combine)
+                                 down_variant, fold_combine, fuse_down)
     if workspace is None:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=x.device)
     o, keep = _opts(block_rows, split_k, stage_events, tile_variant, rotate, routing_kernels,
-                    gather_mode, unfused_swiglu, xcd_order, down_variant, fold_combine)
+                    gather_mode, unfused_swiglu, xcd_order, down_variant, fold_combine, fuse_down)
     rc = lib().moe_forward_router(
         _dev_ptr(x, torch.bfloat16, "x"), _dev_ptr(W_router, torch.bfloat16, "W_router"),
         _dev_ptr(W_gate_up, torch.bfloat16, "W_gate_up"), _dev_ptr(W_down, torch.bfloat16, "W_down"),

@@ -61,14 +61,18 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)); }
 
 // Output of a launch: the fused SwiGLU h (bf16, gate and up rows from one
-// activation tile), fp32 partial sums of one part of a split reduction, or
-// the plain product in bf16 (one projection of the unfused SwiGLU).
-enum { kOutSwiGLU = 0, kOutF32Parts = 1, kOutBF16 = 2 };
+// activation tile), fp32 partial sums of one part of a split reduction, the
+// plain product in bf16 (one projection of the unfused SwiGLU), or -- for
+// small problems -- the down projection of the workgroup's own h columns:
+// h stays in LDS and the workgroup writes the fp32 partial
+// y[tile] = h[:, tile cols] . W_down[:, tile cols]^T, one part per column
+// tile, which the combination adds in tile order.
+enum { kOutSwiGLU = 0, kOutF32Parts = 1, kOutBF16 = 2, kOutSwiGLUDown = 3 };
 
 template <int BM, int NWT, int WAVES, int PF, int MODE>
 struct Gemm {
   static constexpr int kMT = BM / 16;                        // 16-row subtiles
-  static constexpr int kNG = MODE == kOutSwiGLU ? 2 : 1;     // weight groups (gate, up)
+  static constexpr int kNG = (MODE == kOutSwiGLU || MODE == kOutSwiGLUDown) ? 2 : 1;  // gate, up
   static constexpr int kThreads = WAVES * 64;
   static constexpr int kTileCols = WAVES * NWT * 16;         // output columns per workgroup
   static constexpr int kXChunks = BM * (kBK / 8);            // 16-byte chunks per activation tile
@@ -88,7 +92,8 @@ void grouped_gemm_kernel(
     const int32_t* __restrict__ order, const int32_t* __restrict__ offsets,
     void* __restrict__ out, int A, int N, int K, int ksplit,
     int tiles_per_block, int rotate, const int32_t* __restrict__ gather_perm, int gather_k,
-    int x_rows, int xcd_group, int x_tiled, FoldCombine fold) {
+    int x_rows, int xcd_group, int x_tiled, FoldCombine fold, const uint16_t* __restrict__ W2,
+    long long w2_estride, int N2) {
   using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   constexpr int MT = G::kMT, NG = G::kNG, XPT = G::kXPerThread;
   static_assert(PF >= 2, "the activation stage is issued PF-1 steps ahead");
@@ -308,6 +313,76 @@ void grouped_gemm_kernel(
     }
   }
 
+  if constexpr (MODE == kOutSwiGLUDown) {
+    // h tile -> LDS (bf16, [BM][kTileCols + 8]) over the activation buffers;
+    // rows past the block's end hold silu(0) * 0 = 0, subtiles past the
+    // active ones are never read.
+    constexpr int HS = G::kTileCols + 8;
+    static_assert(BM * HS <= 2 * BM * kLdsStride, "h tile fits the staging buffers");
+    static_assert(G::kTileCols % 32 == 0, "whole 32-wide K chunks");
+    constexpr int KC = G::kTileCols / 32;
+    uint16_t* hl = &xs[0][0];
+    __syncthreads();  // every wave is done with the activation tiles
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt < mt_act) {
+#pragma unroll
+        for (int j = 0; j < NWT; ++j) {
+          if (!jok[j]) continue;
+          const f32x4 gv = acc[0][mt][j];
+          const f32x4 uv = acc[1][mt][j];
+          bf16x4 hv;
+          hv[0] = (__bf16)(silu_f32(gv[0]) * uv[0]);
+          hv[1] = (__bf16)(silu_f32(gv[1]) * uv[1]);
+          hv[2] = (__bf16)(silu_f32(gv[2]) * uv[2]);
+          hv[3] = (__bf16)(silu_f32(gv[3]) * uv[3]);
+          *reinterpret_cast<bf16x4*>(hl + (mt * 16 + lrow) * HS + wave * (NWT * 16) + 16 * j +
+                                     4 * (lane >> 4)) = hv;
+        }
+      }
+    }
+    lds_barrier();
+    // y[tile][r0 + m][o] = sum over this tile's columns c of h[m][c] W2[o][c]:
+    // W_down rows as the A operand (16 outputs o per subtile), h as B.
+    const int c0 = tile * G::kTileCols;
+    const int nkc = min(G::kTileCols, N - c0) / 32;
+    const __amdgpu_buffer_rsrc_t w2res = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(W2 + (size_t)e * w2_estride), (short)0, N2 * N * 2, kRsrcWord3);
+    float* y = static_cast<float*>(out) + (size_t)tile * A * N2;
+    for (int o0 = wave * 16; o0 < N2; o0 += WAVES * 16) {  // wave-uniform
+      bf16x8 wa[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        if (kc < nkc)
+          wa[kc] = __builtin_bit_cast(
+              bf16x8, buf_load16(w2res, ((o0 + lrow) * N + c0 + kc * 32 + lk) * 2, 0));
+      f32x4 acc2[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc2[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        if (kc < nkc) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            if (mt < mt_act) {
+              const bf16x8 hb =
+                  *reinterpret_cast<const bf16x8*>(hl + (mt * 16 + lrow) * HS + kc * 32 + lk);
+              acc2[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[kc], hb, acc2[mt], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one operand read in flight per MFMA
+          }
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = mt * 16 + lrow;
+        if (mt < mt_act && m < rows)
+          *reinterpret_cast<f32x4*>(y + (size_t)(r0 + m) * N2 + o0 + 4 * (lane >> 4)) = acc2[mt];
+      }
+    }
+    return;
+  }
+
   // Epilogue.
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -394,7 +469,8 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
                       int A, int N, int K,
                       int split, int ksplit, int nb_max, int rotate, const int32_t* gather_perm,
                       int gather_k, int x_rows, int xcd_group, int x_tiled,
-                      const FoldCombine& fold, hipStream_t s) {
+                      const FoldCombine& fold, hipStream_t s, const uint16_t* W2 = nullptr,
+                      long long w2_estride = 0, int N2 = 0) {
   using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
   const int tiles_per_block = n_tiles * split;
@@ -402,7 +478,7 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   grouped_gemm_kernel<BM, NWT, WAVES, PF, MODE><<<(unsigned)grid, G::kThreads, 0, s>>>(
       X, W, w_estride, blocks, nb, order, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
-      gather_perm, gather_k, x_rows, xcd_group, x_tiled, fold);
+      gather_perm, gather_k, x_rows, xcd_group, x_tiled, fold, W2, w2_estride, N2);
   return hipGetLastError();
 }
 
@@ -451,6 +527,35 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
                                                    gather_perm, k, x_tiled ? (A + 15) / 16 * 16 : T, \
                                                    xcd_group, x_tiled, FoldCombine{}, s);
   MOE_GU_CFGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+// Fused gate/up SwiGLU and down projection (kOutSwiGLUDown): tiles whose
+// column count is a multiple of 32 and whose h tile fits the staging LDS.
+#define MOE_GUD_CFGS(X) X(1, 64, 2, 4, 4) X(1, 128, 1, 4, 4) X(0, 192, 1, 8, 3)
+
+int gate_up_down_tile_cols(int bm, int variant) {
+#define X(V, BM, NWT, WV, PF) \
+  if (bm == BM && variant == V) return Gemm<BM, NWT, WV, PF, kOutSwiGLUDown>::kTileCols;
+  MOE_GUD_CFGS(X)
+#undef X
+  return 0;
+}
+
+hipError_t launch_gate_up_down(int bm, int variant, const uint16_t* x, const int32_t* gather_perm,
+                               int k, int T, const uint16_t* w_gate_up, const uint16_t* w_down,
+                               const int32_t* blocks, const int32_t* nb, const int32_t* order,
+                               const int32_t* offsets, float* y, int A, int d, int ffn,
+                               int nb_max, int rotate, int xcd_group, int x_tiled,
+                               hipStream_t s) {
+#define X(V, BM, NWT, WV, PF)                                                                  \
+  if (bm == BM && variant == V)                                                                \
+    return launch_cfg<BM, NWT, WV, PF, kOutSwiGLUDown>(                                        \
+        x, w_gate_up, 2LL * ffn * d, blocks, nb, order, offsets, y, A, ffn, d, 1, d, nb_max,    \
+        rotate, gather_perm, k, x_tiled ? (A + 15) / 16 * 16 : T, xcd_group, x_tiled,          \
+        FoldCombine{}, s, w_down, (long long)d * ffn, d);
+  MOE_GUD_CFGS(X)
 #undef X
   return hipErrorInvalidValue;
 }

@@ -68,6 +68,8 @@ struct Plan {
   int unfused;        // SwiGLU as gate GEMM, up GEMM and activation (ablation)
   int fold;           // weighted combination in the down GEMM's epilogue
   int dn_tiles;       // column tiles of the down GEMM (d / its tile width)
+  int fused_down;     // gate/up GEMM also does the down projection (split = its column tiles)
+  int plan_error;     // an explicit option the plan cannot honour (MOE_ERR_*), else 0
   // byte offsets into the workspace (256-byte aligned)
   size_t o_ids, o_w, o_counts, o_offsets, o_ccnt, o_cbase, o_perm, o_inv, o_blocks, o_nb;
   size_t o_order;  // longest-first launch order of the blocks [nb_max]
@@ -174,6 +176,19 @@ struct FoldCombine {
   int32_t* cnt;
   uint16_t* out;
 };
+
+// Fused gate/up SwiGLU and down projection for small problems: each
+// (block, column tile) workgroup keeps its h tile in LDS and writes
+// y[tile, A, d] = h[:, tile cols] Wd[:, tile cols]^T (fp32, one part per
+// column tile of gate_up_down_tile_cols columns), so no h buffer and no down
+// GEMM launch; the combination adds the parts in tile order.
+int gate_up_down_tile_cols(int bm, int variant);  // 0: not compiled
+hipError_t launch_gate_up_down(int bm, int variant, const uint16_t* x, const int32_t* gather_perm,
+                               int k, int T, const uint16_t* w_gate_up, const uint16_t* w_down,
+                               const int32_t* blocks, const int32_t* nb, const int32_t* order,
+                               const int32_t* offsets, float* y, int A, int d, int ffn,
+                               int nb_max, int rotate, int xcd_group, int x_tiled,
+                               hipStream_t s);
 
 // Down grouped GEMM: y[split, A, d] = partial sums of h Wd^T per block, and
 // with fold.cnt the weighted combination into fold.out.

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Limits of the library (violations return MOE_ERR_UNSUPPORTED). */
 #define MOE_MAX_EXPERTS 512
@@ -144,6 +144,21 @@ typedef struct moe_options {
      * routing kernels clear the counters (4*T*ceil(d/256) bytes or fewer of
      * workspace) on every call. */
     int fold_combine;
+    /* Down projection fused into the gate/up GEMM, for small problems
+     * (again fewer launches, [R] "Assumptions & free parameters").  0 =
+     * automatic, 1 = off, 2 = on: each (block, column tile) workgroup of the
+     * gate/up GEMM keeps its SwiGLU tile in LDS and multiplies it by the
+     * matching columns of W_down, writing one fp32 partial [A, d] per column
+     * tile; the weighted combination adds those partials in tile order (the
+     * split of the down reduction is then the number of column tiles, and
+     * split_k and fold_combine do not apply).  No h buffer, no down GEMM
+     * launch; the workspace holds ceil(ffn / tile) * A * d * 4 bytes of
+     * partials.  Compiled for block_rows 64 (tile variant 1), 128 (variant
+     * 1, taken automatically when tile_variant is 0) and 192 (variant 0);
+     * other combinations and the unfused ablation return
+     * MOE_ERR_UNSUPPORTED when 2 is asked for.  Rounding differs from the
+     * separate down GEMM (other summation order). */
+    int fuse_down;
     /* NULL, or 7 hipEvent_t handles created by the caller (for instance
      * with moe_timer_create).  events[0] is recorded on the stream before
      * the first kernel and events[i] right after kernel i (1 route, 2
@@ -173,10 +188,12 @@ int moe_workspace_size(int T, int d, int ffn, int E, int top_k, size_t *bytes);
 int moe_workspace_size_ex(int T, int d, int ffn, int E, int top_k, const moe_options *opt,
                           size_t *bytes);
 
-/* Host-only: the block_rows (BLOCK_M) and split_k the library would use for
- * these sizes and options.  Either output pointer may be NULL. */
+/* Host-only: the block_rows (BLOCK_M) and split_k (parts of the down
+ * reduction) the library would use for these sizes and options, and whether
+ * the down projection is fused into the gate/up GEMM (fused_down: 1 or 0).
+ * Any output pointer may be NULL. */
 int moe_plan(int T, int d, int ffn, int E, int top_k, const moe_options *opt,
-             int *block_rows, int *split_k);
+             int *block_rows, int *split_k, int *fused_down);
 
 /*
  * The MoE forward pass ([R] "The reading"; abstract).

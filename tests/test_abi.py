@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
         assert n in _lib.SIGNATURES, n
-    assert moe.moe_abi_version() == 2
+    assert moe.moe_abi_version() == 3
 
 
 def test_status_strings():
@@ -66,9 +66,9 @@ def test_workspace_size_checks():
 
 
 def _o(bm=0, split=0, variant=0, rotate=0, routing=0, gather=0, unfused=0, xcd=0, dvar=0,
-       fold=0):
+       fold=0, fuse=0):
     return ctypes.byref(_lib.MoeOptions(bm, split, variant, dvar, rotate, routing, gather, unfused,
-                                        xcd, fold, None))
+                                        xcd, fold, fuse, None))
 
 
 def test_options_checks():
@@ -135,6 +135,28 @@ def test_fold_combine_option():
     g1 = moe.moe_workspace_size(64, 1024, 512, 8, 2, block_rows=16, fold_combine=1)
     g2 = moe.moe_workspace_size(64, 1024, 512, 8, 2, block_rows=16, fold_combine=2)
     assert g2 - g1 == 64 * 2 * 4
+
+
+def test_fuse_down_option():
+    for bad in (_o(fuse=3), _o(fuse=-1)):
+        assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
+    # compiled for BM 64 (variant 1), 128 (variant 1, the automatic choice
+    # with fusion), 192 (variant 0); option values are variant + 1
+    for bm, v in ((128, 0), (128, 2), (64, 2), (192, 1)):
+        assert _ws(64, 256, 512, 8, 2, _o(bm, variant=v, fuse=2))[0] == OK, (bm, v)
+    for bm, v in ((16, 0), (32, 0), (64, 1), (128, 1), (192, 2)):
+        assert _ws(64, 256, 512, 8, 2, _o(bm, variant=v, fuse=2))[0] == UNSUP, (bm, v)
+    assert _ws(64, 256, 512, 8, 2, _o(128, fuse=2, unfused=1))[0] == UNSUP
+    # automatic: only launches below one round with small partials fuse
+    assert moe.moe_plan(64, 256, 512, 8, 2, with_fusion=True) == (128, 8, True)
+    assert moe.moe_plan(64, 256, 512, 8, 2, fuse_down=1, with_fusion=True)[2] is False
+    assert moe.moe_plan(512, 4096, 14336, 8, 2, with_fusion=True)[2] is False
+    assert moe.moe_plan(512, 7168, 2048, 256, 8, with_fusion=True)[2] is False
+    # fused: no h buffer [A, ffn] bf16; one fp32 part [A, d] per 64-column tile
+    a = moe.moe_workspace_size(64, 256, 512, 8, 2, block_rows=128, tile_variant=2, fuse_down=1,
+                               split_k=1)
+    b = moe.moe_workspace_size(64, 256, 512, 8, 2, block_rows=128, tile_variant=2, fuse_down=2)
+    assert b - a == 8 * 128 * 256 * 4 - 128 * 256 * 4 - 128 * 512 * 2
 
 
 def test_plan_choices_for_the_workloads():

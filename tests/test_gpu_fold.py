@@ -24,6 +24,7 @@ def _gpu():
 
 
 def _fold_matches_separate(x, lg, wgu, wd, k, renorm, score, what, **opts):
+    opts.setdefault("fuse_down", 1)  # the fold lives in the separate down GEMM
     T, d = x.shape
     E, F = lg.shape[1], wd.shape[2]
     sep = moe.moe_forward(x, lg, wgu, wd, k, renorm, score=score, fold_combine=1, **opts)

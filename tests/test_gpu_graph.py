@@ -25,8 +25,9 @@ def _gpu():
 @pytest.mark.parametrize("name,opts", [("tiny", {}), ("mixtral_128", {}),
                                        ("qwen2_128", {"routing_kernels": 2}),
                                        ("tiny", {"gather_mode": 2, "split_k": 2}),
-                                       ("tiny", {"fold_combine": 2, "split_k": 2}),
-                                       ("mixtral_128", {"fold_combine": 2})])
+                                       ("tiny", {"fold_combine": 2, "split_k": 2, "fuse_down": 1}),
+                                       ("mixtral_128", {"fold_combine": 2}),
+                                       ("tiny", {"fuse_down": 2})])
 def test_forward_graph_replays_match_eager(name, opts):
     cfg = synth.CONFIGS[name]
     x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)
