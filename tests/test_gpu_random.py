@@ -69,3 +69,49 @@ def test_random_problem(case):
                       block_rows=opts.get("block_rows", 0),
                       routing_kernels=opts["routing_kernels"])
     parity.check_routing(r, parity.oracle_routing(lg, k, score, renorm, r["bm"]))
+
+
+def _cases_new_options(n=16, seed=4321):
+    """Draws over the later options: the combination folded into the down
+    GEMM, the down projection fused into the gate/up GEMM, the longest-first
+    block order (each with the other options drawn as above)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 5, 8, 13, 32, 60, 64, 100]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([1, 3, 17, 64, 130, 257]))
+        d = int(64 * rng.integers(2, 13))
+        F = int(128 * rng.integers(3, 9))
+        score = int(rng.integers(0, 2))
+        renorm = bool(rng.integers(0, 2))
+        opts = {"routing_kernels": 2 if E > 32 else int(rng.integers(0, 3)),
+                "gather_mode": int(rng.integers(0, 4)),
+                "xcd_order": int(rng.choice([0, 1, 3]))}
+        kind = i % 3
+        if kind == 0:
+            opts["fold_combine"] = 2
+            opts["fuse_down"] = 1
+            if rng.random() < 0.5:
+                opts["split_k"] = int(rng.integers(1, 4))
+            if rng.random() < 0.5:
+                opts["block_rows"] = int(rng.choice([16, 32, 64, 128, 192]))
+        elif kind == 1:
+            opts["fuse_down"] = 2
+            opts["block_rows"], tv = [(64, 2), (128, 0), (192, 1)][int(rng.integers(0, 3))]
+            if tv:
+                opts["tile_variant"] = tv
+        else:
+            opts["block_rows"] = int(rng.choice([16, 32, 64, 128, 192]))
+        out.append((i, T, d, F, E, k, score, renorm, opts))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases_new_options(), ids=lambda c: f"opt{c[0]}")
+def test_random_problem_new_options(case):
+    i, T, d, F, E, k, score, renorm, opts = case
+    cfg, x, lg, wgu, wd = parity.make_case(T, d, F, E, k, score=score, renorm=renorm, seed=500 + i)
+    out = moe.moe_forward(x, lg, wgu, wd, k, renorm, score="sigmoid" if score else "softmax",
+                          **opts)
+    ref = parity.oracle_out(x, lg, wgu, wd, k, score, renorm)
+    parity.check_out(out, ref, f"opt{i} T={T} d={d} F={F} E={E} k={k} {opts}", beyond_format=True)
