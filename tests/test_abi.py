@@ -33,7 +33,10 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
         assert n in _lib.SIGNATURES, n
-    assert moe.moe_abi_version() == 3
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "include", "moe.h")).read()
+    assert moe.moe_abi_version() == int(re.search(r"#define\s+MOE_ABI_VERSION\s+(\d+)",
+                                                  hdr).group(1))
 
 
 def test_status_strings():
