@@ -170,6 +170,38 @@ def cpu_baseline(cfg, x, logits, wgu, wd, target_s=10.0):
                       f"first {n} of {cfg.T} tokens ({dt:.1f} s)"}
 
 
+_SINGLE_THREAD_TINY = r"""
+import json, sys, time
+sys.path.insert(0, sys.argv[1])
+import oracle
+from expert_dispatch_router_amd import synth
+cfg = synth.CONFIGS["tiny"]
+x, lg, wgu, wd = synth.make_inputs(cfg, 0, "cpu")
+xb, lgn = synth.bf16_bits(x), lg.numpy()
+gu, dn = synth.bf16_bits(wgu), synth.bf16_bits(wd)
+passes, t0 = 0, time.perf_counter()
+while time.perf_counter() - t0 < 2.0:
+    oracle.forward(xb, lgn, gu, dn, cfg.top_k, cfg.renormalize, cfg.score, cfg.ffn)
+    passes += 1
+dt = time.perf_counter() - t0
+print(json.dumps({"value": cfg.T * passes / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+                  "kind": "oracle", "sample": f"{passes} whole tiny passes (T={cfg.T}) in {dt:.1f} s"}))
+"""
+
+
+def cpu_single_thread_tiny():
+    """The oracle on the whole tiny workload with one OpenMP thread, in a
+    child process (OMP_NUM_THREADS is read when OpenMP starts)."""
+    import subprocess
+
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", _SINGLE_THREAD_TINY, ROOT], env=env,
+                       capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        return {"error": r.stderr.strip().splitlines()[-1:] or ["failed"]}
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
 def run(args):
     import numpy as np
     import torch
@@ -298,6 +330,7 @@ def run(args):
         res["graph"] = graph_replay(step, args.steps, cfg.T)
     if not args.profile and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, x, logits, wgu, wd, args.cpu_seconds)
+        res["cpu_baseline"]["single_thread_tiny"] = cpu_single_thread_tiny()
     print(json.dumps(res), flush=True)
 
 

@@ -83,3 +83,10 @@ def test_bench_refuses_more_than_one_gpu():
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
 
+
+
+def test_single_thread_tiny_cpu_baseline():
+    """The single-thread oracle figure runs in a child process with one
+    OpenMP thread and reports it."""
+    r = bench.cpu_single_thread_tiny()
+    assert r["cores"] == 1 and r["value"] > 0 and r["kind"] == "oracle", r
