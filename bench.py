@@ -175,6 +175,7 @@ import json, sys, time
 sys.path.insert(0, sys.argv[1])
 import oracle
 from expert_dispatch_router_amd import synth
+oracle.set_threads(1)
 cfg = synth.CONFIGS["tiny"]
 x, lg, wgu, wd = synth.make_inputs(cfg, 0, "cpu")
 xb, lgn = synth.bf16_bits(x), lg.numpy()
@@ -191,11 +192,10 @@ print(json.dumps({"value": cfg.T * passes / dt, "unit": "tokens/s", "cores": ora
 
 def cpu_single_thread_tiny():
     """The oracle on the whole tiny workload with one OpenMP thread, in a
-    child process (OMP_NUM_THREADS is read when OpenMP starts)."""
+    child process (so the parent's oracle keeps all its threads)."""
     import subprocess
 
-    env = dict(os.environ, OMP_NUM_THREADS="1")
-    r = subprocess.run([sys.executable, "-c", _SINGLE_THREAD_TINY, ROOT], env=env,
+    r = subprocess.run([sys.executable, "-c", _SINGLE_THREAD_TINY, ROOT],
                        capture_output=True, text=True, timeout=300)
     if r.returncode != 0:
         return {"error": r.stderr.strip().splitlines()[-1:] or ["failed"]}

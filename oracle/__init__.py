@@ -67,6 +67,8 @@ def _load():
         I = ctypes.c_int
         lib.orc_abi_version.restype = I
         lib.orc_max_threads.restype = I
+        lib.orc_set_threads.argtypes = [I]
+        lib.orc_set_threads.restype = None
         lib.orc_select_topk.argtypes = [P, I, I, I, P]
         lib.orc_weights.argtypes = [P, P, I, I, I, I, I, P]
         lib.orc_counts_offsets.argtypes = [P, I, I, P, P]
@@ -94,6 +96,11 @@ def _check(rc: int, what: str):
 
 def max_threads() -> int:
     return int(_load().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's later calls (results do not depend on it)."""
+    _load().orc_set_threads(int(n))
 
 
 def select_topk(logits: np.ndarray, k: int) -> np.ndarray:

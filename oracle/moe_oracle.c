@@ -77,6 +77,17 @@ int orc_max_threads(void)
 #endif
 }
 
+/* Threads of the following parallel regions (OpenMP over tokens only: the
+ * results do not depend on it). */
+void orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* "a ranks before b" for the top-k order of one token's logits.
  * Reading: the selection key is the raw fp32 logit (softmax and sigmoid are
  * strictly increasing, so the selected set is the same in exact arithmetic);
