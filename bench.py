@@ -191,8 +191,10 @@ print(json.dumps({"value": cfg.T * passes / dt, "unit": "tokens/s", "cores": ora
 
 
 def cpu_single_thread_tiny():
-    """The oracle on the whole tiny workload with one OpenMP thread, in a
-    child process (so the parent's oracle keeps all its threads)."""
+    """The oracle on the whole tiny workload with one OpenMP thread asked
+    for, in a child process (so the parent's oracle keeps all its threads);
+    ``cores`` reports the threads OpenMP actually granted, which an
+    environment may hold above one."""
     import subprocess
 
     r = subprocess.run([sys.executable, "-c", _SINGLE_THREAD_TINY, ROOT],
@@ -330,7 +332,7 @@ def run(args):
         res["graph"] = graph_replay(step, args.steps, cfg.T)
     if not args.profile and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, x, logits, wgu, wd, args.cpu_seconds)
-        res["cpu_baseline"]["single_thread_tiny"] = cpu_single_thread_tiny()
+        res["cpu_baseline"]["tiny_one_thread_requested"] = cpu_single_thread_tiny()
     print(json.dumps(res), flush=True)
 
 
