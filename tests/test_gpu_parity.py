@@ -297,3 +297,41 @@ def test_forward_full_size_sampled(name):
     parity.check_out(out[torch.from_numpy(toks).long().to(DEV)], ref, name)
     del x, lg, wgu, wd, out
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------- limits
+
+def test_forward_maximum_experts_and_topk():
+    """E = MOE_MAX_EXPERTS (512) with top_k = MOE_MAX_TOPK (16): three-launch
+    routing, ~9 rows per expert, every token against the oracle."""
+    cfg, x, lg, wgu, wd = parity.make_case(300, 128, 384, 512, 16, score=1, renorm=True, seed=77)
+    out = moe.moe_forward(x, lg, wgu, wd, 16, True, score=1)
+    parity.check_out(out, parity.oracle_out(x, lg, wgu, wd, 16, 1, True), "E=512 k=16")
+
+
+def test_forward_one_workgroup_routing_at_its_limit():
+    """T = 1024 tokens, E = 32, top_k = 16 through the one-workgroup routing
+    kernel (its largest problem), every token against the oracle.  Rows whose
+    weight is dominated by one expert reach 6.6x the output RMS; an exact
+    computation carrying only the bf16 roundings of h and of the output
+    already errs by 2.27e-2 * RMS there, so max-abs is taken beyond each
+    element's own bf16 rounding (parity.check_out)."""
+    cfg, x, lg, wgu, wd = parity.make_case(1024, 128, 384, 32, 16, seed=78)
+    out = moe.moe_forward(x, lg, wgu, wd, 16, True, routing_kernels=1)
+    parity.check_out(out, parity.oracle_out(x, lg, wgu, wd, 16, 0, True), "T=1024 E=32 k=16",
+                     beyond_format=True)
+
+
+def test_forward_maximum_rows():
+    """T * top_k = MOE_MAX_ROWS (2^20 routed rows): routing bit for bit
+    against the oracle, and a sample of tokens' outputs."""
+    T, k = (1 << 20) // 16, 16
+    cfg, x, lg, wgu, wd = parity.make_case(T, 64, 384, 64, k, seed=79)
+    out = moe.moe_forward(x, lg, wgu, wd, k, True)
+    r = moe.moe_route(lg, k, True, 0)
+    parity.check_routing(r, parity.oracle_routing(lg, k, 0, True, r["bm"]))
+    toks = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(5).choice(T, 6, replace=False)]))
+    ref = parity.oracle_out(x, lg, wgu, wd, k, 0, True, tokens=toks)
+    parity.check_out(out[torch.from_numpy(toks).long().to(DEV)], ref, "max rows")
+    del x, lg, wgu, wd, out, r
+    torch.cuda.empty_cache()
