@@ -22,6 +22,7 @@ namespace moe {
 namespace {
 
 constexpr int kScanThreads = 1024;
+constexpr int kAllChunkCounts = 16384;  // int counters of all (chunk, expert) pairs in LDS
 static_assert(kScanThreads == kChunk, "one thread per row of a chunk");
 static_assert(MOE_MAX_EXPERTS <= kScanThreads, "one thread per expert in the scans");
 
@@ -56,20 +57,41 @@ __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
   __shared__ int hist[MOE_MAX_EXPERTS];
   __shared__ int run[MOE_MAX_EXPERTS];
   __shared__ int sh[MOE_MAX_EXPERTS];
+  __shared__ int chist[kAllChunkCounts];  // [chunk][expert], when they all fit
   const int tid = threadIdx.x;
   if (tid < E) run[tid] = 0;
-  for (int c = 0; c < nchunks; ++c) {
-    if (tid < E) hist[tid] = 0;
+  if (nchunks * E <= kAllChunkCounts) {  // uniform
+    // every chunk's counts in one pass over the rows, then a scan over the
+    // chunks per expert: no barrier per chunk
+    for (int q = tid; q < nchunks * E; q += kScanThreads) chist[q] = 0;
     __syncthreads();
-    const int i = c * kChunk + tid;
-    if (i < A) atomicAdd(&hist[ids[i]], 1);
+    for (int i = tid; i < A; i += kScanThreads) atomicAdd(&chist[(i / kChunk) * E + ids[i]], 1);
     __syncthreads();
     if (tid < E) {
-      chunk_cnt[(size_t)c * E + tid] = hist[tid];
-      chunk_base[(size_t)c * E + tid] = run[tid];
-      run[tid] += hist[tid];
+      int r = 0;
+      for (int c = 0; c < nchunks; ++c) {
+        const int h = chist[c * E + tid];
+        chunk_cnt[(size_t)c * E + tid] = h;
+        chunk_base[(size_t)c * E + tid] = r;
+        r += h;
+      }
+      run[tid] = r;
     }
     __syncthreads();
+  } else {
+    for (int c = 0; c < nchunks; ++c) {
+      if (tid < E) hist[tid] = 0;
+      __syncthreads();
+      const int i = c * kChunk + tid;
+      if (i < A) atomicAdd(&hist[ids[i]], 1);
+      __syncthreads();
+      if (tid < E) {
+        chunk_cnt[(size_t)c * E + tid] = hist[tid];
+        chunk_base[(size_t)c * E + tid] = run[tid];
+        run[tid] += hist[tid];
+      }
+      __syncthreads();
+    }
   }
   const int cnt = tid < E ? run[tid] : 0;
   const int incl = block_inclusive_scan(cnt, sh);
