@@ -496,6 +496,268 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
   X(0, 16, 8, 4, 2) X(0, 32, 8, 4, 2) X(0, 64, 4, 4, 4) X(0, 128, 4, 4, 3) X(1, 128, 2, 8, 3) \
   X(0, 192, 2, 8, 3) X(1, 192, 4, 4, 3)
 
+
+// ---------------------------------------------------------------------------
+// Wide fused gate/up tile: weights staged in LDS.
+//
+// The tile above keeps each wave's weight ring in VGPRs, which leaves room
+// for one 16-column subtile (x gate and up) per wave at BM = 192; every
+// workgroup then streams its block's activation rows through the CU's
+// vector-memory path once per 112 weight columns, ~0.57 activation bytes
+// per weight byte at Mixtral's ~128 rows per block, and those reads share
+// the path with the weight stream.  Here each wave owns two subtiles
+// (WAVES * 32 columns per workgroup: half the activation bytes per weight
+// byte) and its 192 accumulator registers fit only because the weight ring
+// lives in LDS: weights and activations are fetched by direct-to-LDS
+// buffer loads (no VGPRs), STAGES stages of BK of K each.
+//
+// LDS stage: WAVES * 4 weight groups, then BM/16 activation groups; a group
+// is 16 rows x (2 * BK) bytes, written by BK/32 loads of 64 lanes x 16
+// bytes.  Load h of a group fetches rows [R*h, R*h + R) (R = 1024 / row
+// bytes), whole rows of the step: with BK = 64 each load reads whole
+// 128-byte lines (streaming half lines per step measured at ~60% of the
+// whole-line rate).  The 16-byte slot s of row r holds K chunk
+// s ^ swz(r), swz(r) = (r >> 2) & 3 (BK = 32) or (r >> 1) & 7 (BK = 64), so
+// the MFMA fragment reads -- 16 rows at one K chunk per 16 lanes -- hit 64
+// distinct banks.  Every wave issues the same number of loads per stage
+// (4 weight groups, kXPerWave activation groups; surplus activation slots
+// repeat a group: same bytes to the same place), so one immediate
+// "vmcnt" waits for the wave's own loads of a stage; the barrier
+// after it publishes the stage to all waves.
+template <int BM, int WAVES, int BK, int STAGES>
+struct LdsGemm {
+  static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
+  static constexpr int kMT = BM / 16;
+  static constexpr int kKC = BK / 32;                 // MFMA K chunks per step
+  static constexpr int kRowBytes = 2 * BK;
+  static constexpr int kGroupBytes = 16 * kRowBytes;
+  static constexpr int kLoadsPerGroup = kGroupBytes / 1024;
+  static constexpr int kThreads = WAVES * 64;
+  static constexpr int kTileCols = WAVES * 32;
+  static constexpr int kWBytes = WAVES * 4 * kGroupBytes;
+  static constexpr int kXGroups = BM / 16;
+  static constexpr int kXPerWave = (kXGroups + WAVES - 1) / WAVES;
+  static constexpr int kStageBytes = kWBytes + kXGroups * kGroupBytes;
+  static constexpr int kLoadsPerStage = (4 + kXPerWave) * kLoadsPerGroup;
+  static_assert(4 * kLoadsPerGroup <= 63, "immediate vmcnt");
+  static_assert(kXPerWave * WAVES <= 2 * kXGroups, "a surplus slot repeats one group");
+  static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS of one CU");
+  __device__ static int swz(int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, voff, soff, 0, 0);
+}
+
+template <int BM, int WAVES, int BK, int STAGES>
+__global__ __launch_bounds__(WAVES * 64, 1) void gate_up_lds_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
+    const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ offsets,
+    uint16_t* __restrict__ h, int N, int K, int tiles_per_block, int rotate,
+    const int32_t* __restrict__ gather_perm, int gather_k, int x_rows, int xcd_group) {
+  using G = LdsGemm<BM, WAVES, BK, STAGES>;
+  constexpr int MT = G::kMT, KC = G::kKC, SB = G::kStageBytes, XPW = G::kXPerWave;
+  constexpr int LPG = G::kLoadsPerGroup, GB = G::kGroupBytes, RB = G::kRowBytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[STAGES * SB];
+
+  int wg = blockIdx.x;
+  if (xcd_group) {
+    const int r8 = (nb_dev[0] * tiles_per_block + kXcds - 1) / kXcds * kXcds;
+    if (wg >= r8) return;
+    wg = (wg % kXcds) * (r8 / kXcds) + wg / kXcds;
+  }
+  const int bi = wg / tiles_per_block;
+  if (bi >= nb_dev[0]) return;
+  const int b = order ? order[bi] : bi;
+  const int tile = wg - bi * tiles_per_block;
+  const int e = blocks[2 * b];
+  const int r0 = blocks[2 * b + 1];
+  const int rows = min(BM, offsets[e + 1] - r0);
+  const int mt_act = (rows + 15) >> 4;
+  const int nks = K / BK;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = tile * G::kTileCols + wave * 32;
+
+  // loads: load h of a group, lane -> row h * (1024 / RB) + lane / (RB / 16),
+  // slot lane % (RB / 16), which holds K chunk slot ^ swz(row)
+  constexpr int SPR = RB / 16;  // 16-byte slots per row
+  int lrow[LPG], lchk[LPG];
+#pragma unroll
+  for (int hh = 0; hh < LPG; ++hh) {
+    lrow[hh] = hh * (1024 / RB) + lane / SPR;
+    lchk[hh] = (lane % SPR) ^ G::swz(lrow[hh]);
+  }
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (size_t)e * w_estride), (short)0, 2 * N * K * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xres =
+      gather_perm
+          ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, x_rows * K * 2, kRsrcWord3)
+          : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (size_t)r0 * K), (short)0,
+                                              rows * K * 2, kRsrcWord3);
+  int woff[4][LPG];  // groups (gate, j=0), (gate, 1), (up, 0), (up, 1)
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int hh = 0; hh < LPG; ++hh)
+      woff[q][hh] = (((q >> 1) * N + n0 + 16 * (q & 1) + lrow[hh]) * K + lchk[hh] * 8) * 2;
+  int xoff[XPW][LPG];
+  int xgrp[XPW];
+#pragma unroll
+  for (int q = 0; q < XPW; ++q) {
+    const int gs = wave + q * WAVES;
+    const int grp = gs < G::kXGroups ? gs : gs - G::kXGroups;  // surplus slots repeat a group
+    xgrp[q] = grp;
+#pragma unroll
+    for (int hh = 0; hh < LPG; ++hh) {
+      const int row = grp * 16 + lrow[hh];
+      int src = row;
+      if (gather_perm) src = row < rows ? gather_perm[r0 + row] / gather_k : x_rows;
+      else if (row >= rows) src = rows;  // past the range: zeros, no memory request
+      xoff[q][hh] = (src * K + lchk[hh] * 8) * 2;
+    }
+  }
+
+  const unsigned rkey = rotate == 2 ? (unsigned)wg : (unsigned)b;
+  const int shift = rotate ? (int)((rkey * 2654435761u) % (unsigned)max(nks, 1)) : 0;
+  auto soff_of = [&](int ks) {
+    const int kk = ks + shift;
+    return (kk >= nks ? kk - nks : kk) * (BK * 2);
+  };
+  // weights of stage ks into this wave's region of slot ks % STAGES
+  auto issue_w = [&](int ks) {
+    const int soff = soff_of(ks);
+    uint8_t* st = lds + (ks % STAGES) * SB;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int hh = 0; hh < LPG; ++hh)
+        dma16(wres, st + (wave * 4 + q) * GB + hh * 1024, woff[q][hh], soff);
+  };
+  // this wave's share of the activation tile of stage ks
+  auto issue_x = [&](int ks) {
+    const int soff = soff_of(ks);
+    uint8_t* st = lds + (ks % STAGES) * SB;
+#pragma unroll
+    for (int q = 0; q < XPW; ++q)
+#pragma unroll
+      for (int hh = 0; hh < LPG; ++hh)
+        dma16(xres, st + G::kWBytes + xgrp[q] * GB + hh * 1024, xoff[q][hh], soff);
+  };
+
+  f32x4 acc[2][MT][2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[g][mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragment reads: lane -> row (lane & 15), K chunk c * 4 + (lane >> 4) of
+  // the step's chunk c
+  const int rr = lane & 15;
+  int roff[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) roff[c] = rr * RB + ((((lane >> 4) + 4 * c) ^ G::swz(rr)) * 16);
+  static_assert(STAGES == 2, "double-buffered stages");
+  constexpr int WL = 4 * LPG;  // weight loads of one stage (per wave)
+  if (nks > 0) {
+    // Each wave's weight region is its own: the wave refills it with stage
+    // ks + 2 right after its multiplies of stage ks, so its weight stream
+    // keeps two stages in flight without waiting for the other waves.  The
+    // shared activation tile of stage ks + 1 is issued after the barrier of
+    // step ks, once every wave is done with stage ks - 1.
+    // Issue order per wave: W(0), X(0), W(1), then per step ks: X(ks+1),
+    // W(ks+2) -- at the top of step ks the only younger load is W(ks+1).
+    issue_w(0);
+    issue_x(0);
+    if (nks > 1) issue_w(1);
+    for (int ks = 0; ks < nks; ++ks) {
+      if (ks + 1 < nks) wait_vmcnt<WL>();  // W(ks) and X(ks) are in LDS
+      else wait_vmcnt<0>();
+      lds_barrier();  // ... everyone's; and everyone is done with stage ks - 1
+      if (ks + 1 < nks) issue_x(ks + 1);
+      const uint8_t* st = lds + (ks % STAGES) * SB;
+      const uint8_t* xb = st + G::kWBytes;
+      // K chunk outermost: one chunk's weight fragments live at a time (each
+      // output still sums its K chunks in ascending order)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        bf16x8 wa[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          wa[q] = *reinterpret_cast<const bf16x8*>(st + (wave * 4 + q) * GB + roff[c]);
+        bf16x8 xa = *reinterpret_cast<const bf16x8*>(xb + roff[c]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          bf16x8 xn = xa;
+          if (mt + 1 < MT) xn = *reinterpret_cast<const bf16x8*>(xb + (mt + 1) * GB + roff[c]);
+          if (mt < mt_act) {
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+                acc[g][mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[2 * g + j], xa,
+                                                                        acc[g][mt][j], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          xa = xn;
+        }
+      }
+      if (ks + 2 < nks) issue_w(ks + 2);  // this wave is done with its weights of stage ks
+    }
+  }
+
+  // SwiGLU epilogue: lane holds columns n0 + 16j + 4*(lane>>4) + 0..3 of row mt*16 + (lane & 15)
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + rr;
+    if (mt < mt_act && m < rows) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const f32x4 gv = acc[0][mt][j];
+        const f32x4 uv = acc[1][mt][j];
+        bf16x4 hv;
+        hv[0] = (__bf16)(silu_f32(gv[0]) * uv[0]);
+        hv[1] = (__bf16)(silu_f32(gv[1]) * uv[1]);
+        hv[2] = (__bf16)(silu_f32(gv[2]) * uv[2]);
+        hv[3] = (__bf16)(silu_f32(gv[3]) * uv[3]);
+        *reinterpret_cast<bf16x4*>(h + (size_t)(r0 + m) * N + n0 + 16 * j + 4 * (lane >> 4)) = hv;
+      }
+    }
+  }
+}
+
+constexpr int kLdsBK = 64;     // whole 128-byte lines of each weight row per step
+constexpr int kLdsStages = 2;  // 2 x 80 KiB: the whole LDS of a CU at BM = 192, 7 waves
+
+template <int BM, int WAVES>
+hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
+                          const int32_t* blocks, const int32_t* nb, const int32_t* order,
+                          const int32_t* offsets, uint16_t* h, int N, int K, int nb_max,
+                          int rotate, const int32_t* gather_perm, int gather_k, int x_rows,
+                          int xcd_group, hipStream_t s) {
+  using G = LdsGemm<BM, WAVES, kLdsBK, kLdsStages>;
+  // whole tiles and whole K steps only
+  if (N % G::kTileCols != 0 || K % kLdsBK != 0) return hipErrorInvalidValue;
+  const int tiles_per_block = N / G::kTileCols;
+  const long long grid = (long long)tiles_per_block * nb_max;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  gate_up_lds_kernel<BM, WAVES, kLdsBK, kLdsStages><<<(unsigned)grid, G::kThreads, 0, s>>>(
+      X, W, w_estride, blocks, nb, order, offsets, h, N, K, tiles_per_block, rotate, gather_perm,
+      gather_k, x_rows, xcd_group);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int gate_up_tile_cols(int bm, int variant) {
@@ -503,6 +765,7 @@ int gate_up_tile_cols(int bm, int variant) {
   if (bm == BM && variant == V) return Gemm<BM, NWT, WV, PF, kOutSwiGLU>::kTileCols;
   MOE_GU_CFGS(X)
 #undef X
+  if (bm == 192 && variant == kGateUpLdsVariant) return LdsGemm<192, 7, kLdsBK, kLdsStages>::kTileCols;
   return 0;
 }
 
@@ -520,6 +783,11 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
                           uint16_t* h, int A, int d,
                           int ffn, int nb_max, int rotate, int xcd_group, int x_tiled,
                           hipStream_t s) {
+  if (bm == 192 && variant == kGateUpLdsVariant) {
+    if (x_tiled) return hipErrorInvalidValue;  // row-major activations only
+    return launch_lds_cfg<192, 7>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order, offsets, h, ffn,
+                                  d, nb_max, rotate, gather_perm, k, T, xcd_group, s);
+  }
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && variant == V)                                                                \
     return launch_cfg<BM, NWT, WV, PF, kOutSwiGLU>(x, w_gate_up, 2LL * ffn * d, blocks, nb,      \

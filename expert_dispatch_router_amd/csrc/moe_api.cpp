@@ -128,14 +128,24 @@ double round_balance(long long wg, long long slots) {
   return rounds > 0 ? (double)wg / (double)(rounds * slots) : 1.0;
 }
 
+// Whether the LDS-staged 224-column gate/up tile can run: whole column
+// tiles, row-major activations.
+bool gate_up_lds_fits(int ffn, bool x_tiled) {
+  return ffn % gate_up_tile_cols(192, kGateUpLdsVariant) == 0 && !x_tiled;
+}
+
 // Tile variant of the fused gate/up GEMM.  BM = 64 and 128: the narrow
 // variant when the wide one would give at most ~1.5 workgroups per CU.
-// BM = 192: the 112-column variant when its tiles fill the rounds better
+// BM = 192: the LDS-staged 224-column tile when the columns divide into
+// whole tiles (measured 16% faster than the register-ring tiles on
+// Mixtral-shaped blocks: half the activation bytes per weight byte);
+// otherwise the 112-column variant when its tiles fill the rounds better
 // than 128-column tiles do (both hold one workgroup per CU).
-int auto_gu_variant(int A, int E, int ffn, int bm) {
+int auto_gu_variant(int A, int E, int ffn, int bm, bool x_tiled) {
   if (bm == 64 || bm == 128)
     return est_workgroups(A, E, bm, ffn, gate_up_tile_cols(bm, 0)) <= 384 ? 1 : 0;
   if (bm == 192) {
+    if (gate_up_lds_fits(ffn, x_tiled)) return kGateUpLdsVariant;
     const double b0 = round_balance(est_workgroups(A, E, bm, ffn, gate_up_tile_cols(192, 0)), 256);
     const double b1 = round_balance(est_workgroups(A, E, bm, ffn, gate_up_tile_cols(192, 1)), 256);
     const bool exact1 = ffn % gate_up_tile_cols(192, 1) == 0;  // no partial last tile
@@ -214,7 +224,10 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     p->ksplit = per * 64;
     p->split = (ksteps + per - 1) / per;  // every part has at least one K step
     p->gu_variant = (opt && opt->tile_variant) ? opt->tile_variant - 1
-                                               : auto_gu_variant(A, E, ffn, p->bm);
+                                               : auto_gu_variant(A, E, ffn, p->bm, p->x_tiled);
+    if (p->bm == 192 && p->gu_variant == kGateUpLdsVariant && !p->unfused &&
+        !gate_up_lds_fits(ffn, p->x_tiled))
+      p->plan_error = MOE_ERR_UNSUPPORTED;  // forced where it cannot run
     p->dn_variant = (opt && opt->down_variant) ? opt->down_variant - 1 : 0;
     const int rot = opt ? opt->rotate : 0;
     // kernel values: 0 off, 1 per block, 2 per workgroup
@@ -231,7 +244,10 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     // column tile replaces the h buffer and the down GEMM.
     // At BM = 128 it takes the narrow tile unless the caller fixed one.
     const int fd = opt ? opt->fuse_down : 0;
-    const int fv = (p->bm == 128 && !(opt && opt->tile_variant)) ? 1 : p->gu_variant;
+    const bool gv_auto = !(opt && opt->tile_variant);
+    const int fv = (p->bm == 128 && gv_auto) ? 1
+                   : (p->bm == 192 && gv_auto && p->gu_variant == kGateUpLdsVariant) ? 0
+                                                                                    : p->gu_variant;
     const int tc = gate_up_down_tile_cols(p->bm, fv);
     const bool fd_ok = tc > 0 && !p->unfused && (long long)d * ffn * 2 < (1LL << 31);
     if (fd == 2 && !fd_ok) p->plan_error = MOE_ERR_UNSUPPORTED;

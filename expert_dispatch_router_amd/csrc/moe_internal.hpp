@@ -205,6 +205,9 @@ hipError_t launch_combine(const float* y, int split, int A, int d, const int32_t
 // Column tile widths (output columns per workgroup) of the two GEMMs for a
 // block size; the planner uses them to size the grids.
 int gate_up_tile_cols(int bm, int variant);
+// Tile variant of the fused gate/up GEMM at BM = 192 that stages its weights in LDS
+// (7 waves x 32 columns).
+constexpr int kGateUpLdsVariant = 2;
 int down_tile_cols(int bm, int variant);
 
 }  // namespace moe
