@@ -363,7 +363,7 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes,
         return int(m.group(1)) if m else None
 
     classes = {
-        "gate_up_swiglu": lambda n: mode(n) == 0,
+        "gate_up_swiglu": lambda n: mode(n) == 0 or "gate_up_lds_kernel" in n,
         "down": lambda n: mode(n) == 1,
         "proj_bf16": lambda n: mode(n) == 2,
         "swiglu_act": lambda n: "swiglu_act_kernel" in n,

@@ -87,8 +87,11 @@ typedef struct moe_options {
      * compiled variant k-1 for the chosen block_rows (which must then be set
      * explicitly).  BM = 64 has variants 0 (256 columns per workgroup) and 1
      * (128 columns); BM = 128 has variants 0 (128 columns, 8 waves) and 1
-     * (64 columns); BM = 192 has variants 0 (128 columns, 8 waves) and 1
-     * (112 columns, 7 waves); every other BM has variant 0 only. */
+     * (64 columns); BM = 192 has variants 0 (128 columns, 8 waves), 1
+     * (112 columns, 7 waves) and 2 (224 columns, 7 waves, weights staged in
+     * LDS; only when ffn is a multiple of 224 and gather_mode is not 3, else
+     * MOE_ERR_UNSUPPORTED -- automatic at BM = 192 where it fits); every
+     * other BM has variant 0 only. */
     int tile_variant;
     /* Tile variant of the down GEMM, like tile_variant (block_rows must be
      * set).  BM = 128 and 192 have variants 0 and 1 (256 columns per
