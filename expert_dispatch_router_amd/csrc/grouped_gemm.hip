@@ -524,9 +524,14 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
 // repeat a group: same bytes to the same place), so one immediate
 // "vmcnt" waits for the wave's own loads of a stage; the barrier
 // after it publishes the stage to all waves.
-template <int BM, int WAVES, int BK, int STAGES>
+// MODE kOutSwiGLU: gate and up rows (NG = 2), bf16 h; kOutF32Parts: one
+// operand (the down projection), fp32 partial sums of a split reduction.
+template <int BM, int WAVES, int BK, int STAGES, int MODE = kOutSwiGLU>
 struct LdsGemm {
   static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
+  static_assert(MODE == kOutSwiGLU || MODE == kOutF32Parts, "SwiGLU or fp32 parts");
+  static constexpr int kNG = MODE == kOutSwiGLU ? 2 : 1;
+  static constexpr int kGPW = 2 * kNG;                // 16-row weight groups per wave
   static constexpr int kMT = BM / 16;
   static constexpr int kKC = BK / 32;                 // MFMA K chunks per step
   static constexpr int kRowBytes = 2 * BK;
@@ -534,12 +539,12 @@ struct LdsGemm {
   static constexpr int kLoadsPerGroup = kGroupBytes / 1024;
   static constexpr int kThreads = WAVES * 64;
   static constexpr int kTileCols = WAVES * 32;
-  static constexpr int kWBytes = WAVES * 4 * kGroupBytes;
+  static constexpr int kWBytes = WAVES * kGPW * kGroupBytes;
   static constexpr int kXGroups = BM / 16;
   static constexpr int kXPerWave = (kXGroups + WAVES - 1) / WAVES;
   static constexpr int kStageBytes = kWBytes + kXGroups * kGroupBytes;
-  static constexpr int kLoadsPerStage = (4 + kXPerWave) * kLoadsPerGroup;
-  static_assert(4 * kLoadsPerGroup <= 63, "immediate vmcnt");
+  static constexpr int kLoadsPerStage = (kGPW + kXPerWave) * kLoadsPerGroup;
+  static_assert(kGPW * kLoadsPerGroup <= 63, "immediate vmcnt");
   static_assert(kXPerWave * WAVES <= 2 * kXGroups, "a surplus slot repeats one group");
   static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS of one CU");
   __device__ static int swz(int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
@@ -555,15 +560,18 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds,
       r, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, voff, soff, 0, 0);
 }
 
-template <int BM, int WAVES, int BK, int STAGES>
-__global__ __launch_bounds__(WAVES * 64, 1) void gate_up_lds_kernel(
+// out: kOutSwiGLU -> bf16 h [A, N]; kOutF32Parts -> fp32 y [split, A, N]
+// (part p sums K steps [p * ksplit, (p + 1) * ksplit)).
+template <int BM, int WAVES, int BK, int STAGES, int MODE>
+__global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
     const int32_t* __restrict__ order, const int32_t* __restrict__ offsets,
-    uint16_t* __restrict__ h, int N, int K, int tiles_per_block, int rotate,
+    void* __restrict__ out, int A, int N, int K, int ksplit, int tiles_per_block, int rotate,
     const int32_t* __restrict__ gather_perm, int gather_k, int x_rows, int xcd_group) {
-  using G = LdsGemm<BM, WAVES, BK, STAGES>;
+  using G = LdsGemm<BM, WAVES, BK, STAGES, MODE>;
   constexpr int MT = G::kMT, KC = G::kKC, SB = G::kStageBytes, XPW = G::kXPerWave;
+  constexpr int NG = G::kNG, GPW = G::kGPW;
   constexpr int LPG = G::kLoadsPerGroup, GB = G::kGroupBytes, RB = G::kRowBytes;
   __shared__ __attribute__((aligned(16))) uint8_t lds[STAGES * SB];
 
@@ -576,12 +584,16 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gate_up_lds_kernel(
   const int bi = wg / tiles_per_block;
   if (bi >= nb_dev[0]) return;
   const int b = order ? order[bi] : bi;
-  const int tile = wg - bi * tiles_per_block;
+  const int rem = wg - bi * tiles_per_block;
+  const int n_tiles = N / G::kTileCols;
+  const int tile = rem % n_tiles;
+  const int part = rem / n_tiles;
+  const int kb = part * ksplit;
   const int e = blocks[2 * b];
   const int r0 = blocks[2 * b + 1];
   const int rows = min(BM, offsets[e + 1] - r0);
   const int mt_act = (rows + 15) >> 4;
-  const int nks = K / BK;
+  const int nks = max(0, min(K - kb, ksplit) / BK);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -598,18 +610,19 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gate_up_lds_kernel(
     lchk[hh] = (lane % SPR) ^ G::swz(lrow[hh]);
   }
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (size_t)e * w_estride), (short)0, 2 * N * K * 2, kRsrcWord3);
+      (void*)(W + (size_t)e * w_estride), (short)0, NG * N * K * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t xres =
       gather_perm
           ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, x_rows * K * 2, kRsrcWord3)
           : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (size_t)r0 * K), (short)0,
                                               rows * K * 2, kRsrcWord3);
-  int woff[4][LPG];  // groups (gate, j=0), (gate, 1), (up, 0), (up, 1)
+  // weight groups of this wave: q = 2 * g + j -> operand g (gate, up), subtile j
+  int woff[GPW][LPG];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
+  for (int q = 0; q < GPW; ++q)
 #pragma unroll
     for (int hh = 0; hh < LPG; ++hh)
-      woff[q][hh] = (((q >> 1) * N + n0 + 16 * (q & 1) + lrow[hh]) * K + lchk[hh] * 8) * 2;
+      woff[q][hh] = (((q >> 1) * N + n0 + 16 * (q & 1) + lrow[hh]) * K + kb + lchk[hh] * 8) * 2;
   int xoff[XPW][LPG];
   int xgrp[XPW];
 #pragma unroll
@@ -623,7 +636,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gate_up_lds_kernel(
       int src = row;
       if (gather_perm) src = row < rows ? gather_perm[r0 + row] / gather_k : x_rows;
       else if (row >= rows) src = rows;  // past the range: zeros, no memory request
-      xoff[q][hh] = (src * K + lchk[hh] * 8) * 2;
+      xoff[q][hh] = (src * K + kb + lchk[hh] * 8) * 2;
     }
   }
 
@@ -638,10 +651,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gate_up_lds_kernel(
     const int soff = soff_of(ks);
     uint8_t* st = lds + (ks % STAGES) * SB;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < GPW; ++q)
 #pragma unroll
       for (int hh = 0; hh < LPG; ++hh)
-        dma16(wres, st + (wave * 4 + q) * GB + hh * 1024, woff[q][hh], soff);
+        dma16(wres, st + (wave * GPW + q) * GB + hh * 1024, woff[q][hh], soff);
   };
   // this wave's share of the activation tile of stage ks
   auto issue_x = [&](int ks) {
@@ -654,9 +667,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gate_up_lds_kernel(
         dma16(xres, st + G::kWBytes + xgrp[q] * GB + hh * 1024, xoff[q][hh], soff);
   };
 
-  f32x4 acc[2][MT][2];
+  f32x4 acc[NG][MT][2];
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+  for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -669,7 +682,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gate_up_lds_kernel(
 #pragma unroll
   for (int c = 0; c < KC; ++c) roff[c] = rr * RB + ((((lane >> 4) + 4 * c) ^ G::swz(rr)) * 16);
   static_assert(STAGES == 2, "double-buffered stages");
-  constexpr int WL = 4 * LPG;  // weight loads of one stage (per wave)
+  constexpr int WL = GPW * LPG;  // weight loads of one stage (per wave)
   if (nks > 0) {
     // Each wave's weight region is its own: the wave refills it with stage
     // ks + 2 right after its multiplies of stage ks, so its weight stream
@@ -692,10 +705,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gate_up_lds_kernel(
       // output still sums its K chunks in ascending order)
 #pragma unroll
       for (int c = 0; c < KC; ++c) {
-        bf16x8 wa[4];
+        bf16x8 wa[GPW];
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          wa[q] = *reinterpret_cast<const bf16x8*>(st + (wave * 4 + q) * GB + roff[c]);
+        for (int q = 0; q < GPW; ++q)
+          wa[q] = *reinterpret_cast<const bf16x8*>(st + (wave * GPW + q) * GB + roff[c]);
         bf16x8 xa = *reinterpret_cast<const bf16x8*>(xb + roff[c]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -703,7 +716,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gate_up_lds_kernel(
           if (mt + 1 < MT) xn = *reinterpret_cast<const bf16x8*>(xb + (mt + 1) * GB + roff[c]);
           if (mt < mt_act) {
 #pragma unroll
-            for (int g = 0; g < 2; ++g)
+            for (int g = 0; g < NG; ++g)
 #pragma unroll
               for (int j = 0; j < 2; ++j)
                 acc[g][mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[2 * g + j], xa,
@@ -717,21 +730,27 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gate_up_lds_kernel(
     }
   }
 
-  // SwiGLU epilogue: lane holds columns n0 + 16j + 4*(lane>>4) + 0..3 of row mt*16 + (lane & 15)
+  // epilogue: lane holds columns n0 + 16j + 4*(lane>>4) + 0..3 of row mt*16 + (lane & 15)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + rr;
     if (mt < mt_act && m < rows) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const f32x4 gv = acc[0][mt][j];
-        const f32x4 uv = acc[1][mt][j];
-        bf16x4 hv;
-        hv[0] = (__bf16)(silu_f32(gv[0]) * uv[0]);
-        hv[1] = (__bf16)(silu_f32(gv[1]) * uv[1]);
-        hv[2] = (__bf16)(silu_f32(gv[2]) * uv[2]);
-        hv[3] = (__bf16)(silu_f32(gv[3]) * uv[3]);
-        *reinterpret_cast<bf16x4*>(h + (size_t)(r0 + m) * N + n0 + 16 * j + 4 * (lane >> 4)) = hv;
+        const int n = n0 + 16 * j + 4 * (lane >> 4);
+        if constexpr (MODE == kOutSwiGLU) {
+          const f32x4 gv = acc[0][mt][j];
+          const f32x4 uv = acc[NG - 1][mt][j];
+          bf16x4 hv;
+          hv[0] = (__bf16)(silu_f32(gv[0]) * uv[0]);
+          hv[1] = (__bf16)(silu_f32(gv[1]) * uv[1]);
+          hv[2] = (__bf16)(silu_f32(gv[2]) * uv[2]);
+          hv[3] = (__bf16)(silu_f32(gv[3]) * uv[3]);
+          *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(out) + (size_t)(r0 + m) * N + n) = hv;
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + ((size_t)part * A + r0 + m) * N + n) =
+              acc[0][mt][j];
+        }
       }
     }
   }
@@ -740,21 +759,22 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gate_up_lds_kernel(
 constexpr int kLdsBK = 64;     // whole 128-byte lines of each weight row per step
 constexpr int kLdsStages = 2;  // 2 x 80 KiB: the whole LDS of a CU at BM = 192, 7 waves
 
-template <int BM, int WAVES>
+template <int BM, int WAVES, int MODE>
 hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
                           const int32_t* blocks, const int32_t* nb, const int32_t* order,
-                          const int32_t* offsets, uint16_t* h, int N, int K, int nb_max,
-                          int rotate, const int32_t* gather_perm, int gather_k, int x_rows,
-                          int xcd_group, hipStream_t s) {
-  using G = LdsGemm<BM, WAVES, kLdsBK, kLdsStages>;
+                          const int32_t* offsets, void* out, int A, int N, int K, int split,
+                          int ksplit, int nb_max, int rotate, const int32_t* gather_perm,
+                          int gather_k, int x_rows, int xcd_group, hipStream_t s) {
+  using G = LdsGemm<BM, WAVES, kLdsBK, kLdsStages, MODE>;
   // whole tiles and whole K steps only
-  if (N % G::kTileCols != 0 || K % kLdsBK != 0) return hipErrorInvalidValue;
-  const int tiles_per_block = N / G::kTileCols;
+  if (N % G::kTileCols != 0 || K % kLdsBK != 0 || ksplit % kLdsBK != 0 || split < 1)
+    return hipErrorInvalidValue;
+  const int tiles_per_block = N / G::kTileCols * split;
   const long long grid = (long long)tiles_per_block * nb_max;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  gate_up_lds_kernel<BM, WAVES, kLdsBK, kLdsStages><<<(unsigned)grid, G::kThreads, 0, s>>>(
-      X, W, w_estride, blocks, nb, order, offsets, h, N, K, tiles_per_block, rotate, gather_perm,
-      gather_k, x_rows, xcd_group);
+  gemm_lds_kernel<BM, WAVES, kLdsBK, kLdsStages, MODE><<<(unsigned)grid, G::kThreads, 0, s>>>(
+      X, W, w_estride, blocks, nb, order, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
+      gather_perm, gather_k, x_rows, xcd_group);
   return hipGetLastError();
 }
 
@@ -766,6 +786,7 @@ int gate_up_tile_cols(int bm, int variant) {
   MOE_GU_CFGS(X)
 #undef X
   if (bm == 192 && variant == kGateUpLdsVariant) return LdsGemm<192, 7, kLdsBK, kLdsStages>::kTileCols;
+  if (bm == 128 && variant == kGateUpLdsVariant) return LdsGemm<128, 8, kLdsBK, kLdsStages>::kTileCols;
   return 0;
 }
 
@@ -774,6 +795,8 @@ int down_tile_cols(int bm, int variant) {
   if (bm == BM && V == variant) return Gemm<BM, NWT, WV, PF, kOutF32Parts>::kTileCols;
   MOE_DN_CFGS(X)
 #undef X
+  if ((bm == 192 || bm == 128) && variant == kDownLdsVariant)
+    return LdsGemm<192, 8, kLdsBK, kLdsStages, kOutF32Parts>::kTileCols;  // 256 at both
   return 0;
 }
 
@@ -785,8 +808,15 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
                           hipStream_t s) {
   if (bm == 192 && variant == kGateUpLdsVariant) {
     if (x_tiled) return hipErrorInvalidValue;  // row-major activations only
-    return launch_lds_cfg<192, 7>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order, offsets, h, ffn,
-                                  d, nb_max, rotate, gather_perm, k, T, xcd_group, s);
+    return launch_lds_cfg<192, 7, kOutSwiGLU>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order,
+                                              offsets, h, A, ffn, d, 1, d, nb_max, rotate,
+                                              gather_perm, k, T, xcd_group, s);
+  }
+  if (bm == 128 && variant == kGateUpLdsVariant) {
+    if (x_tiled) return hipErrorInvalidValue;
+    return launch_lds_cfg<128, 8, kOutSwiGLU>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order,
+                                              offsets, h, A, ffn, d, 1, d, nb_max, rotate,
+                                              gather_perm, k, T, xcd_group, s);
   }
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && variant == V)                                                                \
@@ -833,6 +863,18 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
                        const int32_t* offsets, float* y,
                        int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
                        int xcd_group, const FoldCombine& fold, hipStream_t s) {
+  if (bm == 192 && variant == kDownLdsVariant) {
+    if (fold.cnt) return hipErrorInvalidValue;  // the fold runs in the register-ring tiles
+    return launch_lds_cfg<192, 8, kOutF32Parts>(h, w_down, (long long)d * ffn, blocks, nb, order,
+                                                offsets, y, A, d, ffn, split, ksplit, nb_max,
+                                                rotate, nullptr, 1, A, xcd_group, s);
+  }
+  if (bm == 128 && variant == kDownLdsVariant) {
+    if (fold.cnt) return hipErrorInvalidValue;
+    return launch_lds_cfg<128, 8, kOutF32Parts>(h, w_down, (long long)d * ffn, blocks, nb, order,
+                                                offsets, y, A, d, ffn, split, ksplit, nb_max,
+                                                rotate, nullptr, 1, A, xcd_group, s);
+  }
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && V == variant)                                                                      \
     return launch_cfg<BM, NWT, WV, PF, kOutF32Parts>(h, w_down, (long long)d * ffn, blocks, nb,  \

@@ -128,10 +128,11 @@ double round_balance(long long wg, long long slots) {
   return rounds > 0 ? (double)wg / (double)(rounds * slots) : 1.0;
 }
 
-// Whether the LDS-staged 224-column gate/up tile can run: whole column
-// tiles, row-major activations.
-bool gate_up_lds_fits(int ffn, bool x_tiled) {
-  return ffn % gate_up_tile_cols(192, kGateUpLdsVariant) == 0 && !x_tiled;
+// Whether the LDS-staged gate/up tile (224 columns at BM = 192, 256 at
+// BM = 128) can run: whole column tiles, row-major activations.
+bool gate_up_lds_fits(int bm, int ffn, bool x_tiled) {
+  const int tc = gate_up_tile_cols(bm, kGateUpLdsVariant);
+  return (bm == 128 || bm == 192) && tc > 0 && ffn % tc == 0 && !x_tiled;
 }
 
 // Tile variant of the fused gate/up GEMM.  BM = 64 and 128: the narrow
@@ -145,7 +146,7 @@ int auto_gu_variant(int A, int E, int ffn, int bm, bool x_tiled) {
   if (bm == 64 || bm == 128)
     return est_workgroups(A, E, bm, ffn, gate_up_tile_cols(bm, 0)) <= 384 ? 1 : 0;
   if (bm == 192) {
-    if (gate_up_lds_fits(ffn, x_tiled)) return kGateUpLdsVariant;
+    if (gate_up_lds_fits(192, ffn, x_tiled)) return kGateUpLdsVariant;
     const double b0 = round_balance(est_workgroups(A, E, bm, ffn, gate_up_tile_cols(192, 0)), 256);
     const double b1 = round_balance(est_workgroups(A, E, bm, ffn, gate_up_tile_cols(192, 1)), 256);
     const bool exact1 = ffn % gate_up_tile_cols(192, 1) == 0;  // no partial last tile
@@ -176,6 +177,22 @@ bool auto_xcd_order(int A, int E, int bm) {
 // equal on every MoE workload shape, so it is on unless the caller turns it
 // off.
 int auto_rotate(int) { return 1; }
+
+// Whether the LDS-staged down tile (8 waves x 32 columns, BM = 128 or 192)
+// can run: whole 256-column tiles, and the combination not folded into the
+// down GEMM (the fold lives in the register-ring tiles).
+bool down_lds_fits(int bm, int d, bool fold) {
+  return (bm == 128 || bm == 192) && d % down_tile_cols(bm, kDownLdsVariant) == 0 && !fold;
+}
+
+// Tile variant of the down GEMM: the LDS-staged tile wherever it fits --
+// measured faster or equal on every MoE workload shape (down GEMM, µs:
+// skewed T=512 45.9 -> 39.5, Qwen2 T=512 267 -> 244, Mixtral T=512
+// 205 -> 188, DeepSeek-V3 T=4096 1726 -> 1678, Mixtral T=128 162 -> 160) --
+// else variant 0.
+int auto_dn_variant(int bm, int d, bool fold) {
+  return down_lds_fits(bm, d, fold) ? kDownLdsVariant : 0;
+}
 
 // The down projection fused into the gate/up GEMM: for launches of less
 // than one round of workgroups, whose time is latency and launches, and
@@ -225,10 +242,15 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     p->split = (ksteps + per - 1) / per;  // every part has at least one K step
     p->gu_variant = (opt && opt->tile_variant) ? opt->tile_variant - 1
                                                : auto_gu_variant(A, E, ffn, p->bm, p->x_tiled);
-    if (p->bm == 192 && p->gu_variant == kGateUpLdsVariant && !p->unfused &&
-        !gate_up_lds_fits(ffn, p->x_tiled))
+    if ((p->bm == 128 || p->bm == 192) && p->gu_variant == kGateUpLdsVariant && !p->unfused &&
+        !gate_up_lds_fits(p->bm, ffn, p->x_tiled))
       p->plan_error = MOE_ERR_UNSUPPORTED;  // forced where it cannot run
-    p->dn_variant = (opt && opt->down_variant) ? opt->down_variant - 1 : 0;
+    const int fc = opt ? opt->fold_combine : 0;
+    p->fold = fc == 0 ? auto_fold(T, d, E, k) : fc == 2;
+    p->dn_variant = (opt && opt->down_variant) ? opt->down_variant - 1
+                                               : auto_dn_variant(p->bm, d, p->fold);
+    if (p->dn_variant == kDownLdsVariant && !down_lds_fits(p->bm, d, p->fold))
+      p->plan_error = MOE_ERR_UNSUPPORTED;  // forced where it cannot run
     const int rot = opt ? opt->rotate : 0;
     // kernel values: 0 off, 1 per block, 2 per workgroup
     p->gu_rotate = rot == 0 ? auto_rotate(d) : rot - 1;
@@ -236,8 +258,6 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     const int xo = opt ? opt->xcd_order : 0;
     p->gu_xcd = p->dn_xcd = xo == 0 ? auto_xcd_order(A, E, p->bm) : xo == 2;
     p->longest_first = xo == 3 || (xo == 0 && !p->gu_xcd && auto_longest_first(A, E, p->bm));
-    const int fc = opt ? opt->fold_combine : 0;
-    p->fold = fc == 0 ? auto_fold(T, d, E, k) : fc == 2;
     const int dcols = down_tile_cols(p->bm, p->dn_variant);
     p->dn_tiles = dcols > 0 ? (d + dcols - 1) / dcols : 0;
     // The down projection inside the gate/up GEMM: one fp32 part per gate/up

@@ -208,6 +208,9 @@ int gate_up_tile_cols(int bm, int variant);
 // Tile variant of the fused gate/up GEMM at BM = 192 that stages its weights in LDS
 // (7 waves x 32 columns).
 constexpr int kGateUpLdsVariant = 2;
+// Tile variant of the down GEMM at BM = 192 that stages its weights in LDS (8 waves x 32
+// columns).
+constexpr int kDownLdsVariant = 2;
 int down_tile_cols(int bm, int variant);
 
 }  // namespace moe

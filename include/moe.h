@@ -86,17 +86,22 @@ typedef struct moe_options {
     /* Tile variant of the fused gate/up GEMM.  0 = automatic; k >= 1 selects
      * compiled variant k-1 for the chosen block_rows (which must then be set
      * explicitly).  BM = 64 has variants 0 (256 columns per workgroup) and 1
-     * (128 columns); BM = 128 has variants 0 (128 columns, 8 waves) and 1
-     * (64 columns); BM = 192 has variants 0 (128 columns, 8 waves), 1
-     * (112 columns, 7 waves) and 2 (224 columns, 7 waves, weights staged in
-     * LDS; only when ffn is a multiple of 224 and gather_mode is not 3, else
-     * MOE_ERR_UNSUPPORTED -- automatic at BM = 192 where it fits); every
-     * other BM has variant 0 only. */
+     * (128 columns); BM = 128 has variants 0 (128 columns, 8 waves), 1
+     * (64 columns) and 2 (256 columns, 8 waves, weights staged in LDS;
+     * only when ffn is a multiple of 256 and gather_mode is not 3, else
+     * MOE_ERR_UNSUPPORTED); BM = 192 has variants 0 (128 columns, 8 waves),
+     * 1 (112 columns, 7 waves) and 2 (224 columns, 7 waves, weights staged
+     * in LDS; only when ffn is a multiple of 224 and gather_mode is not 3,
+     * else MOE_ERR_UNSUPPORTED -- automatic at BM = 192 where it fits);
+     * every other BM has variant 0 only. */
     int tile_variant;
     /* Tile variant of the down GEMM, like tile_variant (block_rows must be
      * set).  BM = 128 and 192 have variants 0 and 1 (256 columns per
      * workgroup: 4 waves of 64 and 8 waves of 32 at BM = 128, the reverse
-     * at BM = 192); every other BM has variant 0 only.  0 = automatic. */
+     * at BM = 192) and 2 (256 columns, 8 waves, weights staged in LDS; only
+     * when d is a multiple of 256 and the combination is not folded into
+     * the down GEMM, else MOE_ERR_UNSUPPORTED -- automatic where it fits);
+     * every other BM has variant 0 only.  0 = automatic. */
     int down_variant;
     /* K-start rotation of the GEMMs: a workgroup starts its reduction at a
      * step derived from its schedule block (2) or from its own id (3), and

@@ -85,7 +85,19 @@ def test_options_checks():
     assert _ws(64, 256, 512, 8, 2, _o(64, 0, 2))[0] == OK
     assert _ws(64, 256, 512, 8, 2, _o(192, 0, 2))[0] == OK
     assert _ws(64, 256, 512, 8, 2, _o(128, 0, 2))[0] == OK
-    assert _ws(64, 256, 512, 8, 2, _o(128, 0, 3))[0] == UNSUP
+    # the LDS-staged tiles (variant 2 of BM = 128 and 192, option value 3):
+    # whole column tiles only -- gate/up 256 columns at BM = 128 (ffn = 512
+    # fits, 384 does not), 224 at BM = 192 (512 does not fit: bad list
+    # above); down 256 columns at both, not with the folded combination
+    assert _ws(64, 256, 512, 8, 2, _o(128, 0, 3))[0] == OK
+    assert _ws(64, 256, 384, 8, 2, _o(128, 0, 3))[0] == UNSUP
+    assert _ws(64, 256, 448, 8, 2, _o(192, 0, 3))[0] == OK
+    assert _ws(64, 256, 448, 8, 2, _o(192, 0, 3, gather=3))[0] == UNSUP
+    assert _ws(64, 256, 512, 8, 2, _o(128, 0, 4))[0] == UNSUP
+    for bm in (128, 192):
+        assert _ws(64, 256, 512, 8, 2, _o(bm, dvar=3))[0] == OK
+        assert _ws(64, 320, 512, 8, 2, _o(bm, dvar=3))[0] == UNSUP
+        assert _ws(64, 256, 512, 8, 2, _o(bm, dvar=3, fold=2))[0] == UNSUP
     for r in (1, 2, 3):
         assert _ws(64, 256, 512, 8, 2, _o(0, 0, 0, r))[0] == OK
 
@@ -112,7 +124,7 @@ def test_routing_and_gather_options():
     for x in (0, 1, 2, 3):
         assert _ws(64, 256, 512, 8, 2, _o(xcd=x))[0] == OK
     for bad in (_o(unfused=2), _o(unfused=-1), _o(xcd=4), _o(xcd=-1), _o(dvar=1), _o(dvar=-1),
-                _o(64, dvar=2), _o(192, dvar=3)):
+                _o(64, dvar=2), _o(192, dvar=4)):
         assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
     u0 = moe.moe_workspace_size(512, 4096, 14336, 8, 2)
     u1 = moe.moe_workspace_size(512, 4096, 14336, 8, 2, unfused_swiglu=1)

@@ -1,5 +1,7 @@
-"""GPU parity of the LDS-staged gate/up tile (BM = 192, 7 waves x 32
-columns, weights and activations fetched into LDS by direct-to-LDS loads).
+"""GPU parity of the LDS-staged GEMM tiles: the gate/up tile of BM = 192
+(7 waves x 32 columns) and of BM = 128 (8 waves x 32), and the down tile of
+BM = 128 and 192 (8 waves x 32), all with weights and activations fetched
+into LDS by direct-to-LDS loads.
 
 Each case meets the output tolerance against the oracle and, because the
 tile sums every output's K chunks in the same order as the register-ring
@@ -106,3 +108,63 @@ def test_lds_tile_rejected_where_it_cannot_run():
     # the automatic choice falls back to a register-ring tile there
     out = moe.moe_forward(x2, lg2, wgu2, wd2, 2, True, block_rows=192)
     parity.check_out(out, parity.oracle_out(x2, lg2, wgu2, wd2, 2, 0, True), "fallback")
+
+
+# ------------------------------------------------- the LDS-staged down tile
+
+DOWN_LDS = 3   # down_variant option value of the LDS-staged down tile (variant 2)
+
+
+def _down_case():
+    # d = 512 (two 256-column tiles), F = 384 (6 K steps), ~50 rows per expert
+    return _case("down", 200, 512, 384, 12, 3, 37)
+
+
+@pytest.mark.parametrize("split", [1, 2, 3])
+@pytest.mark.parametrize("bm", [128, 192])
+def test_lds_down_matches_oracle_and_register_tile(bm, split):
+    """The down GEMM with its weights staged in LDS (8 waves x 32 columns):
+    within the tolerance, and the same bytes as the register-ring down tile
+    (variant 0), which sums every output's K chunks in the same order."""
+    x, lg, wgu, wd, k, ref = _down_case()
+    out = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, split_k=split,
+                          down_variant=DOWN_LDS)
+    parity.check_out(out, ref, f"lds down bm={bm} split={split}")
+    base = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, split_k=split, down_variant=1)
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+
+
+def test_lds_down_several_blocks_per_expert():
+    x, lg, wgu, wd, k, ref = _case("multi_block_down", 400, 256, 448, 3, 2, 38)
+    for bm in (128, 192):
+        out = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, split_k=2,
+                              down_variant=DOWN_LDS)
+        parity.check_out(out, ref, f"lds down multi-block bm={bm}")
+
+
+def test_lds_down_is_automatic():
+    """At BM = 128 and 192 with d a multiple of 256 the automatic options
+    run the LDS-staged down tile (the same bytes as forcing it); with the
+    combination folded into the down GEMM they keep the register tile, and
+    forcing the LDS tile there is an error."""
+    x, lg, wgu, wd, k, ref = _down_case()
+    for bm in (128, 192):
+        auto = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm)
+        forced = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, down_variant=DOWN_LDS)
+        assert torch.equal(auto.view(torch.int16), forced.view(torch.int16))
+        folded = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, fold_combine=2)
+        parity.check_out(folded, ref, f"folded bm={bm}")
+        with pytest.raises(moe.MoeError):
+            moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, fold_combine=2,
+                            down_variant=DOWN_LDS)
+
+
+def test_lds_gate_up_at_128_rows():
+    """The 256-column LDS-staged gate/up tile of BM = 128 (an option: the
+    register-ring tiles measured faster on the MoE workload shapes there);
+    ffn = 512 is two whole tiles."""
+    x, lg, wgu, wd, k, ref = _case("gate_up_128", 200, 512, 512, 12, 3, 39)
+    out = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=128, tile_variant=3)
+    parity.check_out(out, ref, "lds gate/up bm=128")
+    base = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=128, tile_variant=1)
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
