@@ -358,12 +358,12 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes,
             raise SystemExit(f"no {counter} rows under {d}")
         return rows
 
-    def mode(name):  # output mode of a grouped GEMM instantiation
-        m = re.search(r"grouped_gemm_kernel<\d+, \d+, \d+, \d+, (\d)>", name)
+    def mode(name):  # output mode of a grouped GEMM instantiation (its last template argument)
+        m = re.search(r"(?:grouped_gemm_kernel|gemm_lds_kernel)<(?:\d+, )+(\d)>", name)
         return int(m.group(1)) if m else None
 
     classes = {
-        "gate_up_swiglu": lambda n: mode(n) == 0 or "gate_up_lds_kernel" in n,
+        "gate_up_swiglu": lambda n: mode(n) == 0,
         "down": lambda n: mode(n) == 1,
         "proj_bf16": lambda n: mode(n) == 2,
         "swiglu_act": lambda n: "swiglu_act_kernel" in n,
