@@ -566,7 +566,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds,
 
 // out: kOutSwiGLU -> bf16 h [A, N]; kOutF32Parts -> fp32 y [split, A, N]
 // (part p sums K steps [p * ksplit, (p + 1) * ksplit)).
-template <int BM, int WAVES, int BK, int STAGES, int MODE>
+template <int BM, int WAVES, int BK, int STAGES, int MODE, int WCPOL>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
@@ -658,10 +658,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     for (int q = 0; q < GPW; ++q)
 #pragma unroll
       for (int hh = 0; hh < LPG; ++hh)
-        // gate/up weights are each read once: non-temporal (measured 7% faster
-        // at Mixtral T=512; the down tile measured mixed, so it keeps the default)
-        dma16<MODE == kOutSwiGLU ? kCpolNT : 0>(wres, st + (wave * GPW + q) * GB + hh * 1024,
-                                                woff[q][hh], soff);
+        dma16<WCPOL>(wres, st + (wave * GPW + q) * GB + hh * 1024, woff[q][hh], soff);
   };
   // this wave's share of the activation tile of stage ks
   auto issue_x = [&](int ks) {
@@ -766,7 +763,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
 constexpr int kLdsBK = 64;     // whole 128-byte lines of each weight row per step
 constexpr int kLdsStages = 2;  // 2 x 80 KiB: the whole LDS of a CU at BM = 192, 7 waves
 
-template <int BM, int WAVES, int MODE>
+// WCPOL: cache policy of the weight loads.
+template <int BM, int WAVES, int MODE, int WCPOL>
 hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
                           const int32_t* blocks, const int32_t* nb, const int32_t* order,
                           const int32_t* offsets, void* out, int A, int N, int K, int split,
@@ -779,7 +777,7 @@ hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estr
   const int tiles_per_block = N / G::kTileCols * split;
   const long long grid = (long long)tiles_per_block * nb_max;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  gemm_lds_kernel<BM, WAVES, kLdsBK, kLdsStages, MODE><<<(unsigned)grid, G::kThreads, 0, s>>>(
+  gemm_lds_kernel<BM, WAVES, kLdsBK, kLdsStages, MODE, WCPOL><<<(unsigned)grid, G::kThreads, 0, s>>>(
       X, W, w_estride, blocks, nb, order, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
       gather_perm, gather_k, x_rows, xcd_group);
   return hipGetLastError();
@@ -813,15 +811,17 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
                           uint16_t* h, int A, int d,
                           int ffn, int nb_max, int rotate, int xcd_group, int x_tiled,
                           hipStream_t s) {
+  // The LDS-staged tiles read their weights once: non-temporal weight loads
+  // (Mixtral T=512 gate/up measured 360.8 -> 334.9 us).
   if (bm == 192 && variant == kGateUpLdsVariant) {
     if (x_tiled) return hipErrorInvalidValue;  // row-major activations only
-    return launch_lds_cfg<192, 7, kOutSwiGLU>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order,
+    return launch_lds_cfg<192, 7, kOutSwiGLU, kCpolNT>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order,
                                               offsets, h, A, ffn, d, 1, d, nb_max, rotate,
                                               gather_perm, k, T, xcd_group, s);
   }
   if (bm == 128 && variant == kGateUpLdsVariant) {
     if (x_tiled) return hipErrorInvalidValue;
-    return launch_lds_cfg<128, 8, kOutSwiGLU>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order,
+    return launch_lds_cfg<128, 8, kOutSwiGLU, kCpolNT>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order,
                                               offsets, h, A, ffn, d, 1, d, nb_max, rotate,
                                               gather_perm, k, T, xcd_group, s);
   }
@@ -870,17 +870,25 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
                        const int32_t* offsets, float* y,
                        int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
                        int xcd_group, const FoldCombine& fold, hipStream_t s) {
-  if (bm == 192 && variant == kDownLdsVariant) {
+  if ((bm == 192 || bm == 128) && variant == kDownLdsVariant) {
     if (fold.cnt) return hipErrorInvalidValue;  // the fold runs in the register-ring tiles
-    return launch_lds_cfg<192, 8, kOutF32Parts>(h, w_down, (long long)d * ffn, blocks, nb, order,
-                                                offsets, y, A, d, ffn, split, ksplit, nb_max,
-                                                rotate, nullptr, 1, A, xcd_group, s);
-  }
-  if (bm == 128 && variant == kDownLdsVariant) {
-    if (fold.cnt) return hipErrorInvalidValue;
-    return launch_lds_cfg<128, 8, kOutF32Parts>(h, w_down, (long long)d * ffn, blocks, nb, order,
-                                                offsets, y, A, d, ffn, split, ksplit, nb_max,
-                                                rotate, nullptr, 1, A, xcd_group, s);
+    // Weights are read once.  Non-temporal weight loads measured faster on
+    // every workload whose fp32 partials fit the 256 MiB MALL (down GEMM, µs:
+    // Mixtral T=128 159 -> 143, Qwen2 T=512 245 -> 230, DeepSeek-V3 T=512
+    // 1336 -> 1284) and slower where they do not (DeepSeek-V3 T=4096, 940 MB
+    // of partials: down 1694 -> 1726, combination 188 -> 219).
+    const bool nt = (long long)split * A * d * 4 <= (256LL << 20);
+#define MOE_DOWN_LDS(BMV, CP)                                                                    \
+  return launch_lds_cfg<BMV, 8, kOutF32Parts, CP>(h, w_down, (long long)d * ffn, blocks, nb, order, \
+                                                  offsets, y, A, d, ffn, split, ksplit, nb_max,   \
+                                                  rotate, nullptr, 1, A, xcd_group, s)
+    if (bm == 192) {
+      if (nt) MOE_DOWN_LDS(192, kCpolNT);
+      MOE_DOWN_LDS(192, 0);
+    }
+    if (nt) MOE_DOWN_LDS(128, kCpolNT);
+    MOE_DOWN_LDS(128, 0);
+#undef MOE_DOWN_LDS
   }
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && V == variant)                                                                      \
