@@ -135,14 +135,20 @@ bool gate_up_lds_fits(int bm, int ffn, bool x_tiled) {
   return (bm == 128 || bm == 192) && tc > 0 && ffn % tc == 0 && !x_tiled;
 }
 
-// Tile variant of the fused gate/up GEMM.  BM = 64 and 128: the narrow
-// variant when the wide one would give at most ~1.5 workgroups per CU.
-// BM = 192: the LDS-staged 224-column tile when the columns divide into
-// whole tiles (measured 16% faster than the register-ring tiles on
-// Mixtral-shaped blocks: half the activation bytes per weight byte);
-// otherwise the 112-column variant when its tiles fill the rounds better
-// than 128-column tiles do (both hold one workgroup per CU).
+// Tile variant of the fused gate/up GEMM.  BM = 128: the LDS-staged
+// 256-column tile when the columns divide into whole tiles and the launch
+// fills at least one round (measured faster on every such MoE workload
+// shape, gate/up µs: DeepSeek-V3 T=512 2434 -> 2169, Mixtral T=128
+// 355 -> 328, Qwen2 T=512 413 -> 393).  BM = 64 and 128 otherwise: the
+// narrow variant when the wide one would give at most ~1.5 workgroups per
+// CU.  BM = 192: the LDS-staged 224-column tile when the columns divide
+// into whole tiles (Mixtral T=512: half the activation bytes per weight
+// byte); otherwise the 112-column variant when its tiles fill the rounds
+// better than 128-column tiles do (both hold one workgroup per CU).
 int auto_gu_variant(int A, int E, int ffn, int bm, bool x_tiled) {
+  if (bm == 128 && gate_up_lds_fits(128, ffn, x_tiled) &&
+      est_workgroups(A, E, bm, ffn, gate_up_tile_cols(128, kGateUpLdsVariant)) >= 256)
+    return kGateUpLdsVariant;
   if (bm == 64 || bm == 128)
     return est_workgroups(A, E, bm, ffn, gate_up_tile_cols(bm, 0)) <= 384 ? 1 : 0;
   if (bm == 192) {

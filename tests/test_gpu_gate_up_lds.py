@@ -160,11 +160,23 @@ def test_lds_down_is_automatic():
 
 
 def test_lds_gate_up_at_128_rows():
-    """The 256-column LDS-staged gate/up tile of BM = 128 (an option: the
-    register-ring tiles measured faster on the MoE workload shapes there);
-    ffn = 512 is two whole tiles."""
+    """The 256-column LDS-staged gate/up tile of BM = 128; ffn = 512 is two
+    whole tiles.  Within the tolerance, the same bytes as the register-ring
+    tile, and chosen automatically when the launch fills a round (here 12
+    blocks x 2 tiles do not: the automatic choice keeps a register tile)."""
     x, lg, wgu, wd, k, ref = _case("gate_up_128", 200, 512, 512, 12, 3, 39)
     out = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=128, tile_variant=3)
     parity.check_out(out, ref, "lds gate/up bm=128")
     base = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=128, tile_variant=1)
     assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+
+
+def test_lds_gate_up_at_128_rows_is_automatic():
+    """64 experts x 4 tiles of ffn = 1024 fill a round: the automatic
+    options run the BM = 128 LDS-staged tile (the same bytes as forcing it)."""
+    x, lg, wgu, wd, k, ref = _case("gate_up_128_auto", 256, 256, 1024, 64, 8, 40)
+    assert moe.moe_plan(256, 256, 1024, 64, 8)[0] == 128
+    auto = moe.moe_forward(x, lg, wgu, wd, k, True)
+    forced = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=128, tile_variant=3)
+    assert torch.equal(auto.view(torch.int16), forced.view(torch.int16))
+    parity.check_out(auto, ref, "lds gate/up bm=128 automatic")
