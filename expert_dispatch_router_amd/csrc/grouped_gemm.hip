@@ -589,7 +589,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
   if (bi >= nb_dev[0]) return;
   const int b = order ? order[bi] : bi;
   const int rem = wg - bi * tiles_per_block;
-  const int n_tiles = N / G::kTileCols;
+  const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;  // the last may be partial
   const int tile = rem % n_tiles;
   const int part = rem / n_tiles;
   const int kb = part * ksplit;
@@ -620,13 +620,18 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
           ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, x_rows * K * 2, kRsrcWord3)
           : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (size_t)r0 * K), (short)0,
                                               rows * K * 2, kRsrcWord3);
-  // weight groups of this wave: q = 2 * g + j -> operand g (gate, up), subtile j
+  // weight groups of this wave: q = 2 * g + j -> operand g (gate, up), subtile j.
+  // Columns past N (a partial last tile) get an offset past the
+  // descriptor's range: zeros, no memory request; their outputs are not
+  // stored.
   int woff[GPW][LPG];
 #pragma unroll
   for (int q = 0; q < GPW; ++q)
 #pragma unroll
-    for (int hh = 0; hh < LPG; ++hh)
-      woff[q][hh] = (((q >> 1) * N + n0 + 16 * (q & 1) + lrow[hh]) * K + kb + lchk[hh] * 8) * 2;
+    for (int hh = 0; hh < LPG; ++hh) {
+      const int col = n0 + 16 * (q & 1) + lrow[hh];
+      woff[q][hh] = col < N ? (((q >> 1) * N + col) * K + kb + lchk[hh] * 8) * 2 : NG * N * K * 2;
+    }
   int xoff[XPW][LPG];
   int xgrp[XPW];
 #pragma unroll
@@ -741,6 +746,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     if (mt < mt_act && m < rows) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
+        if (n0 + 16 * j >= N) continue;  // subtile past the last column (N % 16 == 0)
         const int n = n0 + 16 * j + 4 * (lane >> 4);
         if constexpr (MODE == kOutSwiGLU) {
           const f32x4 gv = acc[0][mt][j];
@@ -771,10 +777,10 @@ hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estr
                           int ksplit, int nb_max, int rotate, const int32_t* gather_perm,
                           int gather_k, int x_rows, int xcd_group, hipStream_t s) {
   using G = LdsGemm<BM, WAVES, kLdsBK, kLdsStages, MODE>;
-  // whole tiles and whole K steps only
-  if (N % G::kTileCols != 0 || K % kLdsBK != 0 || ksplit % kLdsBK != 0 || split < 1)
+  // whole 16-column subtiles and whole K steps
+  if (N % 16 != 0 || K % kLdsBK != 0 || ksplit % kLdsBK != 0 || split < 1)
     return hipErrorInvalidValue;
-  const int tiles_per_block = N / G::kTileCols * split;
+  const int tiles_per_block = (N + G::kTileCols - 1) / G::kTileCols * split;
   const long long grid = (long long)tiles_per_block * nb_max;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   gemm_lds_kernel<BM, WAVES, kLdsBK, kLdsStages, MODE, WCPOL><<<(unsigned)grid, G::kThreads, 0, s>>>(

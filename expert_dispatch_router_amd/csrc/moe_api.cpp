@@ -129,30 +129,50 @@ double round_balance(long long wg, long long slots) {
 }
 
 // Whether the LDS-staged gate/up tile (224 columns at BM = 192, 256 at
-// BM = 128) can run: whole column tiles, row-major activations.
+// BM = 128) can run: row-major activations (the last column tile may be
+// partial).
 bool gate_up_lds_fits(int bm, int ffn, bool x_tiled) {
-  const int tc = gate_up_tile_cols(bm, kGateUpLdsVariant);
-  return (bm == 128 || bm == 192) && tc > 0 && ffn % tc == 0 && !x_tiled;
+  (void)ffn;
+  return (bm == 128 || bm == 192) && gate_up_tile_cols(bm, kGateUpLdsVariant) > 0 && !x_tiled;
 }
 
-// Tile variant of the fused gate/up GEMM.  BM = 128: the LDS-staged
-// 256-column tile when the columns divide into whole tiles and the launch
-// fills at least one round (measured faster on every such MoE workload
-// shape, gate/up µs: DeepSeek-V3 T=512 2434 -> 2169, Mixtral T=128
-// 355 -> 328, Qwen2 T=512 413 -> 393).  BM = 64 and 128 otherwise: the
-// narrow variant when the wide one would give at most ~1.5 workgroups per
-// CU.  BM = 192: the LDS-staged 224-column tile when the columns divide
-// into whole tiles (Mixtral T=512: half the activation bytes per weight
-// byte); otherwise the 112-column variant when its tiles fill the rounds
-// better than 128-column tiles do (both hold one workgroup per CU).
+// Automatic use of a partial last LDS tile: at most this share of extra
+// columns, and only for launches of at least two rounds (DeepSeek-V3 T=4096
+// gate/up measured 3064 -> 2738 us with 2048 columns in 224-column tiles;
+// skewed T=128/256, ~20 active blocks of 1408 columns in 256-column tiles,
+// 42 -> 66 us: too few workgroups).
+constexpr double kMaxLdsTileWaste = 0.1;
+constexpr long long kPartialLdsMinWorkgroups = 512;
+
+
+// Columns a launch of `tc`-column tiles covers beyond n, as a fraction of n
+// (a partial last tile still reads its block's activation rows in full).
+double tile_waste(int n, int tc) {
+  return tc > 0 ? (double)((n + tc - 1) / tc * tc - n) / n : 1.0;
+}
+
+// Tile variant of the fused gate/up GEMM.  The LDS-staged tile (256
+// columns at BM = 128, 224 at BM = 192) when its columns divide into whole
+// tiles -- at BM = 128 only for launches of at least one round -- or nearly
+// so on large launches (kMaxLdsTileWaste); measured faster on every such
+// MoE workload shape (gate/up µs: Mixtral T=512 427.6 -> 334.9 with half
+// the activation bytes per weight byte, DeepSeek-V3 T=512 2434 -> 2169,
+// T=4096 3064 -> 2738, Mixtral T=128 355 -> 328, Qwen2 T=512 413 -> 393).
+// Otherwise, BM = 64 and 128: the narrow variant when the wide one would
+// give at most ~1.5 workgroups per CU; BM = 192: the 112-column variant
+// when its tiles fill the rounds better than 128-column tiles do.
 int auto_gu_variant(int A, int E, int ffn, int bm, bool x_tiled) {
-  if (bm == 128 && gate_up_lds_fits(128, ffn, x_tiled) &&
-      est_workgroups(A, E, bm, ffn, gate_up_tile_cols(128, kGateUpLdsVariant)) >= 256)
-    return kGateUpLdsVariant;
+  if ((bm == 128 || bm == 192) && gate_up_lds_fits(bm, ffn, x_tiled)) {
+    const int tc = gate_up_tile_cols(bm, kGateUpLdsVariant);
+    const double waste = tile_waste(ffn, tc);
+    const long long wg = est_workgroups(A, E, bm, ffn, tc);
+    if (waste == 0.0 ? (bm == 192 || wg >= 256)
+                     : (waste <= kMaxLdsTileWaste && wg >= kPartialLdsMinWorkgroups))
+      return kGateUpLdsVariant;
+  }
   if (bm == 64 || bm == 128)
     return est_workgroups(A, E, bm, ffn, gate_up_tile_cols(bm, 0)) <= 384 ? 1 : 0;
   if (bm == 192) {
-    if (gate_up_lds_fits(192, ffn, x_tiled)) return kGateUpLdsVariant;
     const double b0 = round_balance(est_workgroups(A, E, bm, ffn, gate_up_tile_cols(192, 0)), 256);
     const double b1 = round_balance(est_workgroups(A, E, bm, ffn, gate_up_tile_cols(192, 1)), 256);
     const bool exact1 = ffn % gate_up_tile_cols(192, 1) == 0;  // no partial last tile

@@ -75,7 +75,7 @@ def _o(bm=0, split=0, variant=0, rotate=0, routing=0, gather=0, unfused=0, xcd=0
 
 
 def test_options_checks():
-    for bad in (_o(8), _o(0, 9), _o(0, -1), _o(0, 0, 1), _o(32, 0, 2), _o(64, 0, 3), _o(192, 0, 3), _o(0, 0, 0, 4),
+    for bad in (_o(8), _o(0, 9), _o(0, -1), _o(0, 0, 1), _o(32, 0, 2), _o(64, 0, 3), _o(192, 0, 4), _o(0, 0, 0, 4),
                 _o(0, 0, -1), _o(0, 0, 0, -1)):
         assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
     for bm in (16, 32, 64, 128, 192):
@@ -86,11 +86,12 @@ def test_options_checks():
     assert _ws(64, 256, 512, 8, 2, _o(192, 0, 2))[0] == OK
     assert _ws(64, 256, 512, 8, 2, _o(128, 0, 2))[0] == OK
     # the LDS-staged tiles (variant 2 of BM = 128 and 192, option value 3):
-    # whole column tiles only -- gate/up 256 columns at BM = 128 (ffn = 512
-    # fits, 384 does not), 224 at BM = 192 (512 does not fit: bad list
-    # above); down 256 columns at both, not with the folded combination
+    # gate/up at any ffn (a partial last tile), not with K-step-tiled
+    # activations; down at d a multiple of 256, not with the folded
+    # combination
     assert _ws(64, 256, 512, 8, 2, _o(128, 0, 3))[0] == OK
-    assert _ws(64, 256, 384, 8, 2, _o(128, 0, 3))[0] == UNSUP
+    assert _ws(64, 256, 384, 8, 2, _o(128, 0, 3))[0] == OK
+    assert _ws(64, 256, 512, 8, 2, _o(192, 0, 3))[0] == OK
     assert _ws(64, 256, 448, 8, 2, _o(192, 0, 3))[0] == OK
     assert _ws(64, 256, 448, 8, 2, _o(192, 0, 3, gather=3))[0] == UNSUP
     assert _ws(64, 256, 512, 8, 2, _o(128, 0, 4))[0] == UNSUP

@@ -10,9 +10,8 @@ as the 112-column tile (variant 2) on the same inputs -- except under the
 per-workgroup rotation, whose start depends on the tiling.  Cases cover ragged
 blocks (rows ending mid-subtile), experts spanning several blocks, one and
 two K steps, an odd number of K steps, both row-gather paths, every K
-rotation and the XCD-grouped order; forcing the tile where it cannot run
-(ffn not a multiple of 224, K-step-tiled activations) is an error.  (ffn
-is a multiple of 64 as well, so the cases use multiples of 448.)"""
+rotation, the XCD-grouped order and a partial last column tile; forcing
+the tile with K-step-tiled activations is an error."""
 import numpy as np
 import pytest
 import torch
@@ -102,12 +101,22 @@ def test_lds_tile_rejected_where_it_cannot_run():
     x, lg, wgu, wd, k, _ = _case("ragged", *CASES["ragged"])
     with pytest.raises(moe.MoeError):  # K-step-tiled activations
         moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=192, tile_variant=LDS, gather_mode=3)
-    cfg, x2, lg2, wgu2, wd2 = parity.make_case(64, 128, 384, 4, 2, seed=36)
-    with pytest.raises(moe.MoeError):  # ffn = 384 is not a multiple of 224
-        moe.moe_forward(x2, lg2, wgu2, wd2, 2, True, block_rows=192, tile_variant=LDS)
-    # the automatic choice falls back to a register-ring tile there
-    out = moe.moe_forward(x2, lg2, wgu2, wd2, 2, True, block_rows=192)
-    parity.check_out(out, parity.oracle_out(x2, lg2, wgu2, wd2, 2, 0, True), "fallback")
+
+
+@pytest.mark.parametrize("bm", [128, 192])
+def test_lds_tile_partial_last_tile(bm):
+    """ffn = 576 is 2.57 tiles of 224 columns and 2.25 of 256: the last tile
+    holds 128 (BM = 192) or 64 (BM = 128) real columns.  Its weight rows
+    past ffn read as zeros and its outputs there are not stored: within the
+    tolerance and the same bytes as the register-ring tile (both with the
+    separate down GEMM: at this size the 64-column tile of BM = 128 would
+    otherwise take the fused small-launch path)."""
+    x, lg, wgu, wd, k, ref = _case("partial", 180, 256, 576, 6, 2, 41)
+    out = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, tile_variant=LDS, fuse_down=1)
+    parity.check_out(out, ref, f"lds partial tile bm={bm}")
+    base = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, tile_variant=REGRING,
+                           fuse_down=1)
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
 
 
 # ------------------------------------------------- the LDS-staged down tile
