@@ -358,9 +358,12 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes,
             raise SystemExit(f"no {counter} rows under {d}")
         return rows
 
-    def mode(name):  # output mode of a grouped GEMM instantiation (its last template argument)
-        m = re.search(r"(?:grouped_gemm_kernel|gemm_lds_kernel)<(?:\d+, )+(\d)>", name)
-        return int(m.group(1)) if m else None
+    def mode(name):  # output mode of a grouped GEMM instantiation (its fifth template argument)
+        m = re.search(r"(?:grouped_gemm_kernel|gemm_lds_kernel)<((?:\d+, )*\d+)>", name)
+        if not m:
+            return None
+        args = [int(a) for a in m.group(1).split(", ")]
+        return args[4] if len(args) > 4 else None
 
     classes = {
         "gate_up_swiglu": lambda n: mode(n) == 0,
