@@ -367,7 +367,7 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes,
 
     classes = {
         "gate_up_swiglu": lambda n: mode(n) == 0,
-        "down": lambda n: mode(n) == 1,
+        "down": lambda n: mode(n) in (1, 4),   # fp32 parts: 32 or 64 columns per wave
         "proj_bf16": lambda n: mode(n) == 2,
         "swiglu_act": lambda n: "swiglu_act_kernel" in n,
     }

@@ -67,7 +67,7 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)
 // h stays in LDS and the workgroup writes the fp32 partial
 // y[tile] = h[:, tile cols] . W_down[:, tile cols]^T, one part per column
 // tile, which the combination adds in tile order.
-enum { kOutSwiGLU = 0, kOutF32Parts = 1, kOutBF16 = 2, kOutSwiGLUDown = 3 };
+enum { kOutSwiGLU = 0, kOutF32Parts = 1, kOutBF16 = 2, kOutSwiGLUDown = 3, kOutF32Wide = 4 };
 
 template <int BM, int NWT, int WAVES, int PF, int MODE>
 struct Gemm {
@@ -525,12 +525,18 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
 // "vmcnt" waits for the wave's own loads of a stage; the barrier
 // after it publishes the stage to all waves.
 // MODE kOutSwiGLU: gate and up rows (NG = 2), bf16 h; kOutF32Parts: one
-// operand (the down projection), fp32 partial sums of a split reduction.
+// operand (the down projection), fp32 partial sums of a split reduction;
+// kOutF32Wide: the same output with 64 columns per wave, taken as two
+// adjacent 32-column groups in the places of gate and up, so a stage holds
+// twice the weight rows per activation row.
 template <int BM, int WAVES, int BK, int STAGES, int MODE = kOutSwiGLU>
 struct LdsGemm {
   static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
-  static_assert(MODE == kOutSwiGLU || MODE == kOutF32Parts, "SwiGLU or fp32 parts");
-  static constexpr int kNG = MODE == kOutSwiGLU ? 2 : 1;
+  static_assert(MODE == kOutSwiGLU || MODE == kOutF32Parts || MODE == kOutF32Wide,
+                "SwiGLU or fp32 parts");
+  static constexpr bool kWide = MODE == kOutF32Wide;
+  static constexpr int kNG = (MODE == kOutSwiGLU || kWide) ? 2 : 1;
+  static constexpr int kWaveCols = kWide ? 64 : 32;  // output columns of one wave
   static constexpr int kGPW = 2 * kNG;                // 16-row weight groups per wave
   static constexpr int kMT = BM / 16;
   static constexpr int kKC = BK / 32;                 // MFMA K chunks per step
@@ -538,7 +544,7 @@ struct LdsGemm {
   static constexpr int kGroupBytes = 16 * kRowBytes;
   static constexpr int kLoadsPerGroup = kGroupBytes / 1024;
   static constexpr int kThreads = WAVES * 64;
-  static constexpr int kTileCols = WAVES * 32;
+  static constexpr int kTileCols = WAVES * kWaveCols;
   static constexpr int kWBytes = WAVES * kGPW * kGroupBytes;
   static constexpr int kXGroups = BM / 16;
   static constexpr int kXPerWave = (kXGroups + WAVES - 1) / WAVES;
@@ -564,8 +570,8 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds,
       r, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, voff, soff, 0, CPOL);
 }
 
-// out: kOutSwiGLU -> bf16 h [A, N]; kOutF32Parts -> fp32 y [split, A, N]
-// (part p sums K steps [p * ksplit, (p + 1) * ksplit)).
+// out: kOutSwiGLU -> bf16 h [A, N]; kOutF32Parts and kOutF32Wide -> fp32
+// y [split, A, N] (part p sums K steps [p * ksplit, (p + 1) * ksplit)).
 template <int BM, int WAVES, int BK, int STAGES, int MODE, int WCPOL>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
@@ -602,7 +608,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n0 = tile * G::kTileCols + wave * 32;
+  const int n0 = tile * G::kTileCols + wave * G::kWaveCols;
 
   // loads: load h of a group, lane -> row h * (1024 / RB) + lane / (RB / 16),
   // slot lane % (RB / 16), which holds K chunk slot ^ swz(row)
@@ -613,14 +619,18 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     lrow[hh] = hh * (1024 / RB) + lane / SPR;
     lchk[hh] = (lane % SPR) ^ G::swz(lrow[hh]);
   }
+  // weight rows of the expert: NG operands of N rows (SwiGLU), else N rows
+  constexpr int kWOps = G::kWide ? 1 : NG;
+  const int wbytes = kWOps * N * K * 2;
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (size_t)e * w_estride), (short)0, NG * N * K * 2, kRsrcWord3);
+      (void*)(W + (size_t)e * w_estride), (short)0, wbytes, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t xres =
       gather_perm
           ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, x_rows * K * 2, kRsrcWord3)
           : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (size_t)r0 * K), (short)0,
                                               rows * K * 2, kRsrcWord3);
-  // weight groups of this wave: q = 2 * g + j -> operand g (gate, up), subtile j.
+  // weight groups of this wave: q = 2 * g + j -> operand g (gate, up), subtile j;
+  // wide: column group g of the wave's 64 columns, subtile j.
   // Columns past N (a partial last tile) get an offset past the
   // descriptor's range: zeros, no memory request; their outputs are not
   // stored.
@@ -629,8 +639,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
   for (int q = 0; q < GPW; ++q)
 #pragma unroll
     for (int hh = 0; hh < LPG; ++hh) {
-      const int col = n0 + 16 * (q & 1) + lrow[hh];
-      woff[q][hh] = col < N ? (((q >> 1) * N + col) * K + kb + lchk[hh] * 8) * 2 : NG * N * K * 2;
+      const int col = n0 + (G::kWide ? 32 * (q >> 1) : 0) + 16 * (q & 1) + lrow[hh];
+      const int wrow = G::kWide ? col : (q >> 1) * N + col;
+      woff[q][hh] = col < N ? (wrow * K + kb + lchk[hh] * 8) * 2 : wbytes;
     }
   int xoff[XPW][LPG];
   int xgrp[XPW];
@@ -740,9 +751,25 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
   }
 
   // epilogue: lane holds columns n0 + 16j + 4*(lane>>4) + 0..3 of row mt*16 + (lane & 15)
+  // (wide: n0 + 32g + 16j + ...)
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + rr;
+    if constexpr (G::kWide) {
+      if (mt < mt_act && m < rows) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int c0 = n0 + 32 * g + 16 * j;
+            if (c0 >= N) continue;  // subtile past the last column (N % 16 == 0)
+            const int n = c0 + 4 * (lane >> 4);
+            *reinterpret_cast<f32x4*>(static_cast<float*>(out) +
+                                      ((size_t)part * A + r0 + m) * N + n) = acc[g][mt][j];
+          }
+      }
+      continue;
+    }
     if (mt < mt_act && m < rows) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -808,6 +835,10 @@ int down_tile_cols(int bm, int variant) {
 #undef X
   if ((bm == 192 || bm == 128) && variant == kDownLdsVariant)
     return LdsGemm<192, 8, kLdsBK, kLdsStages, kOutF32Parts>::kTileCols;  // 256 at both
+  if (bm == 192 && variant == kDownLdsWideVariant)
+    return LdsGemm<192, 7, kLdsBK, kLdsStages, kOutF32Wide>::kTileCols;  // 448
+  if (bm == 128 && variant == kDownLdsWideVariant)
+    return LdsGemm<128, 8, kLdsBK, kLdsStages, kOutF32Wide>::kTileCols;  // 512
   return 0;
 }
 
@@ -895,6 +926,24 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
     if (nt) MOE_DOWN_LDS(128, kCpolNT);
     MOE_DOWN_LDS(128, 0);
 #undef MOE_DOWN_LDS
+  }
+  // The wide LDS-staged tile: 64 columns per wave (7 waves at BM = 192, 8 at
+  // BM = 128), half the activation bytes per weight byte of the tile above;
+  // the last column tile may be partial.  Same weight cache policy rule.
+  if ((bm == 192 || bm == 128) && variant == kDownLdsWideVariant) {
+    if (fold.cnt) return hipErrorInvalidValue;
+    const bool nt = (long long)split * A * d * 4 <= (256LL << 20);
+#define MOE_DOWN_WIDE(BMV, WV, CP)                                                                \
+  return launch_lds_cfg<BMV, WV, kOutF32Wide, CP>(h, w_down, (long long)d * ffn, blocks, nb, order, \
+                                                  offsets, y, A, d, ffn, split, ksplit, nb_max,    \
+                                                  rotate, nullptr, 1, A, xcd_group, s)
+    if (bm == 192) {
+      if (nt) MOE_DOWN_WIDE(192, 7, kCpolNT);
+      MOE_DOWN_WIDE(192, 7, 0);
+    }
+    if (nt) MOE_DOWN_WIDE(128, 8, kCpolNT);
+    MOE_DOWN_WIDE(128, 8, 0);
+#undef MOE_DOWN_WIDE
   }
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && V == variant)                                                                      \

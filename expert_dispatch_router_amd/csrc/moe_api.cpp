@@ -211,12 +211,32 @@ bool down_lds_fits(int bm, int d, bool fold) {
   return (bm == 128 || bm == 192) && d % down_tile_cols(bm, kDownLdsVariant) == 0 && !fold;
 }
 
-// Tile variant of the down GEMM: the LDS-staged tile wherever it fits --
-// measured faster or equal on every MoE workload shape (down GEMM, µs:
-// skewed T=512 45.9 -> 39.5, Qwen2 T=512 267 -> 244, Mixtral T=512
+// Tile variant of the down GEMM.  The wide LDS-staged tile (64 columns per
+// wave) when its columns divide into whole tiles or nearly so
+// (kMaxLdsTileWaste), the launch, every expert active, has at least a round
+// of workgroups, and each block has at least kWideDownMinTiles column tiles
+// (skewed routing leaves most experts idle, and the host cannot see it: the
+// launch must keep its workgroups through the columns).  Measured faster
+// there (down GEMM, µs: Qwen2 T=128 215.6 -> 202.5, T=256 222.7 -> 204.6,
+// T=512 231.6 -> 214.4, DeepSeek-V3 T=512 1255 -> 1237, T=4096
+// 1688 -> 1662), slower on launches of a few long blocks (Mixtral T=512,
+// 160-240 workgroups: 194 -> 206-262; T=128 144 -> 148-193) and on skewed
+// routing with 4 tiles per block (T=128 25.4 -> 35.0, T=256 33.2 -> 36.5;
+// T=512 42.6 -> 40.4).
+// Else the 256-column LDS-staged tile wherever it fits -- measured faster
+// or equal on every MoE workload shape than the register tiles (down GEMM,
+// µs: skewed T=512 45.9 -> 39.5, Qwen2 T=512 267 -> 244, Mixtral T=512
 // 205 -> 188, DeepSeek-V3 T=4096 1726 -> 1678, Mixtral T=128 162 -> 160) --
 // else variant 0.
-int auto_dn_variant(int bm, int d, bool fold) {
+constexpr int kWideDownMinTiles = 6;
+
+int auto_dn_variant(int A, int E, int bm, int d, int split, bool fold) {
+  if (!fold && (bm == 128 || bm == 192)) {
+    const int wc = down_tile_cols(bm, kDownLdsWideVariant);
+    if (wc > 0 && tile_waste(d, wc) <= kMaxLdsTileWaste && (d + wc - 1) / wc >= kWideDownMinTiles &&
+        est_workgroups(A, E, bm, d, wc) * split >= 256)
+      return kDownLdsWideVariant;
+  }
   return down_lds_fits(bm, d, fold) ? kDownLdsVariant : 0;
 }
 
@@ -274,9 +294,11 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     const int fc = opt ? opt->fold_combine : 0;
     p->fold = fc == 0 ? auto_fold(T, d, E, k) : fc == 2;
     p->dn_variant = (opt && opt->down_variant) ? opt->down_variant - 1
-                                               : auto_dn_variant(p->bm, d, p->fold);
+                                               : auto_dn_variant(A, E, p->bm, d, p->split, p->fold);
     if (p->dn_variant == kDownLdsVariant && !down_lds_fits(p->bm, d, p->fold))
       p->plan_error = MOE_ERR_UNSUPPORTED;  // forced where it cannot run
+    if (p->dn_variant == kDownLdsWideVariant && p->fold)
+      p->plan_error = MOE_ERR_UNSUPPORTED;  // the fold lives in the register-ring tiles
     const int rot = opt ? opt->rotate : 0;
     // kernel values: 0 off, 1 per block, 2 per workgroup
     p->gu_rotate = rot == 0 ? auto_rotate(d) : rot - 1;

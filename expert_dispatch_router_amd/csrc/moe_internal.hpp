@@ -211,6 +211,9 @@ constexpr int kGateUpLdsVariant = 2;
 // Tile variant of the down GEMM at BM = 192 that stages its weights in LDS (8 waves x 32
 // columns).
 constexpr int kDownLdsVariant = 2;
+// Tile variant of the down GEMM at BM = 128 and 192 that stages its weights in LDS with 64
+// columns per wave (8 waves, 512 columns at BM = 128; 7 waves, 448 at BM = 192).
+constexpr int kDownLdsWideVariant = 3;
 int down_tile_cols(int bm, int variant);
 
 }  // namespace moe

@@ -88,20 +88,26 @@ typedef struct moe_options {
      * explicitly).  BM = 64 has variants 0 (256 columns per workgroup) and 1
      * (128 columns); BM = 128 has variants 0 (128 columns, 8 waves), 1
      * (64 columns) and 2 (256 columns, 8 waves, weights staged in LDS;
-     * only when ffn is a multiple of 256 and gather_mode is not 3, else
+     * the last column tile may be partial; not with gather_mode 3, else
      * MOE_ERR_UNSUPPORTED); BM = 192 has variants 0 (128 columns, 8 waves),
      * 1 (112 columns, 7 waves) and 2 (224 columns, 7 waves, weights staged
-     * in LDS; only when ffn is a multiple of 224 and gather_mode is not 3,
-     * else MOE_ERR_UNSUPPORTED -- automatic at BM = 192 where it fits);
+     * in LDS; the last column tile may be partial; not with gather_mode 3,
+     * else MOE_ERR_UNSUPPORTED -- automatic at BM = 192 where ffn is a
+     * multiple of 224 or the launch is large);
      * every other BM has variant 0 only. */
     int tile_variant;
     /* Tile variant of the down GEMM, like tile_variant (block_rows must be
      * set).  BM = 128 and 192 have variants 0 and 1 (256 columns per
      * workgroup: 4 waves of 64 and 8 waves of 32 at BM = 128, the reverse
-     * at BM = 192) and 2 (256 columns, 8 waves, weights staged in LDS; only
-     * when d is a multiple of 256 and the combination is not folded into
-     * the down GEMM, else MOE_ERR_UNSUPPORTED -- automatic where it fits);
-     * every other BM has variant 0 only.  0 = automatic. */
+     * at BM = 192), 2 (256 columns, 8 waves of 32, weights staged in LDS;
+     * only when d is a multiple of 256) and 3 (64 columns per wave staged
+     * in LDS: 512 columns, 8 waves at BM = 128; 448 columns, 7 waves at
+     * BM = 192; the last column tile may be partial); variants 2 and 3
+     * only when the combination is not folded into the down GEMM, else
+     * MOE_ERR_UNSUPPORTED.  Automatic: variant 3 on launches with many
+     * workgroups and at least six column tiles per block, else 2 where it
+     * fits; every other BM has variant 0 only.  0 = automatic.  All
+     * variants give the same bytes (the same per-output K order). */
     int down_variant;
     /* K-start rotation of the GEMMs: a workgroup starts its reduction at a
      * step derived from its schedule block (2) or from its own id (3), and

@@ -99,6 +99,12 @@ def test_options_checks():
         assert _ws(64, 256, 512, 8, 2, _o(bm, dvar=3))[0] == OK
         assert _ws(64, 320, 512, 8, 2, _o(bm, dvar=3))[0] == UNSUP
         assert _ws(64, 256, 512, 8, 2, _o(bm, dvar=3, fold=2))[0] == UNSUP
+        # the wide LDS-staged down tile (variant 3, option value 4): any d (a
+        # partial last tile), not with the folded combination
+        assert _ws(64, 256, 512, 8, 2, _o(bm, dvar=4))[0] == OK
+        assert _ws(64, 320, 512, 8, 2, _o(bm, dvar=4))[0] == OK
+        assert _ws(64, 256, 512, 8, 2, _o(bm, dvar=4, fold=2))[0] == UNSUP
+    assert _ws(64, 256, 512, 8, 2, _o(64, dvar=4))[0] == UNSUP
     for r in (1, 2, 3):
         assert _ws(64, 256, 512, 8, 2, _o(0, 0, 0, r))[0] == OK
 
@@ -125,7 +131,7 @@ def test_routing_and_gather_options():
     for x in (0, 1, 2, 3):
         assert _ws(64, 256, 512, 8, 2, _o(xcd=x))[0] == OK
     for bad in (_o(unfused=2), _o(unfused=-1), _o(xcd=4), _o(xcd=-1), _o(dvar=1), _o(dvar=-1),
-                _o(64, dvar=2), _o(192, dvar=4)):
+                _o(64, dvar=2), _o(192, dvar=5)):
         assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
     u0 = moe.moe_workspace_size(512, 4096, 14336, 8, 2)
     u1 = moe.moe_workspace_size(512, 4096, 14336, 8, 2, unfused_swiglu=1)

@@ -57,6 +57,7 @@ K5 = "void moe::(anonymous namespace)::grouped_gemm_kernel<192, 2, 8, 3, 1>(unsi
 # the output mode is still the fifth
 K4L = "void moe::(anonymous namespace)::gemm_lds_kernel<192, 7, 64, 2, 0, 2>(unsigned short const*)"
 K5L = "void moe::(anonymous namespace)::gemm_lds_kernel<192, 8, 64, 2, 1, 2>(unsigned short const*)"
+K5W = "void moe::(anonymous namespace)::gemm_lds_kernel<128, 8, 64, 2, 4, 0>(unsigned short const*)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -83,14 +84,15 @@ def test_traffic_summary_scales_by_the_copy_calibration(tmp_path):
 def test_traffic_summary_classifies_lds_staged_tiles_by_their_mode(tmp_path):
     gib = 1 << 30
     _counter_csv(str(tmp_path / "f" / "run_counter_collection.csv"), "FETCH_SIZE",
-                 [(COPY, 524288.0), (K4L, 500.0), (K5L, 9.0)])
+                 [(COPY, 524288.0), (K4L, 500.0), (K5L, 9.0), (K5W, 9.0)])
     _counter_csv(str(tmp_path / "w" / "run_counter_collection.csv"), "WRITE_SIZE",
-                 [(COPY, 1048576.0), (K4L, 50.0), (K5L, 2.0)])
+                 [(COPY, 1048576.0), (K4L, 50.0), (K5L, 2.0), (K5W, 2.0)])
     out = bench.summarize_traffic(str(tmp_path / "f"), str(tmp_path / "w"), "lds", gib,
                                   out_dir=str(tmp_path))
     assert set(out["kernels"]) == {"gate_up_swiglu", "down"}
     assert out["bytes_per_launch"] == pytest.approx(500.0 * 2048 + 50.0 * 1024)
     assert out["kernels"]["down"]["bytes_per_launch"] == pytest.approx(9.0 * 2048 + 2.0 * 1024)
+    assert out["kernels"]["down"]["launches"] == [2, 2]
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -189,3 +189,61 @@ def test_lds_gate_up_at_128_rows_is_automatic():
     forced = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=128, tile_variant=3)
     assert torch.equal(auto.view(torch.int16), forced.view(torch.int16))
     parity.check_out(auto, ref, "lds gate/up bm=128 automatic")
+
+
+# ------------------------------------------- the wide LDS-staged down tile
+
+DOWN_WIDE = 4  # down_variant option value of the wide LDS-staged down tile (variant 3)
+
+WIDE_CASES = {
+    # d = 512: one whole 512-column tile at BM = 128; 448 + a partial 64 at BM = 192
+    "d512": (200, 512, 384, 12, 3, 37),
+    # d = 256: half a tile at BM = 128 (waves past the last column store nothing)
+    "d256_multi_block": (400, 256, 448, 3, 2, 38),
+    # d = 1024: two whole tiles at BM = 128; 448 + 448 + 128 at BM = 192; one K step
+    "d1024_one_step": (96, 1024, 64, 5, 2, 39),
+}
+
+
+@pytest.mark.parametrize("split", [1, 2, 3])
+@pytest.mark.parametrize("bm", [128, 192])
+@pytest.mark.parametrize("name", sorted(WIDE_CASES))
+def test_lds_wide_down_matches_oracle_and_register_tile(name, bm, split):
+    """The down GEMM with 64 columns per wave staged in LDS (512 columns at
+    BM = 128, 448 at BM = 192, the last tile possibly partial): within the
+    tolerance, and the same bytes as the register-ring down tile (variant
+    0), which sums every output's K chunks in the same order."""
+    x, lg, wgu, wd, k, ref = _case(name, *WIDE_CASES[name])
+    out = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, split_k=split,
+                          down_variant=DOWN_WIDE)
+    parity.check_out(out, ref, f"wide down {name} bm={bm} split={split}")
+    base = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, split_k=split, down_variant=1)
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+
+
+@pytest.mark.parametrize("xcd", [1, 2])
+@pytest.mark.parametrize("rotate", [1, 2, 3])
+def test_lds_wide_down_orders_and_rotation(rotate, xcd):
+    """Every K rotation and both workgroup orders: within the tolerance;
+    without the per-workgroup rotation (whose start depends on the tiling)
+    the same bytes as the 256-column LDS-staged down tile."""
+    x, lg, wgu, wd, k, ref = _case("d512", *WIDE_CASES["d512"])
+    for bm in (128, 192):
+        out = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, split_k=2,
+                              down_variant=DOWN_WIDE, rotate=rotate, xcd_order=xcd)
+        parity.check_out(out, ref, f"wide down bm={bm} rotate={rotate} xcd={xcd}")
+        if rotate != 3:
+            base = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, split_k=2,
+                                   down_variant=DOWN_LDS, rotate=rotate, xcd_order=xcd)
+            assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+
+
+def test_lds_wide_down_rejected_where_it_cannot_run():
+    """Forcing the wide tile with the combination folded into the down GEMM,
+    or at a block size that has no wide tile, is an error."""
+    x, lg, wgu, wd, k, ref = _case("d512", *WIDE_CASES["d512"])
+    with pytest.raises(moe.MoeError):
+        moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=128, fold_combine=2,
+                        down_variant=DOWN_WIDE)
+    with pytest.raises(moe.MoeError):
+        moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=64, down_variant=DOWN_WIDE)
