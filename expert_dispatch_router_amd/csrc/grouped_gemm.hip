@@ -67,7 +67,14 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + expf(-g)
 // h stays in LDS and the workgroup writes the fp32 partial
 // y[tile] = h[:, tile cols] . W_down[:, tile cols]^T, one part per column
 // tile, which the combination adds in tile order.
-enum { kOutSwiGLU = 0, kOutF32Parts = 1, kOutBF16 = 2, kOutSwiGLUDown = 3, kOutF32Wide = 4 };
+enum {
+  kOutSwiGLU = 0,
+  kOutF32Parts = 1,
+  kOutBF16 = 2,
+  kOutSwiGLUDown = 3,
+  kOutF32Wide = 4,
+  kOutF32Dense = 5,
+};
 
 template <int BM, int NWT, int WAVES, int PF, int MODE>
 struct Gemm {
@@ -528,11 +535,14 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
 // operand (the down projection), fp32 partial sums of a split reduction;
 // kOutF32Wide: the same output with 64 columns per wave, taken as two
 // adjacent 32-column groups in the places of gate and up, so a stage holds
-// twice the weight rows per activation row.
+// twice the weight rows per activation row; kOutF32Dense: fp32 parts of one
+// dense product (no schedule: block b is rows [b * BM, b * BM + BM) of X,
+// all against W) -- the router scores.
 template <int BM, int WAVES, int BK, int STAGES, int MODE = kOutSwiGLU>
 struct LdsGemm {
   static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
-  static_assert(MODE == kOutSwiGLU || MODE == kOutF32Parts || MODE == kOutF32Wide,
+  static_assert(MODE == kOutSwiGLU || MODE == kOutF32Parts || MODE == kOutF32Wide ||
+                    MODE == kOutF32Dense,
                 "SwiGLU or fp32 parts");
   static constexpr bool kWide = MODE == kOutF32Wide;
   static constexpr int kNG = (MODE == kOutSwiGLU || kWide) ? 2 : 1;
@@ -570,8 +580,10 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds,
       r, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, voff, soff, 0, CPOL);
 }
 
-// out: kOutSwiGLU -> bf16 h [A, N]; kOutF32Parts and kOutF32Wide -> fp32
-// y [split, A, N] (part p sums K steps [p * ksplit, (p + 1) * ksplit)).
+// out: kOutSwiGLU -> bf16 h [A, N]; kOutF32Parts, kOutF32Wide and
+// kOutF32Dense -> fp32 y [split, A, N] (part p sums K steps
+// [p * ksplit, (p + 1) * ksplit)).  kOutF32Dense reads no schedule
+// (blocks, nb_dev, order and offsets may be null).
 template <int BM, int WAVES, int BK, int STAGES, int MODE, int WCPOL>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
@@ -591,17 +603,22 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     if (wg >= r8) return;
     wg = (wg % kXcds) * (r8 / kXcds) + wg / kXcds;
   }
+  constexpr bool kDense = MODE == kOutF32Dense;
   const int bi = wg / tiles_per_block;
-  if (bi >= nb_dev[0]) return;
-  const int b = order ? order[bi] : bi;
+  if constexpr (kDense) {
+    if (bi * BM >= A) return;
+  } else {
+    if (bi >= nb_dev[0]) return;
+  }
+  const int b = (!kDense && order) ? order[bi] : bi;
   const int rem = wg - bi * tiles_per_block;
   const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;  // the last may be partial
   const int tile = rem % n_tiles;
   const int part = rem / n_tiles;
   const int kb = part * ksplit;
-  const int e = blocks[2 * b];
-  const int r0 = blocks[2 * b + 1];
-  const int rows = min(BM, offsets[e + 1] - r0);
+  const int e = kDense ? 0 : blocks[2 * b];
+  const int r0 = kDense ? b * BM : blocks[2 * b + 1];
+  const int rows = min(BM, (kDense ? A : offsets[e + 1]) - r0);
   const int mt_act = (rows + 15) >> 4;
   const int nks = max(0, min(K - kb, ksplit) / BK);
 
@@ -954,6 +971,19 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
   MOE_DN_CFGS(X)
 #undef X
   return hipErrorInvalidValue;
+}
+
+// Router scores through the LDS-staged tile: logits parts [parts, T, E] of
+// x [T, d] . W_r [E, d]^T, BM = 128 rows of x per block, 256 experts per
+// column tile, part p over K steps [p * ksplit, (p + 1) * ksplit).
+hipError_t launch_router_lds(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
+                             int parts, int ksplit, float* out, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (E % 16 != 0 || parts < 1 || (long long)(parts - 1) * ksplit >= d) return hipErrorInvalidValue;
+  const int nb = (T + 127) / 128;
+  return launch_lds_cfg<128, 8, kOutF32Dense, 0>(x, w_router, 0, nullptr, nullptr, nullptr, nullptr,
+                                                 out, T, E, d, parts, ksplit, nb, 0, nullptr, 1, T,
+                                                 0, s);
 }
 
 hipError_t launch_proj_bf16(int bm, const uint16_t* x, const int32_t* gather_perm, int k, int T,

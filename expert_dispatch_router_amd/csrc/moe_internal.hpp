@@ -43,6 +43,8 @@ struct RouterPlan {
   int ts;     // 16-token subtiles per wave (1, 2 or 4)
   int nsub;   // 16-expert subtiles per wave (1, 2 or 4)
   int parts;  // split of the reduction over d (partial sums added in order)
+  int lds;    // 1: the LDS-staged GEMM tile (launch_router_lds), ksplit d per part
+  int ksplit;
 };
 RouterPlan plan_router(int T, int d, int E);
 
@@ -88,6 +90,10 @@ struct Plan {
 // logits [T, E] into `out`, else rp.parts partial sums [parts, T, E].
 hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
                          const RouterPlan& rp, float* out, hipStream_t s);
+// Router score parts [parts, T, E] by the LDS-staged GEMM tile (E % 16 == 0;
+// part p sums d in [p * ksplit, (p + 1) * ksplit), ksplit a multiple of 64).
+hipError_t launch_router_lds(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
+                             int parts, int ksplit, float* out, hipStream_t s);
 // logits = the partial sums added in part order.
 hipError_t launch_router_reduce(const float* parts, int nparts, long long n, float* logits,
                                 hipStream_t s);

@@ -23,7 +23,9 @@
 // the logits; otherwise it writes its partial sums [part][T][E], which the
 // routing kernels (or launch_router_reduce) add in part order -- the result
 // does not depend on timing.  Rows past T or E load as zeros (the buffer
-// range ends there) and are not stored.
+// range ends there) and are not stored.  Large problems (T >= 1024,
+// E >= 128) instead run the expert GEMMs' LDS-staged tile in its dense
+// mode (plan_router below).
 #include "buffer_load.hpp"
 #include "moe_internal.hpp"
 
@@ -130,8 +132,37 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const float* __restr
 
 }  // namespace
 
+// Large problems (T >= 1024, E >= 128, E a multiple of 16) take the
+// LDS-staged GEMM tile of the expert GEMMs in its dense mode: a workgroup
+// stages 128 rows of x and 256 rows of W_r per K step in LDS, so x is read
+// once per 256 experts and W_r once per 128 tokens (the wave tiles above
+// read them once per 64).  The split over d is sized for about one round of
+// workgroups, under the same bounds as above.
+constexpr int kRouterLdsRows = 128;
+constexpr int kRouterLdsCols = 256;
+
 RouterPlan plan_router(int T, int d, int E) {
   RouterPlan rp;
+  rp.lds = 0;
+  rp.ksplit = 0;
+  const bool lds_ok = T >= 1024 && E >= 128 && E % 16 == 0 && d % 64 == 0 &&
+                      (long long)(E + kRouterLdsCols) * d * 2 < (1LL << 31) &&
+                      (long long)kRouterLdsRows * d * 2 < (1LL << 31);
+  if (lds_ok) {
+    const int nch = d / 64;
+    const long long wgs = (long long)((T + kRouterLdsRows - 1) / kRouterLdsRows) *
+                          ((E + kRouterLdsCols - 1) / kRouterLdsCols);
+    long long parts = (256 + wgs - 1) / wgs;
+    parts = std::min<long long>(parts, std::max(1, nch / 4));
+    parts = std::min<long long>(parts, std::max(1, d / (4 * E)));
+    parts = std::max<long long>(parts, 1);
+    const int per = (int)((nch + parts - 1) / parts);  // K steps per part
+    rp.lds = 1;
+    rp.ts = rp.nsub = 0;
+    rp.parts = (nch + per - 1) / per;  // every part has at least one K step
+    rp.ksplit = per * 64;
+    return rp;
+  }
   // 64-row tiles of x and W_r need 64*d*2 bytes within a 32-bit buffer range
   const bool wide_ok = 128LL * d < (1LL << 31);
   rp.ts = (T >= 1024 && wide_ok) ? 4 : T >= 64 ? 2 : 1;
@@ -151,6 +182,7 @@ RouterPlan plan_router(int T, int d, int E) {
 hipError_t launch_router(const uint16_t* x, const uint16_t* w_router, int T, int d, int E,
                          const RouterPlan& rp, float* out, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  if (rp.lds) return launch_router_lds(x, w_router, T, d, E, rp.parts, rp.ksplit, out, s);
   const int e_tiles = (E + 16 * rp.nsub - 1) / (16 * rp.nsub);
   const int wg_e = e_tiles >= 2 ? 2 : 1;
   const int wg_t = kRouterWaves / wg_e;

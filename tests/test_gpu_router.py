@@ -60,11 +60,14 @@ def _check_scores(got, x, wr):
                                    (40, 7168, 256), (5, 64, 512), (300, 256, 16), (64, 4096, 8),
                                    (130, 2048, 33), (513, 1024, 17), (97, 3584, 64),
                                    (1030, 192, 130), (1024, 64, 16), (2000, 320, 40),
-                                   (1100, 7168, 256)])
+                                   (1100, 7168, 256), (1024, 64, 128), (1300, 1024, 144),
+                                   (2049, 512, 512), (1500, 4096, 160)])
 def test_router_scores_within_the_summation_bound(T, d, E):
     """Shapes with one part and with the reduction split in several (the
     partial sums added in order), ragged in tokens and experts, for every
-    wave tile (16..64 tokens x 16..64 experts)."""
+    wave tile (16..64 tokens x 16..64 experts) and for the LDS-staged tile
+    of large problems (T >= 1024, E >= 128 a multiple of 16: one K step,
+    a partial column tile, two column tiles, a last block of one row)."""
     x, wr = _router_case(T, d, E, seed=T + d + E)
     got = moe.moe_router_logits(x, wr)
     _check_scores(got, x, wr)
@@ -90,7 +93,7 @@ def test_router_scores_deterministic_and_stream():
 
 
 @pytest.mark.parametrize("name,sample", [("tiny", None), ("mixtral_512", 6), ("qwen2_128", 6),
-                                         ("dsv3_512", 4)])
+                                         ("dsv3_512", 4), ("dsv3_4096", 4)])
 def test_forward_from_hidden_states(name, sample):
     cfg = synth.CONFIGS[name]
     x = synth.make_x(cfg, 0, DEV)
