@@ -49,30 +49,46 @@ __device__ int block_inclusive_scan(int v, int* sh) {
 // longest-first launch order of the blocks: the full blocks in block order,
 // then each expert's partial last block by rows descending, ties to the
 // lower expert -- a stable sort of the blocks by decreasing row count.
+// With `perm` (fused_reorder_fits), also the reorder: the counts are then
+// kept per 64-row group in LDS instead of per chunk in memory, and each
+// wave places the rows of its groups: the lanes of a group OR their bits
+// into a per-expert mask in LDS, so each row lands at offsets[e] + (rows of
+// e in earlier groups) + (lanes below it holding e) -- ascending flat order
+// within the expert.
 __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
     const int32_t* __restrict__ ids, int A, int E, int bm, int nchunks,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ chunk_cnt,
     int32_t* __restrict__ chunk_base, int32_t* __restrict__ blocks, int32_t* __restrict__ nb,
-    int32_t* __restrict__ order) {
+    int32_t* __restrict__ order, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   __shared__ int hist[MOE_MAX_EXPERTS];
   __shared__ int run[MOE_MAX_EXPERTS];
   __shared__ int sh[MOE_MAX_EXPERTS];
   __shared__ int chist[kAllChunkCounts];  // [chunk][expert], when they all fit
+  // fused reorder: per wave and expert, the lanes of the current group that
+  // hold the expert
+  __shared__ unsigned long long lanes_of[(kScanThreads / 64) * MOE_MAX_EXPERTS];
   const int tid = threadIdx.x;
+  const bool fused = perm != nullptr;  // uniform
+  const int ngroups = fused ? (A + 63) >> 6 : nchunks;
   if (tid < E) run[tid] = 0;
-  if (nchunks * E <= kAllChunkCounts) {  // uniform
-    // every chunk's counts in one pass over the rows, then a scan over the
-    // chunks per expert: no barrier per chunk
-    for (int q = tid; q < nchunks * E; q += kScanThreads) chist[q] = 0;
+  if (ngroups * E <= kAllChunkCounts) {  // uniform
+    // every chunk's (group's) counts in one pass over the rows, then a scan
+    // over the chunks per expert: no barrier per chunk
+    for (int q = tid; q < ngroups * E; q += kScanThreads) chist[q] = 0;
     __syncthreads();
-    for (int i = tid; i < A; i += kScanThreads) atomicAdd(&chist[(i / kChunk) * E + ids[i]], 1);
+    for (int i = tid; i < A; i += kScanThreads)
+      atomicAdd(&chist[(fused ? i >> 6 : i / kChunk) * E + ids[i]], 1);
     __syncthreads();
     if (tid < E) {
       int r = 0;
-      for (int c = 0; c < nchunks; ++c) {
+      for (int c = 0; c < ngroups; ++c) {
         const int h = chist[c * E + tid];
-        chunk_cnt[(size_t)c * E + tid] = h;
-        chunk_base[(size_t)c * E + tid] = r;
+        if (fused) {
+          chist[c * E + tid] = r;  // rows of this expert in earlier groups
+        } else {
+          chunk_cnt[(size_t)c * E + tid] = h;
+          chunk_base[(size_t)c * E + tid] = r;
+        }
         r += h;
       }
       run[tid] = r;
@@ -129,6 +145,31 @@ __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
         rank += (q > rem) || (q == rem && e < tid);
       }
       order[ftotal + rank] = bincl - 1;
+    }
+  }
+  if (fused) {  // uniform
+    if (tid < E) run[tid] = row0;  // free: cnt was read before the scans
+    __syncthreads();
+    const int lane = tid & 63;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    unsigned long long* wm = lanes_of + (tid >> 6) * E;  // this wave's masks, one per expert
+    for (int e = lane; e < E; e += 64) wm[e] = 0ull;
+    for (int g = tid >> 6; g < ngroups; g += kScanThreads / 64) {
+      const int i = g * 64 + lane;
+      const int e = i < A ? ids[i] : 0;
+      // the lanes of the group that hold each expert: OR is order-free, and a
+      // wave's LDS operations complete in program order
+      if (i < A) atomicOr(&wm[e], 1ull << lane);
+      asm volatile("" ::: "memory");
+      if (i < A) {
+        const unsigned long long m = wm[e];
+        const int p = run[e] + chist[g * E + e] + __popcll(m & below);
+        perm[p] = i;
+        inv[i] = p;
+      }
+      asm volatile("" ::: "memory");
+      if (i < A) wm[e] = 0ull;  // every lane that read it has read it
+      asm volatile("" ::: "memory");
     }
   }
 }
@@ -362,11 +403,18 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
 
 }  // namespace
 
+bool fused_reorder_fits(int A, int E) {
+  return (long long)((A + 63) / 64) * E <= kAllChunkCounts;
+}
+
 hipError_t launch_hist_scan(const int32_t* ids, int A, int E, int bm, int nchunks, int32_t* counts,
                             int32_t* offsets, int32_t* chunk_cnt, int32_t* chunk_base,
-                            int32_t* blocks, int32_t* nb, int32_t* order, hipStream_t s) {
+                            int32_t* blocks, int32_t* nb, int32_t* order, int32_t* perm,
+                            int32_t* inv, hipStream_t s) {
+  if ((perm != nullptr) != (inv != nullptr) || (perm && !fused_reorder_fits(A, E)))
+    return hipErrorInvalidValue;
   hist_scan_kernel<<<1, kScanThreads, 0, s>>>(ids, A, E, bm, nchunks, counts, offsets, chunk_cnt,
-                                              chunk_base, blocks, nb, order);
+                                              chunk_base, blocks, nb, order, perm, inv);
   return hipGetLastError();
 }
 

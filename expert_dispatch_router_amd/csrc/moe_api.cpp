@@ -47,6 +47,7 @@ int check_sizes(int T, int d, int ffn, int E, int k, bool dims) {
 int check_paths(int T, int d, int E, int k, const moe_options* opt) {
   if (!opt) return MOE_OK;
   if (opt->routing_kernels == 1 && !small_routing_fits(T, E, k)) return MOE_ERR_UNSUPPORTED;
+  if (opt->routing_kernels == 3 && !fused_reorder_fits(T * k, E)) return MOE_ERR_UNSUPPORTED;
   if (opt->gather_mode == 1 && (long long)T * d * 2 + 2LL * d >= (1LL << 31))
     return MOE_ERR_UNSUPPORTED;
   if (opt->gather_mode == 3 && ((long long)T * k + 16) * d * 2 >= (1LL << 31))
@@ -59,7 +60,7 @@ int check_options(const moe_options* opt) {
   if (opt->block_rows != 0 && !is_block_rows(opt->block_rows)) return MOE_ERR_UNSUPPORTED;
   if (opt->split_k < 0 || opt->split_k > kMaxSplit) return MOE_ERR_UNSUPPORTED;
   if (opt->tile_variant < 0 || opt->rotate < 0 || opt->rotate > 3) return MOE_ERR_UNSUPPORTED;
-  if (opt->routing_kernels < 0 || opt->routing_kernels > 2) return MOE_ERR_UNSUPPORTED;
+  if (opt->routing_kernels < 0 || opt->routing_kernels > 3) return MOE_ERR_UNSUPPORTED;
   if (opt->gather_mode < 0 || opt->gather_mode > 3) return MOE_ERR_UNSUPPORTED;
   if (opt->unfused_swiglu < 0 || opt->unfused_swiglu > 1) return MOE_ERR_UNSUPPORTED;
   if (opt->xcd_order < 0 || opt->xcd_order > 3) return MOE_ERR_UNSUPPORTED;
@@ -274,6 +275,9 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   const int rk = opt ? opt->routing_kernels : 0;
   p->small_routing = rk == 1 || (rk == 0 && small_routing_fits(T, E, k) &&
                                   (long long)T * E * k <= kSmallRoutingAutoWork);
+  // Otherwise two launches (route; histogram, scan, schedule and reorder in
+  // one workgroup) where the per-group counts fit in LDS, else three.
+  p->fused_reorder = !p->small_routing && (rk == 3 || (rk == 0 && fused_reorder_fits(A, E)));
   // The fused gate/up GEMM addresses x [T, d] with 32-bit buffer offsets.
   const int gm = opt ? opt->gather_mode : 0;
   const bool x_fits = (long long)T * d * 2 + 2LL * d < (1LL << 31);
@@ -382,7 +386,8 @@ int record(const moe_options* opt, int i, hipStream_t s) {
   } while (0)
 
 // K1..K3 into the workspace's routing section: one workgroup for small
-// problems, else three launches.
+// problems, else two launches where the reorder fits the histogram kernel,
+// else three.
 int run_routing(const LogitSrc& logits, const Plan& p, int renorm, int score, void* ws,
                 const moe_options* opt, int32_t* order, ZeroRange zero, hipStream_t s) {
   int32_t* ids = at<int32_t>(ws, p.o_ids);
@@ -401,10 +406,14 @@ int run_routing(const LogitSrc& logits, const Plan& p, int renorm, int score, vo
   }
   MOE_TRY_HIP(launch_route(logits, p.T, p.E, p.k, renorm, score, ids, w, zero, s));
   MOE_TRY(record(opt, 1, s));
+  int32_t* fperm = p.fused_reorder ? at<int32_t>(ws, p.o_perm) : nullptr;
+  int32_t* finv = p.fused_reorder ? at<int32_t>(ws, p.o_inv) : nullptr;
   MOE_TRY_HIP(launch_hist_scan(ids, p.A, p.E, p.bm, p.nchunks, at<int32_t>(ws, p.o_counts),
                                offsets, at<int32_t>(ws, p.o_ccnt), at<int32_t>(ws, p.o_cbase),
-                               at<int32_t>(ws, p.o_blocks), at<int32_t>(ws, p.o_nb), order, s));
+                               at<int32_t>(ws, p.o_blocks), at<int32_t>(ws, p.o_nb), order, fperm,
+                               finv, s));
   MOE_TRY(record(opt, 2, s));
+  if (p.fused_reorder) return MOE_OK;
   MOE_TRY_HIP(launch_permute(ids, p.A, p.E, p.nchunks, offsets, at<int32_t>(ws, p.o_ccnt),
                              at<int32_t>(ws, p.o_cbase), at<int32_t>(ws, p.o_perm),
                              at<int32_t>(ws, p.o_inv), s));

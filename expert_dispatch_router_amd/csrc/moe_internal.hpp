@@ -65,6 +65,7 @@ struct Plan {
   int longest_first;   // else launch the blocks longest first (device-built order)
   int dn_rotate;  // same for the down GEMM
   int small_routing;  // one-workgroup routing kernel instead of three launches
+  int fused_reorder;  // two launches: the histogram kernel also does the reorder
   int gather_in_gemm; // the fused gate/up GEMM reads token rows through perm
   int x_tiled;        // else x_perm is written in K-step tiles (gather mode 3)
   int unfused;        // SwiGLU as gate GEMM, up GEMM and activation (ablation)
@@ -114,7 +115,10 @@ hipError_t launch_route(const LogitSrc& logits, int T, int E, int k, int renorm,
 hipError_t launch_hist_scan(const int32_t* ids, int A, int E, int bm, int nchunks,
                             int32_t* counts, int32_t* offsets, int32_t* chunk_cnt,
                             int32_t* chunk_base, int32_t* blocks, int32_t* nb, int32_t* order,
-                            hipStream_t s);
+                            int32_t* perm, int32_t* inv, hipStream_t s);
+// Whether the histogram kernel can also do the reorder (perm, inv non-null):
+// its per-64-row-group counts of every expert fit in LDS.
+bool fused_reorder_fits(int A, int E);
 
 hipError_t launch_permute(const int32_t* ids, int A, int E, int nchunks, const int32_t* offsets,
                           const int32_t* chunk_cnt, const int32_t* chunk_base, int32_t* perm,

@@ -116,9 +116,13 @@ typedef struct moe_options {
     int rotate;
     /* Routing kernels.  0 = automatic: one workgroup does the route,
      * histogram, scan, schedule and reorder when T <= 1024, E <= 32 and
-     * T*E*top_k <= 32768, else three launches; 1 = the one-workgroup kernel
-     * (MOE_ERR_UNSUPPORTED beyond T <= 1024 and E <= 32); 2 = three
-     * launches.  Same results either way. */
+     * T*E*top_k <= 32768; else two launches (the route, then one workgroup
+     * for the histogram, scan, schedule and reorder) when
+     * ceil(T*top_k/64)*E <= 16384; else three launches; 1 = the
+     * one-workgroup kernel (MOE_ERR_UNSUPPORTED beyond T <= 1024 and
+     * E <= 32); 2 = three launches; 3 = two launches
+     * (MOE_ERR_UNSUPPORTED beyond ceil(T*top_k/64)*E <= 16384).  Same
+     * results either way. */
     int routing_kernels;
     /* Row gather of moe_forward.  0 = automatic (1 when 2*T*d < 2^31);
      * 1 = the fused gate/up GEMM reads each sorted row straight from x

@@ -110,9 +110,13 @@ def test_options_checks():
 
 
 def test_routing_and_gather_options():
-    for bad in (_o(routing=3), _o(routing=-1), _o(gather=4), _o(gather=-1)):
+    for bad in (_o(routing=4), _o(routing=-1), _o(gather=4), _o(gather=-1)):
         assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
-    for r in (0, 1, 2):
+    # two launches: the histogram kernel keeps every 64-row group's counts in LDS
+    assert _ws(4096, 256, 512, 256, 1, _o(routing=3))[0] == OK          # 64 groups x 256
+    assert _ws(4097, 256, 512, 256, 1, _o(routing=3))[0] == UNSUP       # 65 groups x 256
+    assert _ws(512, 256, 512, 64, 4, _o(routing=3))[0] == OK
+    for r in (0, 1, 2, 3):
         for g in (0, 1, 2, 3):
             assert _ws(64, 256, 512, 8, 2, _o(routing=r, gather=g))[0] == OK
     # the one-workgroup routing kernel: one token per thread, at most 32 experts

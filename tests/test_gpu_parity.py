@@ -41,10 +41,17 @@ def _small_routing_fits(T, E, k):
     return T <= 1024 and E <= 32
 
 
-@pytest.mark.parametrize("routing", [0, 2])
+def _fused_reorder_fits(A, E):
+    # limit of the two-launch routing (the reorder inside the histogram kernel)
+    return (A + 63) // 64 * E <= 16384
+
+
+@pytest.mark.parametrize("routing", [0, 2, 3])
 @pytest.mark.parametrize("name", sorted(synth.CONFIGS))
 def test_route_workloads_bit_exact(name, routing):
     cfg = synth.CONFIGS[name]
+    if routing == 3 and not _fused_reorder_fits(cfg.T * cfg.top_k, cfg.E):
+        pytest.skip("beyond the two-launch routing's limit")
     lg = synth.make_logits(cfg, 0, DEV)
     x = synth.make_x(cfg, 0, DEV)
     g = moe.moe_route(lg, cfg.top_k, cfg.renormalize, cfg.score, x=x, routing_kernels=routing)
@@ -77,18 +84,20 @@ def _edge_logits():
     return cases
 
 
-@pytest.mark.parametrize("routing", [1, 2])
+@pytest.mark.parametrize("routing", [1, 2, 3])
 @pytest.mark.parametrize("case", _edge_logits(), ids=lambda c: c[0])
 def test_route_edge_cases_bit_exact(case, routing):
     _, lg, k, score, renorm = case
     if routing == 1 and not _small_routing_fits(lg.shape[0], lg.shape[1], k):
         pytest.skip("beyond the one-workgroup routing kernel's limits")
+    if routing == 3 and not _fused_reorder_fits(lg.shape[0] * k, lg.shape[1]):
+        pytest.skip("beyond the two-launch routing's limit")
     lg = lg.to(DEV)
     g = moe.moe_route(lg, k, renorm, score, routing_kernels=routing)
     parity.check_routing(g, parity.oracle_routing(lg, k, score, renorm, g["bm"]))
 
 
-@pytest.mark.parametrize("routing", [1, 2])
+@pytest.mark.parametrize("routing", [1, 2, 3])
 @pytest.mark.parametrize("bm", ALL_BM)
 def test_route_every_block_size(bm, routing):
     gen = torch.Generator().manual_seed(bm)
@@ -98,6 +107,22 @@ def test_route_every_block_size(bm, routing):
     g = moe.moe_route(lg, 3, True, 0, block_rows=bm, routing_kernels=routing)
     assert g["bm"] == bm
     parity.check_routing(g, parity.oracle_routing(lg, 3, 0, True, bm))
+
+
+def test_route_two_launches_at_its_limit():
+    """The histogram kernel doing the reorder at its limit (ceil(A/64) * E =
+    16384 counters: 64 groups x 256 experts, and 1024 groups x 16 with a
+    last group of one row), with groups of several partial ones, and at
+    one row: the oracle's artefacts, and the same as three launches."""
+    gen = torch.Generator().manual_seed(23)
+    for T, E, k in ((512, 256, 8), (4096, 256, 1), (65473, 16, 1), (16321, 16, 4), (1, 64, 1)):
+        assert _fused_reorder_fits(T * k, E)
+        lg = torch.randn(T, E, generator=gen).to(DEV)
+        g = moe.moe_route(lg, k, True, 0, routing_kernels=3)
+        parity.check_routing(g, parity.oracle_routing(lg, k, 0, True, g["bm"]))
+        g2 = moe.moe_route(lg, k, True, 0, routing_kernels=2)
+        for key in ("counts", "offsets", "perm", "inv"):
+            assert torch.equal(g[key], g2[key]), key
 
 
 def test_route_small_kernel_at_its_limits():
