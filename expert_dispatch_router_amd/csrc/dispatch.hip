@@ -67,6 +67,7 @@ __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
   // fused reorder: per wave and expert, the lanes of the current group that
   // hold the expert
   __shared__ unsigned long long lanes_of[(kScanThreads / 64) * MOE_MAX_EXPERTS];
+  __shared__ int part[kScanThreads];  // fused reorder: slice totals of the group scan
   const int tid = threadIdx.x;
   const bool fused = perm != nullptr;  // uniform
   const int ngroups = fused ? (A + 63) >> 6 : nchunks;
@@ -79,16 +80,35 @@ __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
     for (int i = tid; i < A; i += kScanThreads)
       atomicAdd(&chist[(fused ? i >> 6 : i / kChunk) * E + ids[i]], 1);
     __syncthreads();
-    if (tid < E) {
+    if (fused) {
+      // per expert, the exclusive prefix over the groups in two levels: S
+      // slices of the groups per expert (thread e + E * s), each slice's
+      // total, then each slice's base -- the same sums as one serial pass
+      const int S = min(kScanThreads / E, ngroups);
+      const int e = tid % E, sl = tid / E;
+      const int g0 = sl * ngroups / S, g1 = (sl + 1) * ngroups / S;
+      if (sl < S) {
+        int r = 0;
+        for (int c = g0; c < g1; ++c) r += chist[c * E + e];
+        part[sl * E + e] = r;
+      }
+      __syncthreads();
+      if (sl < S) {
+        int r = 0;
+        for (int q = 0; q < sl; ++q) r += part[q * E + e];
+        for (int c = g0; c < g1; ++c) {
+          const int h = chist[c * E + e];
+          chist[c * E + e] = r;  // rows of this expert in earlier groups
+          r += h;
+        }
+        if (sl == S - 1) run[e] = r;
+      }
+    } else if (tid < E) {
       int r = 0;
       for (int c = 0; c < ngroups; ++c) {
         const int h = chist[c * E + tid];
-        if (fused) {
-          chist[c * E + tid] = r;  // rows of this expert in earlier groups
-        } else {
-          chunk_cnt[(size_t)c * E + tid] = h;
-          chunk_base[(size_t)c * E + tid] = r;
-        }
+        chunk_cnt[(size_t)c * E + tid] = h;
+        chunk_base[(size_t)c * E + tid] = r;
         r += h;
       }
       run[tid] = r;
