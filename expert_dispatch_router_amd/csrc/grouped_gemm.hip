@@ -481,7 +481,10 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
   using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
   const int tiles_per_block = n_tiles * split;
-  const long long grid = (long long)tiles_per_block * nb_max;
+  // XCD grouping renumbers the real workgroups rounded up to kXcds: every
+  // id below that must be launched
+  const long long grid = xcd_group ? ((long long)tiles_per_block * nb_max + kXcds - 1) / kXcds * kXcds
+                                   : (long long)tiles_per_block * nb_max;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   grouped_gemm_kernel<BM, NWT, WAVES, PF, MODE><<<(unsigned)grid, G::kThreads, 0, s>>>(
       X, W, w_estride, blocks, nb, order, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
@@ -825,7 +828,10 @@ hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estr
   if (N % 16 != 0 || K % kLdsBK != 0 || ksplit % kLdsBK != 0 || split < 1)
     return hipErrorInvalidValue;
   const int tiles_per_block = (N + G::kTileCols - 1) / G::kTileCols * split;
-  const long long grid = (long long)tiles_per_block * nb_max;
+  // XCD grouping renumbers the real workgroups rounded up to kXcds: every
+  // id below that must be launched
+  const long long grid = xcd_group ? ((long long)tiles_per_block * nb_max + kXcds - 1) / kXcds * kXcds
+                                   : (long long)tiles_per_block * nb_max;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   gemm_lds_kernel<BM, WAVES, kLdsBK, kLdsStages, MODE, WCPOL><<<(unsigned)grid, G::kThreads, 0, s>>>(
       X, W, w_estride, blocks, nb, order, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,

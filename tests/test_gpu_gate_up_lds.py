@@ -247,3 +247,20 @@ def test_lds_wide_down_rejected_where_it_cannot_run():
                         down_variant=DOWN_WIDE)
     with pytest.raises(moe.MoeError):
         moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=64, down_variant=DOWN_WIDE)
+
+
+def test_xcd_order_when_real_workgroups_round_past_the_grid():
+    """XCD grouping renumbers the real workgroups (blocks x tiles) rounded
+    up to a multiple of eight; the launch must hold every id below that.
+    Here A = 192 rows at BM = 192 (nb_max = 6, five blocks): the down GEMM's
+    2 x 5 real workgroups round to 16 while 2 x 6 would be launched.  Every
+    GEMM tile with the grouped order meets the tolerance and gives the same
+    bytes as the plain order."""
+    x, lg, wgu, wd, k, ref = _case("xcd_round", 64, 704, 448, 5, 3, 44)
+    for tv, dv in ((0, 1), (LDS, 1), (0, 2), (LDS, DOWN_WIDE)):
+        grouped = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=192, tile_variant=tv,
+                                  down_variant=dv, xcd_order=2, fuse_down=1)
+        parity.check_out(grouped, ref, f"xcd grouped tv={tv} dv={dv}")
+        plain = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=192, tile_variant=tv,
+                                down_variant=dv, xcd_order=1, fuse_down=1)
+        assert torch.equal(grouped.view(torch.int16), plain.view(torch.int16))

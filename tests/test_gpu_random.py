@@ -115,3 +115,46 @@ def test_random_problem_new_options(case):
                           **opts)
     ref = parity.oracle_out(x, lg, wgu, wd, k, score, renorm)
     parity.check_out(out, ref, f"opt{i} T={T} d={d} F={F} E={E} k={k} {opts}", beyond_format=True)
+
+
+def _cases_lds_tiles(n=16, seed=2468):
+    """Draws over the LDS-staged tiles (the gate/up tile of BM = 128 and 192,
+    the 32- and 64-column-per-wave down tiles, partial last column tiles
+    included) and the two-launch routing, with the other options drawn."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 5, 8, 13, 32, 60, 64, 100]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([1, 3, 17, 64, 130, 257, 600]))
+        d = int(64 * rng.integers(2, 17))
+        F = int(64 * rng.integers(3, 17))
+        score = int(rng.integers(0, 2))
+        renorm = bool(rng.integers(0, 2))
+        bm = int(rng.choice([128, 192]))
+        opts = {"block_rows": bm, "gather_mode": int(rng.integers(0, 3)),
+                "rotate": int(rng.integers(0, 4)), "xcd_order": int(rng.integers(0, 3)),
+                "fuse_down": 1}
+        if rng.random() < 0.7:
+            opts["tile_variant"] = 3          # the LDS-staged gate/up tile
+        dv = [0, 4] + ([3] if d % 256 == 0 else [])
+        opts["down_variant"] = int(rng.choice(dv))
+        if rng.random() < 0.6:
+            opts["split_k"] = int(rng.integers(1, 5))
+        fits = (T * k + 63) // 64 * E <= 16384
+        opts["routing_kernels"] = int(rng.choice([0, 2, 3] if fits else [0, 2]))
+        out.append((i, T, d, F, E, k, score, renorm, opts))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases_lds_tiles(), ids=lambda c: f"lds{c[0]}")
+def test_random_problem_lds_tiles(case):
+    i, T, d, F, E, k, score, renorm, opts = case
+    cfg, x, lg, wgu, wd = parity.make_case(T, d, F, E, k, score=score, renorm=renorm, seed=900 + i)
+    out = moe.moe_forward(x, lg, wgu, wd, k, renorm, score="sigmoid" if score else "softmax",
+                          **opts)
+    ref = parity.oracle_out(x, lg, wgu, wd, k, score, renorm)
+    parity.check_out(out, ref, f"lds{i} T={T} d={d} F={F} E={E} k={k} {opts}", beyond_format=True)
+    r = moe.moe_route(lg, k, renorm, "sigmoid" if score else "softmax", block_rows=opts["block_rows"],
+                      routing_kernels=opts["routing_kernels"])
+    parity.check_routing(r, parity.oracle_routing(lg, k, score, renorm, r["bm"]))
