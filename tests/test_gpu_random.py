@@ -158,3 +158,51 @@ def test_random_problem_lds_tiles(case):
     r = moe.moe_route(lg, k, renorm, "sigmoid" if score else "softmax", block_rows=opts["block_rows"],
                       routing_kernels=opts["routing_kernels"])
     parity.check_routing(r, parity.oracle_routing(lg, k, score, renorm, r["bm"]))
+
+
+def _cases_many_blocks(n=12, seed=97531):
+    """Larger draws (many schedule blocks: the automatic XCD order, the
+    two-launch routing at larger A, several blocks per expert), every
+    option drawn; the oracle checks a sample of tokens."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([16, 64, 128, 256]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([700, 1300, 2000]))
+        d = int(64 * rng.integers(2, 7))
+        F = int(64 * rng.integers(2, 7))
+        score = int(rng.integers(0, 2))
+        renorm = bool(rng.integers(0, 2))
+        opts = {"gather_mode": int(rng.integers(0, 3)), "rotate": int(rng.integers(0, 4)),
+                "xcd_order": int(rng.integers(0, 4))}
+        if rng.random() < 0.6:
+            bm = int(rng.choice([16, 32, 64, 128, 192]))
+            opts["block_rows"] = bm
+            if bm in (128, 192):
+                opts["tile_variant"] = int(rng.choice([0, 3]))
+                opts["down_variant"] = int(rng.choice([0, 4]))
+        if rng.random() < 0.4:
+            opts["split_k"] = int(rng.integers(1, 4))
+        fits = (T * k + 63) // 64 * E <= 16384
+        opts["routing_kernels"] = int(rng.choice([0, 2, 3] if fits else [0, 2]))
+        out.append((i, T, d, F, E, k, score, renorm, opts))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases_many_blocks(), ids=lambda c: f"big{c[0]}")
+def test_random_problem_many_blocks(case):
+    i, T, d, F, E, k, score, renorm, opts = case
+    cfg, x, lg, wgu, wd = parity.make_case(T, d, F, E, k, score=score, renorm=renorm,
+                                           seed=1300 + i)
+    out = moe.moe_forward(x, lg, wgu, wd, k, renorm, score="sigmoid" if score else "softmax",
+                          **opts)
+    rng = np.random.default_rng(i)
+    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 62, replace=False)]))
+    ref = parity.oracle_out(x, lg, wgu, wd, k, score, renorm, tokens=toks)
+    got = out[torch.from_numpy(toks).long().to(out.device)]
+    parity.check_out(got, ref, f"big{i} T={T} d={d} F={F} E={E} k={k} {opts}", beyond_format=True)
+    r = moe.moe_route(lg, k, renorm, "sigmoid" if score else "softmax",
+                      block_rows=opts.get("block_rows", 0),
+                      routing_kernels=opts["routing_kernels"])
+    parity.check_routing(r, parity.oracle_routing(lg, k, score, renorm, r["bm"]))
