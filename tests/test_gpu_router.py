@@ -130,3 +130,23 @@ def test_forward_router_without_logits_out_matches():
     lg = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=DEV)
     b = moe.moe_forward_router(x, wr, wgu, wd, cfg.top_k, cfg.renormalize, logits_out=lg)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def _random_router_shapes(n=10, seed=8642):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        T = int(rng.integers(1, 3000))
+        E = int(rng.choice([1, 7, 16, 100, 128, 144, 256, 400, 512]))
+        d = int(64 * rng.integers(1, 40))
+        out.append((T, d, E))
+    return out
+
+
+@pytest.mark.parametrize("T,d,E", _random_router_shapes())
+def test_router_scores_random_shapes(T, d, E):
+    """Random sizes across both router tilings (the wave tiles, and the
+    LDS-staged tile where T >= 1024 and E >= 128 is a multiple of 16)."""
+    x, wr = _router_case(T, d, E, seed=3 * T + d + E)
+    got = moe.moe_router_logits(x, wr)
+    _check_scores(got, x, wr)
