@@ -206,3 +206,57 @@ def test_random_problem_many_blocks(case):
                       block_rows=opts.get("block_rows", 0),
                       routing_kernels=opts["routing_kernels"])
     parity.check_routing(r, parity.oracle_routing(lg, k, score, renorm, r["bm"]))
+
+
+def _cases_all_options(n=60, seed=31337):
+    """Every option drawn at once (block size, both tile variants, split,
+    rotation, routing kernels, gather mode, workgroup order, folded
+    combination, fused down projection, unfused ablation), over shapes from
+    one token to 1500 and from 1 to 256 experts with top-k up to 16.  Option
+    sets the library refuses up front are left out; the rest must meet the
+    tolerance (the unfused ablation its wider one)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        E = int(rng.choice([1, 2, 3, 8, 16, 33, 64, 100, 128, 256]))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        T = int(rng.choice([1, 2, 5, 31, 64, 100, 257, 513, 1000, 1500]))
+        d = int(64 * rng.integers(1, 14))
+        F = int(64 * rng.integers(1, 14))
+        score = int(rng.integers(0, 2))
+        renorm = bool(rng.integers(0, 2))
+        opts = {}
+        if rng.random() < 0.7:
+            opts["block_rows"] = int(rng.choice([16, 32, 64, 128, 192]))
+            if rng.random() < 0.5:
+                opts["tile_variant"] = int(rng.integers(0, 4))
+            if rng.random() < 0.5:
+                opts["down_variant"] = int(rng.integers(0, 5))
+        for key, hi in (("split_k", 5), ("rotate", 4), ("routing_kernels", 4), ("gather_mode", 4),
+                        ("xcd_order", 4), ("fold_combine", 3), ("fuse_down", 3),
+                        ("unfused_swiglu", 2)):
+            if rng.random() < 0.4:
+                opts[key] = int(rng.integers(0, hi))
+        try:
+            moe.moe_workspace_size(T, d, F, E, k, **opts)
+        except moe.MoeError:
+            continue
+        out.append((len(out), T, d, F, E, k, score, renorm, opts))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases_all_options(), ids=lambda c: f"all{c[0]}")
+def test_random_problem_all_options(case):
+    i, T, d, F, E, k, score, renorm, opts = case
+    cfg, x, lg, wgu, wd = parity.make_case(T, d, F, E, k, score=score, renorm=renorm,
+                                           seed=2000 + i)
+    out = moe.moe_forward(x, lg, wgu, wd, k, renorm, score="sigmoid" if score else "softmax",
+                          **opts)
+    toks = None
+    if T > 300:
+        rng = np.random.default_rng(i)
+        toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 40, replace=False)]))
+    ref = parity.oracle_out(x, lg, wgu, wd, k, score, renorm, tokens=toks)
+    got = out if toks is None else out[torch.from_numpy(toks).long().to(out.device)]
+    parity.check_out(got, ref, f"all{i} T={T} d={d} F={F} E={E} k={k} {opts}", beyond_format=True,
+                     scale=parity.UNFUSED_SCALE if opts.get("unfused_swiglu") else 1.0)
