@@ -27,7 +27,10 @@ def _gpu():
                                        ("tiny", {"gather_mode": 2, "split_k": 2}),
                                        ("tiny", {"fold_combine": 2, "split_k": 2, "fuse_down": 1}),
                                        ("mixtral_128", {"fold_combine": 2}),
-                                       ("tiny", {"fuse_down": 2})])
+                                       ("tiny", {"fuse_down": 2}),
+                                       # two-launch routing, the 64-column-per-wave down tile
+                                       ("qwen2_128", {}), ("skewed_256", {}),
+                                       ("qwen2_128", {"routing_kernels": 3, "xcd_order": 2})])
 def test_forward_graph_replays_match_eager(name, opts):
     cfg = synth.CONFIGS[name]
     x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)
