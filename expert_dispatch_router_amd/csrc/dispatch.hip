@@ -174,22 +174,34 @@ __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
     const unsigned long long below = (1ull << lane) - 1ull;
     unsigned long long* wm = lanes_of + (tid >> 6) * E;  // this wave's masks, one per expert
     for (int e = lane; e < E; e += 64) wm[e] = 0ull;
-    for (int g = tid >> 6; g < ngroups; g += kScanThreads / 64) {
-      const int i = g * 64 + lane;
-      const int e = i < A ? ids[i] : 0;
-      // the lanes of the group that hold each expert: OR is order-free, and a
-      // wave's LDS operations complete in program order
-      if (i < A) atomicOr(&wm[e], 1ull << lane);
-      asm volatile("" ::: "memory");
-      if (i < A) {
-        const unsigned long long m = wm[e];
-        const int p = run[e] + chist[g * E + e] + __popcll(m & below);
-        perm[p] = i;
-        inv[i] = p;
+    constexpr int kWaves = kScanThreads / 64;
+    constexpr int kAhead = 4;  // groups whose ids one wave loads at once
+    for (int g0 = tid >> 6; g0 < ngroups; g0 += kAhead * kWaves) {
+      int ev[kAhead];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) {
+        const int i = (g0 + u * kWaves) * 64 + lane;
+        ev[u] = i < A ? ids[i] : 0;
       }
-      asm volatile("" ::: "memory");
-      if (i < A) wm[e] = 0ull;  // every lane that read it has read it
-      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) {
+        const int g = g0 + u * kWaves;
+        const int i = g * 64 + lane;
+        const int e = ev[u];
+        // the lanes of the group that hold each expert: OR is order-free, and
+        // a wave's LDS operations complete in program order
+        if (i < A) atomicOr(&wm[e], 1ull << lane);
+        asm volatile("" ::: "memory");
+        if (i < A) {
+          const unsigned long long m = wm[e];
+          const int p = run[e] + chist[g * E + e] + __popcll(m & below);
+          perm[p] = i;
+          inv[i] = p;
+        }
+        asm volatile("" ::: "memory");
+        if (i < A) wm[e] = 0ull;  // every lane that read it has read it
+        asm volatile("" ::: "memory");
+      }
     }
   }
 }
