@@ -5,19 +5,28 @@
 
 A step is one complete forward pass (route, histogram/scan/schedule,
 reorder+gather, fused gate/up SwiGLU GEMM, down GEMM, weighted combination)
-over one batch of seeded synthetic inputs already resident in HBM.  W
-untimed steps, then K timed steps between two device synchronisations.
-Prints ONE JSON line.
+over one batch of seeded synthetic inputs already resident in HBM.  The
+inputs are generated on the GPU and the W untimed warm-up steps follow at
+once; then K timed steps between two device synchronisations.  Prints ONE
+JSON line.
 
 ``value`` = tokens/s of the whole job.  ``roofline`` covers the dominant
 kernel (the fused gate/up GEMM): its algorithmic bytes per launch divided by
-its mean duration, measured with HIP events recorded on the stream the
-library launches on, against 8 TB/s.  ``cpu_baseline`` times the CPU oracle
-(test infrastructure, imported only for this leg) on a bounded sample of the
-same workload on this host's cores.
+its mean duration over the timed steps, measured with two HIP events the
+library records on its own stream right before and after that kernel,
+against 8 TB/s.  After the timed region: the routing counts (for the
+algorithmic work), a separate set of K steps with all seven stage events
+(the per-stage breakdown and the down GEMM), rep-by-rep passes after a
+1 GiB cache-flush write for workloads whose active weights would fit the
+caches, the router scores kernel on its own, other workloads asked for with
+``--also`` (by default DeepSeek-V3-shaped T=512 beside the default
+Mixtral-shaped T=512), and ``cpu_baseline``: the CPU oracle (test
+infrastructure, imported only for this leg) on a bounded sample of the same
+workload on this host's cores, with the CPU model, input hashes and a
+one-core figure on the tiny workload.
 
 Other modes (not used by the default run):
-  --profile            few steps, no CPU baseline (for rocprofv3 runs)
+  --profile            no CPU baseline, no other workloads (for rocprofv3 runs)
   --copy-bytes N       also run one plain N-byte device copy per step (the
                        calibration kernel of the HBM byte counters)
   --traffic FETCH_DIR WRITE_DIR
@@ -41,9 +50,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE fwd tokens/s + TFLOP/s, HBM GB/s (% roofline) at T=128-512, 1 MI355X"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
-DOMINANT = "grouped_gemm_kernel<...SWIGLU>"   # K4, the fused gate/up SwiGLU GEMM
 GEMM_SRC = os.path.join(ROOT, "expert_dispatch_router_amd", "csrc", "grouped_gemm.hip")
-STAGES = ["route", "hist_scan_schedule", "reorder_gather", "gate_up_swiglu", "down", "combine"]
+DEFAULT_WORKLOAD = "mixtral_512"
 
 
 def source_sha(path=GEMM_SRC) -> str:
@@ -133,6 +141,31 @@ def traffic_for(cfg_name):
     return t.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def input_hashes(x, logits, wgu, wd):
+    """sha256 of the bytes of every input, taken from host copies of the
+    device tensors the timed passes read (the same copies feed the oracle);
+    weights hashed one expert at a time, experts in order."""
+    from expert_dispatch_router_amd import synth
+
+    def weights(w):
+        h = hashlib.sha256()
+        for e in range(w.shape[0]):
+            h.update(synth.bf16_bits(w[e]).tobytes())
+        return h.hexdigest()
+    return {"x": synth.sha256(x), "router_logits": synth.sha256(logits),
+            "W_gate_up": weights(wgu), "W_down": weights(wd)}
+
+
 def cpu_baseline(cfg, x, logits, wgu, wd, target_s=10.0):
     """The oracle as it stands, timed on this host on a bounded sample:
     routing of all T tokens plus the expert FFN of the first n tokens,
@@ -167,11 +200,16 @@ def cpu_baseline(cfg, x, logits, wgu, wd, target_s=10.0):
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"routing of all {cfg.T} tokens + expert FFN and combination of the "
-                      f"first {n} of {cfg.T} tokens ({dt:.1f} s)"}
+                      f"first {n} of {cfg.T} tokens ({dt:.1f} s)",
+            "cpu_model": cpu_model(),
+            "cores_available": len(os.sched_getaffinity(0))}
 
 
-_SINGLE_THREAD_TINY = r"""
-import json, sys, time
+_SINGLE_CORE_TINY = r"""
+import os, sys
+# one core before anything starts threads: OpenMP then sees one CPU
+os.sched_setaffinity(0, {int(sys.argv[2])})
+import json, time
 sys.path.insert(0, sys.argv[1])
 import oracle
 from expert_dispatch_router_amd import synth
@@ -185,30 +223,205 @@ while time.perf_counter() - t0 < 2.0:
     oracle.forward(xb, lgn, gu, dn, cfg.top_k, cfg.renormalize, cfg.score, cfg.ffn)
     passes += 1
 dt = time.perf_counter() - t0
-print(json.dumps({"value": cfg.T * passes / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
-                  "kind": "oracle", "sample": f"{passes} whole tiny passes (T={cfg.T}) in {dt:.1f} s"}))
+print(json.dumps({"value": cfg.T * passes / dt, "unit": "tokens/s",
+                  "cores": len(os.sched_getaffinity(0)), "omp_threads": oracle.max_threads(),
+                  "kind": "oracle",
+                  "sample": f"{passes} whole tiny passes (T={cfg.T}) in {dt:.1f} s, "
+                            f"pinned to CPU {sys.argv[2]}"}))
 """
 
 
-def cpu_single_thread_tiny():
-    """The oracle on the whole tiny workload with one OpenMP thread asked
-    for, in a child process (so the parent's oracle keeps all its threads);
-    ``cores`` reports the threads OpenMP actually granted, which an
-    environment may hold above one."""
+def cpu_single_core_tiny():
+    """The oracle on the whole tiny workload in a child process pinned to
+    one CPU (sched_setaffinity before OpenMP starts) with OMP_NUM_THREADS=1:
+    a one-core figure whatever thread count the environment sets."""
     import subprocess
 
-    r = subprocess.run([sys.executable, "-c", _SINGLE_THREAD_TINY, ROOT],
-                       capture_output=True, text=True, timeout=300)
+    cpu = sorted(os.sched_getaffinity(0))[0]
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", _SINGLE_CORE_TINY, ROOT, str(cpu)],
+                       capture_output=True, text=True, timeout=300, env=env)
     if r.returncode != 0:
         return {"error": r.stderr.strip().splitlines()[-1:] or ["failed"]}
     return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def stage_names(plan):
+    """Names of the six intervals between the seven stage events, from the
+    launch plan; an interval with no kernel in it measures only the cost of
+    two back-to-back event records and is named None."""
+    rl = plan["routing_launches"]
+    names = ["route_histogram_scan_schedule_reorder" if rl == 1 else "route",
+             None if rl == 1 else ("histogram_scan_schedule_reorder" if rl == 2
+                                   else "histogram_scan_schedule"),
+             "reorder" if rl == 3 else None,
+             "gate_up_swiglu_down" if plan["fused_down"] else
+             ("gate_up_unfused" if plan["unfused_swiglu"] else "gate_up_swiglu"),
+             None if plan["fused_down"] else "down",
+             None if plan["fold_combine"] else "combine"]
+    if plan["gather_launch"]:
+        names[2] = "reorder_gather" if rl == 3 else "gather"
+    return names
+
+
+class Runner:
+    """One workload's inputs, workspace and launch plan on the GPU, and the
+    timing loops around moe_forward."""
+
+    def __init__(self, cfg, seed, dev, unfused=0, copy_bytes=0):
+        import torch
+
+        import expert_dispatch_router_amd as moe
+        from expert_dispatch_router_amd import synth
+
+        self.cfg, self.dev, self.unfused = cfg, dev, unfused
+        self.x, self.logits, self.wgu, self.wd = synth.make_inputs(cfg, seed, dev)
+        self.plan = moe.moe_plan_ex(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k,
+                                    unfused_swiglu=unfused)
+        self.out = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty(moe.moe_workspace_size(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k,
+                                                     unfused_swiglu=unfused),
+                              dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self.copy_src = self.copy_dst = None
+        if copy_bytes:
+            self.copy_src = torch.empty(copy_bytes, dtype=torch.uint8, device=dev).fill_(1)
+            self.copy_dst = torch.empty_like(self.copy_src)
+
+    def step(self, stage_events=None, strm=None):
+        import expert_dispatch_router_amd as moe
+
+        c = self.cfg
+        moe.moe_forward(self.x, self.logits, self.wgu, self.wd, c.top_k, c.renormalize,
+                        out=self.out, score=c.score, workspace=self.ws, stream=strm or self.stream,
+                        stage_events=stage_events, unfused_swiglu=self.unfused)
+        if self.copy_src is not None:
+            self.copy_dst.copy_(self.copy_src)
+
+    def timed(self, warmup, steps):
+        """warmup untimed passes, then `steps` passes between two device
+        synchronisations.  In every timed pass the library records two
+        fence-free HIP events on its stream, right before and right after
+        the fused gate/up GEMM (stage events 3 and 4; measured at ~1.5 us of
+        GPU time each): that kernel's duration over the timed region."""
+        import numpy as np
+        import torch
+
+        import expert_dispatch_router_amd as moe
+
+        for _ in range(warmup):
+            self.step()
+        ev = [(moe.Timer(), moe.Timer()) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            a, b = ev[i]
+            self.step(stage_events=[None, None, None, a.handle, b.handle, None, None])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        return elapsed, np.array([a.elapsed_ms(b) for a, b in ev])
+
+    def stages(self, steps):
+        """A separate run of `steps` passes with the seven stage events
+        (each record adds a few microseconds of its own)."""
+        import numpy as np
+        import torch
+
+        import expert_dispatch_router_amd as moe
+
+        timers = [[moe.Timer() for _ in range(7)] for _ in range(steps)]
+        for i in range(steps):
+            self.step(stage_events=[t.handle for t in timers[i]])
+        torch.cuda.synchronize()
+        ms = np.array([[timers[i][s].elapsed_ms(timers[i][s + 1]) for s in range(6)]
+                       for i in range(steps)])
+        whole = np.array([timers[i][0].elapsed_ms(timers[i][6]) for i in range(steps)])
+        return ms, whole
+
+    def flushed(self, reps, warmup=3, flush_bytes=1 << 30):
+        """The pass timed rep by rep with a 1 GiB write between reps, outside
+        the timed interval, so that no weight byte is served from the 256 MiB
+        MALL or the L2s: (median, p10, p90) ms from the first to the last
+        stage event."""
+        import numpy as np
+        import torch
+
+        import expert_dispatch_router_amd as moe
+
+        buf = torch.empty(flush_bytes, dtype=torch.uint8, device=self.dev)
+        for _ in range(warmup):
+            self.step()
+        vals = []
+        for _ in range(reps):
+            buf.fill_(7)
+            t = [moe.Timer() for _ in range(7)]
+            self.step(stage_events=[t[0].handle] + [None] * 5 + [t[6].handle])
+            torch.cuda.synchronize()
+            vals.append(t[0].elapsed_ms(t[6]))
+        del buf
+        v = np.array(vals)
+        return float(np.median(v)), float(np.percentile(v, 10)), float(np.percentile(v, 90))
+
+    def routing_counts(self):
+        import expert_dispatch_router_amd as moe
+
+        c = self.cfg
+        r = moe.moe_route(self.logits, c.top_k, c.renormalize, c.score)
+        return r["counts"].cpu().numpy()
+
+
+def pct(v):
+    import numpy as np
+
+    return {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
+            "p90": float(np.percentile(v, 90))}
+
+
+def workload_label(cfg):
+    return (f"{cfg.name}: MoE layer T={cfg.T} d={cfg.d} ffn={cfg.ffn} E={cfg.E} top-{cfg.top_k} "
+            f"{'sigmoid' if cfg.score else 'softmax'}{' renormalised' if cfg.renormalize else ''}")
+
+
+def k4_algorithmic(cfg, alg, plan):
+    """(bytes, FLOP) of one launch of the dominant kernel: the fused gate/up
+    GEMM (with the down projection when that is fused into it)."""
+    if plan["fused_down"]:
+        return alg["e_act"] * 6.0 * cfg.ffn * cfg.d + 2.0 * alg["A"] * cfg.d, alg["flop"]
+    return alg["bytes_k4"], alg["flop_k4"]
+
+
+def also_workload(name, seed, dev, warmup, steps):
+    """Another workload measured in the same process, same warm-up and step
+    counts: ms per pass, tokens/s, pass roofline, and the gate/up kernel's
+    mean over the timed region against 8 TB/s."""
+    import torch
+
+    from expert_dispatch_router_amd import synth
+
+    cfg = synth.CONFIGS[name]
+    r = Runner(cfg, seed, dev)
+    elapsed, k4 = r.timed(warmup, steps)
+    alg = algorithmic(cfg, r.routing_counts())
+    t_step = elapsed / steps
+    t_roof = max(alg["bytes"] / (HBM_PEAK_GBS * 1e9), alg["flop"] / (BF16_PEAK_TFLOPS * 1e12))
+    kb, _ = k4_algorithmic(cfg, alg, r.plan)
+    k4_ms = float(k4.mean())
+    res = {"workload": workload_label(cfg), "steps": steps, "warmup": warmup,
+           "ms_per_step": t_step * 1e3, "tokens_per_s": cfg.T / t_step,
+           "tflops": alg["flop"] / t_step / 1e12, "hbm_gbs": alg["bytes"] / t_step / 1e9,
+           "roofline_frac_step": t_roof / t_step, "t_roof_ms": t_roof * 1e3,
+           "gate_up": {"mean_launch_ms": k4_ms, "alg_bytes_per_launch": kb,
+                       "achieved_gbs": kb / (k4_ms * 1e-3) / 1e9,
+                       "frac": kb / (k4_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+    del r
+    torch.cuda.empty_cache()
+    return res
 
 
 def run(args):
     import numpy as np
     import torch
 
-    import expert_dispatch_router_amd as moe
     from expert_dispatch_router_amd import synth
 
     if not torch.cuda.is_available():
@@ -216,70 +429,26 @@ def run(args):
     cfg = synth.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    x, logits, wgu, wd = synth.make_inputs(cfg, args.seed, dev)
     unfused = 1 if args.unfused else 0
-    bm, split, fused_down = moe.moe_plan(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k,
-                                         unfused_swiglu=unfused, with_fusion=True)
-    out = torch.empty(cfg.T, cfg.d, dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(moe.moe_workspace_size(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k,
-                                            unfused_swiglu=unfused),
-                     dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    copy_src = copy_dst = None
-    if args.copy_bytes:
-        copy_src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev).fill_(1)
-        copy_dst = torch.empty_like(copy_src)
-
-    routing = moe.moe_route(logits, cfg.top_k, cfg.renormalize, cfg.score)
-    counts = routing["counts"].cpu().numpy()
-    alg = algorithmic(cfg, counts)
-    if fused_down:
-        # one kernel streams the gate/up and the down weights
-        alg["bytes_k4"] = alg["e_act"] * 6.0 * cfg.ffn * cfg.d + 2.0 * alg["A"] * cfg.d
-
-    def step(events=None, strm=None):
-        moe.moe_forward(x, logits, wgu, wd, cfg.top_k, cfg.renormalize, out=out, score=cfg.score,
-                        workspace=ws, stream=strm or stream, stage_events=events,
-                        unfused_swiglu=unfused)
-        if copy_src is not None:
-            copy_dst.copy_(copy_src)
-
-    for _ in range(args.warmup):
-        step()
-    # Timed region: the fused gate/up GEMM (the dominant kernel) is bracketed
-    # by two events on the library's stream in every step (stage points 3, 4).
-    k4_timers = [(moe.Timer(), moe.Timer()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        a, b = k4_timers[i]
-        step([None, None, None, a.handle, b.handle, None, None])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
+    # Inputs are generated on the GPU, and the warm-up passes follow at once:
+    # nothing that waits on the host runs between them (the routing counts
+    # used for the report are read after the timed region).
+    r = Runner(cfg, args.seed, dev, unfused, args.copy_bytes)
+    elapsed, k4_each = r.timed(args.warmup, args.steps)
     ms_step = elapsed * 1e3 / args.steps
-    k4_each = np.array([a.elapsed_ms(b) for a, b in k4_timers])
-    k4_ms = float(k4_each.mean())
-    # Stage breakdown: a second, separately run set of steps with all seven
-    # stage events (each event adds a little time of its own).
-    timers = [[moe.Timer() for _ in range(7)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step([t.handle for t in timers[i]])
-    torch.cuda.synchronize()
-    stage_ms = np.zeros(6)
-    for i in range(args.steps):
-        for s in range(6):
-            stage_ms[s] += timers[i][s].elapsed_ms(timers[i][s + 1])
-    stage_ms /= args.steps
-    pass_each = np.array([timers[i][0].elapsed_ms(timers[i][6]) for i in range(args.steps)])
-    pct = lambda v: {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
-                     "p90": float(np.percentile(v, 90))}
+    plan = r.plan
+    alg = algorithmic(cfg, r.routing_counts())
+    stage_each, pass_each = r.stages(args.steps)
+    stage_mean = stage_each.mean(axis=0)
+    k5_each = None if plan["fused_down"] else stage_each[:, 4]
 
     t_step = elapsed / args.steps
     t_roof = max(alg["bytes"] / (HBM_PEAK_GBS * 1e9), alg["flop"] / (BF16_PEAK_TFLOPS * 1e12))
+    k4_ms = float(k4_each.mean())
     k4_s = k4_ms * 1e-3
-    achieved = alg["bytes_k4"] / k4_s / 1e9
-    k4_flop = alg["flop"] if fused_down else alg["flop_k4"]
+    k4_bytes, k4_flop = k4_algorithmic(cfg, alg, plan)
+    achieved = k4_bytes / k4_s / 1e9
+    names = stage_names(plan)
     res = {
         "metric": METRIC,
         "value": cfg.T * args.steps / elapsed,
@@ -293,33 +462,41 @@ def run(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: MoE layer T={cfg.T} d={cfg.d} ffn={cfg.ffn} "
-                               f"E={cfg.E} top-{cfg.top_k} "
-                               f"{'sigmoid' if cfg.score else 'softmax'}"
-                               f"{' renormalised' if cfg.renormalize else ''}",
+        "config": {"workload": workload_label(cfg),
                    "tokens": cfg.T, "hidden": cfg.d, "ffn": cfg.ffn, "experts": cfg.E,
-                   "top_k": cfg.top_k, "block_rows": bm, "split_k": split,
+                   "top_k": cfg.top_k, "block_rows": plan["block_rows"], "split_k": plan["split_k"],
                    "active_experts": alg["e_act"], "seed": args.seed,
+                   "launches_per_pass": plan["launches"],
                    "swiglu": "unfused ablation" if unfused else "fused",
-                   "down_projection": "in the gate/up GEMM" if fused_down else "own GEMM"},
+                   "down_projection": "in the gate/up GEMM" if plan["fused_down"] else "own GEMM"},
         "tflops": alg["flop"] / t_step / 1e12,
         "hbm_gbs": alg["bytes"] / t_step / 1e9,
         "roofline_frac_step": t_roof / t_step,
-        "stage_ms": {n: round(float(v), 5) for n, v in zip(STAGES, stage_ms)},
-        # distributions: the fused kernel over the timed steps; the whole
-        # pass (first to last stage event) over the stage-breakdown steps
+        "t_roof_ms": t_roof * 1e3,
+        # a second, separately run set of passes with seven stage events;
+        # intervals with no kernel (the one-workgroup routing covers three
+        # stages, for instance) only measure two back-to-back event records
+        "stage_ms": {n: round(float(v), 5) for n, v in zip(names, stage_mean) if n},
+        "event_only_intervals_ms": [round(float(v), 5) for n, v in zip(names, stage_mean)
+                                    if not n],
+        # distributions: the fused gate/up GEMM over the timed passes, the
+        # down GEMM and the whole pass (first to last event) over the
+        # stage-event passes
         "k4_ms_pct": pct(k4_each),
+        "k5_ms_pct": None if k5_each is None else pct(k5_each),
         "pass_ms_pct": pct(pass_each),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if (unfused or fused_down) else traffic_for(cfg.name),
+                     "traffic": None if (unfused or plan["fused_down"]) else traffic_for(cfg.name),
                      "kernel": ("gate/up stage of the unfused ablation (gate GEMM + up GEMM + "
                                 "activation)") if unfused else
                                ("gate_up_swiglu_down (fused gate/up SwiGLU grouped GEMM with "
-                                "the down projection in its epilogue)") if fused_down else
+                                "the down projection in its epilogue)") if plan["fused_down"] else
                                "gate_up_swiglu (fused gate/up SwiGLU grouped GEMM)",
-                     "alg_bytes_per_launch": alg["bytes_k4"],
-                     "mean_launch_ms": float(k4_ms)},
+                     "alg_bytes_per_launch": k4_bytes,
+                     "mean_launch_ms": k4_ms,
+                     "timing": "two fence-free HIP events on the library's stream around the "
+                               "kernel in every timed pass"},
         # the same kernel against the bf16 dense MFMA peak (its FLOPs over its
         # mean duration): the hot experts of skewed routing are locally
         # MFMA-bound even where the launch as a whole is HBM-bound
@@ -327,12 +504,35 @@ def run(args):
                     "unit": "TFLOP/s", "frac": k4_flop / k4_s / 1e12 / BF16_PEAK_TFLOPS},
         "cpu_baseline": None,
     }
-    res["router_gemm"] = router_gemm(cfg, x, args.seed, args.steps, stream)
+    if k5_each is not None:
+        dn_bytes = alg["e_act"] * 2.0 * cfg.ffn * cfg.d + alg["A"] * (2.0 * cfg.ffn + 4.0 * cfg.d)
+        k5_ms = float(k5_each.mean())
+        res["down"] = {"mean_launch_ms": k5_ms, "alg_bytes_per_launch": dn_bytes,
+                       "timing": "stage events of the stage-breakdown passes",
+                       "achieved_gbs": dn_bytes / (k5_ms * 1e-3) / 1e9,
+                       "frac": dn_bytes / (k5_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if args.flush or (args.flush is None and alg["e_act"] * 6.0 * cfg.ffn * cfg.d < (1 << 30)):
+        med, p10, p90 = r.flushed(args.steps)
+        res["cache_flushed"] = {
+            "ms_per_pass_p50": med, "p10": p10, "p90": p90, "roofline_frac": t_roof / (med * 1e-3),
+            "protocol": f"{args.steps} reps after 3 warm-ups, a 1 GiB write before each rep "
+                        "outside the timed interval (first to last stage event)"}
+    res["router_gemm"] = router_gemm(cfg, r.x, args.seed, args.steps, r.stream)
     if args.graph:
-        res["graph"] = graph_replay(step, args.steps, cfg.T)
+        res["graph"] = graph_replay(lambda strm=None: r.step(strm=strm), args.steps, cfg.T)
+    x, logits, wgu, wd = r.x, r.logits, r.wgu, r.wd
+    for name in ([] if args.also is None else [a for a in args.also.split(",") if a]):
+        if name == cfg.name:
+            continue
+        del r
+        torch.cuda.empty_cache()
+        res.setdefault("also", {})[name] = also_workload(name, args.seed, dev, args.warmup,
+                                                         args.steps)
+        r = None
     if not args.profile and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, x, logits, wgu, wd, args.cpu_seconds)
-        res["cpu_baseline"]["tiny_one_thread_requested"] = cpu_single_thread_tiny()
+        res["cpu_baseline"]["inputs_sha256"] = input_hashes(x, logits, wgu, wd)
+        res["cpu_baseline"]["tiny_one_core"] = cpu_single_core_tiny()
     print(json.dumps(res), flush=True)
 
 
@@ -421,7 +621,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     # the GPU's clocks settle within ~20 forward passes of sustained load
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="mixtral_512")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--profile", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -432,6 +632,13 @@ def main():
                     help="also time the pass captured in a HIP graph and replayed")
     ap.add_argument("--unfused", action="store_true",
                     help="SwiGLU ablation: gate GEMM, up GEMM and activation kernel")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads also measured in the same process "
+                         "(default: dsv3_512 with the default workload, else none)")
+    ap.add_argument("--flush", dest="flush", action="store_true", default=None,
+                    help="also time passes rep by rep after a 1 GiB cache-flush write "
+                         "(default: when the active expert weights are under 1 GiB)")
+    ap.add_argument("--no-flush", dest="flush", action="store_false")
     args = ap.parse_args()
     if args.traffic:
         summarize_traffic(args.traffic[0], args.traffic[1], args.workload,
@@ -443,6 +650,8 @@ def main():
         raise SystemExit(2)
     if os.environ.get("WORLD_SIZE", "1") not in ("1", ""):
         raise SystemExit("one GPU only: run without torch.distributed")
+    if args.also is None and args.workload == DEFAULT_WORKLOAD and not args.profile:
+        args.also = "dsv3_512"
     run(args)
 
 

@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     moe_forward,
     moe_forward_router,
     moe_plan,
+    moe_plan_ex,
     moe_route,
     moe_route_workspace_size,
     moe_router_logits,

@@ -42,6 +42,7 @@ SIGNATURES = {
     "moe_router_workspace_size": (_I, [_I, _I, _I, ctypes.POINTER(_SZ)]),
     "moe_forward_router": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ,
                                 _P]),
+    "moe_plan_ex": (_I, [_I, _I, _I, _I, _I, _P, _P]),
     "moe_route_workspace_size": (_I, [_I, _I, _I, _P, ctypes.POINTER(_SZ)]),
     "moe_route": (_I, [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I,
                        _P, ctypes.POINTER(_I), _P, _SZ, _P]),
@@ -61,6 +62,14 @@ class MoeOptions(ctypes.Structure):
                 ("unfused_swiglu", ctypes.c_int), ("xcd_order", ctypes.c_int),
                 ("fold_combine", ctypes.c_int), ("fuse_down", ctypes.c_int),
                 ("stage_events", ctypes.c_void_p)]
+
+
+class MoePlanInfo(ctypes.Structure):
+    """struct moe_plan_info of include/moe.h."""
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "block_rows", "split_k", "fused_down", "routing_launches", "gather_launch",
+        "gate_up_variant", "down_variant", "unfused_swiglu", "fold_combine", "xcd_grouped",
+        "launches")]
 
 
 class MoeError(RuntimeError):
@@ -114,10 +123,13 @@ def _opts(block_rows=0, split_k=0, stage_events=None, tile_variant=0, rotate=0,
     o = MoeOptions(int(block_rows), int(split_k), int(tile_variant), int(down_variant),
                    int(rotate), int(routing_kernels), int(gather_mode), int(unfused_swiglu),
                    int(xcd_order), int(fold_combine), int(fuse_down), None)
-    keep = None
+    keep = []
     if stage_events is not None:
-        keep = (ctypes.c_void_p * len(stage_events))(*stage_events)
-        o.stage_events = ctypes.cast(keep, ctypes.c_void_p)
+        if len(stage_events) != 7:
+            raise ValueError("stage_events takes 7 event handles")
+        a = (ctypes.c_void_p * 7)(*stage_events)
+        keep.append(a)
+        o.stage_events = ctypes.cast(a, ctypes.c_void_p)
     return o, keep
 
 
@@ -147,6 +159,16 @@ def moe_plan(T, d, ffn, E, top_k, block_rows=0, split_k=0, tile_variant=0, rotat
     return int(bm.value), int(sk.value)
 
 
+def moe_plan_ex(T, d, ffn, E, top_k, **options) -> dict:
+    """The launch plan moe_forward_ex follows for these sizes and options
+    (the fields of struct moe_plan_info)."""
+    o, _ = _opts(**options)
+    info = MoePlanInfo()
+    _check("moe_plan_ex", lib().moe_plan_ex(T, d, ffn, E, top_k, ctypes.byref(o) if o else None,
+                                             ctypes.byref(info)))
+    return {n: int(getattr(info, n)) for n, _ in MoePlanInfo._fields_}
+
+
 def moe_route_workspace_size(T, E, top_k, block_rows=0, routing_kernels=0) -> int:
     o, _ = _opts(block_rows, routing_kernels=routing_kernels)
     n = _SZ(0)
@@ -173,6 +195,22 @@ def _dev_ptr(t, dtype, name):
     return t.data_ptr()
 
 
+def _same_device(tensors):
+    """All given tensors on one GPU (checked before any launch: a kernel
+    reading another device's memory faults)."""
+    devs = {t.device for _, t in tensors if t is not None}
+    if len(devs) > 1:
+        raise ValueError("tensors on different devices: " +
+                         ", ".join(f"{n} on {t.device}" for n, t in tensors if t is not None))
+
+
+def _check_out(out, shape, name="out"):
+    """A caller's output buffer must have exactly the shape the kernels
+    write (a smaller one would be written past its end)."""
+    if out is not None and tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {list(shape)}, got {list(out.shape)}")
+
+
 def _stream_ptr(stream, device):
     s = torch.cuda.current_stream(device) if stream is None else stream
     return s.cuda_stream
@@ -186,13 +224,17 @@ def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=Non
 
     x bf16 [T,d]; router_logits fp32 [T,E]; W_gate_up bf16 [E,2F,d];
     W_down bf16 [E,d,F].  ``out`` and ``workspace`` (uint8) are allocated
-    with torch when not given.  ``stage_events``: 7 HIP event handles."""
+    with torch when not given.  ``stage_events``: 7 HIP event handles
+    recorded between the stages (moe_options; None entries skipped)."""
     T, d = x.shape
     E = router_logits.shape[1]
     F = W_down.shape[2]
     if router_logits.shape[0] != T or tuple(W_gate_up.shape) != (E, 2 * F, d) or \
             tuple(W_down.shape) != (E, d, F):
         raise ValueError("inconsistent shapes")
+    _check_out(out, (T, d))
+    _same_device([("x", x), ("router_logits", router_logits), ("W_gate_up", W_gate_up),
+                  ("W_down", W_down), ("out", out), ("workspace", workspace)])
     if out is None:
         out = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
     ws_need = moe_workspace_size(T, d, F, E, top_k, block_rows, split_k, tile_variant, rotate,
@@ -227,10 +269,10 @@ def moe_router_logits(x, W_router, out=None, workspace=None, stream=None):
     E = W_router.shape[0]
     if tuple(W_router.shape) != (E, d):
         raise ValueError("inconsistent shapes")
+    _check_out(out, (T, E))
+    _same_device([("x", x), ("W_router", W_router), ("out", out), ("workspace", workspace)])
     if out is None:
         out = torch.empty(T, E, dtype=torch.float32, device=x.device)
-    if tuple(out.shape) != (T, E):
-        raise ValueError("out must be [T, E]")
     need = moe_router_workspace_size(T, d, E)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
@@ -257,8 +299,10 @@ def moe_forward_router(x, W_router, W_gate_up, W_down, top_k, renormalize, out=N
     if tuple(W_router.shape) != (E, d) or tuple(W_gate_up.shape) != (E, 2 * F, d) or \
             tuple(W_down.shape) != (E, d, F):
         raise ValueError("inconsistent shapes")
-    if logits_out is not None and tuple(logits_out.shape) != (T, E):
-        raise ValueError("logits_out must be [T, E]")
+    _check_out(logits_out, (T, E), "logits_out")
+    _check_out(out, (T, d))
+    _same_device([("x", x), ("W_router", W_router), ("W_gate_up", W_gate_up), ("W_down", W_down),
+                  ("out", out), ("logits_out", logits_out), ("workspace", workspace)])
     if out is None:
         out = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
     ws_need = moe_workspace_size(T, d, F, E, top_k, block_rows, split_k, tile_variant, rotate,
@@ -289,6 +333,11 @@ def moe_route(router_logits, top_k, renormalize, score="softmax", x=None, block_
     T, E = router_logits.shape
     dev = router_logits.device
     A = T * top_k
+    if x is not None and x.dim() != 2:
+        raise ValueError("x must be [T, d]")
+    if x is not None and x.shape[0] != T:
+        raise ValueError(f"x must have one row per token: {x.shape[0]} rows for T = {T}")
+    _same_device([("router_logits", router_logits), ("x", x), ("workspace", workspace)])
     i32 = dict(dtype=torch.int32, device=dev)
     res = dict(ids=torch.empty(T, top_k, **i32),
                w=torch.empty(T, top_k, dtype=torch.float32, device=dev),

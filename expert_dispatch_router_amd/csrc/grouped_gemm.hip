@@ -438,23 +438,29 @@ void grouped_gemm_kernel(
 
   if constexpr (MODE == kOutF32Parts) {
     if (fold.cnt) {
-      // The partials went out as agent-scope stores; once every thread's
-      // stores have completed (the wait below, then the barrier), one thread
-      // per row counts the row's token for this column tile.  Whoever
-      // completes a count owns that token's combination for the tile and
-      // reads the partials with agent-scope loads.  No L2 writeback or
-      // invalidation is needed on either side.
+      // The partials went out as agent-scope stores.  After the barrier
+      // (every thread's stores are ordered before it) each thread issues an
+      // agent-scope release fence, then counts its rows' tokens for this
+      // column tile with relaxed agent-scope increments: the counter's
+      // modification order carries every earlier workgroup's release to the
+      // workgroup whose increment completes a count, which acquires (agent
+      // scope) before it owns that token's combination for the tile and
+      // reads the partials with agent-scope loads.  The barrier below hands
+      // the acquired view to the workgroup's other threads.
       __shared__ int n_last;
       __shared__ int last_tok[BM];
       if (tid == 0) n_last = 0;
-      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       const int nsplit = tiles_per_block / n_tiles;
       const int need = fold.k * nsplit;  // k routed rows x split parts
       for (int m = tid; m < rows; m += G::kThreads) {
         const int t = fold.perm[r0 + m] / fold.k;
-        if (atomicAdd(&fold.cnt[(size_t)t * n_tiles + tile], 1) == need - 1)
+        if (__hip_atomic_fetch_add(&fold.cnt[(size_t)t * n_tiles + tile], 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) == need - 1) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
           last_tok[atomicAdd(&n_last, 1)] = t;
+        }
       }
       __syncthreads();
       const int nl = n_last;

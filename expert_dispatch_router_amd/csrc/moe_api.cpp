@@ -550,6 +550,32 @@ int moe_plan(int T, int d, int ffn, int E, int top_k, const moe_options* opt, in
   return MOE_OK;
 }
 
+int moe_plan_ex(int T, int d, int ffn, int E, int top_k, const moe_options* opt,
+                moe_plan_info* info) {
+  MOE_TRY(check_sizes(T, d, ffn, E, top_k, true));
+  MOE_TRY(check_options(opt));
+  MOE_TRY(check_paths(T, d, E, top_k, opt));
+  if (!info) return MOE_ERR_NULL;
+  memset(info, 0, sizeof(*info));
+  if (T == 0) return MOE_OK;
+  Plan p;
+  make_plan(T, d, ffn, E, top_k, opt, &p);
+  MOE_TRY(p.plan_error);
+  info->block_rows = p.bm;
+  info->split_k = p.split;
+  info->fused_down = p.fused_down ? 1 : 0;
+  info->routing_launches = p.small_routing ? 1 : p.fused_reorder ? 2 : 3;
+  info->gather_launch = p.gather_in_gemm ? 0 : 1;
+  info->gate_up_variant = p.gu_variant;
+  info->down_variant = p.fused_down ? -1 : p.dn_variant;
+  info->unfused_swiglu = p.unfused ? 1 : 0;
+  info->fold_combine = p.fold ? 1 : 0;
+  info->xcd_grouped = p.gu_xcd ? 1 : 0;
+  info->launches = info->routing_launches + info->gather_launch + (p.unfused ? 3 : 1) +
+                   (p.fused_down ? 0 : 1) + (p.fold ? 0 : 1);
+  return MOE_OK;
+}
+
 int moe_route_workspace_size(int T, int E, int top_k, const moe_options* opt, size_t* bytes) {
   MOE_TRY(check_sizes(T, 0, 0, E, top_k, false));
   MOE_TRY(check_options(opt));

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* Limits of the library (violations return MOE_ERR_UNSUPPORTED). */
 #define MOE_MAX_EXPERTS 512
@@ -212,6 +212,29 @@ int moe_workspace_size_ex(int T, int d, int ffn, int E, int top_k, const moe_opt
  * Any output pointer may be NULL. */
 int moe_plan(int T, int d, int ffn, int E, int top_k, const moe_options *opt,
              int *block_rows, int *split_k, int *fused_down);
+
+/* What moe_forward_ex would launch for these sizes and options. */
+typedef struct moe_plan_info {
+    int block_rows;        /* BLOCK_M of the schedule                          */
+    int split_k;           /* parts of the down reduction (column tiles of the
+                              gate/up GEMM when the down projection is fused) */
+    int fused_down;        /* 1: the down projection runs inside the gate/up GEMM */
+    int routing_launches;  /* 1, 2 or 3 kernels for route, histogram/scan/
+                              schedule and reorder                            */
+    int gather_launch;     /* 1: a separate gather kernel writes x_perm        */
+    int gate_up_variant;   /* tile variant of the gate/up GEMM (moe_options)   */
+    int down_variant;      /* tile variant of the down GEMM (-1 when fused)    */
+    int unfused_swiglu;    /* 1: the ablation's three kernels replace the fused GEMM */
+    int fold_combine;      /* 1: the combination runs in the down GEMM         */
+    int xcd_grouped;       /* 1: GEMM workgroups grouped by XCD                */
+    int launches;          /* kernels per forward pass                         */
+} moe_plan_info;
+
+/* Host-only: fills *info with the launch plan moe_forward_ex would follow.
+ * Same checks and error codes as moe_workspace_size_ex; info NULL returns
+ * MOE_ERR_NULL.  T = 0 plans nothing (every field 0). */
+int moe_plan_ex(int T, int d, int ffn, int E, int top_k, const moe_options *opt,
+                moe_plan_info *info);
 
 /*
  * The MoE forward pass ([R] "The reading"; abstract).

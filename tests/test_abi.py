@@ -344,3 +344,76 @@ def test_product_path_never_imports_the_oracle():
                 text = open(os.path.join(root, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "moe_oracle" not in text and "liboracle" not in text, f
+
+
+def test_binding_rejects_wrong_output_shapes_before_any_call():
+    """The binding raises before it reaches the library when a caller's
+    output buffer does not have the shape the kernels write ([T, d] for the
+    forward pass, [T, E] for the scores) or when moe_route's x does not have
+    one row per token.  Host tensors suffice: the shape checks come first."""
+    import torch
+
+    T, d, F, E, k = 8, 64, 64, 4, 2
+    x = torch.zeros(T, d, dtype=torch.bfloat16)
+    lg = torch.zeros(T, E)
+    wgu = torch.zeros(E, 2 * F, d, dtype=torch.bfloat16)
+    wd = torch.zeros(E, d, F, dtype=torch.bfloat16)
+    wr = torch.zeros(E, d, dtype=torch.bfloat16)
+    for bad in (torch.empty(T - 1, d, dtype=torch.bfloat16), torch.empty(T, d // 2, dtype=torch.bfloat16),
+                torch.empty(T * d, dtype=torch.bfloat16)):
+        with pytest.raises(ValueError, match="out must be"):
+            moe.moe_forward(x, lg, wgu, wd, k, True, out=bad)
+        with pytest.raises(ValueError, match="out must be"):
+            moe.moe_forward_router(x, wr, wgu, wd, k, True, out=bad)
+    with pytest.raises(ValueError, match="logits_out must be"):
+        moe.moe_forward_router(x, wr, wgu, wd, k, True, logits_out=torch.empty(T, E + 1))
+    with pytest.raises(ValueError, match="out must be"):
+        moe.moe_router_logits(x, wr, out=torch.empty(T - 1, E))
+    with pytest.raises(ValueError, match="one row per token"):
+        moe.moe_route(lg, k, True, x=torch.zeros(T + 1, d, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="x must be"):
+        moe.moe_route(lg, k, True, x=torch.zeros(T * d, dtype=torch.bfloat16))
+
+
+def test_binding_rejects_tensors_on_different_devices():
+    """Tensors on two devices are refused before any launch (checked by
+    device identity, so a host tensor beside a meta tensor is enough)."""
+    import torch
+
+    T, d, F, E, k = 8, 64, 64, 4, 2
+    x = torch.zeros(T, d, dtype=torch.bfloat16)
+    lg = torch.zeros(T, E)
+    wgu = torch.zeros(E, 2 * F, d, dtype=torch.bfloat16, device="meta")
+    wd = torch.zeros(E, d, F, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="different devices"):
+        moe.moe_forward(x, lg, wgu, wd, k, True)
+
+
+def test_plan_ex_reports_the_launches():
+    """moe_plan_ex (host only) agrees with moe_plan and counts the kernels
+    of each path: one-workgroup routing + gate/up + down + combination at
+    Mixtral T=512 (4 launches), the down projection fused at tiny (3), the
+    unfused ablation's three kernels, a separate gather, the folded
+    combination."""
+    mix = CONFIGS["mixtral_512"]
+    info = moe.moe_plan_ex(mix.T, mix.d, mix.ffn, mix.E, mix.top_k)
+    bm, split, fd = moe.moe_plan(mix.T, mix.d, mix.ffn, mix.E, mix.top_k, with_fusion=True)
+    assert (info["block_rows"], info["split_k"], info["fused_down"]) == (bm, split, int(fd))
+    assert info["routing_launches"] == 1 and info["launches"] == 4
+    tiny = CONFIGS["tiny"]
+    t = moe.moe_plan_ex(tiny.T, tiny.d, tiny.ffn, tiny.E, tiny.top_k)
+    assert t["fused_down"] == 1 and t["down_variant"] == -1 and t["launches"] == 3
+    dsv = CONFIGS["dsv3_4096"]
+    dv = moe.moe_plan_ex(dsv.T, dsv.d, dsv.ffn, dsv.E, dsv.top_k)
+    assert dv["routing_launches"] == 3 and dv["xcd_grouped"] == 1 and dv["launches"] == 6
+    u = moe.moe_plan_ex(mix.T, mix.d, mix.ffn, mix.E, mix.top_k, unfused_swiglu=1)
+    assert u["unfused_swiglu"] == 1 and u["launches"] == 6
+    g = moe.moe_plan_ex(mix.T, mix.d, mix.ffn, mix.E, mix.top_k, gather_mode=2, routing_kernels=2)
+    assert g["gather_launch"] == 1 and g["routing_launches"] == 3 and g["launches"] == 7
+    f = moe.moe_plan_ex(mix.T, mix.d, mix.ffn, mix.E, mix.top_k, block_rows=192, down_variant=1,
+                        fold_combine=2)
+    assert f["fold_combine"] == 1 and f["launches"] == 3
+    assert moe.moe_plan_ex(0, 64, 64, 4, 2)["launches"] == 0
+    assert moe.lib().moe_plan_ex(4, 64, 64, 4, 2, None, None) == NULL
+    with pytest.raises(moe.MoeError):
+        moe.moe_plan_ex(4, 96, 64, 4, 2)

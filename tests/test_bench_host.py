@@ -104,8 +104,33 @@ def test_bench_refuses_more_than_one_gpu():
 
 
 
-def test_single_thread_tiny_cpu_baseline():
-    """The tiny oracle figure runs in a child process that asks for one
-    OpenMP thread and reports the threads it got (one, in this container)."""
-    r = bench.cpu_single_thread_tiny()
-    assert r["cores"] >= 1 and r["value"] > 0 and r["kind"] == "oracle", r
+def test_single_core_tiny_cpu_baseline():
+    """The tiny oracle figure runs in a child process pinned to one CPU with
+    OMP_NUM_THREADS=1: it reports one core and one OpenMP thread."""
+    r = bench.cpu_single_core_tiny()
+    assert r["cores"] == 1 and r["omp_threads"] == 1, r
+    assert r["value"] > 0 and r["kind"] == "oracle", r
+
+
+def _plan(rl=1, gather=0, fused_down=0, unfused=0, fold=0):
+    return {"routing_launches": rl, "gather_launch": gather, "fused_down": fused_down,
+            "unfused_swiglu": unfused, "fold_combine": fold}
+
+
+def test_stage_names_follow_the_launch_plan():
+    """An interval between two stage events with no kernel in it is named
+    None (it measures only the event records)."""
+    assert bench.stage_names(_plan(1)) == ["route_histogram_scan_schedule_reorder", None, None,
+                                           "gate_up_swiglu", "down", "combine"]
+    assert bench.stage_names(_plan(2)) == ["route", "histogram_scan_schedule_reorder", None,
+                                           "gate_up_swiglu", "down", "combine"]
+    assert bench.stage_names(_plan(3, gather=1)) == ["route", "histogram_scan_schedule",
+                                                     "reorder_gather", "gate_up_swiglu", "down",
+                                                     "combine"]
+    assert bench.stage_names(_plan(1, fused_down=1))[3:] == ["gate_up_swiglu_down", None,
+                                                             "combine"]
+    assert bench.stage_names(_plan(2, unfused=1, fold=1))[3:] == ["gate_up_unfused", "down", None]
+
+
+def test_cpu_model_is_reported():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()
