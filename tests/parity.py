@@ -19,11 +19,16 @@ from expert_dispatch_router_amd import synth
 REL_FRO_TOL = 1e-2
 MAX_ABS_TOL = 2e-2
 W_RTOL = 4e-6
-# The unfused SwiGLU ablation stores the gate and up products in bf16 before
-# SiLU and the product (the activation dtype of an unfused pipeline), so each
-# h element carries three independent bf16 roundings instead of one: its
-# rounding noise is ~sqrt(3) times the fused path's, and so are its bounds.
-UNFUSED_SCALE = 3.0 ** 0.5
+# Where the data formats alone cannot meet MAX_ABS_TOL (tests/format_model.py:
+# small ffn, rows far from unit weight sum, the unfused ablation's bf16 gate
+# and up products), an element may be off by its format floor plus this
+# much of max(RMS, its row's RMS): fp32 summation order and the occasional
+# bf16 rounding of h (or of g, u) that goes the other way, whose effect
+# scales with the row.  tests/test_format_floor.py measures what an
+# independent fp32 implementation needs beyond the floor on the same input
+# distributions (at most ~2e-3 over its draws: one flipped rounding of a
+# large h element times a large down weight).
+FLOOR_EPS = 5e-3
 
 
 def to_np_u16(t: torch.Tensor) -> np.ndarray:
@@ -83,6 +88,31 @@ def oracle_out(x, logits, wgu, wd, k, score, renorm, tokens=None):
     return oracle.ffn(to_np_u16(x), ids, w, gu, dn, F, tokens=toks)
 
 
+_WORKLOAD_REF = {}
+
+
+def workload_reference(name, x, logits, wgu, wd, cfg):
+    """The oracle's fp32 output for every token of a workload's seeded
+    inputs (computed once per process: the GPU tests that run the same
+    workload on the same inputs share it)."""
+    key = (name, synth.sha256(x), synth.sha256(logits))
+    if key not in _WORKLOAD_REF:
+        _WORKLOAD_REF[key] = oracle_out(x, logits, wgu, wd, cfg.top_k, cfg.score, cfg.renormalize)
+    return _WORKLOAD_REF[key]
+
+
+def tokens_per_block(logits, k, score, renorm, bm):
+    """Tokens that cover every schedule block of the oracle's block table at
+    block size bm: each block's first and last sorted row, as token ids."""
+    r = oracle_routing(logits, k, score, renorm, bm)
+    toks = set()
+    for e, r0 in r["blocks"]:
+        end = min(int(r0) + bm, int(r["offsets"][int(e) + 1]))
+        toks.add(int(r["perm"][int(r0)]) // k)
+        toks.add(int(r["perm"][end - 1]) // k)
+    return np.array(sorted(toks), dtype=np.int32)
+
+
 def bf16_half_ulp(ref: np.ndarray) -> np.ndarray:
     """Half a bf16 ulp at each value: the error of rounding it to bf16 is at
     most this (8 significand bits: ulp = 2^(floor(log2|v|) - 7))."""
@@ -91,33 +121,79 @@ def bf16_half_ulp(ref: np.ndarray) -> np.ndarray:
     return np.where(a > 0, np.exp2(e - 8.0), 0.0)
 
 
-def errors(out_bf16_rows: torch.Tensor, ref32: np.ndarray, beyond_format=False):
-    """(rel-Frobenius, max-abs / RMS).  With ``beyond_format`` the max-abs
-    term counts only the error in excess of each element's own bf16 rounding
-    (|got - ref| - half_ulp(ref), floored at 0)."""
+def errors(out_bf16_rows: torch.Tensor, ref32: np.ndarray, floor=None):
+    """(rel-Frobenius, max-abs / RMS).  With ``floor`` (per-element format
+    floors, tests/format_model.py) the second value is the largest ratio of
+    an element's error to the bound it is held to,
+    max(MAX_ABS_TOL * RMS, floor + FLOOR_EPS * max(RMS, row RMS)), scaled by
+    MAX_ABS_TOL so that it compares with MAX_ABS_TOL like the plain max-abs
+    does."""
     got = out_bf16_rows.detach().float().cpu().numpy().astype(np.float64)
     ref = ref32.astype(np.float64)
     rms = np.sqrt(np.mean(ref * ref))
     rel_fro = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
     diff = np.abs(got - ref)
-    if beyond_format:
-        diff = np.maximum(diff - bf16_half_ulp(ref), 0.0)
-    max_abs = np.max(diff) / max(rms, 1e-300)
-    return rel_fro, max_abs
+    if floor is None:
+        return rel_fro, np.max(diff) / max(rms, 1e-300)
+    row = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    bound = np.maximum(MAX_ABS_TOL * rms,
+                       np.asarray(floor, dtype=np.float64) + FLOOR_EPS * np.maximum(rms, row))
+    return rel_fro, MAX_ABS_TOL * np.max(diff / np.maximum(bound, 1e-300))
 
 
-def check_out(out_bf16_rows, ref32, what="", scale=1.0, beyond_format=False):
-    """Asserts the output tolerance; ``scale`` widens both bounds (only the
-    unfused ablation passes UNFUSED_SCALE).
+def format_floor(x, logits, wgu, wd, k, score, renorm, ref32, tokens=None, rounding="fused",
+                 with_best=False):
+    """Per-element format floors of the listed tokens' outputs (all when
+    None): what exact arithmetic with the GPU path's bf16 roundings errs by
+    (rounding "fused": h and the output; "unfused": also the gate and up
+    products).  With ``with_best`` also that computation's max-abs / RMS
+    (the best an implementation with those stores can do)."""
+    from tests import format_model
 
-    ``beyond_format`` is for inputs whose exact output has elements far above
-    its RMS (rows with very different routing-weight sums, as unrenormalised
-    softmax over many experts gives): bf16 itself cannot hold an element
-    |y| > 5.12 * RMS to within 2e-2 * RMS (its rounding error reaches
-    2^-8 * |y|), so the max-abs bound is applied to the error beyond that
-    rounding.  The rel-Frobenius bound is unchanged."""
-    rel_fro, max_abs = errors(out_bf16_rows, ref32, beyond_format)
+    m = format_model.moe_output(x, logits, wgu, wd, k, score, renorm, tokens=tokens,
+                                rounding=rounding)
+    fl = format_model.floor(m, ref32)
+    if not with_best:
+        return fl
+    ref = np.asarray(ref32, dtype=np.float64)
+    best = float(np.max(np.abs(format_model.bf16_round(m) - ref)) / np.sqrt(np.mean(ref * ref)))
+    return fl, best
+
+
+# the two target configurations (Mixtral- and DeepSeek-V3-shaped, T = 512):
+# held to the required bounds as they are
+LITERAL_WORKLOADS = ("mixtral_512", "dsv3_512")
+
+
+def check_workload(out_rows, ref32, name, x, logits, wgu, wd, cfg, tokens=None, what=None):
+    """A workload-shaped output (the rows of ``tokens``, all when None)
+    against the oracle: rel-Frobenius <= 1e-2, and every element within
+    2e-2 * RMS or within its format floor plus the slack where the bf16
+    formats alone cannot reach that; the two target workloads must also meet
+    2e-2 * RMS outright.  Returns (rel-Frobenius, max-abs / RMS, the
+    format-exact best max-abs / RMS)."""
+    what = what or name
+    rel, plain = errors(out_rows, ref32)
+    fl, best = format_floor(x, logits, wgu, wd, cfg.top_k, cfg.score, cfg.renormalize, ref32,
+                            tokens=tokens, with_best=True)
+    print(f"{what}: rel-Frobenius {rel:.3e}, max-abs/RMS {plain:.4e} "
+          f"(format-exact best {best:.4e})", flush=True)
+    check_out(out_rows, ref32, what, floor=fl)
+    if name in LITERAL_WORKLOADS:
+        check_out(out_rows, ref32, what)
+    return rel, plain, best
+
+
+def check_out(out_bf16_rows, ref32, what="", floor=None):
+    """Asserts the output tolerance against the oracle's fp32 result:
+    rel-Frobenius <= REL_FRO_TOL and every element within MAX_ABS_TOL * RMS,
+    or -- given ``floor``, for inputs or paths whose data formats cannot
+    meet that -- within its own format floor plus FLOOR_EPS * max(RMS, row
+    RMS) where that is larger.  Workload-shaped tests pass no floor: the required bounds
+    apply as they are."""
+    rel_fro, max_abs = errors(out_bf16_rows, ref32, floor)
     assert np.all(np.isfinite(out_bf16_rows.float().cpu().numpy())), f"{what}: non-finite output"
-    assert rel_fro <= REL_FRO_TOL * scale, f"{what}: rel-Frobenius {rel_fro:.3e}"
-    assert max_abs <= MAX_ABS_TOL * scale, f"{what}: max-abs/RMS {max_abs:.3e}"
+    assert rel_fro <= REL_FRO_TOL, f"{what}: rel-Frobenius {rel_fro:.3e}"
+    assert max_abs <= MAX_ABS_TOL, f"{what}: max-abs/RMS {max_abs:.3e}" + \
+        (" (scaled to the per-element floor bound)" if floor is not None else "")
     return rel_fro, max_abs

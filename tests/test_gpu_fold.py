@@ -106,13 +106,11 @@ def test_fold_hot_expert_many_blocks():
 @pytest.mark.parametrize("name", ["tiny", "mixtral_512", "dsv3_512", "skewed_512"])
 def test_fold_full_size(name):
     """Workload sizes with automatic options: every token equal to the
-    separate combination; a token sample against the oracle."""
+    separate combination, and every token against the oracle."""
     cfg = synth.CONFIGS[name]
     x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)
     out = _fold_matches_separate(x, lg, wgu, wd, cfg.top_k, cfg.renormalize, cfg.score, name)
-    rng = np.random.default_rng(len(name) + 7)
-    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 6, replace=False)]))
-    ref = parity.oracle_out(x, lg, wgu, wd, cfg.top_k, cfg.score, cfg.renormalize, tokens=toks)
-    parity.check_out(out[torch.from_numpy(toks).long().to(DEV)], ref, name + " fold")
+    ref = parity.workload_reference(name, x, lg, wgu, wd, cfg)
+    parity.check_workload(out, ref, name, x, lg, wgu, wd, cfg, what=name + " fold")
     del x, lg, wgu, wd, out
     torch.cuda.empty_cache()

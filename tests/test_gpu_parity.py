@@ -2,11 +2,11 @@
 same seeded inputs.
 
 Routing artefacts must match bit for bit at every size, including the full
-workload sizes.  The bf16 output must meet the tolerance of tests/parity.py:
-on every token for shapes the oracle finishes in seconds (several tiles and
+workload sizes.  The bf16 output must meet the tolerance of tests/parity.py
+on every token: for shapes the oracle finishes in seconds (several tiles and
 ragged tails in every dimension, every compiled block size and several
-splits of the down projection), and on sampled tokens at the full workload
-sizes in the launch configuration the benchmark times.
+splits of the down projection) and at the full workload sizes in the launch
+configuration the benchmark times.
 """
 import numpy as np
 import pytest
@@ -232,7 +232,8 @@ def test_forward_unfused_swiglu_ablation(bm, gather):
     cfg, x, lg, wgu, wd, ref = _mid_case()
     out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm, gather_mode=gather,
                           unfused_swiglu=1)
-    parity.check_out(out, ref, f"unfused bm={bm} gather={gather}", scale=parity.UNFUSED_SCALE)
+    fl = parity.format_floor(x, lg, wgu, wd, 3, 0, True, ref, rounding="unfused")
+    parity.check_out(out, ref, f"unfused bm={bm} gather={gather}", floor=fl)
 
 
 @pytest.mark.parametrize("xcd", [1, 2, 3])
@@ -293,33 +294,38 @@ FULL = ["mixtral_128", "mixtral_256", "mixtral_512", "qwen2_128", "qwen2_256", "
         "skewed_128", "skewed_256", "skewed_512", "dsv3_512", "dsv3_4096"]
 
 
-@pytest.mark.parametrize("name", ["mixtral_512", "dsv3_512", "qwen2_128"])
-def test_forward_unfused_full_size_sampled(name):
-    """The unfused ablation at full workload sizes, as the benchmark runs it."""
+@pytest.mark.parametrize("name", ["mixtral_512", "qwen2_512", "dsv3_512"])
+def test_forward_unfused_full_size_every_token(name):
+    """The unfused ablation at full workload sizes, as the benchmark runs it,
+    every token against the oracle; its bf16 gate and up products put it
+    under its format floor (tests/format_model.py)."""
     cfg = synth.CONFIGS[name]
     x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)
     out = moe.moe_forward(x, lg, wgu, wd, cfg.top_k, cfg.renormalize, score=cfg.score,
                           unfused_swiglu=1)
-    rng = np.random.default_rng(len(name) + 1)
-    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 4, replace=False)]))
-    ref = parity.oracle_out(x, lg, wgu, wd, cfg.top_k, cfg.score, cfg.renormalize, tokens=toks)
-    parity.check_out(out[torch.from_numpy(toks).long().to(DEV)], ref, name + " unfused",
-                     scale=parity.UNFUSED_SCALE)
+    ref = parity.workload_reference(name, x, lg, wgu, wd, cfg)
+    fl = parity.format_floor(x, lg, wgu, wd, cfg.top_k, cfg.score, cfg.renormalize, ref,
+                             rounding="unfused")
+    parity.check_out(out, ref, name + " unfused", floor=fl)
     del x, lg, wgu, wd, out
     torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_forward_full_size_sampled(name):
-    """Full workload sizes, automatic options (what the benchmark runs);
-    the oracle evaluates a sample of tokens one by one."""
+def test_forward_full_size_every_token(name):
+    """Full workload sizes, automatic options (what the benchmark runs):
+    every token's output against the oracle.  rel-Frobenius <= 1e-2; every
+    element within 2e-2 * RMS, or within its format floor plus the slack
+    where the bf16 formats alone cannot reach that (tests/format_model.py:
+    Qwen2-shaped rows under unrenormalised softmax reach 7x the RMS, and
+    there exact arithmetic rounded to bf16 already errs by more).  The
+    Mixtral- and DeepSeek-V3-shaped T=512 workloads must meet 2e-2 * RMS
+    outright.  The plain max-abs and the format-exact best are printed."""
     cfg = synth.CONFIGS[name]
     x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)
     out = moe.moe_forward(x, lg, wgu, wd, cfg.top_k, cfg.renormalize, score=cfg.score)
-    rng = np.random.default_rng(len(name))
-    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 6, replace=False)]))
-    ref = parity.oracle_out(x, lg, wgu, wd, cfg.top_k, cfg.score, cfg.renormalize, tokens=toks)
-    parity.check_out(out[torch.from_numpy(toks).long().to(DEV)], ref, name)
+    ref = parity.workload_reference(name, x, lg, wgu, wd, cfg)
+    parity.check_workload(out, ref, name, x, lg, wgu, wd, cfg)
     del x, lg, wgu, wd, out
     torch.cuda.empty_cache()
 
@@ -337,26 +343,31 @@ def test_forward_maximum_experts_and_topk():
 def test_forward_one_workgroup_routing_at_its_limit():
     """T = 1024 tokens, E = 32, top_k = 16 through the one-workgroup routing
     kernel (its largest problem), every token against the oracle.  Rows whose
-    weight is dominated by one expert reach 6.6x the output RMS; an exact
-    computation carrying only the bf16 roundings of h and of the output
-    already errs by 2.27e-2 * RMS there, so max-abs is taken beyond each
-    element's own bf16 rounding (parity.check_out)."""
+    weight is dominated by one expert reach several times the output RMS,
+    where exact arithmetic carrying only the bf16 roundings of h and of the
+    output already misses 2e-2 * RMS (tests/test_format_floor.py): the
+    elements are held to their format floor where that is larger."""
     cfg, x, lg, wgu, wd = parity.make_case(1024, 128, 384, 32, 16, seed=78)
     out = moe.moe_forward(x, lg, wgu, wd, 16, True, routing_kernels=1)
-    parity.check_out(out, parity.oracle_out(x, lg, wgu, wd, 16, 0, True), "T=1024 E=32 k=16",
-                     beyond_format=True)
+    ref = parity.oracle_out(x, lg, wgu, wd, 16, 0, True)
+    parity.check_out(out, ref, "T=1024 E=32 k=16",
+                     floor=parity.format_floor(x, lg, wgu, wd, 16, 0, True, ref))
 
 
 def test_forward_maximum_rows():
     """T * top_k = MOE_MAX_ROWS (2^20 routed rows): routing bit for bit
-    against the oracle, and a sample of tokens' outputs."""
+    against the oracle, and the outputs of the tokens that hold the first and
+    last row of every schedule block (every block of both GEMMs), held to
+    their format floor where top-16 rows make the required bound out of
+    reach of the format."""
     T, k = (1 << 20) // 16, 16
     cfg, x, lg, wgu, wd = parity.make_case(T, 64, 384, 64, k, seed=79)
     out = moe.moe_forward(x, lg, wgu, wd, k, True)
     r = moe.moe_route(lg, k, True, 0)
     parity.check_routing(r, parity.oracle_routing(lg, k, 0, True, r["bm"]))
-    toks = np.unique(np.concatenate([[0, T - 1], np.random.default_rng(5).choice(T, 6, replace=False)]))
+    toks = parity.tokens_per_block(lg, k, 0, True, r["bm"])
     ref = parity.oracle_out(x, lg, wgu, wd, k, 0, True, tokens=toks)
-    parity.check_out(out[torch.from_numpy(toks).long().to(DEV)], ref, "max rows")
+    fl = parity.format_floor(x, lg, wgu, wd, k, 0, True, ref, tokens=toks)
+    parity.check_out(out[torch.from_numpy(toks).long().to(DEV)], ref, "max rows", floor=fl)
     del x, lg, wgu, wd, out, r
     torch.cuda.empty_cache()

@@ -2,15 +2,16 @@
 routing paths drawn from a fixed seed, each checked against the oracle
 (routing bit for bit, output within the tolerance).
 
-The draws include unrenormalised softmax over up to 100 experts, whose rows
-differ widely in scale: single elements reach 8x the output RMS, where the
-bf16 output format alone errs by up to 3e-2 * RMS.  The max-abs bound is
-therefore applied beyond each element's own bf16 rounding (see
-parity.check_out).  ffn is drawn from 384..1024: with fewer ffn terms the
-bf16 rounding of the SwiGLU intermediate h (the down GEMM's operand) adds
-noise of the order of the bound itself -- an exact computation carrying just
-that rounding and the output's gives 2.9e-2 * RMS at ffn = 64, 1.9e-2 at
-ffn = 128, 1.5e-2 at ffn = 384 on these input distributions."""
+The draws leave the workloads' regimes on purpose: ffn down to 64,
+unrenormalised softmax over up to 256 experts (rows of very different
+scale), top-k up to 16, the unfused ablation.  There the bf16 formats of h
+(g and u in the ablation) and of the output alone can miss the required
+max-abs bound (tests/test_format_floor.py), so each element is held to the
+larger of that bound and its own format floor (tests/format_model.py: exact
+arithmetic with just those roundings) plus a small slack; the relative
+Frobenius bound applies as it is.  Every token is compared, except in the
+draws with many blocks, which compare the tokens holding the first and last
+row of every schedule block."""
 import numpy as np
 import pytest
 import torch
@@ -30,7 +31,7 @@ def _cases(n=24, seed=1234):
         k = int(rng.integers(1, min(E, 8) + 1))
         T = int(rng.choice([1, 3, 17, 64, 130, 257]))
         d = int(64 * rng.integers(2, 13))
-        F = int(128 * rng.integers(3, 9))
+        F = int(64 * rng.integers(1, 17))
         score = int(rng.integers(0, 2))
         renorm = bool(rng.integers(0, 2))
         opts = {}
@@ -48,6 +49,14 @@ def _cases(n=24, seed=1234):
     return out
 
 
+def _check(out, x, lg, wgu, wd, k, score, renorm, what, unfused=False, tokens=None):
+    ref = parity.oracle_out(x, lg, wgu, wd, k, score, renorm, tokens=tokens)
+    fl = parity.format_floor(x, lg, wgu, wd, k, score, renorm, ref, tokens=tokens,
+                             rounding="unfused" if unfused else "fused")
+    got = out if tokens is None else out[torch.from_numpy(tokens).long().to(out.device)]
+    parity.check_out(got, ref, what, floor=fl)
+
+
 @pytest.fixture(autouse=True)
 def _gpu():
     if not torch.cuda.is_available():
@@ -62,9 +71,7 @@ def test_random_problem(case):
     cfg, x, lg, wgu, wd = parity.make_case(T, d, F, E, k, score=score, renorm=renorm, seed=100 + i)
     out = moe.moe_forward(x, lg, wgu, wd, k, renorm, score="sigmoid" if score else "softmax",
                           **opts)
-    ref = parity.oracle_out(x, lg, wgu, wd, k, score, renorm)
-    parity.check_out(out, ref, f"case{i} T={T} d={d} F={F} E={E} k={k} {opts}",
-                     beyond_format=True)
+    _check(out, x, lg, wgu, wd, k, score, renorm, f"case{i} T={T} d={d} F={F} E={E} k={k} {opts}")
     r = moe.moe_route(lg, k, renorm, "sigmoid" if score else "softmax",
                       block_rows=opts.get("block_rows", 0),
                       routing_kernels=opts["routing_kernels"])
@@ -82,7 +89,7 @@ def _cases_new_options(n=16, seed=4321):
         k = int(rng.integers(1, min(E, 8) + 1))
         T = int(rng.choice([1, 3, 17, 64, 130, 257]))
         d = int(64 * rng.integers(2, 13))
-        F = int(128 * rng.integers(3, 9))
+        F = int(64 * rng.integers(1, 17))
         score = int(rng.integers(0, 2))
         renorm = bool(rng.integers(0, 2))
         opts = {"routing_kernels": 2 if E > 32 else int(rng.integers(0, 3)),
@@ -113,8 +120,7 @@ def test_random_problem_new_options(case):
     cfg, x, lg, wgu, wd = parity.make_case(T, d, F, E, k, score=score, renorm=renorm, seed=500 + i)
     out = moe.moe_forward(x, lg, wgu, wd, k, renorm, score="sigmoid" if score else "softmax",
                           **opts)
-    ref = parity.oracle_out(x, lg, wgu, wd, k, score, renorm)
-    parity.check_out(out, ref, f"opt{i} T={T} d={d} F={F} E={E} k={k} {opts}", beyond_format=True)
+    _check(out, x, lg, wgu, wd, k, score, renorm, f"opt{i} T={T} d={d} F={F} E={E} k={k} {opts}")
 
 
 def _cases_lds_tiles(n=16, seed=2468):
@@ -153,8 +159,7 @@ def test_random_problem_lds_tiles(case):
     cfg, x, lg, wgu, wd = parity.make_case(T, d, F, E, k, score=score, renorm=renorm, seed=900 + i)
     out = moe.moe_forward(x, lg, wgu, wd, k, renorm, score="sigmoid" if score else "softmax",
                           **opts)
-    ref = parity.oracle_out(x, lg, wgu, wd, k, score, renorm)
-    parity.check_out(out, ref, f"lds{i} T={T} d={d} F={F} E={E} k={k} {opts}", beyond_format=True)
+    _check(out, x, lg, wgu, wd, k, score, renorm, f"lds{i} T={T} d={d} F={F} E={E} k={k} {opts}")
     r = moe.moe_route(lg, k, renorm, "sigmoid" if score else "softmax", block_rows=opts["block_rows"],
                       routing_kernels=opts["routing_kernels"])
     parity.check_routing(r, parity.oracle_routing(lg, k, score, renorm, r["bm"]))
@@ -163,7 +168,8 @@ def test_random_problem_lds_tiles(case):
 def _cases_many_blocks(n=12, seed=97531):
     """Larger draws (many schedule blocks: the automatic XCD order, the
     two-launch routing at larger A, several blocks per expert), every
-    option drawn; the oracle checks a sample of tokens."""
+    option drawn; the oracle checks the tokens of every block's first and
+    last row."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -197,15 +203,13 @@ def test_random_problem_many_blocks(case):
                                            seed=1300 + i)
     out = moe.moe_forward(x, lg, wgu, wd, k, renorm, score="sigmoid" if score else "softmax",
                           **opts)
-    rng = np.random.default_rng(i)
-    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 62, replace=False)]))
-    ref = parity.oracle_out(x, lg, wgu, wd, k, score, renorm, tokens=toks)
-    got = out[torch.from_numpy(toks).long().to(out.device)]
-    parity.check_out(got, ref, f"big{i} T={T} d={d} F={F} E={E} k={k} {opts}", beyond_format=True)
     r = moe.moe_route(lg, k, renorm, "sigmoid" if score else "softmax",
                       block_rows=opts.get("block_rows", 0),
                       routing_kernels=opts["routing_kernels"])
     parity.check_routing(r, parity.oracle_routing(lg, k, score, renorm, r["bm"]))
+    toks = parity.tokens_per_block(lg, k, score, renorm, r["bm"])
+    _check(out, x, lg, wgu, wd, k, score, renorm, f"big{i} T={T} d={d} F={F} E={E} k={k} {opts}",
+           tokens=toks)
 
 
 def _cases_all_options(n=60, seed=31337):
@@ -214,7 +218,7 @@ def _cases_all_options(n=60, seed=31337):
     combination, fused down projection, unfused ablation), over shapes from
     one token to 1500 and from 1 to 256 experts with top-k up to 16.  Option
     sets the library refuses up front are left out; the rest must meet the
-    tolerance (the unfused ablation its wider one)."""
+    tolerance (held to the ablation's own format floor where it runs)."""
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
@@ -252,11 +256,5 @@ def test_random_problem_all_options(case):
                                            seed=2000 + i)
     out = moe.moe_forward(x, lg, wgu, wd, k, renorm, score="sigmoid" if score else "softmax",
                           **opts)
-    toks = None
-    if T > 300:
-        rng = np.random.default_rng(i)
-        toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 40, replace=False)]))
-    ref = parity.oracle_out(x, lg, wgu, wd, k, score, renorm, tokens=toks)
-    got = out if toks is None else out[torch.from_numpy(toks).long().to(out.device)]
-    parity.check_out(got, ref, f"all{i} T={T} d={d} F={F} E={E} k={k} {opts}", beyond_format=True,
-                     scale=parity.UNFUSED_SCALE if opts.get("unfused_swiglu") else 1.0)
+    _check(out, x, lg, wgu, wd, k, score, renorm, f"all{i} T={T} d={d} F={F} E={E} k={k} {opts}",
+           unfused=bool(opts.get("unfused_swiglu")))

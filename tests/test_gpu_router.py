@@ -92,9 +92,14 @@ def test_router_scores_deterministic_and_stream():
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
-@pytest.mark.parametrize("name,sample", [("tiny", None), ("mixtral_512", 6), ("qwen2_128", 6),
-                                         ("dsv3_512", 4), ("dsv3_4096", 4)])
-def test_forward_from_hidden_states(name, sample):
+@pytest.mark.parametrize("name,per_block", [("tiny", False), ("mixtral_512", False),
+                                            ("qwen2_128", False), ("dsv3_512", False),
+                                            ("dsv3_4096", True)])
+def test_forward_from_hidden_states(name, per_block):
+    """The forward pass from hidden states at workload sizes: every token
+    against the oracle on the same scores (DeepSeek-V3 T=4096: the tokens
+    holding the first and last row of every schedule block, so every block
+    of both GEMMs is compared)."""
     cfg = synth.CONFIGS[name]
     x = synth.make_x(cfg, 0, DEV)
     wr = synth.make_router_weight(cfg, 0, DEV)
@@ -111,12 +116,13 @@ def test_forward_from_hidden_states(name, sample):
     assert torch.equal(out.view(torch.int16), ref_path.view(torch.int16))
     # and meets the forward tolerance against the oracle on the same scores
     toks = None
-    if sample:
-        rng = np.random.default_rng(7)
-        toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, sample, replace=False)]))
+    if per_block:
+        bm, _ = moe.moe_plan(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k)
+        toks = parity.tokens_per_block(logits, cfg.top_k, cfg.score, cfg.renormalize, bm)
     ref = parity.oracle_out(x, logits, wgu, wd, cfg.top_k, cfg.score, cfg.renormalize, tokens=toks)
     got = out if toks is None else out[torch.from_numpy(toks).long().to(DEV)]
-    parity.check_out(got, ref, name)
+    parity.check_workload(got, ref, name, x, logits, wgu, wd, cfg, tokens=toks,
+                          what=name + " from hidden states")
     del x, wr, wgu, wd, out
     torch.cuda.empty_cache()
 
