@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     MOE_SCORE_SIGMOID,
     MOE_SCORE_SOFTMAX,
+    MOE_STATIC_WORKSPACE_BYTES,
     SIGNATURES,
     MoeError,
     MoeOptions,
@@ -18,6 +19,7 @@ from ._lib import (  # noqa: F401
     moe_abi_version,
     moe_forward,
     moe_forward_router,
+    moe_forward_static,
     moe_plan,
     moe_plan_ex,
     moe_route,

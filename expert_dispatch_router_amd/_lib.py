@@ -23,7 +23,8 @@ MOE_SCORE_SIGMOID = 1
 MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_TOPK",
           -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_UNSUPPORTED",
-          -7: "MOE_ERR_HIP"}
+          -7: "MOE_ERR_HIP", -8: "MOE_ERR_STATIC_LIMIT"}
+MOE_STATIC_WORKSPACE_BYTES = 256 << 20  # include/moe.h
 
 # Every symbol include/moe.h declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -38,6 +39,7 @@ SIGNATURES = {
                       ctypes.POINTER(_I)]),
     "moe_forward": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _SZ, _P]),
     "moe_forward_ex": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P]),
+    "moe_forward_static": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _I, _P]),
     "moe_router_logits": (_I, [_P, _P, _P, _I, _I, _I, _P, _SZ, _P]),
     "moe_router_workspace_size": (_I, [_I, _I, _I, ctypes.POINTER(_SZ)]),
     "moe_forward_router": (_I, [_P, _P, _P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _I, _P, _P, _SZ,
@@ -253,6 +255,31 @@ def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=Non
         _stream_ptr(stream, x.device))
     del keep
     _check("moe_forward_ex", rc)
+    return out
+
+
+def moe_forward_static(x, router_logits, W_gate_up, W_down, top_k, renormalize, out,
+                       score="softmax", stream=None):
+    """moe_forward with the library's own fixed device workspace (no device
+    memory allocated by the call; the caller passes ``out``, bf16 [T, d]).
+    Calls on one GPU must not overlap (they share its workspace array)."""
+    T, d = x.shape
+    E = router_logits.shape[1]
+    F = W_down.shape[2]
+    if router_logits.shape[0] != T or tuple(W_gate_up.shape) != (E, 2 * F, d) or \
+            tuple(W_down.shape) != (E, d, F):
+        raise ValueError("inconsistent shapes")
+    if out is None:
+        raise ValueError("out is required: this entry point allocates nothing")
+    _check_out(out, (T, d))
+    _same_device([("x", x), ("router_logits", router_logits), ("W_gate_up", W_gate_up),
+                  ("W_down", W_down), ("out", out)])
+    rc = lib().moe_forward_static(
+        _dev_ptr(x, torch.bfloat16, "x"), _dev_ptr(router_logits, torch.float32, "router_logits"),
+        _dev_ptr(W_gate_up, torch.bfloat16, "W_gate_up"), _dev_ptr(W_down, torch.bfloat16, "W_down"),
+        int(top_k), int(bool(renormalize)), _dev_ptr(out, torch.bfloat16, "out"),
+        T, d, F, E, _score_code(score), _stream_ptr(stream, x.device))
+    _check("moe_forward_static", rc)
     return out
 
 

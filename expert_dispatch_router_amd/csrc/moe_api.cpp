@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "moe_internal.hpp"
@@ -482,6 +483,36 @@ int forward_from_logits(const uint16_t* x, const LogitSrc& router_logits, const 
   return MOE_OK;
 }
 
+// The workspace of moe_forward_static: a fixed device array, one per GPU
+// (each device holds its own copy of a __device__ variable).  In host code
+// `scratch` names a host-side stand-in, not device memory: kernels get the
+// address hipGetSymbolAddress returns for the current device, kept per
+// device below.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// Address of this device's array: looked up once per device, with that
+// device current (restored afterwards).
+int static_workspace(int device, void** ptr) {
+  if (device < 0 || device >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[device]) {
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) return MOE_ERR_HIP;
+    if (prev != device && hipSetDevice(device) != hipSuccess) return MOE_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t rc = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (prev != device) (void)hipSetDevice(prev);
+    if (rc != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return MOE_OK;
+}
+
 // Size checks of the router scores alone (x [T, d], W_r [E, d]).
 int check_router_sizes(int T, int d, int E) {
   if (T < 0 || d < 1 || E < 1) return MOE_ERR_SHAPE;
@@ -511,6 +542,8 @@ const char* moe_status_string(int status) {
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_UNSUPPORTED: return "outside the library's limits or an unsupported option";
     case MOE_ERR_HIP: return "a HIP call failed";
+    case MOE_ERR_STATIC_LIMIT:
+      return "the problem needs more workspace than the static array (MOE_STATIC_WORKSPACE_BYTES)";
     default: return "unknown status";
   }
 }
@@ -695,6 +728,32 @@ int moe_forward(const uint16_t* x, const float* router_logits, const uint16_t* W
                 void* hip_stream) {
   return moe_forward_ex(x, router_logits, W_gate_up, W_down, top_k, renormalize, out, T, d, ffn,
                         E, score_func, nullptr, workspace, workspace_bytes, hip_stream);
+}
+
+int moe_forward_static(const uint16_t* x, const float* router_logits, const uint16_t* W_gate_up,
+                       const uint16_t* W_down, int top_k, int renormalize, uint16_t* out, int T,
+                       int d, int ffn, int E, int score_func, void* hip_stream) {
+  MOE_TRY(check_sizes(T, d, ffn, E, top_k, true));
+  if (score_func != MOE_SCORE_SOFTMAX && score_func != MOE_SCORE_SIGMOID)
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!x || !router_logits || !W_gate_up || !W_down || !out) return MOE_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(router_logits, 16) || !aligned(W_gate_up, 16) ||
+      !aligned(W_down, 16) || !aligned(out, 16))
+    return MOE_ERR_ALIGN;
+  Plan p;
+  make_plan(T, d, ffn, E, top_k, nullptr, &p);
+  MOE_TRY(p.plan_error);
+  if (p.total_bytes > (size_t)MOE_STATIC_WORKSPACE_BYTES) return MOE_ERR_STATIC_LIMIT;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  int device = -1;
+  if (s ? hipStreamGetDevice(s, &device) != hipSuccess : hipGetDevice(&device) != hipSuccess)
+    return MOE_ERR_HIP;
+  void* ws = nullptr;
+  MOE_TRY(static_workspace(device, &ws));
+  (void)hipGetLastError();
+  return forward_from_logits(x, LogitSrc{router_logits, 1, 0, nullptr}, W_gate_up, W_down, top_k,
+                             renormalize ? 1 : 0, out, score_func, p, nullptr, ws, s);
 }
 
 int moe_route(const float* router_logits, int T, int E, int top_k, int renormalize,

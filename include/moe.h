@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 /* Limits of the library (violations return MOE_ERR_UNSUPPORTED). */
 #define MOE_MAX_EXPERTS 512
@@ -66,8 +66,14 @@ enum moe_status {
                                  not 16-byte aligned (workspace: 256)       */
     MOE_ERR_WORKSPACE = -5,   /* workspace smaller than the size query      */
     MOE_ERR_UNSUPPORTED = -6, /* beyond the library limits, bad option      */
-    MOE_ERR_HIP = -7          /* a HIP launch or record call failed         */
+    MOE_ERR_HIP = -7,         /* a HIP launch or record call failed         */
+    MOE_ERR_STATIC_LIMIT = -8 /* moe_forward_static: the problem needs more
+                                 than MOE_STATIC_WORKSPACE_BYTES of workspace */
 };
+
+/* Size of the device array moe_forward_static uses as its workspace (one
+ * array per GPU the library runs on, held until the process ends). */
+#define MOE_STATIC_WORKSPACE_BYTES (256u << 20)
 
 /* Optional knobs of moe_forward_ex / moe_route.  Zero-initialise for the
  * automatic choices. */
@@ -265,6 +271,32 @@ int moe_forward(const uint16_t *x, const float *router_logits, const uint16_t *W
                 const uint16_t *W_down, int top_k, int renormalize, uint16_t *out,
                 int T, int d, int ffn, int E, int score_func,
                 void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results as moe_forward with the automatic options,
+ * with the workspace taken from a fixed device array inside the library
+ * (MOE_STATIC_WORKSPACE_BYTES, one per GPU) instead of a caller's buffer.
+ * Nothing is allocated or freed by this call.
+ *
+ * Arguments, layouts, ownership and checks as moe_forward (the caller still
+ * passes x, router_logits, the weights and out).  The array belongs to the
+ * GPU of hip_stream (the current device for a NULL stream); its address is
+ * looked up once per GPU, on the first call there.
+ *
+ * Errors: as moe_forward, plus MOE_ERR_STATIC_LIMIT (nothing enqueued) when
+ * moe_workspace_size for these sizes exceeds MOE_STATIC_WORKSPACE_BYTES --
+ * Mixtral-shaped T <= 512 and DeepSeek-V3-shaped T <= 512 fit; and
+ * MOE_ERR_HIP when the device or the array's address cannot be obtained.
+ *
+ * Every call on one GPU shares that GPU's array, and each call leaves its
+ * own intermediates there: calls on one GPU must be ordered (one stream, or
+ * streams synchronised with each other); calls that overlap race on the
+ * array and give wrong results.  The array starts with no contract: the
+ * kernels write every byte they read within a call. */
+int moe_forward_static(const uint16_t *x, const float *router_logits, const uint16_t *W_gate_up,
+                       const uint16_t *W_down, int top_k, int renormalize, uint16_t *out,
+                       int T, int d, int ffn, int E, int score_func, void *hip_stream);
 
 /* moe_forward with options (NULL = automatic, identical to moe_forward).
  * The workspace must hold moe_workspace_size_ex(..., opt, ...) bytes. */

@@ -417,3 +417,41 @@ def test_plan_ex_reports_the_launches():
     assert moe.lib().moe_plan_ex(4, 64, 64, 4, 2, None, None) == NULL
     with pytest.raises(moe.MoeError):
         moe.moe_plan_ex(4, 96, 64, 4, 2)
+
+
+def test_forward_static_host_checks():
+    """moe_forward_static rejects, before any HIP call, problems whose
+    workspace exceeds the static array (MOE_ERR_STATIC_LIMIT) and the same
+    bad arguments as moe_forward; the binding's constant is the header's."""
+    hdr = open(HEADER).read()
+    want = int(re.search(r"#define\s+MOE_STATIC_WORKSPACE_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)",
+                         hdr).group(1))
+    shift = int(re.search(r"#define\s+MOE_STATIC_WORKSPACE_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)",
+                          hdr).group(2))
+    assert _lib.MOE_STATIC_WORKSPACE_BYTES == want << shift
+    L = moe.lib()
+    P = 4096  # aligned stand-ins: every call below fails a host check first
+    big = CONFIGS["dsv3_4096"]
+    assert moe.moe_workspace_size(big.T, big.d, big.ffn, big.E, big.top_k) > \
+        _lib.MOE_STATIC_WORKSPACE_BYTES
+    assert L.moe_forward_static(P, P, P, P, big.top_k, 1, P, big.T, big.d, big.ffn, big.E, 1,
+                                None) == -8
+    assert "static" in moe.status_string(-8)
+    mix = CONFIGS["mixtral_512"]
+    assert moe.moe_workspace_size(mix.T, mix.d, mix.ffn, mix.E, mix.top_k) <= \
+        _lib.MOE_STATIC_WORKSPACE_BYTES
+    dsv = CONFIGS["dsv3_512"]
+    assert moe.moe_workspace_size(dsv.T, dsv.d, dsv.ffn, dsv.E, dsv.top_k) <= \
+        _lib.MOE_STATIC_WORKSPACE_BYTES
+    assert L.moe_forward_static(None, P, P, P, 2, 1, P, 64, 256, 512, 8, 0, None) == NULL
+    assert L.moe_forward_static(P, P, P, P, 2, 1, None, 64, 256, 512, 8, 0, None) == NULL
+    assert L.moe_forward_static(P + 8, P, P, P, 2, 1, P, 64, 256, 512, 8, 0, None) == ALIGN
+    assert L.moe_forward_static(P, P, P, P, 9, 1, P, 64, 256, 512, 8, 0, None) == TOPK
+    assert L.moe_forward_static(P, P, P, P, 2, 1, P, 64, 96, 512, 8, 0, None) == ALIGN
+    assert L.moe_forward_static(P, P, P, P, 2, 1, P, 64, 256, 512, 8, 7, None) == UNSUP
+    assert L.moe_forward_static(None, None, None, None, 2, 1, None, 0, 256, 512, 8, 0, None) == OK
+    import torch
+    with pytest.raises(ValueError, match="out is required"):
+        moe.moe_forward_static(torch.zeros(4, 64, dtype=torch.bfloat16), torch.zeros(4, 4),
+                               torch.zeros(4, 128, 64, dtype=torch.bfloat16),
+                               torch.zeros(4, 64, 64, dtype=torch.bfloat16), 2, True, None)
