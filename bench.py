@@ -26,7 +26,8 @@ workload on this host's cores, with the CPU model, input hashes and a
 one-core figure on the tiny workload.
 
 Other modes (not used by the default run):
-  --profile            no CPU baseline, no other workloads (for rocprofv3 runs)
+  --profile            no CPU baseline, no other workloads, no cache-flushed or
+                       hot-expert passes (for rocprofv3 runs)
   --copy-bytes N       also run one plain N-byte device copy per step (the
                        calibration kernel of the HBM byte counters)
   --traffic FETCH_DIR WRITE_DIR
@@ -370,6 +371,40 @@ class Runner:
         return r["counts"].cpu().numpy()
 
 
+def hot_experts(r, counts, steps, n_hot=4):
+    """The full-tile regime of skewed routing on its own: the same tokens,
+    weights and top-k, with every token routed to the n_hot experts the
+    workload's routing loads most (each then holds T rows: full blocks).
+    The fused gate/up GEMM's FLOPs over its mean duration (two events around
+    it, as in the timed passes) against the bf16 dense MFMA peak."""
+    import numpy as np
+    import torch
+
+    import expert_dispatch_router_amd as moe
+
+    cfg = r.cfg
+    hot = [int(e) for e in np.argsort(-counts, kind="stable")[:n_hot]]
+    lg = r.logits.clone()
+    lg[:, hot] += 40.0  # far above the N(0, 1) scores and the skew biases
+    k = cfg.top_k
+    f = lambda se=None: moe.moe_forward(r.x, lg, r.wgu, r.wd, k, cfg.renormalize, out=r.out,
+                                        score=cfg.score, workspace=r.ws, stage_events=se)
+    for _ in range(5):
+        f()
+    ev = [(moe.Timer(), moe.Timer()) for _ in range(steps)]
+    for a, b in ev:
+        f([None, None, None, a.handle, b.handle, None, None])
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_ms(b) for a, b in ev]))
+    rows = cfg.T * min(k, n_hot)
+    flop = 4.0 * rows * cfg.ffn * cfg.d
+    return {"experts": hot, "rows_per_expert": cfg.T, "gate_up_mean_ms": ms,
+            "gate_up_tflops": flop / (ms * 1e-3) / 1e12,
+            "mfma_frac": flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "note": f"every token routed to the {n_hot} experts the workload loads most "
+                    "(full 128-row blocks); gate/up GEMM FLOPs over its mean duration"}
+
+
 def pct(v):
     import numpy as np
 
@@ -511,12 +546,16 @@ def run(args):
                        "timing": "stage events of the stage-breakdown passes",
                        "achieved_gbs": dn_bytes / (k5_ms * 1e-3) / 1e9,
                        "frac": dn_bytes / (k5_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    if args.flush or (args.flush is None and alg["e_act"] * 6.0 * cfg.ffn * cfg.d < (1 << 30)):
+    if args.flush or (args.flush is None and not args.profile and
+                      alg["e_act"] * 6.0 * cfg.ffn * cfg.d < (1 << 30)):
         med, p10, p90 = r.flushed(args.steps)
         res["cache_flushed"] = {
             "ms_per_pass_p50": med, "p10": p10, "p90": p90, "roofline_frac": t_roof / (med * 1e-3),
             "protocol": f"{args.steps} reps after 3 warm-ups, a 1 GiB write before each rep "
                         "outside the timed interval (first to last stage event)"}
+    if cfg.skew_alpha > 0 and not args.profile:
+        res["hot_experts"] = hot_experts(r, r.routing_counts(), args.steps,
+                                         n_hot=min(cfg.top_k, 4))
     res["router_gemm"] = router_gemm(cfg, r.x, args.seed, args.steps, r.stream)
     if args.graph:
         res["graph"] = graph_replay(lambda strm=None: r.step(strm=strm), args.steps, cfg.T)

@@ -207,15 +207,17 @@ void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < NWT; ++j) acc[g][mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K-step order: with `rotate` (1: per block, 2: per workgroup), a
-  // workgroup starts its reduction at a step derived from its block b (or
-  // its own id) and wraps around.  Workgroups walking K in lockstep address
-  // the same memory channels at once -- weight rows 2^n bytes apart share
-  // their low address bits -- and different starting steps spread them.
-  // Per block, the column tiles of one block still read the same activation
-  // K-slice at the same time (shared in L2); per workgroup spreads further.
-  // The order is fixed by (block, tile): results stay deterministic.
-  const unsigned rkey = rotate == 2 ? (unsigned)wg : (unsigned)b;
+  // K-step order: with `rotate` (1: per block, 2: per workgroup, 3: per
+  // expert), a workgroup starts its reduction at a step derived from its
+  // block b (its own id, its expert e) and wraps around.  Workgroups walking
+  // K in lockstep address the same memory channels at once -- weight rows
+  // 2^n bytes apart share their low address bits -- and different starting
+  // steps spread them.  Per block, the column tiles of one block still read
+  // the same activation K-slice at the same time (shared in L2); per expert,
+  // the blocks of one expert also read the same weights at the same time;
+  // per workgroup spreads further.  The order is fixed by (block, tile):
+  // results stay deterministic.
+  const unsigned rkey = rotate == 2 ? (unsigned)wg : rotate == 3 ? (unsigned)e : (unsigned)b;
   const int shift = rotate ? (int)((rkey * 2654435761u) % (unsigned)max(nks, 1)) : 0;
   auto step_of = [&](int ks) {
     const int p = ks + shift;
@@ -686,7 +688,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     }
   }
 
-  const unsigned rkey = rotate == 2 ? (unsigned)wg : (unsigned)b;
+  const unsigned rkey = rotate == 2 ? (unsigned)wg : rotate == 3 ? (unsigned)e : (unsigned)b;
   const int shift = rotate ? (int)((rkey * 2654435761u) % (unsigned)max(nks, 1)) : 0;
   auto soff_of = [&](int ks) {
     const int kk = ks + shift;

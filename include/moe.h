@@ -116,9 +116,10 @@ typedef struct moe_options {
      * variants give the same bytes (the same per-output K order). */
     int down_variant;
     /* K-start rotation of the GEMMs: a workgroup starts its reduction at a
-     * step derived from its schedule block (2) or from its own id (3), and
-     * wraps around.  0 = automatic (per block), 1 = off.  Results are
-     * deterministic either way; rounding differs slightly. */
+     * step derived from its schedule block (2), from its own id (3) or from
+     * its expert (4), and wraps around.  0 = automatic (per expert), 1 =
+     * off.  Results are deterministic either way; rounding differs
+     * slightly. */
     int rotate;
     /* Routing kernels.  0 = automatic: one workgroup does the route,
      * histogram, scan, schedule and reorder when T <= 1024, E <= 32 and

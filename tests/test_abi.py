@@ -75,7 +75,7 @@ def _o(bm=0, split=0, variant=0, rotate=0, routing=0, gather=0, unfused=0, xcd=0
 
 
 def test_options_checks():
-    for bad in (_o(8), _o(0, 9), _o(0, -1), _o(0, 0, 1), _o(32, 0, 2), _o(64, 0, 3), _o(192, 0, 4), _o(0, 0, 0, 4),
+    for bad in (_o(8), _o(0, 9), _o(0, -1), _o(0, 0, 1), _o(32, 0, 2), _o(64, 0, 3), _o(192, 0, 4), _o(0, 0, 0, 5),
                 _o(0, 0, -1), _o(0, 0, 0, -1)):
         assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
     for bm in (16, 32, 64, 128, 192):

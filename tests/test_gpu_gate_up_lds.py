@@ -64,7 +64,7 @@ def test_lds_tile_matches_oracle_and_register_tile(name):
 
 
 @pytest.mark.parametrize("gather", [1, 2])
-@pytest.mark.parametrize("rotate", [1, 2, 3])
+@pytest.mark.parametrize("rotate", [1, 2, 3, 4])
 def test_lds_tile_gather_and_rotation(gather, rotate):
     x, lg, wgu, wd, k, ref = _case("ragged", *CASES["ragged"])
     out = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=192, tile_variant=LDS,
@@ -222,7 +222,7 @@ def test_lds_wide_down_matches_oracle_and_register_tile(name, bm, split):
 
 
 @pytest.mark.parametrize("xcd", [1, 2])
-@pytest.mark.parametrize("rotate", [1, 2, 3])
+@pytest.mark.parametrize("rotate", [1, 2, 3, 4])
 def test_lds_wide_down_orders_and_rotation(rotate, xcd):
     """Every K rotation and both workgroup orders: within the tolerance;
     without the per-workgroup rotation (whose start depends on the tiling)

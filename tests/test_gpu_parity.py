@@ -172,7 +172,7 @@ def test_forward_every_block_size_and_split(bm, split):
 
 
 @pytest.mark.parametrize("bm", ALL_BM)
-@pytest.mark.parametrize("rotate", [1, 2, 3])
+@pytest.mark.parametrize("rotate", [1, 2, 3, 4])
 def test_forward_rotation_on_and_off(bm, rotate):
     cfg, x, lg, wgu, wd, ref = _mid_case()
     out = moe.moe_forward(x, lg, wgu, wd, 3, True, score=0, block_rows=bm, split_k=2, rotate=rotate)
