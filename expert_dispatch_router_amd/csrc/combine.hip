@@ -21,22 +21,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       int A, int d,
                                                       const int32_t* __restrict__ inv,
                                                       const float* __restrict__ w, int k,
-                                                      int col_blocks, uint16_t* __restrict__ out) {
+                                                      int col_blocks, uint16_t* __restrict__ out,
+                                                      DynSplit dyn) {
   const int t = blockIdx.x / col_blocks;
   const int cb = blockIdx.x - t * col_blocks;
   const int c = (cb * 256 + threadIdx.x) * 4;
   if (c >= d) return;
-  combine_quad(y, split, A, d, inv, w, k, t, c, out, PlainLoad{});
+  // the parts the down GEMM of this call wrote (decided there from nb)
+  const int parts = dyn.nb ? device_down_split(dyn.nb[0], dyn.dn_tiles, split, dyn.ffn).parts
+                           : split;
+  combine_quad(y, parts, A, d, inv, w, k, t, c, out, PlainLoad{});
 }
 
 }  // namespace
 
 hipError_t launch_combine(const float* y, int split, int A, int d, const int32_t* inv,
-                          const float* w, int k, int T, uint16_t* out, hipStream_t s) {
+                          const float* w, int k, int T, uint16_t* out, hipStream_t s,
+                          DynSplit dyn) {
   const int col_blocks = (d / 4 + 255) / 256;
   const long long grid = (long long)col_blocks * T;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  combine_kernel<<<(unsigned)grid, 256, 0, s>>>(y, split, A, d, inv, w, k, col_blocks, out);
+  combine_kernel<<<(unsigned)grid, 256, 0, s>>>(y, split, A, d, inv, w, k, col_blocks, out, dyn);
   return hipGetLastError();
 }
 

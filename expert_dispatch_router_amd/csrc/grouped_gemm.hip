@@ -100,11 +100,21 @@ void grouped_gemm_kernel(
     void* __restrict__ out, int A, int N, int K, int ksplit,
     int tiles_per_block, int rotate, const int32_t* __restrict__ gather_perm, int gather_k,
     int x_rows, int xcd_group, int x_tiled, FoldCombine fold, const uint16_t* __restrict__ W2,
-    long long w2_estride, int N2) {
+    long long w2_estride, int N2, int dyn_split) {
   using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   constexpr int MT = G::kMT, NG = G::kNG, XPT = G::kXPerThread;
   static_assert(PF >= 2, "the activation stage is issued PF-1 steps ahead");
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kLdsStride];
+
+  // The split of the reduction: as launched (tiles_per_block = column tiles
+  // x parts, ksplit per part), or with dyn_split decided here from the
+  // routed block count (device_down_split; at most the launched parts).
+  const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
+  if (dyn_split) {
+    const DownSplit ds = device_down_split(nb_dev[0], n_tiles, tiles_per_block / n_tiles, K);
+    tiles_per_block = n_tiles * ds.parts;
+    ksplit = ds.ksplit;
+  }
 
   // Workgroup -> (block, tile).  Workgroups are dispatched to the XCDs
   // round-robin (workgroup i to XCD i % kXcds).  With xcd_group, the real
@@ -130,7 +140,6 @@ void grouped_gemm_kernel(
   const int rows = min(BM, offsets[e + 1] - r0);
   const int mt_act = (rows + 15) >> 4;
 
-  const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
   const int tile = rem % n_tiles;
   const int part = rem / n_tiles;
   const int kb = part * ksplit;
@@ -485,7 +494,7 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
                       int split, int ksplit, int nb_max, int rotate, const int32_t* gather_perm,
                       int gather_k, int x_rows, int xcd_group, int x_tiled,
                       const FoldCombine& fold, hipStream_t s, const uint16_t* W2 = nullptr,
-                      long long w2_estride = 0, int N2 = 0) {
+                      long long w2_estride = 0, int N2 = 0, int dyn_split = 0) {
   using G = Gemm<BM, NWT, WAVES, PF, MODE>;
   const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
   const int tiles_per_block = n_tiles * split;
@@ -496,7 +505,7 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   grouped_gemm_kernel<BM, NWT, WAVES, PF, MODE><<<(unsigned)grid, G::kThreads, 0, s>>>(
       X, W, w_estride, blocks, nb, order, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
-      gather_perm, gather_k, x_rows, xcd_group, x_tiled, fold, W2, w2_estride, N2);
+      gather_perm, gather_k, x_rows, xcd_group, x_tiled, fold, W2, w2_estride, N2, dyn_split);
   return hipGetLastError();
 }
 
@@ -601,12 +610,23 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
     const int32_t* __restrict__ order, const int32_t* __restrict__ offsets,
     void* __restrict__ out, int A, int N, int K, int ksplit, int tiles_per_block, int rotate,
-    const int32_t* __restrict__ gather_perm, int gather_k, int x_rows, int xcd_group) {
+    const int32_t* __restrict__ gather_perm, int gather_k, int x_rows, int xcd_group,
+    int dyn_split) {
   using G = LdsGemm<BM, WAVES, BK, STAGES, MODE>;
   constexpr int MT = G::kMT, KC = G::kKC, SB = G::kStageBytes, XPW = G::kXPerWave;
   constexpr int NG = G::kNG, GPW = G::kGPW;
   constexpr int LPG = G::kLoadsPerGroup, GB = G::kGroupBytes, RB = G::kRowBytes;
   __shared__ __attribute__((aligned(16))) uint8_t lds[STAGES * SB];
+
+  // The split of the reduction: as launched, or with dyn_split decided here
+  // from the routed block count (device_down_split; at most the launched
+  // parts).
+  const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;  // the last may be partial
+  if (dyn_split) {
+    const DownSplit ds = device_down_split(nb_dev[0], n_tiles, tiles_per_block / n_tiles, K);
+    tiles_per_block = n_tiles * ds.parts;
+    ksplit = ds.ksplit;
+  }
 
   int wg = blockIdx.x;
   if (xcd_group) {
@@ -623,7 +643,6 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
   }
   const int b = (!kDense && order) ? order[bi] : bi;
   const int rem = wg - bi * tiles_per_block;
-  const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;  // the last may be partial
   const int tile = rem % n_tiles;
   const int part = rem / n_tiles;
   const int kb = part * ksplit;
@@ -830,7 +849,8 @@ hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estr
                           const int32_t* blocks, const int32_t* nb, const int32_t* order,
                           const int32_t* offsets, void* out, int A, int N, int K, int split,
                           int ksplit, int nb_max, int rotate, const int32_t* gather_perm,
-                          int gather_k, int x_rows, int xcd_group, hipStream_t s) {
+                          int gather_k, int x_rows, int xcd_group, hipStream_t s,
+                          int dyn_split = 0) {
   using G = LdsGemm<BM, WAVES, kLdsBK, kLdsStages, MODE>;
   // whole 16-column subtiles and whole K steps
   if (N % 16 != 0 || K % kLdsBK != 0 || ksplit % kLdsBK != 0 || split < 1)
@@ -843,7 +863,7 @@ hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estr
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
   gemm_lds_kernel<BM, WAVES, kLdsBK, kLdsStages, MODE, WCPOL><<<(unsigned)grid, G::kThreads, 0, s>>>(
       X, W, w_estride, blocks, nb, order, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
-      gather_perm, gather_k, x_rows, xcd_group);
+      gather_perm, gather_k, x_rows, xcd_group, dyn_split);
   return hipGetLastError();
 }
 
@@ -937,7 +957,8 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
                        const int32_t* blocks, const int32_t* nb, const int32_t* order,
                        const int32_t* offsets, float* y,
                        int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
-                       int xcd_group, const FoldCombine& fold, hipStream_t s) {
+                       int xcd_group, const FoldCombine& fold, hipStream_t s, int dyn_split) {
+  if (dyn_split && fold.cnt) return hipErrorInvalidValue;  // the fold counts parts as launched
   if ((bm == 192 || bm == 128) && variant == kDownLdsVariant) {
     if (fold.cnt) return hipErrorInvalidValue;  // the fold runs in the register-ring tiles
     // Weights are read once.  Non-temporal weight loads measured faster on
@@ -949,7 +970,7 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
 #define MOE_DOWN_LDS(BMV, CP)                                                                    \
   return launch_lds_cfg<BMV, 8, kOutF32Parts, CP>(h, w_down, (long long)d * ffn, blocks, nb, order, \
                                                   offsets, y, A, d, ffn, split, ksplit, nb_max,   \
-                                                  rotate, nullptr, 1, A, xcd_group, s)
+                                                  rotate, nullptr, 1, A, xcd_group, s, dyn_split)
     if (bm == 192) {
       if (nt) MOE_DOWN_LDS(192, kCpolNT);
       MOE_DOWN_LDS(192, 0);
@@ -968,17 +989,19 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
     if (bm == 192)
       return launch_lds_cfg<192, 7, kOutF32Wide, kCpolNT>(h, w_down, (long long)d * ffn, blocks, nb,
                                                          order, offsets, y, A, d, ffn, split, ksplit,
-                                                         nb_max, rotate, nullptr, 1, A, xcd_group, s);
+                                                         nb_max, rotate, nullptr, 1, A, xcd_group, s,
+                                                         dyn_split);
     return launch_lds_cfg<128, 8, kOutF32Wide, kCpolNT>(h, w_down, (long long)d * ffn, blocks, nb,
                                                        order, offsets, y, A, d, ffn, split, ksplit,
-                                                       nb_max, rotate, nullptr, 1, A, xcd_group, s);
+                                                       nb_max, rotate, nullptr, 1, A, xcd_group, s,
+                                                       dyn_split);
   }
 #define X(V, BM, NWT, WV, PF)                                                                  \
   if (bm == BM && V == variant)                                                                      \
     return launch_cfg<BM, NWT, WV, PF, kOutF32Parts>(h, w_down, (long long)d * ffn, blocks, nb,  \
                                                      order, offsets, y, A, d, ffn, split, ksplit,       \
                                                      nb_max, rotate, nullptr, 1, A, xcd_group, 0,\
-                                                     fold, s);
+                                                     fold, s, nullptr, 0, 0, dyn_split);
   MOE_DN_CFGS(X)
 #undef X
   return hipErrorInvalidValue;

@@ -335,6 +335,15 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
       p->split = (ffn + tc - 1) / tc;
       p->fold = 0;
     }
+    // An automatic split is an upper bound: the host's estimate assumes
+    // every expert is active, and under skewed routing far fewer blocks
+    // exist, so the down GEMM and the combination take the parts from the
+    // routed block count on the device (device_down_split).  Measured
+    // (us per pass, split 1 / 2 / 3 forced): skewed T=512 (30 blocks x 8
+    // tiles) 136.9 / 143.7 / 152.7 -- one part; skewed T=128 (16 x 8)
+    // 97.1 / 89.0 / 91.4 and Mixtral T=512 (8 x 16) 637.3 / 558.8 / 588.0 --
+    // two; the device rule picks those.
+    p->dyn_split = !(opt && opt->split_k) && !p->fold && !p->fused_down && p->split > 1;
   }
   size_t o = 0;
   auto seg = [&](size_t bytes) {
@@ -480,10 +489,11 @@ int forward_from_logits(const uint16_t* x, const LogitSrc& router_logits, const 
   if (!p.fused_down)
     MOE_TRY_HIP(launch_down(p.bm, p.dn_variant, h, W_down, blocks, nb, order, offsets, y, p.A, d,
                             ffn, p.split, p.ksplit, p.nb_max, p.dn_rotate, p.dn_xcd,
-                            p.fold ? fold : FoldCombine{}, s));
+                            p.fold ? fold : FoldCombine{}, s, p.dyn_split));
   MOE_TRY(record(opt, 5, s));
   if (!p.fold)
-    MOE_TRY_HIP(launch_combine(y, p.split, p.A, d, inv, wts, top_k, T, out, s));
+    MOE_TRY_HIP(launch_combine(y, p.split, p.A, d, inv, wts, top_k, T, out, s,
+                               p.dyn_split ? DynSplit{nb, p.dn_tiles, ffn} : DynSplit{nullptr, 0, 0}));
   MOE_TRY(record(opt, 6, s));
   return MOE_OK;
 }
@@ -609,6 +619,7 @@ int moe_plan_ex(int T, int d, int ffn, int E, int top_k, const moe_options* opt,
   info->unfused_swiglu = p.unfused ? 1 : 0;
   info->fold_combine = p.fold ? 1 : 0;
   info->xcd_grouped = p.gu_xcd ? 1 : 0;
+  info->split_on_device = p.dyn_split ? 1 : 0;
   info->launches = info->routing_launches + info->gather_launch + (p.unfused ? 3 : 1) +
                    (p.fused_down ? 0 : 1) + (p.fold ? 0 : 1);
   return MOE_OK;

@@ -72,6 +72,8 @@ struct Plan {
   int fold;           // weighted combination in the down GEMM's epilogue
   int dn_tiles;       // column tiles of the down GEMM (d / its tile width)
   int fused_down;     // gate/up GEMM also does the down projection (split = its column tiles)
+  int dyn_split;      // the down GEMM and the combination take the parts from the device
+                      // (device_down_split, at most `split`)
   int plan_error;     // an explicit option the plan cannot honour (MOE_ERR_*), else 0
   // byte offsets into the workspace (256-byte aligned)
   size_t o_ids, o_w, o_counts, o_offsets, o_ccnt, o_cbase, o_perm, o_inv, o_blocks, o_nb;
@@ -84,6 +86,29 @@ struct Plan {
   size_t o_fold;    // arrival counters of the folded combination [T, dn_tiles] int32
   size_t total_bytes;
 };
+
+// Parts of the down projection's reduction in one call, decided on the
+// device from the routed block count nb (the host sizes the partials buffer
+// for split_max parts but cannot see the counts: under skewed routing far
+// fewer blocks exist than its estimate assumes).  parts is the split whose
+// workgroup count nb * n_tiles * parts is nearest to one round of
+// kRoundWorkgroups, at least 1 and at most split_max; ksplit is the
+// reduction length of one part (a multiple of 64), and every part has at
+// least one 64-wide step.  The down GEMM and the combination both call it,
+// so they agree on the parts.
+constexpr int kRoundWorkgroups = 256;  // one workgroup per CU
+struct DownSplit {
+  int parts;
+  int ksplit;
+};
+__host__ __device__ inline DownSplit device_down_split(int nb, int n_tiles, int split_max, int K) {
+  const int wg = nb * n_tiles > 0 ? nb * n_tiles : 1;
+  int s = (2 * kRoundWorkgroups + wg) / (2 * wg);  // round(kRoundWorkgroups / wg)
+  s = s < 1 ? 1 : (s > split_max ? split_max : s);
+  const int ksteps = K / 64;
+  const int per = (ksteps + s - 1) / s;
+  return DownSplit{(ksteps + per - 1) / per, per * 64};
+}
 
 // ---- launchers (enqueue on `s`, return the launch status) ----------------
 
@@ -202,15 +227,25 @@ hipError_t launch_gate_up_down(int bm, int variant, const uint16_t* x, const int
 
 // Down grouped GEMM: y[split, A, d] = partial sums of h Wd^T per block, and
 // with fold.cnt the weighted combination into fold.out.
+// With dyn_split the launch covers split parts at most and the kernel uses
+// device_down_split's parts (not with fold).
 hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w_down,
                        const int32_t* blocks, const int32_t* nb, const int32_t* order,
                        const int32_t* offsets, float* y,
                        int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
-                       int xcd_group, const FoldCombine& fold, hipStream_t s);
+                       int xcd_group, const FoldCombine& fold, hipStream_t s, int dyn_split = 0);
 
 // Weighted combination: out[t] = bf16(sum_j w[t,j] * sum_s y[s, inv[t*k+j]]).
+// With dyn (non-null nb) the parts are device_down_split(*nb, dn_tiles,
+// split, ffn).parts, as in the down GEMM of the same call.
+struct DynSplit {
+  const int32_t* nb;
+  int dn_tiles;
+  int ffn;
+};
 hipError_t launch_combine(const float* y, int split, int A, int d, const int32_t* inv,
-                          const float* w, int k, int T, uint16_t* out, hipStream_t s);
+                          const float* w, int k, int T, uint16_t* out, hipStream_t s,
+                          DynSplit dyn = DynSplit{nullptr, 0, 0});
 
 // Column tile widths (output columns per workgroup) of the two GEMMs for a
 // block size; the planner uses them to size the grids.

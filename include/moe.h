@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 /* Limits of the library (violations return MOE_ERR_UNSUPPORTED). */
 #define MOE_MAX_EXPERTS 512
@@ -87,7 +87,9 @@ typedef struct moe_options {
     int block_rows;
     /* Split of the down projection's reduction (ffn) into this many parts
      * whose partial sums the combination adds in a fixed order.  0 =
-     * automatic; else 1..8. */
+     * automatic (an upper bound chosen on the host; the kernels then take
+     * the parts from the routed block count on the device, see
+     * moe_plan_info.split_on_device); else 1..8, used as given. */
     int split_k;
     /* Tile variant of the fused gate/up GEMM.  0 = automatic; k >= 1 selects
      * compiled variant k-1 for the chosen block_rows (which must then be set
@@ -235,6 +237,12 @@ typedef struct moe_plan_info {
     int fold_combine;      /* 1: the combination runs in the down GEMM         */
     int xcd_grouped;       /* 1: GEMM workgroups grouped by XCD                */
     int launches;          /* kernels per forward pass                         */
+    int split_on_device;   /* 1: split_k is an upper bound; the down GEMM and
+                              the combination take the number of parts from
+                              the routed block count on the device: the split
+                              whose workgroup count (blocks x column tiles x
+                              parts) is nearest to one round of 256, at least
+                              1 and at most split_k                           */
 } moe_plan_info;
 
 /* Host-only: fills *info with the launch plan moe_forward_ex would follow.

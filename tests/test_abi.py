@@ -455,3 +455,21 @@ def test_forward_static_host_checks():
         moe.moe_forward_static(torch.zeros(4, 64, dtype=torch.bfloat16), torch.zeros(4, 4),
                                torch.zeros(4, 128, 64, dtype=torch.bfloat16),
                                torch.zeros(4, 64, 64, dtype=torch.bfloat16), 2, True, None)
+
+
+def test_plan_ex_split_on_device():
+    """An automatic split above one is an upper bound the kernels refine on
+    the device; a forced split, a single part, the folded combination and
+    the fused down projection are used as planned."""
+    sk = CONFIGS["skewed_512"]
+    info = moe.moe_plan_ex(sk.T, sk.d, sk.ffn, sk.E, sk.top_k)
+    assert info["split_k"] == 2 and info["split_on_device"] == 1
+    assert moe.moe_plan_ex(sk.T, sk.d, sk.ffn, sk.E, sk.top_k, split_k=2)["split_on_device"] == 0
+    q = CONFIGS["qwen2_512"]
+    assert moe.moe_plan_ex(q.T, q.d, q.ffn, q.E, q.top_k)["split_on_device"] == 0  # one part
+    mix = CONFIGS["mixtral_512"]
+    assert moe.moe_plan_ex(mix.T, mix.d, mix.ffn, mix.E, mix.top_k)["split_on_device"] == 1
+    assert moe.moe_plan_ex(mix.T, mix.d, mix.ffn, mix.E, mix.top_k, block_rows=192,
+                           down_variant=1, fold_combine=2)["split_on_device"] == 0
+    tiny = CONFIGS["tiny"]
+    assert moe.moe_plan_ex(tiny.T, tiny.d, tiny.ffn, tiny.E, tiny.top_k)["split_on_device"] == 0

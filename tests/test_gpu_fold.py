@@ -27,6 +27,10 @@ def _fold_matches_separate(x, lg, wgu, wd, k, renorm, score, what, **opts):
     opts.setdefault("fuse_down", 1)  # the fold lives in the separate down GEMM
     T, d = x.shape
     E, F = lg.shape[1], wd.shape[2]
+    # the folded combination counts the parts as planned; the separate one is
+    # compared at that same split (left automatic, it may take fewer parts
+    # on the device, another summation order)
+    opts.setdefault("split_k", moe.moe_plan_ex(T, d, F, E, k, fold_combine=2, **opts)["split_k"])
     sep = moe.moe_forward(x, lg, wgu, wd, k, renorm, score=score, fold_combine=1, **opts)
     ws = torch.empty(moe.moe_workspace_size(T, d, F, E, k, fold_combine=2, **opts),
                      dtype=torch.uint8, device=DEV)

@@ -193,6 +193,30 @@ def test_forward_down_variant_two_waves_per_simd():
     parity.check_out(out, ref, "bm=192 down variant 1")
 
 
+@pytest.mark.parametrize("name,parts", [("skewed_512", 1), ("skewed_128", 2), ("mixtral_512", 2)])
+def test_down_split_decided_on_device(name, parts):
+    """With the automatic split the down GEMM and the combination take the
+    number of parts from the routed block count on the device: the split
+    whose workgroups (blocks x column tiles x parts) are nearest to one
+    round of 256 -- skewed T=512 has 30 blocks x 8 tiles (one part), skewed
+    T=128 16 x 8 and Mixtral T=512 8 x 16 (two).  The bytes equal those of
+    that split forced on the host, and meet the tolerance."""
+    cfg = synth.CONFIGS[name]
+    x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)
+    info = moe.moe_plan_ex(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k)
+    assert info["split_on_device"] == 1
+    auto = moe.moe_forward(x, lg, wgu, wd, cfg.top_k, cfg.renormalize, score=cfg.score)
+    forced = moe.moe_forward(x, lg, wgu, wd, cfg.top_k, cfg.renormalize, score=cfg.score,
+                             split_k=parts)
+    assert moe.moe_plan_ex(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k,
+                           split_k=parts)["down_variant"] == info["down_variant"]
+    assert torch.equal(auto.view(torch.int16), forced.view(torch.int16))
+    ref = parity.workload_reference(name, x, lg, wgu, wd, cfg)
+    parity.check_workload(auto, ref, name, x, lg, wgu, wd, cfg, what=name + " device split")
+    del x, lg, wgu, wd, auto, forced
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("score,renorm", [(0, False), (1, True), (1, False)])
 def test_forward_score_functions(score, renorm):
     cfg, x, lg, wgu, wd = parity.make_case(96, 256, 256, 16, 4, score=score, renorm=renorm, seed=9)
