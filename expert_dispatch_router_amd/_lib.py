@@ -16,7 +16,9 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MOE_LIBRARY may name another build of the same library (the host-sanitized
+# libmoe_san.so of build.py); by default the one built in this directory.
+LIB_PATH = os.environ.get("MOE_LIBRARY") or os.path.join(_HERE, "libmoe.so")
 
 MOE_SCORE_SOFTMAX = 0
 MOE_SCORE_SIGMOID = 1

@@ -34,9 +34,20 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+# Host code instrumented with AddressSanitizer and UndefinedBehaviorSanitizer
+# (device code is not: -Xarch_host puts each flag on the host pass only), for
+# `build(sanitize=True)` -> libmoe_san.so, which the binding loads when
+# MOE_LIBRARY names it and the process preloads clang's ASan runtime
+# (tests/sanitize_host.sh).
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+SAN_LIB = os.path.join(PKG, "libmoe_san.so")
+
+
+def _compile(src: str, verbose: bool, sanitize: bool = False) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + (".san.o" if sanitize else ".o"))
+    cmd = [HIPCC, *FLAGS, *(SAN_FLAGS if sanitize else []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -48,18 +59,21 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda s: _compile(s, verbose, sanitize), SOURCES))
+    out = SAN_LIB if sanitize else LIB
+    tmp = out + ".tmp%d" % os.getpid()
+    # (a sanitized build leaves the sanitizer runtime's symbols to the
+    # preloaded runtime)
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))

@@ -43,13 +43,22 @@ _lock = threading.Lock()
 _lib = None
 
 
+# ORACLE_SANITIZE=1: build and load liboracle_san.so instead, compiled with
+# AddressSanitizer and UndefinedBehaviorSanitizer (the process must preload
+# gcc's libasan; oracle/sanitize_check.sh runs the CPU tests that way).
+_SANITIZE = os.environ.get("ORACLE_SANITIZE", "") not in ("", "0")
+if _SANITIZE:
+    _SO = os.path.join(_HERE, "liboracle_san.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
+
+
 def build(force: bool = True) -> str:
     """Compile ``liboracle.so`` with gcc (host only, no GPU headers)."""
     if not force and os.path.exists(_SO) and os.path.getmtime(_SO) >= os.path.getmtime(_SRC):
         return _SO
     tmp = _SO + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"]
+           "-fPIC", "-shared", "-Wall", *(_SAN_FLAGS if _SANITIZE else []), "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _SO)
     return _SO

@@ -43,6 +43,7 @@
 
 #define ORC_OK 0
 #define ORC_EARG (-1)
+#define ORC_ENOMEM (-2)  /* a working buffer could not be allocated */
 
 enum { ORC_SCORE_SOFTMAX = 0, ORC_SCORE_SIGMOID = 1 };
 
@@ -279,13 +280,20 @@ int orc_ffn_tokens(const uint16_t *x, const int32_t *ids, const float *w,
             if (e < 0 || e >= E || !wgu[e] || !wd[e]) return ORC_EARG;
         }
     }
-    int bad = 0;
-#pragma omp parallel for schedule(static) reduction(| : bad)
+    int bad = 0, oom = 0;
+    /* per-thread working rows (x_t, the accumulator, h) on the heap: d and F
+     * can be large enough to overflow a worker thread's stack */
+#pragma omp parallel reduction(| : bad, oom)
+    {
+    float *buf = (float *)malloc(sizeof(float) * ((size_t)2 * d + (size_t)F));
+    if (!buf) oom = 1;
+#pragma omp for schedule(static)
     for (int s = 0; s < ntok; ++s) {
+        if (!buf) continue;
         int t = tokens[s];
-        float xt[d];
-        float acc[d];
-        float h[F];
+        float *xt = buf;
+        float *acc = buf + d;
+        float *h = buf + (size_t)2 * d;
         for (int c = 0; c < d; ++c) xt[c] = orc_bf16_to_f32(x[(size_t)t * d + c]);
         for (int o = 0; o < d; ++o) acc[o] = 0.0f;
         for (int j = 0; j < k; ++j) {
@@ -314,8 +322,10 @@ int orc_ffn_tokens(const uint16_t *x, const int32_t *ids, const float *w,
             if (!isfinite(acc[o])) bad |= 1;
         }
     }
+    free(buf);
+    }
     (void)bad; /* non-finite values are returned as computed */
-    return ORC_OK;
+    return oom ? ORC_ENOMEM : ORC_OK;
 }
 
 /* O0 -- router scores ([R] "The reading": tokens are scored before they are
