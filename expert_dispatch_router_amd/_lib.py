@@ -65,7 +65,7 @@ class MoeOptions(ctypes.Structure):
                 ("routing_kernels", ctypes.c_int), ("gather_mode", ctypes.c_int),
                 ("unfused_swiglu", ctypes.c_int), ("xcd_order", ctypes.c_int),
                 ("fold_combine", ctypes.c_int), ("fuse_down", ctypes.c_int),
-                ("stage_events", ctypes.c_void_p)]
+                ("schedule", ctypes.c_int), ("stage_events", ctypes.c_void_p)]
 
 
 class MoePlanInfo(ctypes.Structure):
@@ -73,7 +73,7 @@ class MoePlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "block_rows", "split_k", "fused_down", "routing_launches", "gather_launch",
         "gate_up_variant", "down_variant", "unfused_swiglu", "fold_combine", "xcd_grouped",
-        "launches", "split_on_device")]
+        "launches", "split_on_device", "stream_k")]
 
 
 class MoeError(RuntimeError):
@@ -119,14 +119,14 @@ def moe_abi_version() -> int:
 
 def _opts(block_rows=0, split_k=0, stage_events=None, tile_variant=0, rotate=0,
           routing_kernels=0, gather_mode=0, unfused_swiglu=0, xcd_order=0, down_variant=0,
-          fold_combine=0, fuse_down=0):
+          fold_combine=0, fuse_down=0, schedule=0):
     if not any((block_rows, split_k, tile_variant, rotate, routing_kernels, gather_mode,
                 unfused_swiglu, xcd_order, down_variant, fold_combine,
-                fuse_down)) and stage_events is None:
+                fuse_down, schedule)) and stage_events is None:
         return None, None
     o = MoeOptions(int(block_rows), int(split_k), int(tile_variant), int(down_variant),
                    int(rotate), int(routing_kernels), int(gather_mode), int(unfused_swiglu),
-                   int(xcd_order), int(fold_combine), int(fuse_down), None)
+                   int(xcd_order), int(fold_combine), int(fuse_down), int(schedule), None)
     keep = []
     if stage_events is not None:
         if len(stage_events) != 7:
@@ -139,9 +139,10 @@ def _opts(block_rows=0, split_k=0, stage_events=None, tile_variant=0, rotate=0,
 
 def moe_workspace_size(T, d, ffn, E, top_k, block_rows=0, split_k=0, tile_variant=0,
                        rotate=0, routing_kernels=0, gather_mode=0, unfused_swiglu=0,
-                       xcd_order=0, down_variant=0, fold_combine=0, fuse_down=0) -> int:
+                       xcd_order=0, down_variant=0, fold_combine=0, fuse_down=0,
+                       schedule=0) -> int:
     o, _ = _opts(block_rows, split_k, None, tile_variant, rotate, routing_kernels, gather_mode,
-                 unfused_swiglu, xcd_order, down_variant, fold_combine, fuse_down)
+                 unfused_swiglu, xcd_order, down_variant, fold_combine, fuse_down, schedule)
     n = _SZ(0)
     _check("moe_workspace_size_ex", lib().moe_workspace_size_ex(
         T, d, ffn, E, top_k, ctypes.byref(o) if o else None, ctypes.byref(n)))
@@ -223,7 +224,8 @@ def _stream_ptr(stream, device):
 def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=None,
                 score="softmax", workspace=None, stream=None, block_rows=0, split_k=0,
                 stage_events=None, tile_variant=0, rotate=0, routing_kernels=0, gather_mode=0,
-                unfused_swiglu=0, xcd_order=0, down_variant=0, fold_combine=0, fuse_down=0):
+                unfused_swiglu=0, xcd_order=0, down_variant=0, fold_combine=0, fuse_down=0,
+                schedule=0):
     """out[T,d] (bf16) = the MoE forward pass, enqueued on ``stream``.
 
     x bf16 [T,d]; router_logits fp32 [T,E]; W_gate_up bf16 [E,2F,d];
@@ -243,11 +245,12 @@ def moe_forward(x, router_logits, W_gate_up, W_down, top_k, renormalize, out=Non
         out = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
     ws_need = moe_workspace_size(T, d, F, E, top_k, block_rows, split_k, tile_variant, rotate,
                                  routing_kernels, gather_mode, unfused_swiglu, xcd_order,
-                                 down_variant, fold_combine, fuse_down)
+                                 down_variant, fold_combine, fuse_down, schedule)
     if workspace is None:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=x.device)
     o, keep = _opts(block_rows, split_k, stage_events, tile_variant, rotate, routing_kernels,
-                    gather_mode, unfused_swiglu, xcd_order, down_variant, fold_combine, fuse_down)
+                    gather_mode, unfused_swiglu, xcd_order, down_variant, fold_combine, fuse_down,
+                    schedule)
     rc = lib().moe_forward_ex(
         _dev_ptr(x, torch.bfloat16, "x"), _dev_ptr(router_logits, torch.float32, "router_logits"),
         _dev_ptr(W_gate_up, torch.bfloat16, "W_gate_up"), _dev_ptr(W_down, torch.bfloat16, "W_down"),
@@ -319,7 +322,7 @@ def moe_forward_router(x, W_router, W_gate_up, W_down, top_k, renormalize, out=N
                        logits_out=None, score="softmax", workspace=None, stream=None,
                        block_rows=0, split_k=0, stage_events=None, tile_variant=0, rotate=0,
                        routing_kernels=0, gather_mode=0, unfused_swiglu=0, xcd_order=0,
-                       down_variant=0, fold_combine=0, fuse_down=0):
+                       down_variant=0, fold_combine=0, fuse_down=0, schedule=0):
     """moe_forward from the hidden states: router scores x . W_router^T
     (written to ``logits_out`` when given), then the forward pass."""
     T, d = x.shape
@@ -336,11 +339,12 @@ def moe_forward_router(x, W_router, W_gate_up, W_down, top_k, renormalize, out=N
         out = torch.empty(T, d, dtype=torch.bfloat16, device=x.device)
     ws_need = moe_workspace_size(T, d, F, E, top_k, block_rows, split_k, tile_variant, rotate,
                                  routing_kernels, gather_mode, unfused_swiglu, xcd_order,
-                                 down_variant, fold_combine, fuse_down)
+                                 down_variant, fold_combine, fuse_down, schedule)
     if workspace is None:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=x.device)
     o, keep = _opts(block_rows, split_k, stage_events, tile_variant, rotate, routing_kernels,
-                    gather_mode, unfused_swiglu, xcd_order, down_variant, fold_combine, fuse_down)
+                    gather_mode, unfused_swiglu, xcd_order, down_variant, fold_combine, fuse_down,
+                    schedule)
     rc = lib().moe_forward_router(
         _dev_ptr(x, torch.bfloat16, "x"), _dev_ptr(W_router, torch.bfloat16, "W_router"),
         _dev_ptr(W_gate_up, torch.bfloat16, "W_gate_up"), _dev_ptr(W_down, torch.bfloat16, "W_down"),

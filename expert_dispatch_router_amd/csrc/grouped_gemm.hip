@@ -558,16 +558,20 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
 // twice the weight rows per activation row; kOutF32Dense: fp32 parts of one
 // dense product (no schedule: block b is rows [b * BM, b * BM + BM) of X,
 // all against W) -- the router scores.
-template <int BM, int WAVES, int BK, int STAGES, int MODE = kOutSwiGLU>
+template <int BM, int WAVES, int BK, int STAGES, int MODE = kOutSwiGLU, int SUB = 2>
 struct LdsGemm {
   static_assert(BK == 32 || BK == 64, "K step of 32 or 64");
+  static_assert(STAGES == 2 || STAGES == 3, "two or three stages");
+  static_assert(SUB == 1 || SUB == 2, "one or two 16-column subtiles per wave and operand");
   static_assert(MODE == kOutSwiGLU || MODE == kOutF32Parts || MODE == kOutF32Wide ||
                     MODE == kOutF32Dense,
                 "SwiGLU or fp32 parts");
   static constexpr bool kWide = MODE == kOutF32Wide;
+  static_assert(!kWide || SUB == 2, "the wide tile takes two subtiles per column group");
   static constexpr int kNG = (MODE == kOutSwiGLU || kWide) ? 2 : 1;
-  static constexpr int kWaveCols = kWide ? 64 : 32;  // output columns of one wave
-  static constexpr int kGPW = 2 * kNG;                // 16-row weight groups per wave
+  static constexpr int kSub = SUB;
+  static constexpr int kWaveCols = kWide ? 64 : 16 * SUB;  // output columns of one wave
+  static constexpr int kGPW = SUB * kNG;                   // 16-row weight groups per wave
   static constexpr int kMT = BM / 16;
   static constexpr int kKC = BK / 32;                 // MFMA K chunks per step
   static constexpr int kRowBytes = 2 * BK;
@@ -580,7 +584,11 @@ struct LdsGemm {
   static constexpr int kXPerWave = (kXGroups + WAVES - 1) / WAVES;
   static constexpr int kStageBytes = kWBytes + kXGroups * kGroupBytes;
   static constexpr int kLoadsPerStage = (kGPW + kXPerWave) * kLoadsPerGroup;
-  static_assert(kGPW * kLoadsPerGroup <= 63, "immediate vmcnt");
+  // loads younger than a stage's activation loads when the wait for that
+  // stage is full (see the main loop): STAGES - 2 whole stages and one
+  // stage's weights
+  static constexpr int kWaitAhead = (STAGES - 2) * kLoadsPerStage + kGPW * kLoadsPerGroup;
+  static_assert(kWaitAhead <= 63, "immediate vmcnt");
   static_assert(kXPerWave * WAVES <= 2 * kXGroups, "a surplus slot repeats one group");
   static_assert(STAGES * kStageBytes <= 160 * 1024, "LDS of one CU");
   __device__ static int swz(int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
@@ -600,11 +608,240 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds,
       r, (__attribute__((address_space(3))) void*)(uintptr_t)lds, 16, voff, soff, 0, CPOL);
 }
 
-// out: kOutSwiGLU -> bf16 h [A, N]; kOutF32Parts, kOutF32Wide and
-// kOutF32Dense -> fp32 y [split, A, N] (part p sums K steps
-// [p * ksplit, (p + 1) * ksplit)).  kOutF32Dense reads no schedule
-// (blocks, nb_dev, order and offsets may be null).
-template <int BM, int WAVES, int BK, int STAGES, int MODE, int WCPOL>
+template <int NG, int MT, int SUB>
+__device__ __forceinline__ void lds_tile_zero(f32x4 (&acc)[NG][MT][SUB]) {
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < SUB; ++j) acc[g][mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// The multiplies of one (block, column tile, part) of the LDS-staged tile
+// over K steps [s_first, s_first + s_count) of the part's step sequence: nks
+// steps of BK from K offset kb, taken in the rotated order that starts at
+// step `shift`.  Accumulates into acc (this wave's NG x MT x SUB fragments of
+// columns n0 ..).  Every wave of the workgroup calls it together; on return
+// the wave's loads have landed and its last LDS reads are done, but other
+// waves may still read the ring: the caller synchronises before reusing it.
+template <int BM, int WAVES, int BK, int STAGES, int MODE, int WCPOL, int SUB>
+__device__ __forceinline__ void lds_tile_mma(
+    uint8_t* lds, const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+    long long w_estride, int e, int r0, int rows, int n0, int kb, int N, int K, int nks_all,
+    int shift, int s_first, int s_count, const int32_t* __restrict__ gather_perm, int gather_k,
+    int x_rows, f32x4 (&acc)[LdsGemm<BM, WAVES, BK, STAGES, MODE, SUB>::kNG][BM / 16][SUB]) {
+  using G = LdsGemm<BM, WAVES, BK, STAGES, MODE, SUB>;
+  constexpr int MT = G::kMT, KC = G::kKC, SB = G::kStageBytes, XPW = G::kXPerWave;
+  constexpr int NG = G::kNG, GPW = G::kGPW;
+  constexpr int LPG = G::kLoadsPerGroup, GB = G::kGroupBytes, RB = G::kRowBytes;
+  const int mt_act = (rows + 15) >> 4;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  (void)tid;
+
+  // loads: load h of a group, lane -> row h * (1024 / RB) + lane / (RB / 16),
+  // slot lane % (RB / 16), which holds K chunk slot ^ swz(row)
+  constexpr int SPR = RB / 16;  // 16-byte slots per row
+  int lrow[LPG], lchk[LPG];
+#pragma unroll
+  for (int hh = 0; hh < LPG; ++hh) {
+    lrow[hh] = hh * (1024 / RB) + lane / SPR;
+    lchk[hh] = (lane % SPR) ^ G::swz(lrow[hh]);
+  }
+  // weight rows of the expert: NG operands of N rows (SwiGLU), else N rows
+  constexpr int kWOps = G::kWide ? 1 : NG;
+  const int wbytes = kWOps * N * K * 2;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (size_t)e * w_estride), (short)0, wbytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t xres =
+      gather_perm
+          ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, x_rows * K * 2, kRsrcWord3)
+          : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (size_t)r0 * K), (short)0,
+                                              rows * K * 2, kRsrcWord3);
+  // weight groups of this wave: q = SUB * g + j -> operand g (gate, up), subtile j;
+  // wide: column group g of the wave's 64 columns, subtile j.
+  // Columns past N (a partial last tile) get an offset past the
+  // descriptor's range: zeros, no memory request; their outputs are not
+  // stored.
+  int woff[GPW][LPG];
+#pragma unroll
+  for (int q = 0; q < GPW; ++q)
+#pragma unroll
+    for (int hh = 0; hh < LPG; ++hh) {
+      const int col = n0 + (G::kWide ? 32 * (q / SUB) : 0) + 16 * (q % SUB) + lrow[hh];
+      const int wrow = G::kWide ? col : (q / SUB) * N + col;
+      woff[q][hh] = col < N ? (wrow * K + kb + lchk[hh] * 8) * 2 : wbytes;
+    }
+  int xoff[XPW][LPG];
+  int xgrp[XPW];
+#pragma unroll
+  for (int q = 0; q < XPW; ++q) {
+    const int gs = wave + q * WAVES;
+    const int grp = gs < G::kXGroups ? gs : gs - G::kXGroups;  // surplus slots repeat a group
+    xgrp[q] = grp;
+#pragma unroll
+    for (int hh = 0; hh < LPG; ++hh) {
+      const int row = grp * 16 + lrow[hh];
+      int src = row;
+      if (gather_perm) src = row < rows ? gather_perm[r0 + row] / gather_k : x_rows;
+      else if (row >= rows) src = rows;  // past the range: zeros, no memory request
+      xoff[q][hh] = (src * K + kb + lchk[hh] * 8) * 2;
+    }
+  }
+
+  auto soff_of = [&](int ks) {
+    const int kk = ks + shift;
+    return (kk >= nks_all ? kk - nks_all : kk) * (BK * 2);
+  };
+  // weights of stage ks into this wave's region of slot ks % STAGES
+  auto issue_w = [&](int ks) {
+    const int soff = soff_of(s_first + ks);
+    uint8_t* st = lds + (ks % STAGES) * SB;
+#pragma unroll
+    for (int q = 0; q < GPW; ++q)
+#pragma unroll
+      for (int hh = 0; hh < LPG; ++hh)
+        dma16<WCPOL>(wres, st + (wave * GPW + q) * GB + hh * 1024, woff[q][hh], soff);
+  };
+  // this wave's share of the activation tile of stage ks
+  auto issue_x = [&](int ks) {
+    const int soff = soff_of(s_first + ks);
+    uint8_t* st = lds + (ks % STAGES) * SB;
+#pragma unroll
+    for (int q = 0; q < XPW; ++q)
+#pragma unroll
+      for (int hh = 0; hh < LPG; ++hh)
+        dma16(xres, st + G::kWBytes + xgrp[q] * GB + hh * 1024, xoff[q][hh], soff);
+  };
+
+  // fragment reads: lane -> row (lane & 15), K chunk c * 4 + (lane >> 4) of
+  // the step's chunk c
+  const int rr = lane & 15;
+  int roff[KC];
+#pragma unroll
+  for (int c = 0; c < KC; ++c) roff[c] = rr * RB + ((((lane >> 4) + 4 * c) ^ G::swz(rr)) * 16);
+  constexpr int SL = G::kLoadsPerStage;
+  const int nks = s_count;  // steps of this call, local indices 0 .. s_count - 1
+  if (nks > 0) {
+    // Each wave's weight region is its own: the wave refills it with stage
+    // ks + STAGES right after its multiplies of stage ks, so its weight
+    // stream keeps STAGES stages in flight without waiting for the other
+    // waves.  The shared activation tile of stage ks + STAGES - 1 is issued
+    // after the barrier of step ks, once every wave is done with stage
+    // ks - 1, whose slot it takes.
+    // Issue order per wave: W(0) X(0) ... W(S-2) X(S-2) W(S-1), then per step
+    // ks: X(ks+S-1), W(ks+S) -- so the loads are W(j) X(j) in stage order,
+    // and at the top of step ks the loads younger than X(ks) are those of
+    // the stages issued beyond ks: S-2 whole stages and W(ks+S-1), or fewer
+    // near the end of the reduction (whole stages only).
+#pragma unroll
+    for (int j = 0; j < STAGES - 1; ++j)
+      if (j < nks) {
+        issue_w(j);
+        issue_x(j);
+      }
+    if (STAGES - 1 < nks) issue_w(STAGES - 1);
+    for (int ks = 0; ks < nks; ++ks) {
+      const int ahead = min(nks - 1 - ks, STAGES - 1);  // stages issued beyond ks
+      if (ahead == STAGES - 1) wait_vmcnt<G::kWaitAhead>();
+      else if (STAGES == 3 && ahead == 1) wait_vmcnt<(STAGES == 3 ? SL : 0)>();
+      else wait_vmcnt<0>();
+      lds_barrier();  // ... everyone's; and everyone is done with stage ks - 1
+      if (ks + STAGES - 1 < nks) issue_x(ks + STAGES - 1);
+      const uint8_t* st = lds + (ks % STAGES) * SB;
+      const uint8_t* xb = st + G::kWBytes;
+      // K chunk outermost: one chunk's weight fragments live at a time (each
+      // output still sums its K chunks in ascending order)
+#pragma unroll
+      for (int c = 0; c < KC; ++c) {
+        bf16x8 wa[GPW];
+#pragma unroll
+        for (int q = 0; q < GPW; ++q)
+          wa[q] = *reinterpret_cast<const bf16x8*>(st + (wave * GPW + q) * GB + roff[c]);
+        bf16x8 xa = *reinterpret_cast<const bf16x8*>(xb + roff[c]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          bf16x8 xn = xa;
+          if (mt + 1 < MT) xn = *reinterpret_cast<const bf16x8*>(xb + (mt + 1) * GB + roff[c]);
+          if (mt < mt_act) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+              for (int j = 0; j < SUB; ++j)
+                acc[g][mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[SUB * g + j], xa,
+                                                                        acc[g][mt][j], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          xa = xn;
+        }
+      }
+      // this wave is done with its weights of stage ks
+      if (ks + STAGES < nks) issue_w(ks + STAGES);
+    }
+  }
+}
+
+// Writes a tile's results: bf16 h = silu(gate) * up (SwiGLU) or fp32 parts
+// [part, A, N].
+template <int BM, int WAVES, int BK, int STAGES, int MODE, int SUB>
+__device__ __forceinline__ void lds_tile_store(
+    const f32x4 (&acc)[LdsGemm<BM, WAVES, BK, STAGES, MODE, SUB>::kNG][BM / 16][SUB], void* out,
+    int A, int N, int r0, int rows, int n0, int part) {
+  using G = LdsGemm<BM, WAVES, BK, STAGES, MODE, SUB>;
+  constexpr int MT = G::kMT, NG = G::kNG;
+  const int mt_act = (rows + 15) >> 4;
+  const int lane = threadIdx.x & 63;
+  const int rr = lane & 15;
+  // epilogue: lane holds columns n0 + 16j + 4*(lane>>4) + 0..3 of row mt*16 + (lane & 15)
+  // (wide: n0 + 32g + 16j + ...)
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + rr;
+    if constexpr (G::kWide) {
+      if (mt < mt_act && m < rows) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int c0 = n0 + 32 * g + 16 * j;
+            if (c0 >= N) continue;  // subtile past the last column (N % 16 == 0)
+            const int n = c0 + 4 * (lane >> 4);
+            *reinterpret_cast<f32x4*>(static_cast<float*>(out) +
+                                      ((size_t)part * A + r0 + m) * N + n) = acc[g][mt][j];
+          }
+      }
+      continue;
+    }
+    if (mt < mt_act && m < rows) {
+#pragma unroll
+      for (int j = 0; j < SUB; ++j) {
+        if (n0 + 16 * j >= N) continue;  // subtile past the last column (N % 16 == 0)
+        const int n = n0 + 16 * j + 4 * (lane >> 4);
+        if constexpr (MODE == kOutSwiGLU) {
+          const f32x4 gv = acc[0][mt][j];
+          const f32x4 uv = acc[NG - 1][mt][j];
+          bf16x4 hv;
+          hv[0] = (__bf16)(silu_f32(gv[0]) * uv[0]);
+          hv[1] = (__bf16)(silu_f32(gv[1]) * uv[1]);
+          hv[2] = (__bf16)(silu_f32(gv[2]) * uv[2]);
+          hv[3] = (__bf16)(silu_f32(gv[3]) * uv[3]);
+          *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(out) + (size_t)(r0 + m) * N + n) = hv;
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + ((size_t)part * A + r0 + m) * N + n) =
+              acc[0][mt][j];
+        }
+      }
+    }
+  }
+}
+
+// One workgroup = one (block, column tile, part).  out: kOutSwiGLU -> bf16
+// h [A, N]; kOutF32Parts, kOutF32Wide and kOutF32Dense -> fp32 y [split, A,
+// N] (part p sums K steps [p * ksplit, (p + 1) * ksplit)).  kOutF32Dense
+// reads no schedule (blocks, nb_dev, order and offsets may be null).
+template <int BM, int WAVES, int BK, int STAGES, int MODE, int WCPOL, int SUB>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
@@ -612,11 +849,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     void* __restrict__ out, int A, int N, int K, int ksplit, int tiles_per_block, int rotate,
     const int32_t* __restrict__ gather_perm, int gather_k, int x_rows, int xcd_group,
     int dyn_split) {
-  using G = LdsGemm<BM, WAVES, BK, STAGES, MODE>;
-  constexpr int MT = G::kMT, KC = G::kKC, SB = G::kStageBytes, XPW = G::kXPerWave;
-  constexpr int NG = G::kNG, GPW = G::kGPW;
-  constexpr int LPG = G::kLoadsPerGroup, GB = G::kGroupBytes, RB = G::kRowBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[STAGES * SB];
+  using G = LdsGemm<BM, WAVES, BK, STAGES, MODE, SUB>;
+  constexpr int MT = G::kMT, NG = G::kNG;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[STAGES * G::kStageBytes];
 
   // The split of the reduction: as launched, or with dyn_split decided here
   // from the routed block count (device_down_split; at most the launched
@@ -649,209 +884,162 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
   const int e = kDense ? 0 : blocks[2 * b];
   const int r0 = kDense ? b * BM : blocks[2 * b + 1];
   const int rows = min(BM, (kDense ? A : offsets[e + 1]) - r0);
-  const int mt_act = (rows + 15) >> 4;
   const int nks = max(0, min(K - kb, ksplit) / BK);
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = tile * G::kTileCols + wave * G::kWaveCols;
-
-  // loads: load h of a group, lane -> row h * (1024 / RB) + lane / (RB / 16),
-  // slot lane % (RB / 16), which holds K chunk slot ^ swz(row)
-  constexpr int SPR = RB / 16;  // 16-byte slots per row
-  int lrow[LPG], lchk[LPG];
-#pragma unroll
-  for (int hh = 0; hh < LPG; ++hh) {
-    lrow[hh] = hh * (1024 / RB) + lane / SPR;
-    lchk[hh] = (lane % SPR) ^ G::swz(lrow[hh]);
-  }
-  // weight rows of the expert: NG operands of N rows (SwiGLU), else N rows
-  constexpr int kWOps = G::kWide ? 1 : NG;
-  const int wbytes = kWOps * N * K * 2;
-  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (size_t)e * w_estride), (short)0, wbytes, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t xres =
-      gather_perm
-          ? __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, x_rows * K * 2, kRsrcWord3)
-          : __builtin_amdgcn_make_buffer_rsrc((void*)(X + (size_t)r0 * K), (short)0,
-                                              rows * K * 2, kRsrcWord3);
-  // weight groups of this wave: q = 2 * g + j -> operand g (gate, up), subtile j;
-  // wide: column group g of the wave's 64 columns, subtile j.
-  // Columns past N (a partial last tile) get an offset past the
-  // descriptor's range: zeros, no memory request; their outputs are not
-  // stored.
-  int woff[GPW][LPG];
-#pragma unroll
-  for (int q = 0; q < GPW; ++q)
-#pragma unroll
-    for (int hh = 0; hh < LPG; ++hh) {
-      const int col = n0 + (G::kWide ? 32 * (q >> 1) : 0) + 16 * (q & 1) + lrow[hh];
-      const int wrow = G::kWide ? col : (q >> 1) * N + col;
-      woff[q][hh] = col < N ? (wrow * K + kb + lchk[hh] * 8) * 2 : wbytes;
-    }
-  int xoff[XPW][LPG];
-  int xgrp[XPW];
-#pragma unroll
-  for (int q = 0; q < XPW; ++q) {
-    const int gs = wave + q * WAVES;
-    const int grp = gs < G::kXGroups ? gs : gs - G::kXGroups;  // surplus slots repeat a group
-    xgrp[q] = grp;
-#pragma unroll
-    for (int hh = 0; hh < LPG; ++hh) {
-      const int row = grp * 16 + lrow[hh];
-      int src = row;
-      if (gather_perm) src = row < rows ? gather_perm[r0 + row] / gather_k : x_rows;
-      else if (row >= rows) src = rows;  // past the range: zeros, no memory request
-      xoff[q][hh] = (src * K + kb + lchk[hh] * 8) * 2;
-    }
-  }
-
   const unsigned rkey = rotate == 2 ? (unsigned)wg : rotate == 3 ? (unsigned)e : (unsigned)b;
   const int shift = rotate ? (int)((rkey * 2654435761u) % (unsigned)max(nks, 1)) : 0;
-  auto soff_of = [&](int ks) {
-    const int kk = ks + shift;
-    return (kk >= nks ? kk - nks : kk) * (BK * 2);
-  };
-  // weights of stage ks into this wave's region of slot ks % STAGES
-  auto issue_w = [&](int ks) {
-    const int soff = soff_of(ks);
-    uint8_t* st = lds + (ks % STAGES) * SB;
-#pragma unroll
-    for (int q = 0; q < GPW; ++q)
-#pragma unroll
-      for (int hh = 0; hh < LPG; ++hh)
-        dma16<WCPOL>(wres, st + (wave * GPW + q) * GB + hh * 1024, woff[q][hh], soff);
-  };
-  // this wave's share of the activation tile of stage ks
-  auto issue_x = [&](int ks) {
-    const int soff = soff_of(ks);
-    uint8_t* st = lds + (ks % STAGES) * SB;
-#pragma unroll
-    for (int q = 0; q < XPW; ++q)
-#pragma unroll
-      for (int hh = 0; hh < LPG; ++hh)
-        dma16(xres, st + G::kWBytes + xgrp[q] * GB + hh * 1024, xoff[q][hh], soff);
-  };
+  f32x4 acc[NG][MT][SUB];
+  lds_tile_zero<NG, MT, SUB>(acc);
+  lds_tile_mma<BM, WAVES, BK, STAGES, MODE, WCPOL, SUB>(lds, X, W, w_estride, e, r0, rows, n0, kb,
+                                                        N, K, nks, shift, 0, nks, gather_perm,
+                                                        gather_k, x_rows, acc);
+  lds_tile_store<BM, WAVES, BK, STAGES, MODE, SUB>(acc, out, A, N, r0, rows, n0, part);
+}
 
-  f32x4 acc[NG][MT][2];
-#pragma unroll
-  for (int g = 0; g < NG; ++g)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[g][mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+// Stream-K schedule of the fused gate/up GEMM (one launch of G persistent
+// workgroups).  The work is every (block, column tile) unit of the schedule
+// built on the device times its nks K steps: I = nb * n_tiles * nks
+// iterations, of which workgroup g takes [g * I / G, (g + 1) * I / G) (G =
+// min(launched workgroups, I), so no range is empty).  So
+// every workgroup streams the same number of weight steps whatever the
+// routing, instead of one unit per workgroup in rounds of G.  A workgroup
+// runs the stretch of each unit its range covers; a unit covered whole is
+// finished on the spot (SwiGLU, h written), a stretch of a split unit leaves
+// its fp32 gate and up sums in a slot of `sk.part` (slot 2g for the first
+// stretch of workgroup g, 2g + 1 for its last) and counts itself on the
+// unit's counter.  The workgroup that completes the count adds the unit's
+// stretches in K order (its own from registers), applies SwiGLU and writes
+// h: the sum order is fixed by the unit's split points, not by which
+// workgroup arrives last.  Nothing waits on another workgroup.  The routing
+// kernels clear the counters on every call.
+//
+// Hand-off: the stretches are written with agent-scope stores, each thread
+// then issues an agent-scope release fence, and after the barrier thread 0
+// increments the counter (relaxed, agent scope); the workgroup whose
+// increment completes the count acquires (agent scope, every thread) before
+// reading the other stretches with agent-scope loads.
+struct SkWork {
+  float* part;   // [2 * G] slots of NG * MT * SUB * threads f32x4
+  int32_t* cnt;  // per unit, zero at entry
+};
 
-  // fragment reads: lane -> row (lane & 15), K chunk c * 4 + (lane >> 4) of
-  // the step's chunk c
-  const int rr = lane & 15;
-  int roff[KC];
+template <int BM, int WAVES, int BK, int STAGES, int WCPOL, int SUB>
+__global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_sk_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
+    const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
+    const int32_t* __restrict__ offsets, uint16_t* __restrict__ h, int N, int K, int rotate,
+    const int32_t* __restrict__ gather_perm, int gather_k, int x_rows, SkWork sk) {
+  using G = LdsGemm<BM, WAVES, BK, STAGES, kOutSwiGLU, SUB>;
+  constexpr int MT = G::kMT, NG = G::kNG;
+  constexpr int kSlotF4 = NG * MT * SUB * G::kThreads;  // f32x4 of one slot
+  __shared__ __attribute__((aligned(16))) uint8_t lds[STAGES * G::kStageBytes];
+  __shared__ int completes;
+
+  const int n_tiles = (N + G::kTileCols - 1) / G::kTileCols;
+  const int nks = K / BK;
+  const long long I = (long long)nb_dev[0] * n_tiles * nks;
+  // With fewer iterations than workgroups only the first I take part, one
+  // iteration each: every taking part workgroup has a non-empty range.
+  const long long NW = min((long long)gridDim.x, I);
+  const int wg = blockIdx.x;
+  if (wg >= NW) return;
+  const long long start = wg * I / NW, end = (wg + 1) * I / NW;
+  // the workgroup whose range holds iteration i
+  auto owner = [&](long long i) { return (int)(((i + 1) * NW - 1) / I); };
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  for (long long it = start; it < end;) {
+    const int u = (int)(it / nks);
+    const int k0 = (int)(it - (long long)u * nks);
+    const int cnt = (int)min((long long)(nks - k0), end - it);
+    const int b = u / n_tiles;
+    const int tile = u - b * n_tiles;
+    const int e = blocks[2 * b];
+    const int r0 = blocks[2 * b + 1];
+    const int rows = min(BM, offsets[e + 1] - r0);
+    const int mt_act = (rows + 15) >> 4;
+    const int n0 = tile * G::kTileCols + wave * G::kWaveCols;
+    // rotation keys: per unit (in place of per workgroup), expert or block
+    const unsigned rkey = rotate == 2 ? (unsigned)u : rotate == 3 ? (unsigned)e : (unsigned)b;
+    const int shift = rotate ? (int)((rkey * 2654435761u) % (unsigned)nks) : 0;
+    f32x4 acc[NG][MT][SUB];
+    lds_tile_zero<NG, MT, SUB>(acc);
+    __syncthreads();  // every wave is done with the ring of the previous stretch
+    lds_tile_mma<BM, WAVES, BK, STAGES, kOutSwiGLU, WCPOL, SUB>(
+        lds, X, W, w_estride, e, r0, rows, n0, 0, N, K, nks, shift, k0, cnt, gather_perm, gather_k,
+        x_rows, acc);
+    if (cnt == nks) {
+      lds_tile_store<BM, WAVES, BK, STAGES, kOutSwiGLU, SUB>(acc, h, 0, N, r0, rows, n0, 0);
+    } else {
+      const int slot = 2 * wg + (it == start ? 0 : 1);
+      float* ps = sk.part + (size_t)slot * kSlotF4 * 4;
 #pragma unroll
-  for (int c = 0; c < KC; ++c) roff[c] = rr * RB + ((((lane >> 4) + 4 * c) ^ G::swz(rr)) * 16);
-  static_assert(STAGES == 2, "double-buffered stages");
-  constexpr int WL = GPW * LPG;  // weight loads of one stage (per wave)
-  if (nks > 0) {
-    // Each wave's weight region is its own: the wave refills it with stage
-    // ks + 2 right after its multiplies of stage ks, so its weight stream
-    // keeps two stages in flight without waiting for the other waves.  The
-    // shared activation tile of stage ks + 1 is issued after the barrier of
-    // step ks, once every wave is done with stage ks - 1.
-    // Issue order per wave: W(0), X(0), W(1), then per step ks: X(ks+1),
-    // W(ks+2) -- at the top of step ks the only younger load is W(ks+1).
-    issue_w(0);
-    issue_x(0);
-    if (nks > 1) issue_w(1);
-    for (int ks = 0; ks < nks; ++ks) {
-      if (ks + 1 < nks) wait_vmcnt<WL>();  // W(ks) and X(ks) are in LDS
-      else wait_vmcnt<0>();
-      lds_barrier();  // ... everyone's; and everyone is done with stage ks - 1
-      if (ks + 1 < nks) issue_x(ks + 1);
-      const uint8_t* st = lds + (ks % STAGES) * SB;
-      const uint8_t* xb = st + G::kWBytes;
-      // K chunk outermost: one chunk's weight fragments live at a time (each
-      // output still sums its K chunks in ascending order)
+      for (int g = 0; g < NG; ++g)
 #pragma unroll
-      for (int c = 0; c < KC; ++c) {
-        bf16x8 wa[GPW];
-#pragma unroll
-        for (int q = 0; q < GPW; ++q)
-          wa[q] = *reinterpret_cast<const bf16x8*>(st + (wave * GPW + q) * GB + roff[c]);
-        bf16x8 xa = *reinterpret_cast<const bf16x8*>(xb + roff[c]);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          bf16x8 xn = xa;
-          if (mt + 1 < MT) xn = *reinterpret_cast<const bf16x8*>(xb + (mt + 1) * GB + roff[c]);
+        for (int mt = 0; mt < MT; ++mt)
           if (mt < mt_act) {
 #pragma unroll
-            for (int g = 0; g < NG; ++g)
+            for (int j = 0; j < SUB; ++j) {
+              float* q = ps + ((size_t)((g * MT + mt) * SUB + j) * G::kThreads + tid) * 4;
 #pragma unroll
-              for (int j = 0; j < 2; ++j)
-                acc[g][mt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[2 * g + j], xa,
-                                                                        acc[g][mt][j], 0, 0, 0);
+              for (int i = 0; i < 4; ++i)
+                __hip_atomic_store(q + i, acc[g][mt][j][i], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
           }
-          __builtin_amdgcn_sched_barrier(0);
-          xa = xn;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __syncthreads();
+      const long long u0 = (long long)u * nks;
+      const int g_lo = owner(u0), g_hi = owner(u0 + nks - 1);
+      if (tid == 0)
+        completes = __hip_atomic_fetch_add(&sk.cnt[u], 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) == g_hi - g_lo;
+      __syncthreads();
+      if (completes) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        f32x4 tot[NG][MT][SUB];
+        lds_tile_zero<NG, MT, SUB>(tot);
+        for (int g = g_lo; g <= g_hi; ++g) {
+          // the stretch of workgroup g: its first one if its range starts in this unit
+          const int sl = 2 * g + ((long long)g * I / NW >= u0 ? 0 : 1);
+          const float* src = sk.part + (size_t)sl * kSlotF4 * 4;
+#pragma unroll
+          for (int gg = 0; gg < NG; ++gg)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              if (mt < mt_act) {
+#pragma unroll
+                for (int j = 0; j < SUB; ++j) {
+                  f32x4 v = acc[gg][mt][j];
+                  if (g != wg)
+                    v = AgentLoad{}(src + ((size_t)((gg * MT + mt) * SUB + j) * G::kThreads + tid) * 4);
+                  tot[gg][mt][j] = g == g_lo ? v : tot[gg][mt][j] + v;
+                }
+              }
         }
-      }
-      if (ks + 2 < nks) issue_w(ks + 2);  // this wave is done with its weights of stage ks
-    }
-  }
-
-  // epilogue: lane holds columns n0 + 16j + 4*(lane>>4) + 0..3 of row mt*16 + (lane & 15)
-  // (wide: n0 + 32g + 16j + ...)
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = mt * 16 + rr;
-    if constexpr (G::kWide) {
-      if (mt < mt_act && m < rows) {
-#pragma unroll
-        for (int g = 0; g < 2; ++g)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int c0 = n0 + 32 * g + 16 * j;
-            if (c0 >= N) continue;  // subtile past the last column (N % 16 == 0)
-            const int n = c0 + 4 * (lane >> 4);
-            *reinterpret_cast<f32x4*>(static_cast<float*>(out) +
-                                      ((size_t)part * A + r0 + m) * N + n) = acc[g][mt][j];
-          }
-      }
-      continue;
-    }
-    if (mt < mt_act && m < rows) {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (n0 + 16 * j >= N) continue;  // subtile past the last column (N % 16 == 0)
-        const int n = n0 + 16 * j + 4 * (lane >> 4);
-        if constexpr (MODE == kOutSwiGLU) {
-          const f32x4 gv = acc[0][mt][j];
-          const f32x4 uv = acc[NG - 1][mt][j];
-          bf16x4 hv;
-          hv[0] = (__bf16)(silu_f32(gv[0]) * uv[0]);
-          hv[1] = (__bf16)(silu_f32(gv[1]) * uv[1]);
-          hv[2] = (__bf16)(silu_f32(gv[2]) * uv[2]);
-          hv[3] = (__bf16)(silu_f32(gv[3]) * uv[3]);
-          *reinterpret_cast<bf16x4*>(static_cast<uint16_t*>(out) + (size_t)(r0 + m) * N + n) = hv;
-        } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + ((size_t)part * A + r0 + m) * N + n) =
-              acc[0][mt][j];
-        }
+        lds_tile_store<BM, WAVES, BK, STAGES, kOutSwiGLU, SUB>(tot, h, 0, N, r0, rows, n0, 0);
       }
     }
+    it += cnt;
   }
 }
 
 constexpr int kLdsBK = 64;     // whole 128-byte lines of each weight row per step
 constexpr int kLdsStages = 2;  // 2 x 80 KiB: the whole LDS of a CU at BM = 192, 7 waves
+constexpr int kLdsNarrowStages = 3;  // 3 x 48 KiB at BM = 128 with one subtile per wave
 
-// WCPOL: cache policy of the weight loads.
-template <int BM, int WAVES, int MODE, int WCPOL>
+// WCPOL: cache policy of the weight loads; STAGES, SUB as in LdsGemm.
+template <int BM, int WAVES, int MODE, int WCPOL, int STAGES = kLdsStages, int SUB = 2>
 hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
                           const int32_t* blocks, const int32_t* nb, const int32_t* order,
                           const int32_t* offsets, void* out, int A, int N, int K, int split,
                           int ksplit, int nb_max, int rotate, const int32_t* gather_perm,
                           int gather_k, int x_rows, int xcd_group, hipStream_t s,
                           int dyn_split = 0) {
-  using G = LdsGemm<BM, WAVES, kLdsBK, kLdsStages, MODE>;
+  using G = LdsGemm<BM, WAVES, kLdsBK, STAGES, MODE, SUB>;
   // whole 16-column subtiles and whole K steps
   if (N % 16 != 0 || K % kLdsBK != 0 || ksplit % kLdsBK != 0 || split < 1)
     return hipErrorInvalidValue;
@@ -861,7 +1049,7 @@ hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estr
   const long long grid = xcd_group ? ((long long)tiles_per_block * nb_max + kXcds - 1) / kXcds * kXcds
                                    : (long long)tiles_per_block * nb_max;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  gemm_lds_kernel<BM, WAVES, kLdsBK, kLdsStages, MODE, WCPOL><<<(unsigned)grid, G::kThreads, 0, s>>>(
+  gemm_lds_kernel<BM, WAVES, kLdsBK, STAGES, MODE, WCPOL, SUB><<<(unsigned)grid, G::kThreads, 0, s>>>(
       X, W, w_estride, blocks, nb, order, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
       gather_perm, gather_k, x_rows, xcd_group, dyn_split);
   return hipGetLastError();
@@ -876,6 +1064,8 @@ int gate_up_tile_cols(int bm, int variant) {
 #undef X
   if (bm == 192 && variant == kGateUpLdsVariant) return LdsGemm<192, 7, kLdsBK, kLdsStages>::kTileCols;
   if (bm == 128 && variant == kGateUpLdsVariant) return LdsGemm<128, 8, kLdsBK, kLdsStages>::kTileCols;
+  if (bm == 128 && variant == kGateUpLdsNarrowVariant)
+    return LdsGemm<128, 8, kLdsBK, kLdsNarrowStages, kOutSwiGLU, 1>::kTileCols;  // 128
   return 0;
 }
 
@@ -907,6 +1097,15 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
                                               offsets, h, A, ffn, d, 1, d, nb_max, rotate,
                                               gather_perm, k, T, xcd_group, s);
   }
+  // One 16-column subtile per wave and operand: 48 KiB stages, three of
+  // them in LDS (more of the weight stream in flight per workgroup), and as
+  // many workgroups as the register-ring tile of the same width.
+  if (bm == 128 && variant == kGateUpLdsNarrowVariant) {
+    if (x_tiled) return hipErrorInvalidValue;
+    return launch_lds_cfg<128, 8, kOutSwiGLU, kCpolNT, kLdsNarrowStages, 1>(
+        x, w_gate_up, 2LL * ffn * d, blocks, nb, order, offsets, h, A, ffn, d, 1, d, nb_max, rotate,
+        gather_perm, k, T, xcd_group, s);
+  }
   if (bm == 128 && variant == kGateUpLdsVariant) {
     if (x_tiled) return hipErrorInvalidValue;
     return launch_lds_cfg<128, 8, kOutSwiGLU, kCpolNT>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order,
@@ -922,6 +1121,28 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
   MOE_GU_CFGS(X)
 #undef X
   return hipErrorInvalidValue;
+}
+
+size_t gate_up_sk_slot_bytes(int bm, int variant) {
+  if (bm == 128 && variant == kGateUpLdsNarrowVariant) {
+    using G = LdsGemm<128, 8, kLdsBK, kLdsNarrowStages, kOutSwiGLU, 1>;
+    return (size_t)G::kNG * G::kMT * G::kSub * G::kThreads * 16;
+  }
+  return 0;
+}
+
+hipError_t launch_gate_up_sk(int bm, int variant, const uint16_t* x, const int32_t* gather_perm,
+                             int k, int T, const uint16_t* w_gate_up, const int32_t* blocks,
+                             const int32_t* nb, const int32_t* offsets, uint16_t* h, int d,
+                             int ffn, int rotate, float* part, int32_t* cnt, hipStream_t s) {
+  if (!(bm == 128 && variant == kGateUpLdsNarrowVariant)) return hipErrorInvalidValue;
+  if (ffn % 16 != 0 || d % kLdsBK != 0 || d <= 0) return hipErrorInvalidValue;
+  using G = LdsGemm<128, 8, kLdsBK, kLdsNarrowStages, kOutSwiGLU, 1>;
+  gemm_lds_sk_kernel<128, 8, kLdsBK, kLdsNarrowStages, kCpolNT, 1>
+      <<<kRoundWorkgroups, G::kThreads, 0, s>>>(x, w_gate_up, 2LL * ffn * d, blocks, nb, offsets,
+                                                 h, ffn, d, rotate, gather_perm, k, T,
+                                                 SkWork{part, cnt});
+  return hipGetLastError();
 }
 
 // Fused gate/up SwiGLU and down projection (kOutSwiGLUDown): tiles whose
@@ -967,16 +1188,16 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
     // 1336 -> 1284) and slower where they do not (DeepSeek-V3 T=4096, 940 MB
     // of partials: down 1694 -> 1726, combination 188 -> 219).
     const bool nt = (long long)split * A * d * 4 <= (256LL << 20);
-#define MOE_DOWN_LDS(BMV, CP)                                                                    \
-  return launch_lds_cfg<BMV, 8, kOutF32Parts, CP>(h, w_down, (long long)d * ffn, blocks, nb, order, \
+#define MOE_DOWN_LDS(BMV, CP, ST)                                                                \
+  return launch_lds_cfg<BMV, 8, kOutF32Parts, CP, ST>(h, w_down, (long long)d * ffn, blocks, nb, order, \
                                                   offsets, y, A, d, ffn, split, ksplit, nb_max,   \
                                                   rotate, nullptr, 1, A, xcd_group, s, dyn_split)
     if (bm == 192) {
-      if (nt) MOE_DOWN_LDS(192, kCpolNT);
-      MOE_DOWN_LDS(192, 0);
+      if (nt) MOE_DOWN_LDS(192, kCpolNT, kLdsStages);
+      MOE_DOWN_LDS(192, 0, kLdsStages);
     }
-    if (nt) MOE_DOWN_LDS(128, kCpolNT);
-    MOE_DOWN_LDS(128, 0);
+    if (nt) MOE_DOWN_LDS(128, kCpolNT, kLdsStages);
+    MOE_DOWN_LDS(128, 0, kLdsStages);
 #undef MOE_DOWN_LDS
   }
   // The wide LDS-staged tile: 64 columns per wave (7 waves at BM = 192, 8 at

@@ -67,6 +67,7 @@ int check_options(const moe_options* opt) {
   if (opt->xcd_order < 0 || opt->xcd_order > 3) return MOE_ERR_UNSUPPORTED;
   if (opt->fold_combine < 0 || opt->fold_combine > 2) return MOE_ERR_UNSUPPORTED;
   if (opt->fuse_down < 0 || opt->fuse_down > 2) return MOE_ERR_UNSUPPORTED;
+  if (opt->schedule < 0 || opt->schedule > 2) return MOE_ERR_UNSUPPORTED;
   if (opt->down_variant < 0) return MOE_ERR_UNSUPPORTED;
   if (opt->down_variant > 0) {
     const int bm = opt->block_rows;
@@ -163,7 +164,15 @@ double tile_waste(int n, int tc) {
 // Otherwise, BM = 64 and 128: the narrow variant when the wide one would
 // give at most ~1.5 workgroups per CU; BM = 192: the 112-column variant
 // when its tiles fill the rounds better than 128-column tiles do.
+// At BM = 128 the narrow LDS-staged tile (8 waves x 16 columns, three
+// stages): measured faster than both the 128-column register-ring tile and
+// the 256-column LDS tile on every BM = 128 workload but one, gate/up us,
+// former automatic choice -> narrow, interleaved in one process: Qwen2
+// T=128/256/512 374 -> 353, 387 -> 363, 393 -> 372; Mixtral T=128/256 325
+// -> 308, 333 -> 330; skewed T=128/512 41.9 -> 39.3, 79.0 -> 74.2;
+// DeepSeek-V3 T=512 2164 -> 2156; skewed T=256 44.5 -> 47.1.
 int auto_gu_variant(int A, int E, int ffn, int bm, bool x_tiled) {
+  if (bm == 128 && gate_up_lds_fits(bm, ffn, x_tiled)) return kGateUpLdsNarrowVariant;
   if ((bm == 128 || bm == 192) && gate_up_lds_fits(bm, ffn, x_tiled)) {
     const int tc = gate_up_tile_cols(bm, kGateUpLdsVariant);
     const double waste = tile_waste(ffn, tc);
@@ -193,6 +202,13 @@ int auto_gu_variant(int A, int E, int ffn, int bm, bool x_tiled) {
 // slower on some uniform ones, so automatic is off.
 bool auto_longest_first(int A, int E, int bm) {
   (void)A, (void)E, (void)bm;
+  return false;
+}
+
+// The stream-K schedule of the gate/up GEMM (see gemm_lds_sk_kernel):
+// automatic choice off until measured.
+bool auto_stream_k(int A, int E, int d, int ffn, int bm) {
+  (void)A, (void)E, (void)d, (void)ffn, (void)bm;
   return false;
 }
 
@@ -275,7 +291,11 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->k = k;
   p->A = T * k;
   const int A = p->A;
-  p->bm = (opt && opt->block_rows) ? opt->block_rows : auto_block_rows(A > 0 ? A : 1, E);
+  // The stream-K schedule runs the 128-row tile: automatic block rows are 128 then.
+  const int sch = opt ? opt->schedule : 0;
+  p->bm = (opt && opt->block_rows) ? opt->block_rows
+          : sch == 2               ? 128
+                                   : auto_block_rows(A > 0 ? A : 1, E);
   p->nb_max = (A + p->bm - 1) / p->bm + (E < A ? E : A);
   p->nchunks = (A + kChunk - 1) / kChunk;
   const int rk = opt ? opt->routing_kernels : 0;
@@ -298,7 +318,9 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     p->split = (ksteps + per - 1) / per;  // every part has at least one K step
     p->gu_variant = (opt && opt->tile_variant) ? opt->tile_variant - 1
                                                : auto_gu_variant(A, E, ffn, p->bm, p->x_tiled);
-    if ((p->bm == 128 || p->bm == 192) && p->gu_variant == kGateUpLdsVariant && !p->unfused &&
+    if ((p->bm == 128 || p->bm == 192) &&
+        (p->gu_variant == kGateUpLdsVariant || p->gu_variant == kGateUpLdsNarrowVariant) &&
+        !p->unfused &&
         !gate_up_lds_fits(p->bm, ffn, p->x_tiled))
       p->plan_error = MOE_ERR_UNSUPPORTED;  // forced where it cannot run
     const int fc = opt ? opt->fold_combine : 0;
@@ -329,7 +351,9 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     const int tc = gate_up_down_tile_cols(p->bm, fv);
     const bool fd_ok = tc > 0 && !p->unfused && (long long)d * ffn * 2 < (1LL << 31);
     if (fd == 2 && !fd_ok) p->plan_error = MOE_ERR_UNSUPPORTED;
-    p->fused_down = fd == 2 ? fd_ok : (fd == 0 && fd_ok && auto_fuse_down(A, d, ffn, E, p->bm, tc));
+    // (an explicit stream-K schedule keeps the separate down GEMM)
+    p->fused_down = fd == 2 ? fd_ok
+                            : (fd == 0 && sch != 2 && fd_ok && auto_fuse_down(A, d, ffn, E, p->bm, tc));
     if (p->fused_down) {
       p->gu_variant = fv;
       p->split = (ffn + tc - 1) / tc;
@@ -344,6 +368,21 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     // 97.1 / 89.0 / 91.4 and Mixtral T=512 (8 x 16) 637.3 / 558.8 / 588.0 --
     // two; the device rule picks those.
     p->dyn_split = !(opt && opt->split_k) && !p->fold && !p->fused_down && p->split > 1;
+    // The gate/up GEMM's schedule: one workgroup per (block, column tile),
+    // or stream-K over the narrow LDS-staged tile at BM = 128.
+    p->gu_sk = sch == 2 || (sch == 0 && auto_stream_k(A, E, d, ffn, p->bm));
+    if (p->gu_sk) {
+      const bool gv_ok = !(opt && opt->tile_variant) || p->gu_variant == kGateUpLdsNarrowVariant;
+      const bool ok = p->bm == 128 && gv_ok && !p->unfused && !p->fused_down && !p->x_tiled;
+      if (ok) {
+        p->gu_variant = kGateUpLdsNarrowVariant;
+        const int tc = gate_up_tile_cols(128, kGateUpLdsNarrowVariant);
+        p->sk_units = p->nb_max * ((ffn + tc - 1) / tc);
+      } else {
+        if (sch == 2) p->plan_error = MOE_ERR_UNSUPPORTED;
+        p->gu_sk = 0;
+      }
+    }
   }
   size_t o = 0;
   auto seg = [&](size_t bytes) {
@@ -372,7 +411,10 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->o_logits = seg((size_t)T * E * 4);
   p->router = plan_router(T, d > 0 ? d : 64, E);
   p->o_rparts = seg(p->router.parts > 1 ? (size_t)p->router.parts * T * E * 4 : 0);
-  p->o_fold = seg(p->fold ? (size_t)T * p->dn_tiles * 4 : 0);
+  p->o_fold = seg(((p->fold ? (size_t)T * p->dn_tiles : 0) + (size_t)p->sk_units) * 4);
+  p->o_skpart = seg(p->gu_sk ? 2 * (size_t)kRoundWorkgroups *
+                                   gate_up_sk_slot_bytes(p->bm, p->gu_variant)
+                             : 0);
   p->total_bytes = o;
 }
 
@@ -440,12 +482,15 @@ int forward_from_logits(const uint16_t* x, const LogitSrc& router_logits, const 
                         const uint16_t* W_down, int top_k, int renorm, uint16_t* out, int score,
                         const Plan& p, const moe_options* opt, void* workspace, hipStream_t s) {
   const int T = p.T, d = p.d, ffn = p.ffn;
-  // With the combination folded into the down GEMM, the routing kernels
-  // clear its arrival counters.
-  int32_t* fold_cnt = p.fold ? at<int32_t>(workspace, p.o_fold) : nullptr;
+  // The routing kernels clear the arrival counters of the combination
+  // folded into the down GEMM and the unit counters of the stream-K
+  // gate/up GEMM (one range: the fold's, then stream-K's).
+  const int n_fold = p.fold ? T * p.dn_tiles : 0;
+  int32_t* counters = (p.fold || p.gu_sk) ? at<int32_t>(workspace, p.o_fold) : nullptr;
+  int32_t* fold_cnt = p.fold ? counters : nullptr;
   int32_t* order = p.longest_first ? at<int32_t>(workspace, p.o_order) : nullptr;
   MOE_TRY(run_routing(router_logits, p, renorm, score, workspace, opt, order,
-                      ZeroRange{fold_cnt, p.fold ? T * p.dn_tiles : 0}, s));
+                      ZeroRange{counters, counters ? n_fold + p.sk_units : 0}, s));
   const int32_t* perm = at<int32_t>(workspace, p.o_perm);
   const int32_t* blocks = at<int32_t>(workspace, p.o_blocks);
   const int32_t* nb = at<int32_t>(workspace, p.o_nb);
@@ -477,6 +522,10 @@ int forward_from_logits(const uint16_t* x, const LogitSrc& router_logits, const 
     MOE_TRY_HIP(launch_gate_up_down(p.bm, p.gu_variant, X, gperm, top_k, T, W_gate_up, W_down,
                                     blocks, nb, order, offsets, y, p.A, d, ffn, p.nb_max,
                                     p.gu_rotate, p.gu_xcd, p.x_tiled, s));
+  } else if (p.gu_sk) {
+    MOE_TRY_HIP(launch_gate_up_sk(p.bm, p.gu_variant, X, gperm, top_k, T, W_gate_up, blocks, nb,
+                                  offsets, h, d, ffn, p.gu_rotate,
+                                  at<float>(workspace, p.o_skpart), counters + n_fold, s));
   } else {
     MOE_TRY_HIP(launch_gate_up(p.bm, p.gu_variant, X, gperm, top_k, T, W_gate_up, blocks, nb,
                                order, offsets, h, p.A, d, ffn, p.nb_max, p.gu_rotate, p.gu_xcd,
@@ -620,6 +669,7 @@ int moe_plan_ex(int T, int d, int ffn, int E, int top_k, const moe_options* opt,
   info->fold_combine = p.fold ? 1 : 0;
   info->xcd_grouped = p.gu_xcd ? 1 : 0;
   info->split_on_device = p.dyn_split ? 1 : 0;
+  info->stream_k = p.gu_sk ? 1 : 0;
   info->launches = info->routing_launches + info->gather_launch + (p.unfused ? 3 : 1) +
                    (p.fused_down ? 0 : 1) + (p.fold ? 0 : 1);
   return MOE_OK;

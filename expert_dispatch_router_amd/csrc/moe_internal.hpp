@@ -74,6 +74,8 @@ struct Plan {
   int fused_down;     // gate/up GEMM also does the down projection (split = its column tiles)
   int dyn_split;      // the down GEMM and the combination take the parts from the device
                       // (device_down_split, at most `split`)
+  int gu_sk;          // the gate/up GEMM runs the stream-K schedule (launch_gate_up_sk)
+  int sk_units;       // its counters: nb_max * column tiles
   int plan_error;     // an explicit option the plan cannot honour (MOE_ERR_*), else 0
   // byte offsets into the workspace (256-byte aligned)
   size_t o_ids, o_w, o_counts, o_offsets, o_ccnt, o_cbase, o_perm, o_inv, o_blocks, o_nb;
@@ -83,7 +85,9 @@ struct Plan {
   size_t o_g, o_u;  // unfused gate and up products [A, ffn] bf16
   size_t o_logits;  // router scores [T, E] fp32 (moe_forward_router)
   size_t o_rparts;  // router partial sums [router.parts, T, E] fp32
-  size_t o_fold;    // arrival counters of the folded combination [T, dn_tiles] int32
+  size_t o_fold;    // arrival counters of the folded combination [T, dn_tiles] int32,
+                    // then the stream-K unit counters [sk_units] int32 (one cleared range)
+  size_t o_skpart;  // stream-K partial sums [2 * kRoundWorkgroups slots]
   size_t total_bytes;
 };
 
@@ -212,6 +216,18 @@ struct FoldCombine {
   uint16_t* out;
 };
 
+// The fused gate/up GEMM on the stream-K schedule: kRoundWorkgroups
+// persistent workgroups share the nb * ceil(ffn / tile) * (d / 64) K steps of
+// all units evenly (see gemm_lds_sk_kernel).  part holds 2 * kRoundWorkgroups
+// slots of gate_up_sk_slot_bytes; cnt [nb_max * ceil(ffn / tile)] must be
+// zero when it starts.  Same arguments otherwise as launch_gate_up (row-major
+// activations only: x_tiled is not supported).
+size_t gate_up_sk_slot_bytes(int bm, int variant);  // 0: not compiled
+hipError_t launch_gate_up_sk(int bm, int variant, const uint16_t* x, const int32_t* gather_perm,
+                             int k, int T, const uint16_t* w_gate_up, const int32_t* blocks,
+                             const int32_t* nb, const int32_t* offsets, uint16_t* h, int d,
+                             int ffn, int rotate, float* part, int32_t* cnt, hipStream_t s);
+
 // Fused gate/up SwiGLU and down projection for small problems: each
 // (block, column tile) workgroup keeps its h tile in LDS and writes
 // y[tile, A, d] = h[:, tile cols] Wd[:, tile cols]^T (fp32, one part per
@@ -253,6 +269,9 @@ int gate_up_tile_cols(int bm, int variant);
 // Tile variant of the fused gate/up GEMM at BM = 192 that stages its weights in LDS
 // (7 waves x 32 columns).
 constexpr int kGateUpLdsVariant = 2;
+// Tile variant of the fused gate/up GEMM at BM = 128 that stages its weights in LDS with
+// one 16-column subtile per wave (8 waves x 16 columns) and three stages.
+constexpr int kGateUpLdsNarrowVariant = 3;
 // Tile variant of the down GEMM at BM = 192 that stages its weights in LDS (8 waves x 32
 // columns).
 constexpr int kDownLdsVariant = 2;

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 /* Limits of the library (violations return MOE_ERR_UNSUPPORTED). */
 #define MOE_MAX_EXPERTS 512
@@ -95,9 +95,11 @@ typedef struct moe_options {
      * compiled variant k-1 for the chosen block_rows (which must then be set
      * explicitly).  BM = 64 has variants 0 (256 columns per workgroup) and 1
      * (128 columns); BM = 128 has variants 0 (128 columns, 8 waves), 1
-     * (64 columns) and 2 (256 columns, 8 waves, weights staged in LDS;
-     * the last column tile may be partial; not with gather_mode 3, else
-     * MOE_ERR_UNSUPPORTED); BM = 192 has variants 0 (128 columns, 8 waves),
+     * (64 columns), 2 (256 columns, 8 waves, weights staged in LDS;
+     * the last column tile may be partial) and 3 (128 columns, 8 waves of
+     * one 16-column subtile, weights staged in LDS in three stages; the
+     * stream-K schedule's tile) -- 2 and 3 not with gather_mode 3, else
+     * MOE_ERR_UNSUPPORTED; BM = 192 has variants 0 (128 columns, 8 waves),
      * 1 (112 columns, 7 waves) and 2 (224 columns, 7 waves, weights staged
      * in LDS; the last column tile may be partial; not with gather_mode 3,
      * else MOE_ERR_UNSUPPORTED -- automatic at BM = 192 where ffn is a
@@ -186,6 +188,26 @@ typedef struct moe_options {
      * MOE_ERR_UNSUPPORTED when 2 is asked for.  Rounding differs from the
      * separate down GEMM (other summation order). */
     int fuse_down;
+    /* Schedule of the fused gate/up GEMM: the skew-aware dynamic work
+     * assignment the method leaves as future work ([R] abstract; "Editorial
+     * extensions").  0 = automatic, 1 = one workgroup per (schedule block,
+     * column tile) unit, in rounds of the GPU's 256 CUs, 2 = stream-K: 256
+     * persistent workgroups share the K steps of all units evenly -- the
+     * unit count is the routed block count times the column tiles, read on
+     * the device -- so a skewed routing that leaves a ragged last round, or
+     * fewer units than CUs, still keeps every CU streaming.  A unit split
+     * between workgroups is finished by the workgroup that completes it,
+     * adding the fp32 partial sums in K order (deterministic).  Runs the
+     * 128-row tile with one 16-column subtile per wave (variant 3 of
+     * tile_variant): block_rows must be 0 (taken as 128) or 128,
+     * tile_variant 0 or 4, and
+     * not with the unfused ablation, the fused down projection or gather
+     * mode 3 (else MOE_ERR_UNSUPPORTED when 2 is asked for).  The
+     * workspace grows by 2 * 256 partial slots of 128 KiB and one counter
+     * per unit, which the routing kernels clear on every call.  Rounding
+     * differs from schedule 1 where a unit is split (other association of
+     * the K sum). */
+    int schedule;
     /* NULL, or 7 hipEvent_t handles created by the caller (for instance
      * with moe_timer_create).  events[0] is recorded on the stream before
      * the first kernel and events[i] right after kernel i (1 route, 2
@@ -243,6 +265,7 @@ typedef struct moe_plan_info {
                               whose workgroup count (blocks x column tiles x
                               parts) is nearest to one round of 256, at least
                               1 and at most split_k                           */
+    int stream_k;          /* 1: the gate/up GEMM runs the stream-K schedule   */
 } moe_plan_info;
 
 /* Host-only: fills *info with the launch plan moe_forward_ex would follow.

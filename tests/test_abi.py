@@ -69,9 +69,9 @@ def test_workspace_size_checks():
 
 
 def _o(bm=0, split=0, variant=0, rotate=0, routing=0, gather=0, unfused=0, xcd=0, dvar=0,
-       fold=0, fuse=0):
+       fold=0, fuse=0, sched=0):
     return ctypes.byref(_lib.MoeOptions(bm, split, variant, dvar, rotate, routing, gather, unfused,
-                                        xcd, fold, fuse, None))
+                                        xcd, fold, fuse, sched, None))
 
 
 def test_options_checks():
@@ -94,7 +94,10 @@ def test_options_checks():
     assert _ws(64, 256, 512, 8, 2, _o(192, 0, 3))[0] == OK
     assert _ws(64, 256, 448, 8, 2, _o(192, 0, 3))[0] == OK
     assert _ws(64, 256, 448, 8, 2, _o(192, 0, 3, gather=3))[0] == UNSUP
-    assert _ws(64, 256, 512, 8, 2, _o(128, 0, 4))[0] == UNSUP
+    # the narrow LDS-staged gate/up tile (variant 3 of BM = 128, option value 4)
+    assert _ws(64, 256, 512, 8, 2, _o(128, 0, 4))[0] == OK
+    assert _ws(64, 256, 448, 8, 2, _o(128, 0, 4, gather=3))[0] == UNSUP
+    assert _ws(64, 256, 512, 8, 2, _o(128, 0, 5))[0] == UNSUP
     for bm in (128, 192):
         assert _ws(64, 256, 512, 8, 2, _o(bm, dvar=3))[0] == OK
         assert _ws(64, 320, 512, 8, 2, _o(bm, dvar=3))[0] == UNSUP
@@ -473,3 +476,27 @@ def test_plan_ex_split_on_device():
                            down_variant=1, fold_combine=2)["split_on_device"] == 0
     tiny = CONFIGS["tiny"]
     assert moe.moe_plan_ex(tiny.T, tiny.d, tiny.ffn, tiny.E, tiny.top_k)["split_on_device"] == 0
+
+
+def test_stream_k_schedule_options():
+    """schedule = 2 (stream-K gate/up GEMM): runs the narrow 128-row LDS tile
+    (automatic block rows become 128), adds 2 x 256 partial slots of 128 KiB
+    and one counter per (block, column tile) unit to the workspace, and is
+    refused where that tile cannot run."""
+    sk = CONFIGS["skewed_128"]
+    args = (sk.T, sk.d, sk.ffn, sk.E, sk.top_k)
+    info = moe.moe_plan_ex(*args, schedule=2)
+    assert info["stream_k"] == 1 and info["block_rows"] == 128 and info["gate_up_variant"] == 3
+    assert moe.moe_plan_ex(*args, schedule=1)["stream_k"] == 0
+    assert moe.moe_plan_ex(*args, schedule=2, block_rows=128, tile_variant=4)["stream_k"] == 1
+    plain = moe.moe_workspace_size(*args, block_rows=128, tile_variant=4)
+    streamed = moe.moe_workspace_size(*args, schedule=2)
+    units = (-(-sk.T * sk.top_k // 128) + min(sk.E, sk.T * sk.top_k)) * (sk.ffn // 128)
+    assert streamed - plain >= 2 * 256 * 128 * 1024 + 4 * units
+    assert streamed - plain <= 2 * 256 * 128 * 1024 + 4 * units + 512
+    for bad in (_o(0, sched=3), _o(0, sched=-1), _o(192, sched=2), _o(128, 0, 1, sched=2),
+                _o(128, 0, 3, sched=2), _o(0, unfused=1, sched=2), _o(0, gather=3, sched=2),
+                _o(0, fuse=2, sched=2)):
+        assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
+    assert _ws(64, 256, 512, 8, 2, _o(0, sched=2))[0] == OK
+    assert _ws(64, 256, 512, 8, 2, _o(128, 0, 4, sched=2))[0] == OK

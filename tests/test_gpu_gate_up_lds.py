@@ -180,15 +180,34 @@ def test_lds_gate_up_at_128_rows():
     assert torch.equal(out.view(torch.int16), base.view(torch.int16))
 
 
+NARROW = 4  # tile_variant option value of the narrow LDS-staged tile (variant 3 of BM = 128)
+
+
 def test_lds_gate_up_at_128_rows_is_automatic():
-    """64 experts x 4 tiles of ffn = 1024 fill a round: the automatic
-    options run the BM = 128 LDS-staged tile (the same bytes as forcing it)."""
+    """At BM = 128 the automatic options run the narrow LDS-staged tile (8
+    waves x 16 columns, three stages): the same bytes as forcing it, as the
+    256-column LDS tile and as the 128-column register-ring tile."""
     x, lg, wgu, wd, k, ref = _case("gate_up_128_auto", 256, 256, 1024, 64, 8, 40)
     assert moe.moe_plan(256, 256, 1024, 64, 8)[0] == 128
+    assert moe.moe_plan_ex(256, 256, 1024, 64, 8)["gate_up_variant"] == NARROW - 1
     auto = moe.moe_forward(x, lg, wgu, wd, k, True)
-    forced = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=128, tile_variant=3)
-    assert torch.equal(auto.view(torch.int16), forced.view(torch.int16))
     parity.check_out(auto, ref, "lds gate/up bm=128 automatic")
+    for tv in (NARROW, 3, 1):
+        forced = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=128, tile_variant=tv)
+        assert torch.equal(auto.view(torch.int16), forced.view(torch.int16)), tv
+
+
+@pytest.mark.parametrize("name", ["ragged", "multi_block", "one_step", "two_steps"])
+def test_narrow_lds_gate_up_tile(name):
+    """The narrow LDS-staged tile at BM = 128 on ragged blocks, experts
+    with several blocks, one and two K steps and a partial last column
+    tile (ffn = 448, 1344): the oracle's tolerance, and the bytes of the
+    128-column register-ring tile."""
+    x, lg, wgu, wd, k, ref = _case(name, *CASES[name])
+    out = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=128, tile_variant=NARROW)
+    parity.check_out(out, ref, f"narrow {name}")
+    base = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=128, tile_variant=1)
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
 
 
 # ------------------------------------------- the wide LDS-staged down tile
