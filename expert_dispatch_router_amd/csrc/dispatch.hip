@@ -14,6 +14,8 @@
 // makes the reorder unique and deterministic; a block never spans two
 // experts; an expert with no rows gets no block; the token-offset of a block
 // is its first sorted row.
+#include <type_traits>
+
 #include "moe_internal.hpp"
 #include "route_core.hpp"
 #include "../../include/moe.h"
@@ -291,7 +293,9 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
     int32_t* __restrict__ blocks, int32_t* __restrict__ nb, int32_t* __restrict__ order,
     ZeroRange zero) {
-  static_assert(EMAX <= 32 && EMAX * kSmallWaves <= kScanThreads, "one thread per (e, wave)");
+  static_assert(EMAX <= 64 && EMAX * kSmallWaves <= kScanThreads, "one thread per (e, wave)");
+  using Mask = typename std::conditional<(EMAX > 32), unsigned long long, unsigned>::type;
+  constexpr int kMaskBits = 8 * sizeof(Mask);
   __shared__ unsigned long long wmask[EMAX * kSmallWaves];  // [e][wave] ballot of expert e
   __shared__ int start[EMAX * kSmallWaves];                 // [e][wave] first sorted position
   __shared__ int wave_sum[kSmallWaves];
@@ -305,8 +309,8 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
   float v[EMAX];
 #pragma unroll
   for (int e = 0; e < EMAX; ++e) v[e] = (ok && e < E) ? load_logit(logits, (size_t)t * E + e) : 0.0f;
-  const unsigned valid = ok ? (E >= 32 ? 0xffffffffu : (1u << E) - 1u) : 0u;
-  unsigned live = valid;
+  const Mask valid = ok ? (E >= kMaskBits ? ~Mask(0) : (Mask(1) << E) - Mask(1)) : Mask(0);
+  Mask live = valid;
   float sel_v[MOE_MAX_TOPK];
   int sel_e[MOE_MAX_TOPK];
 #pragma unroll
@@ -316,11 +320,11 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
     if (j < k) {
 #pragma unroll
       for (int e = 0; e < EMAX; ++e)
-        if (((live >> e) & 1u) && ranks_before(v[e], e, bv, be)) {
+        if (((live >> e) & Mask(1)) && ranks_before(v[e], e, bv, be)) {
           bv = v[e];
           be = e;
         }
-      if (be >= 0) live &= ~(1u << be);
+      if (be >= 0) live &= ~(Mask(1) << be);
     }
     sel_v[j] = bv;
     sel_e[j] = be;
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
   if (score == MOE_SCORE_SOFTMAX && !renorm) {
 #pragma unroll
     for (int e = 0; e < EMAX; ++e)
-      if ((valid >> e) & 1u) z_all += expf(v[e] - sel_v[0]);
+      if ((valid >> e) & Mask(1)) z_all += expf(v[e] - sel_v[0]);
   }
   float wt[MOE_MAX_TOPK];
   topk_weights(sel_v, k, renorm, score, z_all, wt);
@@ -343,9 +347,9 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
   }
 
   // 2. count
-  const unsigned chosen = valid & ~live;
+  const Mask chosen = valid & ~live;
   for (int e = 0; e < E; ++e) {
-    const unsigned long long m = __ballot((chosen >> e) & 1u);
+    const unsigned long long m = __ballot((int)((chosen >> e) & Mask(1)));
     if (lane == 0) wmask[e * kSmallWaves + wave] = m;
   }
   __syncthreads();
@@ -495,8 +499,10 @@ hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int
     MOE_LAUNCH_SMALL(8);
   else if (E <= 16)
     MOE_LAUNCH_SMALL(16);
-  else
+  else if (E <= 32)
     MOE_LAUNCH_SMALL(32);
+  else
+    MOE_LAUNCH_SMALL(64);
 #undef MOE_LAUNCH_SMALL
   return hipGetLastError();
 }

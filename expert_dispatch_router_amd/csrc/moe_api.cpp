@@ -300,6 +300,7 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->nchunks = (A + kChunk - 1) / kChunk;
   const int rk = opt ? opt->routing_kernels : 0;
   p->small_routing = rk == 1 || (rk == 0 && small_routing_fits(T, E, k) &&
+                                  E <= kSmallRoutingAutoMaxExperts &&
                                   (long long)T * E * k <= kSmallRoutingAutoWork);
   // Otherwise two launches (route; histogram, scan, schedule and reorder in
   // one workgroup) where the per-group counts fit in LDS, else three.

@@ -156,10 +156,13 @@ hipError_t launch_permute(const int32_t* ids, int A, int E, int nchunks, const i
 // Whole routing (route + histogram/scan/schedule + reorder) in one
 // workgroup of 1024 threads, one token per thread.
 constexpr int kSmallRoutingMaxTokens = 1024;
-constexpr int kSmallRoutingMaxExperts = 32;
-// The automatic choice also bounds T*E*k: the kernel's top-k runs on one CU
-// (measured faster than the three launches at E = 8, slower at E = 64).
+constexpr int kSmallRoutingMaxExperts = 64;
+// The automatic choice also bounds T*E*k and E: the kernel's top-k runs on
+// one CU (measured faster than the three launches at E = 8; at E = 64 slower
+// than the two launches, pass us: skewed T=128/512 79.2 -> 90.9, 127.4 ->
+// 144.6; Qwen2 T=128 576.5 -> 601.4).
 constexpr long long kSmallRoutingAutoWork = 1 << 15;
+constexpr int kSmallRoutingAutoMaxExperts = 32;
 bool small_routing_fits(int T, int E, int k);
 hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int k, int renorm,
                                        int score, int bm, int32_t* ids, float* w,

@@ -131,7 +131,7 @@ typedef struct moe_options {
      * for the histogram, scan, schedule and reorder) when
      * ceil(T*top_k/64)*E <= 16384; else three launches; 1 = the
      * one-workgroup kernel (MOE_ERR_UNSUPPORTED beyond T <= 1024 and
-     * E <= 32); 2 = three launches; 3 = two launches
+     * E <= 64); 2 = three launches; 3 = two launches
      * (MOE_ERR_UNSUPPORTED beyond ceil(T*top_k/64)*E <= 16384).  Same
      * results either way. */
     int routing_kernels;

@@ -122,10 +122,11 @@ def test_routing_and_gather_options():
     for r in (0, 1, 2, 3):
         for g in (0, 1, 2, 3):
             assert _ws(64, 256, 512, 8, 2, _o(routing=r, gather=g))[0] == OK
-    # the one-workgroup routing kernel: one token per thread, at most 32 experts
+    # the one-workgroup routing kernel: one token per thread, at most 64 experts
     assert _ws(1024, 256, 512, 32, 16, _o(routing=1))[0] == OK
+    assert _ws(1024, 256, 512, 64, 16, _o(routing=1))[0] == OK
     assert _ws(1025, 256, 512, 8, 2, _o(routing=1))[0] == UNSUP
-    assert _ws(512, 256, 512, 33, 2, _o(routing=1))[0] == UNSUP
+    assert _ws(512, 256, 512, 65, 2, _o(routing=1))[0] == UNSUP
     assert _ws(1025, 256, 512, 8, 2, _o(routing=2))[0] == OK
     r = ctypes.c_size_t(0)
     assert moe.lib().moe_route_workspace_size(1025, 8, 2, _o(routing=1), ctypes.byref(r)) == UNSUP

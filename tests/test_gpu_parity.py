@@ -38,7 +38,7 @@ def _gpu():
 
 def _small_routing_fits(T, E, k):
     # limits of the one-workgroup routing kernel (include/moe.h, routing_kernels)
-    return T <= 1024 and E <= 32
+    return T <= 1024 and E <= 64
 
 
 def _fused_reorder_fits(A, E):
@@ -46,12 +46,14 @@ def _fused_reorder_fits(A, E):
     return (A + 63) // 64 * E <= 16384
 
 
-@pytest.mark.parametrize("routing", [0, 2, 3])
+@pytest.mark.parametrize("routing", [0, 1, 2, 3])
 @pytest.mark.parametrize("name", sorted(synth.CONFIGS))
 def test_route_workloads_bit_exact(name, routing):
     cfg = synth.CONFIGS[name]
     if routing == 3 and not _fused_reorder_fits(cfg.T * cfg.top_k, cfg.E):
         pytest.skip("beyond the two-launch routing's limit")
+    if routing == 1 and not _small_routing_fits(cfg.T, cfg.E, cfg.top_k):
+        pytest.skip("beyond the one-workgroup routing's limit")
     lg = synth.make_logits(cfg, 0, DEV)
     x = synth.make_x(cfg, 0, DEV)
     g = moe.moe_route(lg, cfg.top_k, cfg.renormalize, cfg.score, x=x, routing_kernels=routing)
@@ -126,10 +128,12 @@ def test_route_two_launches_at_its_limit():
 
 
 def test_route_small_kernel_at_its_limits():
-    """The one-workgroup kernel at its limits (1024 tokens, 32 experts, top-16)
-    and at E=k: both routing paths give the oracle's artefacts."""
+    """The one-workgroup kernel at its limits (1024 tokens, 64 experts, top-16),
+    at 32 and 33 experts (the 32- and 64-bit expert masks) and at E=k: both
+    routing paths give the oracle's artefacts."""
     gen = torch.Generator().manual_seed(21)
-    for T, E, k in ((1024, 32, 16), (1024, 8, 2), (1000, 17, 5), (3, 4, 4), (1024, 1, 1)):
+    for T, E, k in ((1024, 64, 16), (1024, 32, 16), (1000, 33, 8), (777, 64, 4), (64, 64, 64 // 4),
+                    (1024, 8, 2), (1000, 17, 5), (3, 4, 4), (1024, 1, 1), (5, 64, 16)):
         assert _small_routing_fits(T, E, k)
         lg = torch.randn(T, E, generator=gen).to(DEV)
         ref = None
@@ -365,17 +369,18 @@ def test_forward_maximum_experts_and_topk():
 
 
 def test_forward_one_workgroup_routing_at_its_limit():
-    """T = 1024 tokens, E = 32, top_k = 16 through the one-workgroup routing
-    kernel (its largest problem), every token against the oracle.  Rows whose
+    """T = 1024 tokens, E = 32 and 64, top_k = 16 through the one-workgroup
+    routing kernel (its largest problems), every token against the oracle.  Rows whose
     weight is dominated by one expert reach several times the output RMS,
     where exact arithmetic carrying only the bf16 roundings of h and of the
     output already misses 2e-2 * RMS (tests/test_format_floor.py): the
     elements are held to their format floor where that is larger."""
-    cfg, x, lg, wgu, wd = parity.make_case(1024, 128, 384, 32, 16, seed=78)
-    out = moe.moe_forward(x, lg, wgu, wd, 16, True, routing_kernels=1)
-    ref = parity.oracle_out(x, lg, wgu, wd, 16, 0, True)
-    parity.check_out(out, ref, "T=1024 E=32 k=16",
-                     floor=parity.format_floor(x, lg, wgu, wd, 16, 0, True, ref))
+    for E, seed in ((32, 78), (64, 79)):
+        cfg, x, lg, wgu, wd = parity.make_case(1024, 128, 384, E, 16, seed=seed)
+        out = moe.moe_forward(x, lg, wgu, wd, 16, True, routing_kernels=1)
+        ref = parity.oracle_out(x, lg, wgu, wd, 16, 0, True)
+        parity.check_out(out, ref, f"T=1024 E={E} k=16",
+                         floor=parity.format_floor(x, lg, wgu, wd, 16, 0, True, ref))
 
 
 def test_forward_maximum_rows():

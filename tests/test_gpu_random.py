@@ -40,7 +40,7 @@ def _cases(n=24, seed=1234):
         if rng.random() < 0.4:
             opts["split_k"] = int(rng.integers(1, 4))
         opts["routing_kernels"] = int(rng.integers(0, 3))
-        if opts["routing_kernels"] == 1 and not (T <= 1024 and E <= 32):
+        if opts["routing_kernels"] == 1 and not (T <= 1024 and E <= 64):
             opts["routing_kernels"] = 2
         opts["gather_mode"] = int(rng.integers(0, 4))
         opts["rotate"] = int(rng.integers(0, 4))
