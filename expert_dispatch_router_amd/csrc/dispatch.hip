@@ -28,20 +28,33 @@ constexpr int kAllChunkCounts = 16384;  // int counters of all (chunk, expert) p
 static_assert(kScanThreads == kChunk, "one thread per row of a chunk");
 static_assert(MOE_MAX_EXPERTS <= kScanThreads, "one thread per expert in the scans");
 
-// Inclusive scan of v over the first MOE_MAX_EXPERTS threads (Hillis-Steele
-// in LDS); threads beyond contribute nothing.  Ends with a barrier.
-__device__ int block_inclusive_scan(int v, int* sh) {
+// Inclusive scan of v over the first MOE_MAX_EXPERTS threads; threads
+// beyond contribute nothing and get 0.  Each wave scans its 64 values in
+// registers (shuffles), the wave totals go through LDS (sh, at least
+// MOE_MAX_EXPERTS / 64 ints): two barriers, the last one at the end.
+// *total receives the sum of all values.
+constexpr int kScanWaves = MOE_MAX_EXPERTS / 64;
+__device__ int block_inclusive_scan(int v, int* sh, int* total = nullptr) {
   const int tid = threadIdx.x;
-  if (tid < MOE_MAX_EXPERTS) sh[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < MOE_MAX_EXPERTS; off <<= 1) {
-    int add = 0;
-    if (tid < MOE_MAX_EXPERTS && tid >= off) add = sh[tid - off];
-    __syncthreads();
-    if (tid < MOE_MAX_EXPERTS) sh[tid] += add;
-    __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  int x = tid < MOE_MAX_EXPERTS ? v : 0;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  return tid < MOE_MAX_EXPERTS ? sh[tid] : 0;
+  if (lane == 63 && wave < kScanWaves) sh[wave] = x;
+  __syncthreads();
+  int base = 0, all = 0;
+#pragma unroll
+  for (int q = 0; q < kScanWaves; ++q) {
+    const int t = sh[q];
+    base += q < wave ? t : 0;
+    all += t;
+  }
+  if (total) *total = all;
+  __syncthreads();  // sh is free again
+  return tid < MOE_MAX_EXPERTS ? x + base : 0;
 }
 
 // One workgroup.  Per chunk c of kChunk flat rows: count each expert in LDS,
@@ -152,8 +165,8 @@ __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
   if (order) {  // uniform
     const int nfull = cnt / bm;
     const int rem = cnt - nfull * bm;
-    const int fincl = block_inclusive_scan(nfull, sh);
-    const int ftotal = sh[MOE_MAX_EXPERTS - 1];
+    int ftotal;
+    const int fincl = block_inclusive_scan(nfull, sh, &ftotal);
     if (tid < E) {
       const int b0 = bincl - nbk;
       for (int r = 0; r < nfull; ++r) order[fincl - nfull + r] = b0 + r;
