@@ -30,7 +30,11 @@ def _gpu():
                                        ("tiny", {"fuse_down": 2}),
                                        # two-launch routing, the 64-column-per-wave down tile
                                        ("qwen2_128", {}), ("skewed_256", {}),
-                                       ("qwen2_128", {"routing_kernels": 3, "xcd_order": 2})])
+                                       ("qwen2_128", {"routing_kernels": 3, "xcd_order": 2}),
+                                       # the stream-K gate/up schedule: unit counters cleared
+                                       # by the routing kernels on every replay
+                                       ("skewed_128", {"schedule": 2}),
+                                       ("qwen2_128", {"schedule": 2, "routing_kernels": 2})])
 def test_forward_graph_replays_match_eager(name, opts):
     cfg = synth.CONFIGS[name]
     x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)

@@ -142,7 +142,8 @@ def _cases_lds_tiles(n=16, seed=2468):
                 "rotate": int(rng.integers(0, 4)), "xcd_order": int(rng.integers(0, 3)),
                 "fuse_down": 1}
         if rng.random() < 0.7:
-            opts["tile_variant"] = 3          # the LDS-staged gate/up tile
+            # the LDS-staged gate/up tiles: 2 subtiles per wave, or (BM = 128) one
+            opts["tile_variant"] = int(rng.choice([3, 4])) if bm == 128 else 3
         dv = [0, 4] + ([3] if d % 256 == 0 else [])
         opts["down_variant"] = int(rng.choice(dv))
         if rng.random() < 0.6:
@@ -194,6 +195,40 @@ def _cases_many_blocks(n=12, seed=97531):
         opts["routing_kernels"] = int(rng.choice([0, 2, 3] if fits else [0, 2]))
         out.append((i, T, d, F, E, k, score, renorm, opts))
     return out
+
+
+def _cases_stream_k(n=12, seed=4242):
+    """Draws over the stream-K gate/up schedule (schedule = 2): units from
+    one to thousands, K steps from 2 to 16, ragged blocks and partial last
+    column tiles, with the routing, gather, rotation, split and down tile
+    drawn."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 5, 8, 13, 32, 64, 100]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([1, 3, 17, 64, 130, 257, 600]))
+        d = int(64 * rng.integers(2, 17))
+        F = int(64 * rng.integers(1, 16))  # odd multiples of 64: a partial last column tile
+        score = int(rng.integers(0, 2))
+        renorm = bool(rng.integers(0, 2))
+        opts = {"schedule": 2, "gather_mode": int(rng.integers(0, 3)),
+                "rotate": int(rng.integers(0, 5)), "xcd_order": int(rng.integers(0, 3))}
+        if rng.random() < 0.4:
+            opts["split_k"] = int(rng.integers(1, 4))
+        fits = (T * k + 63) // 64 * E <= 16384
+        opts["routing_kernels"] = int(rng.choice([0, 2, 3] if fits else [0, 2]))
+        out.append((i, T, d, F, E, k, score, renorm, opts))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases_stream_k(), ids=lambda c: f"sk{c[0]}")
+def test_random_problem_stream_k(case):
+    i, T, d, F, E, k, score, renorm, opts = case
+    cfg, x, lg, wgu, wd = parity.make_case(T, d, F, E, k, score=score, renorm=renorm, seed=1300 + i)
+    out = moe.moe_forward(x, lg, wgu, wd, k, renorm, score="sigmoid" if score else "softmax",
+                          **opts)
+    _check(out, x, lg, wgu, wd, k, score, renorm, f"sk{i} T={T} d={d} F={F} E={E} k={k} {opts}")
 
 
 @pytest.mark.parametrize("case", _cases_many_blocks(), ids=lambda c: f"big{c[0]}")
