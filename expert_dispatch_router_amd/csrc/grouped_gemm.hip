@@ -898,13 +898,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
   lds_tile_store<BM, WAVES, BK, STAGES, MODE, SUB>(acc, out, A, N, r0, rows, n0, part);
 }
 
-// Stream-K schedule of the fused gate/up GEMM (one launch of G persistent
+// Stream-K schedule of the fused gate/up GEMM (one launch of persistent
 // workgroups).  The work is every (block, column tile) unit of the schedule
 // built on the device times its nks K steps: I = nb * n_tiles * nks
-// iterations, of which workgroup g takes [g * I / G, (g + 1) * I / G) (G =
-// min(launched workgroups, I), so no range is empty).  So
-// every workgroup streams the same number of weight steps whatever the
-// routing, instead of one unit per workgroup in rounds of G.  A workgroup
+// iterations, of which workgroup g takes [g * I / NW, (g + 1) * I / NW) (NW =
+// min(launched workgroups, I), so no range is empty).  So every workgroup
+// streams the same number of weight steps whatever the routing, instead of
+// one unit per workgroup in rounds of the CU count.  A workgroup
 // runs the stretch of each unit its range covers; a unit covered whole is
 // finished on the spot (SwiGLU, h written), a stretch of a split unit leaves
 // its fp32 gate and up sums in a slot of `sk.part` (slot 2g for the first
@@ -921,7 +921,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
 // increment completes the count acquires (agent scope, every thread) before
 // reading the other stretches with agent-scope loads.
 struct SkWork {
-  float* part;   // [2 * G] slots of NG * MT * SUB * threads f32x4
+  float* part;   // [2 * launched workgroups] slots of NG * MT * SUB * threads f32x4
   int32_t* cnt;  // per unit, zero at entry
 };
 

@@ -206,7 +206,11 @@ bool auto_longest_first(int A, int E, int bm) {
 }
 
 // The stream-K schedule of the gate/up GEMM (see gemm_lds_sk_kernel):
-// automatic choice off until measured.
+// measured slower than one workgroup per unit of the same tile on every
+// workload (gate/up us: skewed T=128 39.3 -> 251.4, Qwen2 T=128 353 -> 362,
+// Mixtral T=128 308 -> 380, DeepSeek-V3 T=512 2156 -> 2203): the hand-off's
+// agent-scope fences write back and invalidate whole L2s, and the units'
+// activation rows are fetched once per workgroup sharing a unit.  Off.
 bool auto_stream_k(int A, int E, int d, int ffn, int bm) {
   (void)A, (void)E, (void)d, (void)ffn, (void)bm;
   return false;
