@@ -136,8 +136,9 @@ double round_balance(long long wg, long long slots) {
 // workgroups fill whole rounds of 256: with few experts each block holds
 // one expert either way, and that tile's launch has no partial round where
 // the narrow 128-column tile's has one (Mixtral-shaped T = 128 / 256, 8
-// blocks: 512 workgroups against 896).  Measured, pass ms, interleaved:
-// Mixtral T=128 0.4666 -> 0.4604, T=256 0.4930 -> 0.4756; the rule leaves
+// blocks: 512 workgroups against 896).  Measured, pass ms, interleaved,
+// on two boxes: Mixtral T=128 0.4666 -> 0.4604 and 0.4664 -> 0.4660, T=256
+// 0.4930 -> 0.4756 and 0.4925 -> 0.4876; the rule leaves
 // Qwen2- and skewed-shaped workloads (ffn not a multiple of 224) at 128
 // rows, where 192 measured slower (Qwen2 T=128 0.5744 -> 0.5775, skewed
 // T=128 0.0798 -> 0.0860).
