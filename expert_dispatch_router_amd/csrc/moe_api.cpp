@@ -211,8 +211,8 @@ int auto_gu_variant(int A, int E, int ffn, int bm, bool x_tiled) {
 
 // XCD-grouped workgroup order: measured 1-2% faster when a launch has many
 // schedule blocks (each XCD then streams its own range of experts and keeps
-// their activation rows in its L2); with few 128-row blocks mixed to a few
-// percent slower, with few 192-row blocks faster (below).
+// their activation rows in its L2), and neutral to a few percent slower with
+// few blocks (a few experts' weights then stream through one XCD each).
 // Launching the blocks longest first when they are not grouped by XCD:
 // measured no faster on the skewed workloads (the tail round of a launch is
 // bound by each workgroup's own stream, not by which blocks run in it) and
@@ -233,17 +233,9 @@ bool auto_stream_k(int A, int E, int d, int ffn, int bm) {
   return false;
 }
 
-// Also grouped at 192-row blocks with few experts: each block is one
-// expert's rows (~1 MiB of activations at Mixtral's d = 4096), re-read by
-// all its 64 column tiles, which grouping keeps in one XCD's L2.  Measured
-// (pass ms, interleaved, plain -> grouped): Mixtral T=128 0.4656 -> 0.4575,
-// T=256 0.4735 -> 0.4676, T=512 0.5389 -> 0.5336 (both GEMMs faster); at
-// 128-row blocks it is mixed (Qwen2 T=128 0.5721 -> 0.5647, T=256 0.5868 ->
-// 0.5960, T=512 0.6138 -> 0.6399) or slower (skewed T=128/256/512 0.0778 ->
-// 0.0794, 0.0951 -> 0.0984, 0.1256 -> 0.1281).
 bool auto_xcd_order(int A, int E, int bm) {
   const long long blocks = std::max<long long>((A + bm - 1) / bm, std::min(E, A));
-  return blocks >= 128 || (bm == 192 && E <= 16);
+  return blocks >= 128;
 }
 
 // Rotating the K start (see the GEMM kernel) was measured faster or equal on
