@@ -40,6 +40,13 @@
 //     the workgroup that writes the last of a token's k * split partials of
 //     a tile computes that token's output columns there, in the same fixed
 //     order as the combination kernel.  No waiting: every workgroup ends.
+//   * The tiles above are the register-ring tiles.  The LDS-staged tiles
+//     (gemm_lds_kernel, the default on most shapes) fetch weights and
+//     activations by direct-to-LDS loads into a ring of two or three stages
+//     instead, which frees the registers for wider tiles (224 columns at
+//     BM = 192) or, with one subtile per wave, for a third stage (the narrow
+//     tile of BM = 128).  gemm_lds_sk_kernel runs the same multiply loop on
+//     a stream-K schedule (an option).
 #include "buffer_load.hpp"
 #include "combine_core.hpp"
 
@@ -532,13 +539,17 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
 // workgroup then streams its block's activation rows through the CU's
 // vector-memory path once per 112 weight columns, ~0.57 activation bytes
 // per weight byte at Mixtral's ~128 rows per block, and those reads share
-// the path with the weight stream.  Here each wave owns two subtiles
-// (WAVES * 32 columns per workgroup: half the activation bytes per weight
-// byte) and its 192 accumulator registers fit only because the weight ring
-// lives in LDS: weights and activations are fetched by direct-to-LDS
-// buffer loads (no VGPRs), STAGES stages of BK of K each.
+// the path with the weight stream.  Here each wave owns SUB subtiles per
+// operand -- two (WAVES * 32 columns per workgroup: half the activation
+// bytes per weight byte; its 192 accumulator registers at BM = 192 fit only
+// because the weight ring lives in LDS), or one (the narrow tile: WAVES * 16
+// columns, smaller stages, so three of them fit) -- and weights and
+// activations are fetched by direct-to-LDS buffer loads (no VGPRs), STAGES
+// (two or three) stages of BK of K each.
 //
-// LDS stage: WAVES * 4 weight groups, then BM/16 activation groups; a group
+// LDS stage: WAVES * kGPW weight groups (kGPW = NG operands -- or the wide
+// mode's two column groups -- times SUB subtiles), then BM/16 activation
+// groups; a group
 // is 16 rows x (2 * BK) bytes, written by BK/32 loads of 64 lanes x 16
 // bytes.  Load h of a group fetches rows [R*h, R*h + R) (R = 1024 / row
 // bytes), whole rows of the step: with BK = 64 each load reads whole
@@ -547,7 +558,7 @@ hipError_t launch_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
 // s ^ swz(r), swz(r) = (r >> 2) & 3 (BK = 32) or (r >> 1) & 7 (BK = 64), so
 // the MFMA fragment reads -- 16 rows at one K chunk per 16 lanes -- hit 64
 // distinct banks.  Every wave issues the same number of loads per stage
-// (4 weight groups, kXPerWave activation groups; surplus activation slots
+// (kGPW weight groups, kXPerWave activation groups; surplus activation slots
 // repeat a group: same bytes to the same place), so one immediate
 // "vmcnt" waits for the wave's own loads of a stage; the barrier
 // after it publishes the stage to all waves.
