@@ -503,7 +503,10 @@ def run(args):
                    "active_experts": alg["e_act"], "seed": args.seed,
                    "launches_per_pass": plan["launches"],
                    "swiglu": "unfused ablation" if unfused else "fused",
-                   "down_projection": "in the gate/up GEMM" if plan["fused_down"] else "own GEMM"},
+                   "down_projection": "in the gate/up GEMM" if plan["fused_down"] else "own GEMM",
+                   "gate_up_blocks": ("variable: 256 rows for experts past 128 where one round "
+                                      "of workgroups needs it (decided on the device)")
+                                     if plan["variable_rows"] else "fixed"},
         "tflops": alg["flop"] / t_step / 1e12,
         "hbm_gbs": alg["bytes"] / t_step / 1e9,
         "roofline_frac_step": t_roof / t_step,
@@ -605,7 +608,8 @@ def summarize_traffic(fetch_dir, write_dir, workload, copy_bytes,
         return args[4] if len(args) > 4 else None
 
     classes = {
-        "gate_up_swiglu": lambda n: mode(n) == 0,
+        # the variable-rows kernel is the same gate/up SwiGLU GEMM
+        "gate_up_swiglu": lambda n: mode(n) == 0 or "gemm_lds_var_kernel" in n,
         "down": lambda n: mode(n) in (1, 4),   # fp32 parts: 32 or 64 columns per wave
         "proj_bf16": lambda n: mode(n) == 2,
         "swiglu_act": lambda n: "swiglu_act_kernel" in n,

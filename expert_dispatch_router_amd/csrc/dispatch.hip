@@ -57,6 +57,63 @@ __device__ int block_inclusive_scan(int v, int* sh, int* total = nullptr) {
   return tid < MOE_MAX_EXPERTS ? x + base : 0;
 }
 
+// block_inclusive_scan of two values at once (the same two barriers; sh
+// holds at least 2 * kScanWaves ints): a and b are replaced by their
+// inclusive scans, ta and tb receive the totals.
+__device__ void block_inclusive_scan2(int& a, int& b, int* sh, int& ta, int& tb) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  int x = tid < MOE_MAX_EXPERTS ? a : 0;
+  int y = tid < MOE_MAX_EXPERTS ? b : 0;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int xs = __shfl_up(x, off, 64);
+    const int ys = __shfl_up(y, off, 64);
+    if (lane >= off) {
+      x += xs;
+      y += ys;
+    }
+  }
+  if (lane == 63 && wave < kScanWaves) {
+    sh[wave] = x;
+    sh[kScanWaves + wave] = y;
+  }
+  __syncthreads();
+  int bx = 0, by = 0, ax = 0, ay = 0;
+#pragma unroll
+  for (int q = 0; q < kScanWaves; ++q) {
+    const int tx = sh[q], ty = sh[kScanWaves + q];
+    bx += q < wave ? tx : 0;
+    by += q < wave ? ty : 0;
+    ax += tx;
+    ay += ty;
+  }
+  ta = ax;
+  tb = ay;
+  __syncthreads();  // sh is free again
+  a = tid < MOE_MAX_EXPERTS ? x + bx : 0;
+  b = tid < MOE_MAX_EXPERTS ? y + by : 0;
+}
+
+// Whether the variable-size table merges (see VarRows): nb_fixed and
+// nb_merged are the block counts of the two cuttings.
+__device__ __forceinline__ bool var_rows_merge(const VarRows& var, int nb_fixed, int nb_merged) {
+  if (var.mode == kVarRowsAlways) return true;
+  return (long long)nb_fixed * var.tiles > kRoundWorkgroups &&
+         (long long)nb_merged * var.tiles <= kRoundWorkgroups;
+}
+
+// n blocks of expert e from table entry b0: `size` rows each from row0, the
+// last holding the rest of the expert's cnt rows.
+__device__ __forceinline__ void write_var_blocks(int32_t* vb, int b0, int n, int e, int row0,
+                                                 int cnt, int size) {
+  for (int r = 0; r < n; ++r) {
+    vb[3 * (b0 + r)] = e;
+    vb[3 * (b0 + r) + 1] = row0 + r * size;
+    vb[3 * (b0 + r) + 2] = min(size, cnt - r * size);
+  }
+}
+
 // One workgroup.  Per chunk c of kChunk flat rows: count each expert in LDS,
 // record the count and the number of earlier rows of that expert.  Then the
 // expert totals, their exclusive prefix (offsets), the number of blocks of
@@ -74,7 +131,8 @@ __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
     const int32_t* __restrict__ ids, int A, int E, int bm, int nchunks,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ chunk_cnt,
     int32_t* __restrict__ chunk_base, int32_t* __restrict__ blocks, int32_t* __restrict__ nb,
-    int32_t* __restrict__ order, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+    int32_t* __restrict__ order, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+    VarRows var) {
   __shared__ int hist[MOE_MAX_EXPERTS];
   __shared__ int run[MOE_MAX_EXPERTS];
   __shared__ int sh[MOE_MAX_EXPERTS];
@@ -153,7 +211,10 @@ __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
   if (tid == 0) offsets[0] = 0;
   const int row0 = incl - cnt;
   const int nbk = (cnt + bm - 1) / bm;
-  const int bincl = block_inclusive_scan(nbk, sh);
+  // blocks of the variable-size table's merged cutting (see VarRows)
+  const int vbk = cnt > bm ? (cnt + 2 * bm - 1) / (2 * bm) : nbk;
+  int bincl = nbk, vincl = vbk, btotal, vtotal;
+  block_inclusive_scan2(bincl, vincl, sh, btotal, vtotal);
   if (tid < E) {
     const int b0 = bincl - nbk;
     for (int r = 0; r < nbk; ++r) {
@@ -162,6 +223,12 @@ __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
     }
   }
   if (tid == E - 1) nb[0] = bincl;
+  if (var.blocks) {  // uniform
+    const bool merge = var_rows_merge(var, btotal, vtotal);
+    if (merge && tid < E)
+      write_var_blocks(var.blocks, vincl - vbk, vbk, tid, row0, cnt, cnt > bm ? 2 * bm : bm);
+    if (tid == 0) var.nb[0] = merge ? vtotal : -1;
+  }
   if (order) {  // uniform
     const int nfull = cnt / bm;
     const int rem = cnt - nfull * bm;
@@ -305,7 +372,7 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
     int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv,
     int32_t* __restrict__ blocks, int32_t* __restrict__ nb, int32_t* __restrict__ order,
-    ZeroRange zero) {
+    ZeroRange zero, VarRows var) {
   static_assert(EMAX <= 64 && EMAX * kSmallWaves <= kScanThreads, "one thread per (e, wave)");
   using Mask = typename std::conditional<(EMAX > 32), unsigned long long, unsigned>::type;
   constexpr int kMaskBits = 8 * sizeof(Mask);
@@ -425,6 +492,20 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
         blocks[2 * (b0 + r) + 1] = first + r * bm;
       }
     }
+    if (var.blocks) {  // uniform; lanes >= E have no rows
+      const int vbk = cnt > bm ? (cnt + 2 * bm - 1) / (2 * bm) : nbk;
+      int vincl = vbk;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(vincl, off, 64);
+        if (lane >= off) vincl += o;
+      }
+      const int btotal = __shfl(bincl, 63, 64), vtotal = __shfl(vincl, 63, 64);
+      const bool merge = var_rows_merge(var, btotal, vtotal);
+      if (merge && lane < E)
+        write_var_blocks(var.blocks, vincl - vbk, vbk, lane, first, cnt, cnt > bm ? 2 * bm : bm);
+      if (lane == 0) var.nb[0] = merge ? vtotal : -1;
+    }
     // longest-first launch order, as in hist_scan_kernel (lanes >= E have
     // no rows and take no part)
     if (order) {
@@ -459,11 +540,12 @@ bool fused_reorder_fits(int A, int E) {
 hipError_t launch_hist_scan(const int32_t* ids, int A, int E, int bm, int nchunks, int32_t* counts,
                             int32_t* offsets, int32_t* chunk_cnt, int32_t* chunk_base,
                             int32_t* blocks, int32_t* nb, int32_t* order, int32_t* perm,
-                            int32_t* inv, hipStream_t s) {
+                            int32_t* inv, VarRows var, hipStream_t s) {
   if ((perm != nullptr) != (inv != nullptr) || (perm && !fused_reorder_fits(A, E)))
     return hipErrorInvalidValue;
+  if (var.blocks && (!var.nb || var.tiles < 1)) return hipErrorInvalidValue;
   hist_scan_kernel<<<1, kScanThreads, 0, s>>>(ids, A, E, bm, nchunks, counts, offsets, chunk_cnt,
-                                              chunk_base, blocks, nb, order, perm, inv);
+                                              chunk_base, blocks, nb, order, perm, inv, var);
   return hipGetLastError();
 }
 
@@ -502,12 +584,14 @@ hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int
                                        int score, int bm, int32_t* ids, float* w,
                                        int32_t* counts, int32_t* offsets, int32_t* perm,
                                        int32_t* inv, int32_t* blocks, int32_t* nb,
-                                       int32_t* order, ZeroRange zero, hipStream_t s) {
+                                       int32_t* order, ZeroRange zero, VarRows var,
+                                       hipStream_t s) {
   if (!small_routing_fits(T, E, k)) return hipErrorInvalidValue;
+  if (var.blocks && (!var.nb || var.tiles < 1)) return hipErrorInvalidValue;
 #define MOE_LAUNCH_SMALL(EMAX)                                                               \
   route_dispatch_small_kernel<EMAX><<<1, kScanThreads, 0, s>>>(                              \
       logits, T, E, k, renorm, score, bm, ids, w, counts, offsets, perm, inv, blocks, nb, order, \
-      zero)
+      zero, var)
   if (E <= 8)
     MOE_LAUNCH_SMALL(8);
   else if (E <= 16)

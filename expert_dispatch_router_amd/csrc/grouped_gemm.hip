@@ -909,6 +909,71 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
   lds_tile_store<BM, WAVES, BK, STAGES, MODE, SUB>(acc, out, A, N, r0, rows, n0, part);
 }
 
+// The fused gate/up GEMM over a block table whose blocks hold up to 2 * BM
+// rows (built on the device by the routing kernels, see VarRows): one
+// workgroup per (block, column tile), and each block takes the tile of its
+// size -- BM rows with SS stages, or 2 * BM rows with SL stages (the LDS of
+// one CU holds three 48 KiB stages of the first or two 64 KiB stages of the
+// second).  Both tiles are 8 waves x 16 columns, so a 2 * BM block reads its
+// expert's weight tile once where two BM blocks would read it twice.  Each
+// output sums the same 64-wide K steps in the same order whichever tile
+// computes it; with the K start rotated per expert (or no rotation) the
+// bytes equal those of the BM tile over the fixed-size table.
+// vblocks: [*, 3] = (expert, first row, rows); vnb: their count, or -1:
+// the fixed table of BM-row blocks (blocks, nb, offsets) instead.
+template <int BM, int BK, int SS, int SL, int WCPOL>
+__global__ __launch_bounds__(512, 1) void gemm_lds_var_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
+    const int32_t* __restrict__ vblocks, const int32_t* __restrict__ vnb,
+    const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_fixed,
+    const int32_t* __restrict__ offsets, uint16_t* __restrict__ h, int N, int K, int rotate,
+    const int32_t* __restrict__ gather_perm, int gather_k, int x_rows) {
+  using GS = LdsGemm<BM, 8, BK, SS, kOutSwiGLU, 1>;
+  using GL = LdsGemm<2 * BM, 8, BK, SL, kOutSwiGLU, 1>;
+  static_assert(GS::kTileCols == GL::kTileCols && GS::kWaveCols == GL::kWaveCols,
+                "one column tiling for both block sizes");
+  constexpr int kSmallBytes = SS * GS::kStageBytes, kLargeBytes = SL * GL::kStageBytes;
+  __shared__ __attribute__((aligned(16)))
+      uint8_t lds[kSmallBytes > kLargeBytes ? kSmallBytes : kLargeBytes];
+
+  const int n_tiles = (N + GS::kTileCols - 1) / GS::kTileCols;
+  const int bi = blockIdx.x / n_tiles;
+  const int nv = vnb[0], nf = nb_fixed[0];  // independent loads
+  const bool merged = nv >= 0;
+  if (bi >= (merged ? nv : nf)) return;
+  const int tile = blockIdx.x - bi * n_tiles;
+  int e, r0, rows;
+  if (merged) {
+    e = vblocks[3 * bi];
+    r0 = vblocks[3 * bi + 1];
+    rows = vblocks[3 * bi + 2];
+  } else {
+    e = blocks[2 * bi];
+    r0 = blocks[2 * bi + 1];
+    rows = min(BM, offsets[e + 1] - r0);
+  }
+  const int nks = K / BK;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = tile * GS::kTileCols + wave * GS::kWaveCols;
+  const unsigned rkey = rotate == 2 ? (unsigned)blockIdx.x : rotate == 3 ? (unsigned)e : (unsigned)bi;
+  const int shift = rotate ? (int)((rkey * 2654435761u) % (unsigned)max(nks, 1)) : 0;
+  if (rows > BM) {
+    f32x4 acc[2][2 * BM / 16][1];
+    lds_tile_zero<2, 2 * BM / 16, 1>(acc);
+    lds_tile_mma<2 * BM, 8, BK, SL, kOutSwiGLU, WCPOL, 1>(lds, X, W, w_estride, e, r0, rows, n0, 0,
+                                                         N, K, nks, shift, 0, nks, gather_perm,
+                                                         gather_k, x_rows, acc);
+    lds_tile_store<2 * BM, 8, BK, SL, kOutSwiGLU, 1>(acc, h, 0, N, r0, rows, n0, 0);
+  } else {
+    f32x4 acc[2][BM / 16][1];
+    lds_tile_zero<2, BM / 16, 1>(acc);
+    lds_tile_mma<BM, 8, BK, SS, kOutSwiGLU, WCPOL, 1>(lds, X, W, w_estride, e, r0, rows, n0, 0, N,
+                                                     K, nks, shift, 0, nks, gather_perm, gather_k,
+                                                     x_rows, acc);
+    lds_tile_store<BM, 8, BK, SS, kOutSwiGLU, 1>(acc, h, 0, N, r0, rows, n0, 0);
+  }
+}
+
 // Stream-K schedule of the fused gate/up GEMM (one launch of persistent
 // workgroups).  The work is every (block, column tile) unit of the schedule
 // built on the device times its nks K steps: I = nb * n_tiles * nks
@@ -1077,6 +1142,8 @@ int gate_up_tile_cols(int bm, int variant) {
   if (bm == 128 && variant == kGateUpLdsVariant) return LdsGemm<128, 8, kLdsBK, kLdsStages>::kTileCols;
   if (bm == 128 && variant == kGateUpLdsNarrowVariant)
     return LdsGemm<128, 8, kLdsBK, kLdsNarrowStages, kOutSwiGLU, 1>::kTileCols;  // 128
+  if (bm == 256 && variant == kGateUpLdsNarrowVariant)
+    return LdsGemm<256, 8, kLdsBK, kLdsStages, kOutSwiGLU, 1>::kTileCols;  // 128
   return 0;
 }
 
@@ -1085,8 +1152,8 @@ int down_tile_cols(int bm, int variant) {
   if (bm == BM && V == variant) return Gemm<BM, NWT, WV, PF, kOutF32Parts>::kTileCols;
   MOE_DN_CFGS(X)
 #undef X
-  if ((bm == 192 || bm == 128) && variant == kDownLdsVariant)
-    return LdsGemm<192, 8, kLdsBK, kLdsStages, kOutF32Parts>::kTileCols;  // 256 at both
+  if ((bm == 192 || bm == 128 || bm == 256) && variant == kDownLdsVariant)
+    return LdsGemm<192, 8, kLdsBK, kLdsStages, kOutF32Parts>::kTileCols;  // 256 at all three
   if (bm == 192 && variant == kDownLdsWideVariant)
     return LdsGemm<192, 7, kLdsBK, kLdsStages, kOutF32Wide>::kTileCols;  // 448
   if (bm == 128 && variant == kDownLdsWideVariant)
@@ -1114,6 +1181,13 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
   if (bm == 128 && variant == kGateUpLdsNarrowVariant) {
     if (x_tiled) return hipErrorInvalidValue;
     return launch_lds_cfg<128, 8, kOutSwiGLU, kCpolNT, kLdsNarrowStages, 1>(
+        x, w_gate_up, 2LL * ffn * d, blocks, nb, order, offsets, h, A, ffn, d, 1, d, nb_max, rotate,
+        gather_perm, k, T, xcd_group, s);
+  }
+  // At BM = 256 (asked for only): 8 waves x 16 columns, two 64 KiB stages.
+  if (bm == 256 && variant == kGateUpLdsNarrowVariant) {
+    if (x_tiled) return hipErrorInvalidValue;
+    return launch_lds_cfg<256, 8, kOutSwiGLU, kCpolNT, kLdsStages, 1>(
         x, w_gate_up, 2LL * ffn * d, blocks, nb, order, offsets, h, A, ffn, d, 1, d, nb_max, rotate,
         gather_perm, k, T, xcd_group, s);
   }
@@ -1156,6 +1230,21 @@ hipError_t launch_gate_up_sk(int bm, int variant, const uint16_t* x, const int32
   return hipGetLastError();
 }
 
+hipError_t launch_gate_up_var(const uint16_t* x, const int32_t* gather_perm, int k, int T,
+                              const uint16_t* w_gate_up, const int32_t* vblocks,
+                              const int32_t* vnb, const int32_t* blocks, const int32_t* nb,
+                              const int32_t* offsets, uint16_t* h, int d, int ffn, int nb_max,
+                              int rotate, hipStream_t s) {
+  if (ffn % 16 != 0 || d % kLdsBK != 0 || d <= 0 || nb_max < 0) return hipErrorInvalidValue;
+  using G = LdsGemm<128, 8, kLdsBK, kLdsNarrowStages, kOutSwiGLU, 1>;
+  const long long grid = (long long)(ffn + G::kTileCols - 1) / G::kTileCols * nb_max;
+  if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  gemm_lds_var_kernel<128, kLdsBK, kLdsNarrowStages, kLdsStages, kCpolNT>
+      <<<(unsigned)grid, G::kThreads, 0, s>>>(x, w_gate_up, 2LL * ffn * d, vblocks, vnb, blocks,
+                                             nb, offsets, h, ffn, d, rotate, gather_perm, k, T);
+  return hipGetLastError();
+}
+
 // Fused gate/up SwiGLU and down projection (kOutSwiGLUDown): tiles whose
 // column count is a multiple of 32 and whose h tile fits the staging LDS.
 #define MOE_GUD_CFGS(X) X(1, 64, 2, 4, 4) X(1, 128, 1, 4, 4) X(0, 192, 1, 8, 3)
@@ -1191,7 +1280,7 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
                        int A, int d, int ffn, int split, int ksplit, int nb_max, int rotate,
                        int xcd_group, const FoldCombine& fold, hipStream_t s, int dyn_split) {
   if (dyn_split && fold.cnt) return hipErrorInvalidValue;  // the fold counts parts as launched
-  if ((bm == 192 || bm == 128) && variant == kDownLdsVariant) {
+  if ((bm == 192 || bm == 128 || bm == 256) && variant == kDownLdsVariant) {
     if (fold.cnt) return hipErrorInvalidValue;  // the fold runs in the register-ring tiles
     // Weights are read once.  Non-temporal weight loads measured faster on
     // every workload whose fp32 partials fit the 256 MiB MALL (down GEMM, µs:
@@ -1206,6 +1295,10 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
     if (bm == 192) {
       if (nt) MOE_DOWN_LDS(192, kCpolNT, kLdsStages);
       MOE_DOWN_LDS(192, 0, kLdsStages);
+    }
+    if (bm == 256) {
+      if (nt) MOE_DOWN_LDS(256, kCpolNT, kLdsStages);
+      MOE_DOWN_LDS(256, 0, kLdsStages);
     }
     if (nt) MOE_DOWN_LDS(128, kCpolNT, kLdsStages);
     MOE_DOWN_LDS(128, 0, kLdsStages);

@@ -22,10 +22,13 @@ constexpr int kTargetDownWorkgroups = 1024;  // ~4 per CU on 256 CUs
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
+// 256-row blocks: only when asked, on the LDS-staged tiles (narrow gate/up,
+// 256-column down).
+constexpr int kLargeBlockRows = 256;
 bool is_block_rows(int bm) {
   for (int b : kBlockRows)
     if (b == bm) return true;
-  return false;
+  return bm == kLargeBlockRows;
 }
 
 // Checks that only depend on sizes.  dims: d and ffn are used.
@@ -67,7 +70,7 @@ int check_options(const moe_options* opt) {
   if (opt->xcd_order < 0 || opt->xcd_order > 3) return MOE_ERR_UNSUPPORTED;
   if (opt->fold_combine < 0 || opt->fold_combine > 2) return MOE_ERR_UNSUPPORTED;
   if (opt->fuse_down < 0 || opt->fuse_down > 2) return MOE_ERR_UNSUPPORTED;
-  if (opt->schedule < 0 || opt->schedule > 2) return MOE_ERR_UNSUPPORTED;
+  if (opt->schedule < 0 || opt->schedule > 3) return MOE_ERR_UNSUPPORTED;
   if (opt->down_variant < 0) return MOE_ERR_UNSUPPORTED;
   if (opt->down_variant > 0) {
     const int bm = opt->block_rows;
@@ -115,7 +118,8 @@ long long est_workgroups(int A, int E, int bm, int n_cols, int tile_cols) {
 // short ones, so split only as far as needed to reach ~256 workgroups, and
 // use two parts when a launch is small (< 640 workgroups).
 int auto_split(int A, int E, int d, int ffn, int bm) {
-  const long long wg = est_workgroups(A, E, bm, d, down_tile_cols(bm, 0));
+  const int dcols = bm == kLargeBlockRows ? down_tile_cols(bm, kDownLdsVariant) : down_tile_cols(bm, 0);
+  const long long wg = est_workgroups(A, E, bm, d, dcols > 0 ? dcols : 256);
   int s = (int)((256 + wg - 1) / wg);
   if (wg < 640 && s < 2) s = 2;
   const int max_by_k = ffn / (8 * 64);  // keep at least 8 K steps per part
@@ -189,6 +193,7 @@ double tile_waste(int n, int tc) {
 // -> 308, 333 -> 330; skewed T=128/512 41.9 -> 39.3, 79.0 -> 74.2;
 // DeepSeek-V3 T=512 2164 -> 2156; skewed T=256 44.5 -> 47.1.
 int auto_gu_variant(int A, int E, int ffn, int bm, bool x_tiled) {
+  if (bm == kLargeBlockRows) return kGateUpLdsNarrowVariant;  // the only tile there
   if (bm == 128 && gate_up_lds_fits(bm, ffn, x_tiled)) return kGateUpLdsNarrowVariant;
   if ((bm == 128 || bm == 192) && gate_up_lds_fits(bm, ffn, x_tiled)) {
     const int tc = gate_up_tile_cols(bm, kGateUpLdsVariant);
@@ -233,6 +238,15 @@ bool auto_stream_k(int A, int E, int d, int ffn, int bm) {
   return false;
 }
 
+// The gate/up GEMM over the variable-size block table (launch_gate_up_var,
+// VarRows): the routing kernels merge a hot expert's 128-row blocks into
+// 256-row ones only when that takes the launch from more than one round of
+// workgroups to one, and otherwise the table is the fixed one.
+bool auto_var_rows(int A, int E, int d, int ffn) {
+  (void)A, (void)E, (void)d, (void)ffn;
+  return true;
+}
+
 bool auto_xcd_order(int A, int E, int bm) {
   const long long blocks = std::max<long long>((A + bm - 1) / bm, std::min(E, A));
   return blocks >= 128;
@@ -252,7 +266,8 @@ int auto_rotate(int) { return kRotatePerExpert; }
 // can run: whole 256-column tiles, and the combination not folded into the
 // down GEMM (the fold lives in the register-ring tiles).
 bool down_lds_fits(int bm, int d, bool fold) {
-  return (bm == 128 || bm == 192) && d % down_tile_cols(bm, kDownLdsVariant) == 0 && !fold;
+  return (bm == 128 || bm == 192 || bm == kLargeBlockRows) &&
+         d % down_tile_cols(bm, kDownLdsVariant) == 0 && !fold;
 }
 
 // Tile variant of the down GEMM.  The wide LDS-staged tile (64 columns per
@@ -312,12 +327,14 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->k = k;
   p->A = T * k;
   const int A = p->A;
-  // The stream-K schedule runs the 128-row tile: automatic block rows are 128 then.
+  // The stream-K and variable-size schedules run the 128-row tile: automatic
+  // block rows are 128 then.
   const int sch = opt ? opt->schedule : 0;
+  const bool sch128 = sch == 2 || sch == 3;
   p->bm = (opt && opt->block_rows) ? opt->block_rows
-          : sch == 2               ? 128
+          : sch128                 ? 128
                                    : auto_block_rows(A > 0 ? A : 1, E);
-  if (!(opt && opt->block_rows) && sch != 2 && p->bm == 128 && prefer_192_rows(A, E, ffn))
+  if (!(opt && opt->block_rows) && !sch128 && p->bm == 128 && prefer_192_rows(A, E, ffn))
     p->bm = 192;
   p->nb_max = (A + p->bm - 1) / p->bm + (E < A ? E : A);
   p->nchunks = (A + kChunk - 1) / kChunk;
@@ -355,12 +372,22 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
       p->plan_error = MOE_ERR_UNSUPPORTED;  // forced where it cannot run
     if (p->dn_variant == kDownLdsWideVariant && p->fold)
       p->plan_error = MOE_ERR_UNSUPPORTED;  // the fold lives in the register-ring tiles
+    // 256-row blocks run only the LDS-staged tiles: the narrow gate/up tile
+    // and the 256-column down tile (d a multiple of 256); not the unfused
+    // ablation, gather mode 3 or the folded combination.
+    if (p->bm == kLargeBlockRows &&
+        (p->gu_variant != kGateUpLdsNarrowVariant || p->dn_variant != kDownLdsVariant ||
+         p->unfused || p->x_tiled || p->fold))
+      p->plan_error = MOE_ERR_UNSUPPORTED;
     const int rot = opt ? opt->rotate : 0;
     // kernel values: 0 off, 1 per block, 2 per workgroup
     p->gu_rotate = rot == 0 ? auto_rotate(d) : rot - 1;
     p->dn_rotate = rot == 0 ? auto_rotate(ffn) : rot - 1;
     const int xo = opt ? opt->xcd_order : 0;
-    p->gu_xcd = p->dn_xcd = xo == 0 ? auto_xcd_order(A, E, p->bm) : xo == 2;
+    // (an explicit variable-size schedule keeps the gate/up GEMM's blocks in
+    // table order)
+    p->dn_xcd = xo == 0 ? auto_xcd_order(A, E, p->bm) : xo == 2;
+    p->gu_xcd = xo == 0 ? (sch != 3 && p->dn_xcd) : xo == 2;
     p->longest_first = xo == 3 || (xo == 0 && !p->gu_xcd && auto_longest_first(A, E, p->bm));
     const int dcols = down_tile_cols(p->bm, p->dn_variant);
     p->dn_tiles = dcols > 0 ? (d + dcols - 1) / dcols : 0;
@@ -375,9 +402,9 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
     const int tc = gate_up_down_tile_cols(p->bm, fv);
     const bool fd_ok = tc > 0 && !p->unfused && (long long)d * ffn * 2 < (1LL << 31);
     if (fd == 2 && !fd_ok) p->plan_error = MOE_ERR_UNSUPPORTED;
-    // (an explicit stream-K schedule keeps the separate down GEMM)
+    // (an explicit stream-K or variable-size schedule keeps the separate down GEMM)
     p->fused_down = fd == 2 ? fd_ok
-                            : (fd == 0 && sch != 2 && fd_ok && auto_fuse_down(A, d, ffn, E, p->bm, tc));
+                            : (fd == 0 && !sch128 && fd_ok && auto_fuse_down(A, d, ffn, E, p->bm, tc));
     if (p->fused_down) {
       p->gu_variant = fv;
       p->split = (ffn + tc - 1) / tc;
@@ -406,6 +433,17 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
         if (sch == 2) p->plan_error = MOE_ERR_UNSUPPORTED;
         p->gu_sk = 0;
       }
+    }
+    // Or over the variable-size block table: the narrow LDS-staged tile at
+    // 128 and 256 rows, the blocks in table order.
+    const bool var_ok = p->bm == 128 && p->gu_variant == kGateUpLdsNarrowVariant && !p->unfused &&
+                        !p->fused_down && !p->gu_sk && !p->x_tiled && !p->gu_xcd &&
+                        !p->longest_first;
+    if (sch == 3) {
+      if (var_ok) p->gu_var = kVarRowsAlways;
+      else p->plan_error = MOE_ERR_UNSUPPORTED;
+    } else if (sch == 0 && var_ok && auto_var_rows(A, E, d, ffn)) {
+      p->gu_var = kVarRowsAuto;
     }
   }
   size_t o = 0;
@@ -439,6 +477,8 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
   p->o_skpart = seg(p->gu_sk ? 2 * (size_t)kRoundWorkgroups *
                                    gate_up_sk_slot_bytes(p->bm, p->gu_variant)
                              : 0);
+  p->o_vblocks = seg(p->gu_var ? (size_t)p->nb_max * 3 * 4 : 0);
+  p->o_vnb = seg(p->gu_var ? 4 : 0);
   p->total_bytes = o;
 }
 
@@ -470,7 +510,8 @@ int record(const moe_options* opt, int i, hipStream_t s) {
 // problems, else two launches where the reorder fits the histogram kernel,
 // else three.
 int run_routing(const LogitSrc& logits, const Plan& p, int renorm, int score, void* ws,
-                const moe_options* opt, int32_t* order, ZeroRange zero, hipStream_t s) {
+                const moe_options* opt, int32_t* order, ZeroRange zero, VarRows var,
+                hipStream_t s) {
   int32_t* ids = at<int32_t>(ws, p.o_ids);
   float* w = at<float>(ws, p.o_w);
   int32_t* offsets = at<int32_t>(ws, p.o_offsets);
@@ -480,7 +521,7 @@ int run_routing(const LogitSrc& logits, const Plan& p, int renorm, int score, vo
                                             at<int32_t>(ws, p.o_counts), offsets,
                                             at<int32_t>(ws, p.o_perm), at<int32_t>(ws, p.o_inv),
                                             at<int32_t>(ws, p.o_blocks), at<int32_t>(ws, p.o_nb),
-                                            order, zero, s));
+                                            order, zero, var, s));
     MOE_TRY(record(opt, 1, s));
     MOE_TRY(record(opt, 2, s));
     return MOE_OK;
@@ -492,7 +533,7 @@ int run_routing(const LogitSrc& logits, const Plan& p, int renorm, int score, vo
   MOE_TRY_HIP(launch_hist_scan(ids, p.A, p.E, p.bm, p.nchunks, at<int32_t>(ws, p.o_counts),
                                offsets, at<int32_t>(ws, p.o_ccnt), at<int32_t>(ws, p.o_cbase),
                                at<int32_t>(ws, p.o_blocks), at<int32_t>(ws, p.o_nb), order, fperm,
-                               finv, s));
+                               finv, var, s));
   MOE_TRY(record(opt, 2, s));
   if (p.fused_reorder) return MOE_OK;
   MOE_TRY_HIP(launch_permute(ids, p.A, p.E, p.nchunks, offsets, at<int32_t>(ws, p.o_ccnt),
@@ -513,8 +554,15 @@ int forward_from_logits(const uint16_t* x, const LogitSrc& router_logits, const 
   int32_t* counters = (p.fold || p.gu_sk) ? at<int32_t>(workspace, p.o_fold) : nullptr;
   int32_t* fold_cnt = p.fold ? counters : nullptr;
   int32_t* order = p.longest_first ? at<int32_t>(workspace, p.o_order) : nullptr;
+  // The variable-size block table of the gate/up GEMM, when it runs over one.
+  int32_t* vblocks = p.gu_var ? at<int32_t>(workspace, p.o_vblocks) : nullptr;
+  int32_t* vnb = p.gu_var ? at<int32_t>(workspace, p.o_vnb) : nullptr;
+  const int gu_tiles = p.gu_var ? (ffn + gate_up_tile_cols(128, kGateUpLdsNarrowVariant) - 1) /
+                                      gate_up_tile_cols(128, kGateUpLdsNarrowVariant)
+                                : 0;
   MOE_TRY(run_routing(router_logits, p, renorm, score, workspace, opt, order,
-                      ZeroRange{counters, counters ? n_fold + p.sk_units : 0}, s));
+                      ZeroRange{counters, counters ? n_fold + p.sk_units : 0},
+                      VarRows{vblocks, vnb, p.gu_var, gu_tiles}, s));
   const int32_t* perm = at<int32_t>(workspace, p.o_perm);
   const int32_t* blocks = at<int32_t>(workspace, p.o_blocks);
   const int32_t* nb = at<int32_t>(workspace, p.o_nb);
@@ -546,6 +594,9 @@ int forward_from_logits(const uint16_t* x, const LogitSrc& router_logits, const 
     MOE_TRY_HIP(launch_gate_up_down(p.bm, p.gu_variant, X, gperm, top_k, T, W_gate_up, W_down,
                                     blocks, nb, order, offsets, y, p.A, d, ffn, p.nb_max,
                                     p.gu_rotate, p.gu_xcd, p.x_tiled, s));
+  } else if (p.gu_var) {
+    MOE_TRY_HIP(launch_gate_up_var(X, gperm, top_k, T, W_gate_up, vblocks, vnb, blocks, nb,
+                                   offsets, h, d, ffn, p.nb_max, p.gu_rotate, s));
   } else if (p.gu_sk) {
     MOE_TRY_HIP(launch_gate_up_sk(p.bm, p.gu_variant, X, gperm, top_k, T, W_gate_up, blocks, nb,
                                   offsets, h, d, ffn, p.gu_rotate,
@@ -694,6 +745,7 @@ int moe_plan_ex(int T, int d, int ffn, int E, int top_k, const moe_options* opt,
   info->xcd_grouped = p.gu_xcd ? 1 : 0;
   info->split_on_device = p.dyn_split ? 1 : 0;
   info->stream_k = p.gu_sk ? 1 : 0;
+  info->variable_rows = p.gu_var;
   info->launches = info->routing_launches + info->gather_launch + (p.unfused ? 3 : 1) +
                    (p.fused_down ? 0 : 1) + (p.fold ? 0 : 1);
   return MOE_OK;
@@ -872,7 +924,7 @@ int moe_route(const float* router_logits, int T, int E, int top_k, int renormali
   (void)hipGetLastError();
   MOE_TRY(run_routing(LogitSrc{router_logits, 1, 0, nullptr}, p, renormalize ? 1 : 0, score_func,
                       workspace, opt, block_order ? at<int32_t>(workspace, p.o_order) : nullptr,
-                      ZeroRange{nullptr, 0}, s));
+                      ZeroRange{nullptr, 0}, VarRows{nullptr, nullptr, 0, 0}, s));
   if (gather)
     MOE_TRY_HIP(launch_gather(x, at<int32_t>(workspace, p.o_perm), p.A, d, top_k, x_perm, s));
   MOE_TRY(record(opt, 3, s));

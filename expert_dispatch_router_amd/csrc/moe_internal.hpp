@@ -76,10 +76,13 @@ struct Plan {
                       // (device_down_split, at most `split`)
   int gu_sk;          // the gate/up GEMM runs the stream-K schedule (launch_gate_up_sk)
   int sk_units;       // its counters: nb_max * column tiles
+  int gu_var;         // the gate/up GEMM runs over the variable-size block table
+                      // (launch_gate_up_var), built with VarRows mode gu_var
   int plan_error;     // an explicit option the plan cannot honour (MOE_ERR_*), else 0
   // byte offsets into the workspace (256-byte aligned)
   size_t o_ids, o_w, o_counts, o_offsets, o_ccnt, o_cbase, o_perm, o_inv, o_blocks, o_nb;
   size_t o_order;  // longest-first launch order of the blocks [nb_max]
+  size_t o_vblocks, o_vnb;  // the variable-size block table [nb_max, 3] and its count
   size_t route_bytes;  // end of the routing section
   size_t o_xperm, o_h, o_y;
   size_t o_g, o_u;  // unfused gate and up products [A, ffn] bf16
@@ -138,13 +141,32 @@ struct ZeroRange {
 hipError_t launch_route(const LogitSrc& logits, int T, int E, int k, int renorm, int score,
                         int32_t* ids, float* w, ZeroRange zero, hipStream_t s);
 
+// The gate/up GEMM's table of variable-size blocks, built by the routing
+// kernels beside the fixed table (blocks null: not built): each expert
+// with more than bm rows cut into blocks of 2 * bm rows and a last block of
+// the rest, the others into blocks of bm rows as in the fixed table.  mode
+// 1 merges when the fixed table needs more than one round of
+// kRoundWorkgroups workgroups at `tiles` column tiles per block and the
+// merged one needs at most one round; mode 2 always merges.  blocks [*, 3]
+// = (expert, first row, rows) and nb[0] = their count when the table
+// merges; else nb[0] = -1 and the table is not written (the GEMM takes the
+// fixed table).
+struct VarRows {
+  int32_t* blocks;
+  int32_t* nb;
+  int mode;
+  int tiles;
+};
+constexpr int kVarRowsAuto = 1;
+constexpr int kVarRowsAlways = 2;
+
 // Histogram, offsets and the block table; with `order` (may be null) also
 // the longest-first launch order of the blocks (a stable sort by decreasing
 // rows: the full blocks in block order, then the partial last blocks).
 hipError_t launch_hist_scan(const int32_t* ids, int A, int E, int bm, int nchunks,
                             int32_t* counts, int32_t* offsets, int32_t* chunk_cnt,
                             int32_t* chunk_base, int32_t* blocks, int32_t* nb, int32_t* order,
-                            int32_t* perm, int32_t* inv, hipStream_t s);
+                            int32_t* perm, int32_t* inv, VarRows var, hipStream_t s);
 // Whether the histogram kernel can also do the reorder (perm, inv non-null):
 // its per-64-row-group counts of every expert fit in LDS.
 bool fused_reorder_fits(int A, int E);
@@ -168,7 +190,8 @@ hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int
                                        int score, int bm, int32_t* ids, float* w,
                                        int32_t* counts, int32_t* offsets, int32_t* perm,
                                        int32_t* inv, int32_t* blocks, int32_t* nb,
-                                       int32_t* order, ZeroRange zero, hipStream_t s);
+                                       int32_t* order, ZeroRange zero, VarRows var,
+                                       hipStream_t s);
 
 hipError_t launch_gather(const uint16_t* x, const int32_t* perm, int A, int d, int k,
                          uint16_t* x_perm, hipStream_t s);
@@ -230,6 +253,18 @@ hipError_t launch_gate_up_sk(int bm, int variant, const uint16_t* x, const int32
                              int k, int T, const uint16_t* w_gate_up, const int32_t* blocks,
                              const int32_t* nb, const int32_t* offsets, uint16_t* h, int d,
                              int ffn, int rotate, float* part, int32_t* cnt, hipStream_t s);
+
+// The fused gate/up GEMM over the variable-size block table (VarRows, bm
+// 128), or over the fixed table (blocks, nb, offsets) when the routing
+// kernels did not merge: blocks of up to 128 rows take the narrow
+// LDS-staged tile, blocks of up to 256 rows the same tile at 256 rows, in
+// one launch of nb_max * ceil(ffn / 128) workgroups (those past the table's
+// count return at once).  Row-major activations only.
+hipError_t launch_gate_up_var(const uint16_t* x, const int32_t* gather_perm, int k, int T,
+                              const uint16_t* w_gate_up, const int32_t* vblocks,
+                              const int32_t* vnb, const int32_t* blocks, const int32_t* nb,
+                              const int32_t* offsets, uint16_t* h, int d, int ffn, int nb_max,
+                              int rotate, hipStream_t s);
 
 // Fused gate/up SwiGLU and down projection for small problems: each
 // (block, column tile) workgroup keeps its h tile in LDS and writes

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 /* Limits of the library (violations return MOE_ERR_UNSUPPORTED). */
 #define MOE_MAX_EXPERTS 512
@@ -81,9 +81,14 @@ typedef struct moe_options {
     /* Rows per schedule block (BLOCK_M, [R] "Assumptions & free
      * parameters": fixed for one launch).  0 = automatic: the smallest size
      * >= 128 that holds the mean rows per expert plus three standard
-     * deviations of a uniform router; else one of 16, 32, 64, 128, 192.
-     * Blocks hold up to block_rows rows; the GEMMs skip 16-row subtiles past
-     * a block's last row. */
+     * deviations of a uniform router; else one of 16, 32, 64, 128, 192, or
+     * 256 (asked for only: the LDS-staged tiles at 256 rows -- the narrow
+     * gate/up tile and down variant 2, so d a multiple of 256 -- not with
+     * the unfused ablation, gather mode 3, the folded combination or the
+     * fused down projection, else MOE_ERR_UNSUPPORTED).  Blocks hold up to
+     * block_rows rows; the GEMMs skip 16-row subtiles past a block's last
+     * row.  The gate/up GEMM may take its own blocks of 256 rows (see
+     * schedule). */
     int block_rows;
     /* Split of the down projection's reduction (ffn) into this many parts
      * whose partial sums the combination adds in a fixed order.  0 =
@@ -190,7 +195,8 @@ typedef struct moe_options {
     int fuse_down;
     /* Schedule of the fused gate/up GEMM: the skew-aware dynamic work
      * assignment the method leaves as future work ([R] abstract; "Editorial
-     * extensions").  0 = automatic, 1 = one workgroup per (schedule block,
+     * extensions").  0 = automatic: schedule 3's table with its merge rule
+     * where it can run, else 1.  1 = one workgroup per (schedule block,
      * column tile) unit, in rounds of the GPU's 256 CUs, 2 = stream-K: 256
      * persistent workgroups share the K steps of all units evenly -- the
      * unit count is the routed block count times the column tiles, read on
@@ -206,7 +212,21 @@ typedef struct moe_options {
      * workspace grows by 2 * 256 partial slots of 128 KiB and one counter
      * per unit, which the routing kernels clear on every call.  Rounding
      * differs from schedule 1 where a unit is split (other association of
-     * the K sum). */
+     * the K sum).  3 = variable block rows: the routing kernels build a
+     * second block table for the gate/up GEMM in which an expert with more
+     * than 128 rows takes blocks of 256 rows (the last one holding the
+     * rest), so its weight tile is read once per 256 rows; the GEMM runs
+     * the 128-row narrow tile on blocks of up to 128 rows and the same tile
+     * at 256 rows on the others, in one launch.  The down GEMM keeps the
+     * 128-row blocks.  Asked for, the table always merges; automatic (0), it
+     * merges only when the 128-row table needs more than one round of 256
+     * workgroups and the merged one at most one, and is the 128-row table
+     * otherwise.  Same conditions as 2 (block_rows 0 or 128, tile_variant 0
+     * or 4, not with the unfused ablation, the fused down projection,
+     * gather mode 3, the XCD-grouped or longest-first orders: else
+     * MOE_ERR_UNSUPPORTED when 3 is asked for); the workspace grows by 12
+     * bytes per block.  With the K start rotated per expert (the automatic
+     * rotation) or not rotated, the bytes equal schedule 1's. */
     int schedule;
     /* NULL, or 7 hipEvent_t handles created by the caller (for instance
      * with moe_timer_create).  events[0] is recorded on the stream before
@@ -266,6 +286,9 @@ typedef struct moe_plan_info {
                               parts) is nearest to one round of 256, at least
                               1 and at most split_k                           */
     int stream_k;          /* 1: the gate/up GEMM runs the stream-K schedule   */
+    int variable_rows;     /* 1: the gate/up GEMM runs over the variable-size
+                              block table, merged when one round needs it;
+                              2: merged always (schedule 3); 0: not        */
 } moe_plan_info;
 
 /* Host-only: fills *info with the launch plan moe_forward_ex would follow.

@@ -490,14 +490,57 @@ def test_stream_k_schedule_options():
     assert info["stream_k"] == 1 and info["block_rows"] == 128 and info["gate_up_variant"] == 3
     assert moe.moe_plan_ex(*args, schedule=1)["stream_k"] == 0
     assert moe.moe_plan_ex(*args, schedule=2, block_rows=128, tile_variant=4)["stream_k"] == 1
-    plain = moe.moe_workspace_size(*args, block_rows=128, tile_variant=4)
+    plain = moe.moe_workspace_size(*args, block_rows=128, tile_variant=4, schedule=1)
     streamed = moe.moe_workspace_size(*args, schedule=2)
     units = (-(-sk.T * sk.top_k // 128) + min(sk.E, sk.T * sk.top_k)) * (sk.ffn // 128)
     assert streamed - plain >= 2 * 256 * 128 * 1024 + 4 * units
     assert streamed - plain <= 2 * 256 * 128 * 1024 + 4 * units + 512
-    for bad in (_o(0, sched=3), _o(0, sched=-1), _o(192, sched=2), _o(128, 0, 1, sched=2),
+    for bad in (_o(0, sched=4), _o(0, sched=-1), _o(192, sched=2), _o(128, 0, 1, sched=2),
                 _o(128, 0, 3, sched=2), _o(0, unfused=1, sched=2), _o(0, gather=3, sched=2),
                 _o(0, fuse=2, sched=2)):
         assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
     assert _ws(64, 256, 512, 8, 2, _o(0, sched=2))[0] == OK
     assert _ws(64, 256, 512, 8, 2, _o(128, 0, 4, sched=2))[0] == OK
+
+
+def test_variable_rows_schedule_options():
+    """schedule = 3 (the gate/up GEMM over the variable-size block table,
+    merged always) and its automatic form (merged on the device when one
+    round needs it): the narrow 128-row tile, 12 bytes per block more
+    workspace, refused where the tile or the table cannot run."""
+    sk = CONFIGS["skewed_512"]
+    args = (sk.T, sk.d, sk.ffn, sk.E, sk.top_k)
+    info = moe.moe_plan_ex(*args, schedule=3)
+    assert info["variable_rows"] == 2 and info["block_rows"] == 128
+    assert info["gate_up_variant"] == 3 and info["fused_down"] == 0 and info["stream_k"] == 0
+    assert moe.moe_plan_ex(*args)["variable_rows"] == 1          # automatic
+    assert moe.moe_plan_ex(*args, schedule=1)["variable_rows"] == 0
+    assert moe.moe_plan_ex(*args, schedule=2)["variable_rows"] == 0
+    nb_max = -(-sk.T * sk.top_k // 128) + min(sk.E, sk.T * sk.top_k)
+    fixed = moe.moe_workspace_size(*args, schedule=1)
+    var = moe.moe_workspace_size(*args, schedule=3)
+    assert 12 * nb_max <= var - fixed <= 12 * nb_max + 512
+    # where the automatic plan takes another tile or order, the table is not built
+    for name in ("mixtral_512", "dsv3_512"):   # 192-row blocks; XCD-grouped order
+        c = CONFIGS[name]
+        assert moe.moe_plan_ex(c.T, c.d, c.ffn, c.E, c.top_k)["variable_rows"] == 0
+    for bad in (_o(192, sched=3), _o(128, 0, 1, sched=3), _o(128, 0, 3, sched=3),
+                _o(0, unfused=1, sched=3), _o(0, gather=3, sched=3), _o(0, fuse=2, sched=3),
+                _o(0, xcd=2, sched=3), _o(0, xcd=3, sched=3)):
+        assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
+    assert _ws(64, 256, 512, 8, 2, _o(0, sched=3))[0] == OK
+    assert _ws(64, 256, 512, 8, 2, _o(128, 0, 4, sched=3))[0] == OK
+
+
+def test_256_row_block_options():
+    """block_rows = 256 (asked for only): the narrow gate/up tile and the
+    256-column down tile, so d must be a multiple of 256; refused with the
+    other tiles, the unfused ablation, gather mode 3, the folded combination
+    and the fused down projection."""
+    info = moe.moe_plan_ex(512, 2048, 1408, 64, 4, block_rows=256)
+    assert info["block_rows"] == 256 and info["gate_up_variant"] == 3 and info["down_variant"] == 2
+    assert _ws(64, 256, 512, 8, 2, _o(256))[0] == OK
+    for bad in (_o(256, 0, 1), _o(256, 0, 3), _o(256, dvar=1), _o(256, dvar=4),
+                _o(256, unfused=1), _o(256, gather=3), _o(256, fold=2), _o(256, fuse=2)):
+        assert _ws(64, 256, 512, 8, 2, bad)[0] == UNSUP
+    assert _ws(64, 128, 512, 8, 2, _o(256))[0] == UNSUP   # d = 128

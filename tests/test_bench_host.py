@@ -58,6 +58,7 @@ K5 = "void moe::(anonymous namespace)::grouped_gemm_kernel<192, 2, 8, 3, 1>(unsi
 K4L = "void moe::(anonymous namespace)::gemm_lds_kernel<192, 7, 64, 2, 0, 2>(unsigned short const*)"
 K5L = "void moe::(anonymous namespace)::gemm_lds_kernel<192, 8, 64, 2, 1, 2>(unsigned short const*)"
 K5W = "void moe::(anonymous namespace)::gemm_lds_kernel<128, 8, 64, 2, 4, 0>(unsigned short const*)"
+K4V = "void moe::(anonymous namespace)::gemm_lds_var_kernel<128, 64, 3, 2, 2>(unsigned short const*)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
@@ -93,6 +94,21 @@ def test_traffic_summary_classifies_lds_staged_tiles_by_their_mode(tmp_path):
     assert out["bytes_per_launch"] == pytest.approx(500.0 * 2048 + 50.0 * 1024)
     assert out["kernels"]["down"]["bytes_per_launch"] == pytest.approx(9.0 * 2048 + 2.0 * 1024)
     assert out["kernels"]["down"]["launches"] == [2, 2]
+
+
+def test_traffic_summary_counts_the_variable_rows_kernel_as_gate_up(tmp_path):
+    """The gate/up GEMM over the variable-size block table is the gate/up
+    stage, although its template arguments carry no output mode."""
+    gib = 1 << 30
+    _counter_csv(str(tmp_path / "f" / "run_counter_collection.csv"), "FETCH_SIZE",
+                 [(COPY, 524288.0), (K4V, 300.0), (K4V, 310.0), (K5L, 9.0)])
+    _counter_csv(str(tmp_path / "w" / "run_counter_collection.csv"), "WRITE_SIZE",
+                 [(COPY, 1048576.0), (K4V, 20.0), (K4V, 20.0), (K5L, 2.0)])
+    out = bench.summarize_traffic(str(tmp_path / "f"), str(tmp_path / "w"), "var", gib,
+                                  out_dir=str(tmp_path))
+    assert out["kernels"]["gate_up_swiglu"]["launches"] == [2, 2]
+    assert out["bytes_per_launch"] == pytest.approx(305.0 * 2048 + 20.0 * 1024)
+    assert out["kernels"]["down"]["launches"] == [1, 1]
 
 
 def test_bench_refuses_more_than_one_gpu():

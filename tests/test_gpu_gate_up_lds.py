@@ -283,3 +283,63 @@ def test_xcd_order_when_real_workgroups_round_past_the_grid():
         plain = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=192, tile_variant=tv,
                                 down_variant=dv, xcd_order=1, fuse_down=1)
         assert torch.equal(grouped.view(torch.int16), plain.view(torch.int16))
+
+
+# ------------------------------------------------------- 256-row blocks
+
+NARROW = 4     # tile_variant option value of the 128-column LDS-staged tile of BM = 128
+DOWN_LDS = 3   # down_variant option value of the 256-column LDS-staged down tile
+
+CASES_256 = {
+    # ~50 rows per expert: one partial block each, rows end mid-subtile
+    "ragged": (150, 512, 448, 6, 2, 51),
+    # ~400 rows per expert: a full 256-row block and a partial one per expert
+    "multi_block": (600, 256, 448, 3, 2, 52),
+    # ffn = 64: one down K step, a gate/up column tile of 64 real columns
+    "short_ffn": (90, 256, 64, 4, 2, 53),
+    # ffn = 576: 4.5 gate/up tiles of 128 columns, 9 down K steps
+    "partial_tile": (180, 256, 576, 6, 2, 54),
+    # d = 1280: 20 gate/up K steps, 5 down column tiles
+    "deep_k": (300, 1280, 448, 4, 2, 55),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES_256))
+def test_256_row_blocks(name):
+    """block_rows = 256 (only when asked for) runs the narrow gate/up tile
+    and the 256-column down tile on blocks of up to 256 rows: within the
+    tolerance, and -- with the K start rotated per expert and one down part
+    on both sides -- the same bytes as the same two tiles on 128-row blocks,
+    since every output sums the same 64-wide K steps in the same order."""
+    x, lg, wgu, wd, k, ref = _case("bm256_" + name, *CASES_256[name])
+    out = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=256, split_k=1)
+    parity.check_out(out, ref, f"bm=256 {name}")
+    base = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=128, tile_variant=NARROW,
+                           down_variant=DOWN_LDS, split_k=1, fuse_down=1)
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+    auto = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=256)
+    parity.check_out(auto, ref, f"bm=256 {name} automatic split")
+
+
+def test_256_row_blocks_rejected_where_they_cannot_run():
+    x, lg, wgu, wd, k, _ = _case("bm256_multi_block", *CASES_256["multi_block"])
+    for opts in ({"tile_variant": 1}, {"unfused_swiglu": 1}, {"gather_mode": 3},
+                 {"fold_combine": 2}, {"down_variant": 1}, {"fuse_down": 2}):
+        with pytest.raises(moe.MoeError):
+            moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=256, **opts)
+    x, lg, wgu, wd, k, _ = _case("two_steps", *CASES["two_steps"])  # d = 128
+    with pytest.raises(moe.MoeError):
+        moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=256)
+
+
+@pytest.mark.parametrize("name", ["skewed_512", "skewed_128"])
+def test_256_row_blocks_skewed_every_token(name):
+    from expert_dispatch_router_amd import synth
+    cfg = synth.CONFIGS[name]
+    x, lg, wgu, wd = synth.make_inputs(cfg, 0, torch.device("cuda:0"))
+    out = moe.moe_forward(x, lg, wgu, wd, cfg.top_k, cfg.renormalize, score=cfg.score,
+                          block_rows=256)
+    ref = parity.workload_reference(name, x, lg, wgu, wd, cfg)
+    parity.check_workload(out, ref, name, x, lg, wgu, wd, cfg, what=name + " bm=256")
+    del x, lg, wgu, wd, out
+    torch.cuda.empty_cache()

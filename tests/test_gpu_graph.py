@@ -34,7 +34,12 @@ def _gpu():
                                        # the stream-K gate/up schedule: unit counters cleared
                                        # by the routing kernels on every replay
                                        ("skewed_128", {"schedule": 2}),
-                                       ("qwen2_128", {"schedule": 2, "routing_kernels": 2})])
+                                       ("qwen2_128", {"schedule": 2, "routing_kernels": 2}),
+                                       # the variable-size gate/up table: merged by the rule
+                                       # (skewed T=512), always (schedule 3, one-workgroup
+                                       # routing), and not merged (skewed T=128)
+                                       ("skewed_512", {}), ("skewed_128", {}),
+                                       ("skewed_128", {"schedule": 3, "routing_kernels": 1})])
 def test_forward_graph_replays_match_eager(name, opts):
     cfg = synth.CONFIGS[name]
     x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)

@@ -231,6 +231,44 @@ def test_random_problem_stream_k(case):
     _check(out, x, lg, wgu, wd, k, score, renorm, f"sk{i} T={T} d={d} F={F} E={E} k={k} {opts}")
 
 
+def _cases_var_rows(n=12, seed=5151):
+    """Draws over the variable-size gate/up table, merged always (schedule
+    = 3): skewed routing (hot experts past 128 and 256 rows) and uniform,
+    ragged K and partial last column tiles, with the routing, gather,
+    rotation, split and workgroup order drawn."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([1, 2, 5, 8, 16, 33, 64]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([1, 17, 130, 257, 600, 1000]))
+        d = int(64 * rng.integers(1, 17))
+        F = int(64 * rng.integers(1, 16))
+        score = int(rng.integers(0, 2))
+        renorm = bool(rng.integers(0, 2))
+        skew = float(rng.choice([0.0, 1.0, 2.0]))
+        opts = {"schedule": 3, "gather_mode": int(rng.integers(0, 3)),
+                "rotate": int(rng.integers(0, 5)), "xcd_order": int(rng.integers(0, 2))}
+        if rng.random() < 0.4:
+            opts["split_k"] = int(rng.integers(1, 4))
+        fits = (T * k + 63) // 64 * E <= 16384
+        opts["routing_kernels"] = int(rng.choice([0, 1, 2, 3] if fits and E <= 64 and T <= 1024
+                                                 else [0, 2]))
+        out.append((i, T, d, F, E, k, score, renorm, skew, opts))
+    return out
+
+
+@pytest.mark.parametrize("case", _cases_var_rows(), ids=lambda c: f"var{c[0]}")
+def test_random_problem_variable_rows(case):
+    i, T, d, F, E, k, score, renorm, skew, opts = case
+    cfg, x, lg, wgu, wd = parity.make_case(T, d, F, E, k, score=score, renorm=renorm,
+                                           seed=1700 + i, skew=skew)
+    out = moe.moe_forward(x, lg, wgu, wd, k, renorm, score="sigmoid" if score else "softmax",
+                          **opts)
+    _check(out, x, lg, wgu, wd, k, score, renorm,
+           f"var{i} T={T} d={d} F={F} E={E} k={k} skew={skew} {opts}")
+
+
 @pytest.mark.parametrize("case", _cases_many_blocks(), ids=lambda c: f"big{c[0]}")
 def test_random_problem_many_blocks(case):
     i, T, d, F, E, k, score, renorm, opts = case
