@@ -214,11 +214,13 @@ import json, time
 sys.path.insert(0, sys.argv[1])
 import oracle
 from expert_dispatch_router_amd import synth
-oracle.set_threads(1)
 cfg = synth.CONFIGS["tiny"]
 x, lg, wgu, wd = synth.make_inputs(cfg, 0, "cpu")
 xb, lgn = synth.bf16_bits(x), lg.numpy()
 gu, dn = synth.bf16_bits(wgu), synth.bf16_bits(wd)
+# after torch's CPU ops: torch sets the OpenMP thread count when it starts
+# its own pool (from MKL_NUM_THREADS, if set, before OMP_NUM_THREADS)
+oracle.set_threads(1)
 passes, t0 = 0, time.perf_counter()
 while time.perf_counter() - t0 < 2.0:
     oracle.forward(xb, lgn, gu, dn, cfg.top_k, cfg.renormalize, cfg.score, cfg.ffn)
@@ -234,12 +236,14 @@ print(json.dumps({"value": cfg.T * passes / dt, "unit": "tokens/s",
 
 def cpu_single_core_tiny():
     """The oracle on the whole tiny workload in a child process pinned to
-    one CPU (sched_setaffinity before OpenMP starts) with OMP_NUM_THREADS=1:
-    a one-core figure whatever thread count the environment sets."""
+    one CPU (sched_setaffinity before OpenMP starts) with OMP_NUM_THREADS and
+    MKL_NUM_THREADS 1 and the oracle's thread count set to 1 after the
+    inputs are made: a one-core, one-thread figure whatever thread counts
+    the environment sets."""
     import subprocess
 
     cpu = sorted(os.sched_getaffinity(0))[0]
-    env = dict(os.environ, OMP_NUM_THREADS="1")
+    env = dict(os.environ, OMP_NUM_THREADS="1", MKL_NUM_THREADS="1")
     r = subprocess.run([sys.executable, "-c", _SINGLE_CORE_TINY, ROOT, str(cpu)],
                        capture_output=True, text=True, timeout=300, env=env)
     if r.returncode != 0:

@@ -120,9 +120,12 @@ def test_bench_refuses_more_than_one_gpu():
 
 
 
-def test_single_core_tiny_cpu_baseline():
+def test_single_core_tiny_cpu_baseline(monkeypatch):
     """The tiny oracle figure runs in a child process pinned to one CPU with
-    OMP_NUM_THREADS=1: it reports one core and one OpenMP thread."""
+    one OpenMP thread, also where the environment asks torch and OpenMP for
+    16 threads (MKL_NUM_THREADS takes precedence in torch's own pool)."""
+    monkeypatch.setenv("OMP_NUM_THREADS", "16")
+    monkeypatch.setenv("MKL_NUM_THREADS", "16")
     r = bench.cpu_single_core_tiny()
     assert r["cores"] == 1 and r["omp_threads"] == 1, r
     assert r["value"] > 0 and r["kind"] == "oracle", r
