@@ -48,9 +48,12 @@ def test_static_workspace_matches_forward_call_after_call():
 
 def test_static_workspace_at_workload_sizes():
     """The Mixtral-shaped T=512 workload (its workspace near a quarter of
-    the array), then the tiny one: byte-equal to moe_forward; then a problem
-    too large for the array is refused with MOE_ERR_STATIC_LIMIT."""
-    for name in ("mixtral_512", "tiny"):
+    the array), the skewed T=512 one (whose gate/up GEMM runs over the
+    variable-size block table the routing kernels merge, in the array),
+    skewed T=128 (the table not merged: its count alone is written over the
+    previous call's), then the tiny one: byte-equal to moe_forward; then a
+    problem too large for the array is refused with MOE_ERR_STATIC_LIMIT."""
+    for name in ("mixtral_512", "skewed_512", "skewed_128", "tiny"):
         print(f"static workspace: {name}", flush=True)
         cfg = synth.CONFIGS[name]
         x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)
