@@ -314,9 +314,11 @@ class Runner:
 
         import expert_dispatch_router_amd as moe
 
+        # the events are made before the warm-up passes, so that nothing but
+        # the synchronisation separates the last warm-up pass from the timed ones
+        ev = [(moe.Timer(), moe.Timer()) for _ in range(steps)]
         for _ in range(warmup):
             self.step()
-        ev = [(moe.Timer(), moe.Timer()) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
@@ -380,7 +382,11 @@ def hot_experts(r, counts, steps, n_hot=4):
     weights and top-k, with every token routed to the n_hot experts the
     workload's routing loads most (each then holds T rows: full blocks).
     The fused gate/up GEMM's FLOPs over its mean duration (two events around
-    it, as in the timed passes) against the bf16 dense MFMA peak."""
+    it, as in the timed passes) against the bf16 dense MFMA peak, over
+    128-row blocks (the automatic table: the launch fits one round) and over
+    256-row blocks (schedule 3, the tile the workload's hot experts take when
+    its routing kernels merge); `active_frac` divides by the peak of the CUs
+    that have a workgroup (blocks x column tiles, at most 256)."""
     import numpy as np
     import torch
 
@@ -391,22 +397,37 @@ def hot_experts(r, counts, steps, n_hot=4):
     lg = r.logits.clone()
     lg[:, hot] += 40.0  # far above the N(0, 1) scores and the skew biases
     k = cfg.top_k
-    f = lambda se=None: moe.moe_forward(r.x, lg, r.wgu, r.wd, k, cfg.renormalize, out=r.out,
-                                        score=cfg.score, workspace=r.ws, stage_events=se)
-    for _ in range(5):
-        f()
-    ev = [(moe.Timer(), moe.Timer()) for _ in range(steps)]
-    for a, b in ev:
-        f([None, None, None, a.handle, b.handle, None, None])
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_ms(b) for a, b in ev]))
     rows = cfg.T * min(k, n_hot)
     flop = 4.0 * rows * cfg.ffn * cfg.d
-    return {"experts": hot, "rows_per_expert": cfg.T, "gate_up_mean_ms": ms,
-            "gate_up_tflops": flop / (ms * 1e-3) / 1e12,
-            "mfma_frac": flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "note": f"every token routed to the {n_hot} experts the workload loads most "
-                    "(full 128-row blocks); gate/up GEMM FLOPs over its mean duration"}
+    tiles = -(-cfg.ffn // 128)
+    res = {"experts": hot, "rows_per_expert": cfg.T}
+    for label, sched, bm in (("blocks_128", 1, 128), ("blocks_256", 3, 256)):
+        ws = torch.empty(moe.moe_workspace_size(cfg.T, cfg.d, cfg.ffn, cfg.E, k, block_rows=128,
+                                                schedule=sched),
+                         dtype=torch.uint8, device=r.dev)
+        f = lambda se=None: moe.moe_forward(r.x, lg, r.wgu, r.wd, k, cfg.renormalize, out=r.out,
+                                            score=cfg.score, workspace=ws, stage_events=se,
+                                            block_rows=128, schedule=sched)
+        for _ in range(5):
+            f()
+        ev = [(moe.Timer(), moe.Timer()) for _ in range(steps)]
+        for a, b in ev:
+            f([None, None, None, a.handle, b.handle, None, None])
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_ms(b) for a, b in ev]))
+        tf = flop / (ms * 1e-3) / 1e12
+        wgs = min(n_hot * -(-cfg.T // bm) * tiles, 256)
+        res[label] = {"gate_up_mean_ms": ms, "gate_up_tflops": tf,
+                      "mfma_frac": tf / BF16_PEAK_TFLOPS, "workgroups": wgs,
+                      "active_frac": tf / (BF16_PEAK_TFLOPS * wgs / 256)}
+        del ws
+    # the figures of the automatic table, as before, at the top level
+    res.update({"gate_up_mean_ms": res["blocks_128"]["gate_up_mean_ms"],
+                "gate_up_tflops": res["blocks_128"]["gate_up_tflops"],
+                "mfma_frac": res["blocks_128"]["mfma_frac"],
+                "note": f"every token routed to the {n_hot} experts the workload loads most "
+                        "(full blocks); gate/up GEMM FLOPs over its mean duration"})
+    return res
 
 
 def pct(v):
