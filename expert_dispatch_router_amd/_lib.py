@@ -73,7 +73,8 @@ class MoePlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "block_rows", "split_k", "fused_down", "routing_launches", "gather_launch",
         "gate_up_variant", "down_variant", "unfused_swiglu", "fold_combine", "xcd_grouped",
-        "launches", "split_on_device", "stream_k", "variable_rows")]
+        "launches", "split_on_device", "stream_k", "variable_rows")] + [
+        ("var_table_offset", ctypes.c_longlong), ("var_count_offset", ctypes.c_longlong)]
 
 
 class MoeError(RuntimeError):

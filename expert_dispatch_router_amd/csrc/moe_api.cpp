@@ -754,6 +754,8 @@ int moe_plan_ex(int T, int d, int ffn, int E, int top_k, const moe_options* opt,
   info->split_on_device = p.dyn_split ? 1 : 0;
   info->stream_k = p.gu_sk ? 1 : 0;
   info->variable_rows = p.gu_var;
+  info->var_table_offset = p.gu_var ? (long long)p.o_vblocks : -1;
+  info->var_count_offset = p.gu_var ? (long long)p.o_vnb : -1;
   info->launches = info->routing_launches + info->gather_launch + (p.unfused ? 3 : 1) +
                    (p.fused_down ? 0 : 1) + (p.fold ? 0 : 1);
   return MOE_OK;

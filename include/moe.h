@@ -289,6 +289,11 @@ typedef struct moe_plan_info {
     int variable_rows;     /* 1: the gate/up GEMM runs over the variable-size
                               block table, merged when one round needs it;
                               2: merged always (schedule 3); 0: not        */
+    long long var_table_offset; /* byte offsets in the workspace of that table
+                              ([nb_max, 3] int32: expert, first row, rows)  */
+    long long var_count_offset; /* and of its block count (int32; -1 when the
+                              routing kernels kept the fixed table), for
+                              inspection after a call; -1 when not built   */
 } moe_plan_info;
 
 /* Host-only: fills *info with the launch plan moe_forward_ex would follow.

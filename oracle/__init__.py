@@ -84,11 +84,13 @@ def _load():
         lib.orc_permute.argtypes = [P, I, I, P, P, P]
         lib.orc_block_table.argtypes = [P, P, I, I, P, I, P]
         lib.orc_block_order.argtypes = [P, I, P, I, P]
+        lib.orc_var_block_table.argtypes = [P, P, I, I, I, I, I, P, I, P]
         lib.orc_ffn_tokens.argtypes = [P, P, P, P, P, I, I, I, I, I, P, I, P]
         lib.orc_round_bf16.argtypes = [P, P, ctypes.c_long]
         lib.orc_router_logits.argtypes = [P, P, I, I, I, P]
         for f in ("orc_select_topk", "orc_weights", "orc_counts_offsets", "orc_permute",
-                  "orc_block_table", "orc_ffn_tokens", "orc_round_bf16", "orc_router_logits"):
+                  "orc_block_table", "orc_var_block_table", "orc_ffn_tokens", "orc_round_bf16",
+                  "orc_router_logits"):
             getattr(lib, f).restype = I
         _lib = lib
         return lib
@@ -177,6 +179,24 @@ def block_order(blocks: np.ndarray, offsets: np.ndarray, BM: int):
     _check(_load().orc_block_order(_ptr(blocks), nb, _ptr(offsets), BM, _ptr(order)),
            "block_order")
     return order[:nb].copy()
+
+
+def var_block_table(counts: np.ndarray, offsets: np.ndarray, BM: int, tiles: int, mode: int,
+                    round_wgs: int = 256):
+    """O5c: the gate/up GEMM's table with a variable block size per expert
+    (experts past BM rows in blocks of 2 BM when the table merges).  Returns
+    (table [n, 3] of (expert, first row, rows), n), or (None, -1) when the
+    rule keeps the fixed table."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    E = counts.size
+    max_blocks = int(sum((int(c) + BM - 1) // BM for c in counts)) + 1
+    vb = np.zeros((max_blocks, 3), dtype=np.int32)
+    vnb = np.zeros(1, dtype=np.int32)
+    _check(_load().orc_var_block_table(_ptr(counts), _ptr(offsets), E, BM, tiles, mode, round_wgs,
+                                       _ptr(vb), max_blocks, _ptr(vnb)), "var_block_table")
+    n = int(vnb[0])
+    return (None, -1) if n < 0 else (vb[:n].copy(), n)
 
 
 def _expert_ptrs(w, E: int):

@@ -252,6 +252,51 @@ int orc_block_order(const int32_t *blocks, int nb, const int32_t *offsets, int B
     return ORC_OK;
 }
 
+/* O5c -- a block table with a variable block size per expert for the
+ * gate/up GEMM.  The pages leave the assignment of blocks to experts under
+ * skew as future work ([R] abstract: dynamic block-to-expert assignment;
+ * "Editorial extensions"); this is the library's reading of it, written
+ * out plainly.  With `tiles` column tiles per block and a round of `round`
+ * workgroups: the fixed cutting has F = sum_e ceil(counts[e] / BM) blocks;
+ * the merged cutting gives an expert with more than BM rows blocks of 2 BM
+ * rows (the last holding the rest) and the others blocks of BM rows, M
+ * blocks in all.  mode 2 always merges; mode 1 merges when F * tiles >
+ * round and M * tiles <= round.  Merged: vb[3 n] = (e, offsets[e] + r,
+ * min(size, counts[e] - r)) for e ascending, r = 0, size, 2 size, ... and
+ * *vnb = M; not merged: *vnb = -1 and vb is not written. */
+int orc_var_block_table(const int32_t *counts, const int32_t *offsets, int E, int BM, int tiles,
+                        int mode, int round, int32_t *vb, int max_blocks, int32_t *vnb)
+{
+    if (!counts || !offsets || !vnb || E < 1 || BM < 1 || tiles < 1 || round < 1 ||
+        (mode != 1 && mode != 2))
+        return ORC_EARG;
+    long long fixed = 0, merged = 0;
+    for (int e = 0; e < E; ++e) {
+        fixed += (counts[e] + BM - 1) / BM;
+        const int size = counts[e] > BM ? 2 * BM : BM;
+        merged += (counts[e] + size - 1) / size;
+    }
+    const int merge = mode == 2 || (fixed * tiles > round && merged * tiles <= round);
+    if (!merge) {
+        *vnb = -1;
+        return ORC_OK;
+    }
+    if (!vb) return ORC_EARG;
+    int n = 0;
+    for (int e = 0; e < E; ++e) {
+        const int size = counts[e] > BM ? 2 * BM : BM;
+        for (int r = 0; r < counts[e]; r += size) {
+            if (n >= max_blocks) return ORC_EARG;
+            vb[3 * n] = e;
+            vb[3 * n + 1] = offsets[e] + r;
+            vb[3 * n + 2] = counts[e] - r < size ? counts[e] - r : size;
+            ++n;
+        }
+    }
+    *vnb = n;
+    return ORC_OK;
+}
+
 /* O6 -- per-token expert FFN and weighted combination ([R] "What carries the
  * argument": SwiGLU with a gate and an up projection; abstract: expert GEMMs
  * and weighted output combination; Eq. (1)-(4)).  For token t:

@@ -514,6 +514,9 @@ def test_variable_rows_schedule_options():
     assert info["variable_rows"] == 2 and info["block_rows"] == 128
     assert info["gate_up_variant"] == 3 and info["fused_down"] == 0 and info["stream_k"] == 0
     assert moe.moe_plan_ex(*args)["variable_rows"] == 1          # automatic
+    assert 0 <= info["var_table_offset"] < info["var_count_offset"]
+    assert info["var_count_offset"] + 4 <= moe.moe_workspace_size(*args, schedule=3)
+    assert moe.moe_plan_ex(*args, schedule=1)["var_table_offset"] == -1
     assert moe.moe_plan_ex(*args, schedule=1)["variable_rows"] == 0
     assert moe.moe_plan_ex(*args, schedule=2)["variable_rows"] == 0
     nb_max = -(-sk.T * sk.top_k // 128) + min(sk.E, sk.T * sk.top_k)

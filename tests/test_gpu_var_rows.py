@@ -16,12 +16,15 @@ cutting has edges: 1, 128, 129, 130, 256, 257 and 384 rows, an expert with
 none; ragged K and a partial last column tile; both row-gather paths; the
 automatic rule on the skewed workloads at full size (T = 512 merges, T = 128
 does not) on every token; one workspace for merging and non-merging calls
-in a row."""
+in a row.  The table the routing kernels build, and their decision to
+merge, equal the oracle's (O5c) bit for bit, read back from the
+workspace."""
 import numpy as np
 import pytest
 import torch
 
 import expert_dispatch_router_amd as moe
+import oracle
 from expert_dispatch_router_amd import synth
 from tests import parity
 
@@ -162,4 +165,64 @@ def test_variable_rows_workloads_every_token(name):
     ref = parity.workload_reference(name, x, lg, wgu, wd, cfg)
     parity.check_workload(out, ref, name, x, lg, wgu, wd, cfg, what=name + " variable rows")
     del x, lg, wgu, wd, out, fixed, forced
+    torch.cuda.empty_cache()
+
+
+def _device_table(T, d, F, E, k, x, lg, wgu, wd, renorm, score, **opts):
+    """Runs the forward pass in a workspace of its own and reads back the
+    variable-size table and its count the routing kernels left there."""
+    info = moe.moe_plan_ex(T, d, F, E, k, **opts)
+    assert info["variable_rows"] in (1, 2)
+    ws = torch.empty(moe.moe_workspace_size(T, d, F, E, k, **opts), dtype=torch.uint8, device=DEV)
+    moe.moe_forward(x, lg, wgu, wd, k, renorm, score=score, workspace=ws, **opts)
+    torch.cuda.synchronize()
+    c0 = info["var_count_offset"]
+    n = int(ws[c0:c0 + 4].view(torch.int32).item())
+    if n < 0:
+        return None, n, info
+    t0 = info["var_table_offset"]
+    return ws[t0:t0 + 12 * n].view(torch.int32).reshape(n, 3).cpu().numpy(), n, info
+
+
+def _oracle_table(lg, k, score, renorm, F, mode):
+    r = parity.oracle_routing(lg, k, score, renorm, 128)
+    return oracle.var_block_table(r["counts"], r["offsets"], 128, -(-F // 128), mode)
+
+
+@pytest.mark.parametrize("name,opts,merged", [
+    ("edges", {"schedule": 3}, True),
+    ("ragged", {"schedule": 3, "routing_kernels": 1}, True),
+    ("ragged", {"schedule": 3, "routing_kernels": 2}, True),
+    ("ragged", {"schedule": 3, "routing_kernels": 3}, True),
+    ("skewed", {"schedule": 3}, True),
+])
+def test_device_table_matches_oracle(name, opts, merged):
+    """The table the routing kernels build equals the oracle's (O5c) bit for
+    bit, and so does the decision to merge."""
+    x, lg, wgu, wd, k, _ = _case(name)
+    T, d = x.shape
+    E, F = lg.shape[1], wd.shape[2]
+    vb, n, info = _device_table(T, d, F, E, k, x, lg, wgu, wd, True, 0, **opts)
+    want, wn = _oracle_table(lg, k, 0, True, F, info["variable_rows"])
+    assert n == wn and (n >= 0) == merged
+    if merged:
+        assert np.array_equal(vb, want)
+
+
+@pytest.mark.parametrize("name,merged", [("skewed_512", True), ("skewed_256", False),
+                                         ("skewed_128", False), ("qwen2_128", False)])
+def test_device_table_rule_on_workloads(name, merged):
+    """The automatic rule at full size: skewed T=512 merges (30 x 11
+    workgroups to 23 x 11), the others keep the fixed table; the device's
+    table and decision equal the oracle's."""
+    cfg = synth.CONFIGS[name]
+    x, lg, wgu, wd = synth.make_inputs(cfg, 0, DEV)
+    vb, n, info = _device_table(cfg.T, cfg.d, cfg.ffn, cfg.E, cfg.top_k, x, lg, wgu, wd,
+                                cfg.renormalize, cfg.score)
+    assert info["variable_rows"] == 1
+    want, wn = _oracle_table(lg, cfg.top_k, cfg.score, cfg.renormalize, cfg.ffn, 1)
+    assert n == wn and (n >= 0) == merged
+    if merged:
+        assert np.array_equal(vb, want)
+    del x, lg, wgu, wd
     torch.cuda.empty_cache()

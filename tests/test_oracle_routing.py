@@ -190,3 +190,70 @@ def test_block_order_is_the_stable_sort_by_rows():
         assert sorted(order.tolist()) == list(range(nb))
         for a, b in zip(order[:-1], order[1:]):
             assert rows[a] > rows[b] or (rows[a] == rows[b] and a < b)
+
+
+# ---------------------------------------------- variable block size per expert
+
+_EDGES = np.array([129, 0, 256, 257, 1, 384, 128, 130], dtype=np.int32)
+
+
+def _offsets(counts):
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+def test_var_block_table_hand_worked():
+    """Experts of 129, 0, 256, 257, 1, 384, 128 and 130 rows at BM = 128:
+    merged, every expert past 128 rows takes 256-row blocks (the last holding
+    the rest), the others 128-row blocks -- worked by hand.  The fixed
+    cutting has 2+0+2+3+1+3+1+2 = 14 blocks, the merged one 9."""
+    off = _offsets(_EDGES)
+    want = [[0, 0, 129],
+            [2, 129, 256],
+            [3, 385, 256], [3, 641, 1],
+            [4, 642, 1],
+            [5, 643, 256], [5, 899, 128],
+            [6, 1027, 128],
+            [7, 1155, 130]]
+    vb, n = oracle.var_block_table(_EDGES, off, 128, 4, 2)      # mode 2: always merged
+    assert n == 9 and vb.tolist() == want
+    # mode 1: merged only when 14 * tiles > round >= 9 * tiles
+    assert oracle.var_block_table(_EDGES, off, 128, 4, 1) == (None, -1)     # 56: one round
+    assert oracle.var_block_table(_EDGES, off, 128, 18, 1) == (None, -1)    # 252: one round
+    assert oracle.var_block_table(_EDGES, off, 128, 19, 1)[1] == 9          # 266 -> 171
+    assert oracle.var_block_table(_EDGES, off, 128, 28, 1)[1] == 9          # 392 -> 252
+    assert oracle.var_block_table(_EDGES, off, 128, 29, 1) == (None, -1)    # 406 -> 261
+    assert oracle.var_block_table(_EDGES, off, 128, 28, 1, round_wgs=252)[1] == 9
+    assert oracle.var_block_table(_EDGES, off, 128, 28, 1, round_wgs=251) == (None, -1)
+
+
+def test_var_block_table_covers_every_row_once():
+    """On skewed random routings, merged always: the blocks tile each
+    expert's rows [offsets[e], offsets[e+1]) in order without gap or
+    overlap, hold at most 2 BM rows (at most BM for an expert of at most BM
+    rows, where they equal the fixed table's blocks), and are no more than
+    the fixed table's."""
+    rng = np.random.default_rng(23)
+    for trial in range(40):
+        E = int(rng.integers(1, 40))
+        k = int(rng.integers(1, min(E, 6) + 1))
+        T = int(rng.integers(0, 600))
+        BM = int(rng.choice([16, 64, 128]))
+        bias = -2.0 * np.log(rng.permutation(E) + 1.0)
+        lg = (rng.standard_normal((T, E)) + bias).astype(np.float32)
+        ids, _ = oracle.route(lg, k, 0, True)
+        counts, offsets = oracle.counts_offsets(ids, E)
+        fixed, nf = oracle.block_table(counts, offsets, BM)
+        vb, n = oracle.var_block_table(counts, offsets, BM, 1, 2)
+        assert n <= nf, trial
+        vb = vb.reshape(-1, 3)
+        for e in range(E):
+            mine = vb[vb[:, 0] == e]
+            at = int(offsets[e])
+            for _, r0, rows in mine:
+                assert r0 == at and 0 < rows <= (2 * BM if counts[e] > BM else BM), trial
+                at += int(rows)
+            assert at == offsets[e + 1], trial
+            if counts[e] <= BM:
+                assert [(int(a), int(b)) for a, b, _ in mine] == \
+                    [(int(a), int(b)) for a, b in fixed[fixed[:, 0] == e]], trial
+        assert vb[:, 0].tolist() == sorted(vb[:, 0].tolist()), trial
