@@ -852,7 +852,7 @@ __device__ __forceinline__ void lds_tile_store(
 // h [A, N]; kOutF32Parts, kOutF32Wide and kOutF32Dense -> fp32 y [split, A,
 // N] (part p sums K steps [p * ksplit, (p + 1) * ksplit)).  kOutF32Dense
 // reads no schedule (blocks, nb_dev, order and offsets may be null).
-template <int BM, int WAVES, int BK, int STAGES, int MODE, int WCPOL, int SUB>
+template <int BM, int WAVES, int BK, int STAGES, int MODE, int WCPOL, int SUB, int BMS = 0>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
@@ -901,6 +901,22 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
   const int n0 = tile * G::kTileCols + wave * G::kWaveCols;
   const unsigned rkey = rotate == 2 ? (unsigned)wg : rotate == 3 ? (unsigned)e : (unsigned)b;
   const int shift = rotate ? (int)((rkey * 2654435761u) % (unsigned)max(nks, 1)) : 0;
+  if constexpr (BMS > 0) {
+    // a block of at most BMS rows runs the same columns at BMS rows (fewer
+    // activation groups per stage and subtiles per wave; the same K order)
+    using GS = LdsGemm<BMS, WAVES, BK, STAGES, MODE, SUB>;
+    static_assert(BMS < BM && GS::kTileCols == G::kTileCols && GS::kWaveCols == G::kWaveCols,
+                  "the smaller tile covers the same columns");
+    if (rows <= BMS) {
+      f32x4 acc[NG][BMS / 16][SUB];
+      lds_tile_zero<NG, BMS / 16, SUB>(acc);
+      lds_tile_mma<BMS, WAVES, BK, STAGES, MODE, WCPOL, SUB>(lds, X, W, w_estride, e, r0, rows, n0,
+                                                             kb, N, K, nks, shift, 0, nks,
+                                                             gather_perm, gather_k, x_rows, acc);
+      lds_tile_store<BMS, WAVES, BK, STAGES, MODE, SUB>(acc, out, A, N, r0, rows, n0, part);
+      return;
+    }
+  }
   f32x4 acc[NG][MT][SUB];
   lds_tile_zero<NG, MT, SUB>(acc);
   lds_tile_mma<BM, WAVES, BK, STAGES, MODE, WCPOL, SUB>(lds, X, W, w_estride, e, r0, rows, n0, kb,
@@ -1108,7 +1124,7 @@ constexpr int kLdsStages = 2;  // 2 x 80 KiB: the whole LDS of a CU at BM = 192,
 constexpr int kLdsNarrowStages = 3;  // 3 x 48 KiB at BM = 128 with one subtile per wave
 
 // WCPOL: cache policy of the weight loads; STAGES, SUB as in LdsGemm.
-template <int BM, int WAVES, int MODE, int WCPOL, int STAGES = kLdsStages, int SUB = 2>
+template <int BM, int WAVES, int MODE, int WCPOL, int STAGES = kLdsStages, int SUB = 2, int BMS = 0>
 hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
                           const int32_t* blocks, const int32_t* nb, const int32_t* order,
                           const int32_t* offsets, void* out, int A, int N, int K, int split,
@@ -1125,7 +1141,7 @@ hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estr
   const long long grid = xcd_group ? ((long long)tiles_per_block * nb_max + kXcds - 1) / kXcds * kXcds
                                    : (long long)tiles_per_block * nb_max;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  gemm_lds_kernel<BM, WAVES, kLdsBK, STAGES, MODE, WCPOL, SUB><<<(unsigned)grid, G::kThreads, 0, s>>>(
+  gemm_lds_kernel<BM, WAVES, kLdsBK, STAGES, MODE, WCPOL, SUB, BMS><<<(unsigned)grid, G::kThreads, 0, s>>>(
       X, W, w_estride, blocks, nb, order, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
       gather_perm, gather_k, x_rows, xcd_group, dyn_split);
   return hipGetLastError();
@@ -1171,7 +1187,7 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
   // (Mixtral T=512 gate/up measured 360.8 -> 334.9 us).
   if (bm == 192 && variant == kGateUpLdsVariant) {
     if (x_tiled) return hipErrorInvalidValue;  // row-major activations only
-    return launch_lds_cfg<192, 7, kOutSwiGLU, kCpolNT>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order,
+    return launch_lds_cfg<192, 7, kOutSwiGLU, kCpolNT, kLdsStages, 2, 128>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order,
                                               offsets, h, A, ffn, d, 1, d, nb_max, rotate,
                                               gather_perm, k, T, xcd_group, s);
   }
@@ -1288,20 +1304,21 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
     // 1336 -> 1284) and slower where they do not (DeepSeek-V3 T=4096, 940 MB
     // of partials: down 1694 -> 1726, combination 188 -> 219).
     const bool nt = (long long)split * A * d * 4 <= (256LL << 20);
-#define MOE_DOWN_LDS(BMV, CP, ST)                                                                \
-  return launch_lds_cfg<BMV, 8, kOutF32Parts, CP, ST>(h, w_down, (long long)d * ffn, blocks, nb, order, \
-                                                  offsets, y, A, d, ffn, split, ksplit, nb_max,   \
-                                                  rotate, nullptr, 1, A, xcd_group, s, dyn_split)
+#define MOE_DOWN_LDS(BMV, CP, ST, BMS)                                                           \
+  return launch_lds_cfg<BMV, 8, kOutF32Parts, CP, ST, 2, BMS>(h, w_down, (long long)d * ffn, blocks, nb, \
+                                                  order, offsets, y, A, d, ffn, split, ksplit,    \
+                                                  nb_max, rotate, nullptr, 1, A, xcd_group, s,    \
+                                                  dyn_split)
     if (bm == 192) {
-      if (nt) MOE_DOWN_LDS(192, kCpolNT, kLdsStages);
-      MOE_DOWN_LDS(192, 0, kLdsStages);
+      if (nt) MOE_DOWN_LDS(192, kCpolNT, kLdsStages, 128);
+      MOE_DOWN_LDS(192, 0, kLdsStages, 128);
     }
     if (bm == 256) {
-      if (nt) MOE_DOWN_LDS(256, kCpolNT, kLdsStages);
-      MOE_DOWN_LDS(256, 0, kLdsStages);
+      if (nt) MOE_DOWN_LDS(256, kCpolNT, kLdsStages, 0);
+      MOE_DOWN_LDS(256, 0, kLdsStages, 0);
     }
-    if (nt) MOE_DOWN_LDS(128, kCpolNT, kLdsStages);
-    MOE_DOWN_LDS(128, 0, kLdsStages);
+    if (nt) MOE_DOWN_LDS(128, kCpolNT, kLdsStages, 0);
+    MOE_DOWN_LDS(128, 0, kLdsStages, 0);
 #undef MOE_DOWN_LDS
   }
   // The wide LDS-staged tile: 64 columns per wave (7 waves at BM = 192, 8 at

@@ -210,6 +210,36 @@ def test_narrow_lds_gate_up_tile(name):
     assert torch.equal(out.view(torch.int16), base.view(torch.int16))
 
 
+# ------------------------ 192-row LDS tiles: blocks of at most 128 rows
+
+def _exact_counts_case(counts, d, F, seed):
+    """top-1 logits giving expert e exactly counts[e] tokens."""
+    E = len(counts)
+    owner = np.repeat(np.arange(E), counts)
+    np.random.default_rng(seed).shuffle(owner)
+    T = len(owner)
+    lg = torch.full((T, E), -3.0)
+    lg[torch.arange(T), torch.from_numpy(owner)] = 3.0
+    _, x, lg, wgu, wd = parity.make_case(T, d, F, E, 1, seed=seed, logits=lg)
+    return x, lg, wgu, wd, parity.oracle_out(x, lg, wgu, wd, 1, 0, True)
+
+
+@pytest.mark.parametrize("split", [1, 2])
+def test_192_row_tiles_switch_at_128_rows(split):
+    """The LDS-staged gate/up (224 columns) and down (256 columns) tiles of
+    BM = 192 run a block of at most 128 rows at 128 rows (the same columns,
+    fewer activation groups): blocks of 1, 64, 128 (128-row path), 129 and
+    192 rows (192-row path) give the same bytes as the register-ring tiles,
+    and meet the tolerance."""
+    x, lg, wgu, wd, ref = _exact_counts_case([128, 129, 1, 192, 64, 0], 512, 448, 43)
+    out = moe.moe_forward(x, lg, wgu, wd, 1, True, block_rows=192, tile_variant=LDS,
+                          down_variant=3, split_k=split)
+    parity.check_out(out, ref, f"192-row tiles split={split}")
+    base = moe.moe_forward(x, lg, wgu, wd, 1, True, block_rows=192, tile_variant=REGRING,
+                           down_variant=1, split_k=split)
+    assert torch.equal(out.view(torch.int16), base.view(torch.int16))
+
+
 # ------------------------------------------- the wide LDS-staged down tile
 
 DOWN_WIDE = 4  # down_variant option value of the wide LDS-staged down tile (variant 3)
