@@ -852,7 +852,11 @@ __device__ __forceinline__ void lds_tile_store(
 // h [A, N]; kOutF32Parts, kOutF32Wide and kOutF32Dense -> fp32 y [split, A,
 // N] (part p sums K steps [p * ksplit, (p + 1) * ksplit)).  kOutF32Dense
 // reads no schedule (blocks, nb_dev, order and offsets may be null).
-template <int BM, int WAVES, int BK, int STAGES, int MODE, int WCPOL, int SUB, int BMS = 0>
+// BMS, BMS2 (0: none): a block of at most that many rows takes the same
+// tile at that many rows, chosen per block (a shorter subtile loop; same
+// columns, same K order, same bytes).
+template <int BM, int WAVES, int BK, int STAGES, int MODE, int WCPOL, int SUB, int BMS = 0,
+          int BMS2 = 0>
 __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, long long w_estride,
     const int32_t* __restrict__ blocks, const int32_t* __restrict__ nb_dev,
@@ -901,9 +905,23 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_lds_kernel(
   const int n0 = tile * G::kTileCols + wave * G::kWaveCols;
   const unsigned rkey = rotate == 2 ? (unsigned)wg : rotate == 3 ? (unsigned)e : (unsigned)b;
   const int shift = rotate ? (int)((rkey * 2654435761u) % (unsigned)max(nks, 1)) : 0;
+  // a block of at most BMS2 (BMS) rows runs the same columns at BMS2 (BMS)
+  // rows: fewer activation groups per stage and subtiles per wave, the same
+  // K order
+  if constexpr (BMS2 > 0) {
+    using GS = LdsGemm<BMS2, WAVES, BK, STAGES, MODE, SUB>;
+    static_assert(BMS2 < BMS && GS::kTileCols == G::kTileCols, "the smallest tile");
+    if (rows <= BMS2) {
+      f32x4 acc[NG][BMS2 / 16][SUB];
+      lds_tile_zero<NG, BMS2 / 16, SUB>(acc);
+      lds_tile_mma<BMS2, WAVES, BK, STAGES, MODE, WCPOL, SUB>(lds, X, W, w_estride, e, r0, rows,
+                                                              n0, kb, N, K, nks, shift, 0, nks,
+                                                              gather_perm, gather_k, x_rows, acc);
+      lds_tile_store<BMS2, WAVES, BK, STAGES, MODE, SUB>(acc, out, A, N, r0, rows, n0, part);
+      return;
+    }
+  }
   if constexpr (BMS > 0) {
-    // a block of at most BMS rows runs the same columns at BMS rows (fewer
-    // activation groups per stage and subtiles per wave; the same K order)
     using GS = LdsGemm<BMS, WAVES, BK, STAGES, MODE, SUB>;
     static_assert(BMS < BM && GS::kTileCols == G::kTileCols && GS::kWaveCols == G::kWaveCols,
                   "the smaller tile covers the same columns");
@@ -1124,7 +1142,8 @@ constexpr int kLdsStages = 2;  // 2 x 80 KiB: the whole LDS of a CU at BM = 192,
 constexpr int kLdsNarrowStages = 3;  // 3 x 48 KiB at BM = 128 with one subtile per wave
 
 // WCPOL: cache policy of the weight loads; STAGES, SUB as in LdsGemm.
-template <int BM, int WAVES, int MODE, int WCPOL, int STAGES = kLdsStages, int SUB = 2, int BMS = 0>
+template <int BM, int WAVES, int MODE, int WCPOL, int STAGES = kLdsStages, int SUB = 2, int BMS = 0,
+          int BMS2 = 0>
 hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estride,
                           const int32_t* blocks, const int32_t* nb, const int32_t* order,
                           const int32_t* offsets, void* out, int A, int N, int K, int split,
@@ -1141,7 +1160,7 @@ hipError_t launch_lds_cfg(const uint16_t* X, const uint16_t* W, long long w_estr
   const long long grid = xcd_group ? ((long long)tiles_per_block * nb_max + kXcds - 1) / kXcds * kXcds
                                    : (long long)tiles_per_block * nb_max;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidValue;
-  gemm_lds_kernel<BM, WAVES, kLdsBK, STAGES, MODE, WCPOL, SUB, BMS><<<(unsigned)grid, G::kThreads, 0, s>>>(
+  gemm_lds_kernel<BM, WAVES, kLdsBK, STAGES, MODE, WCPOL, SUB, BMS, BMS2><<<(unsigned)grid, G::kThreads, 0, s>>>(
       X, W, w_estride, blocks, nb, order, offsets, out, A, N, K, ksplit, tiles_per_block, rotate,
       gather_perm, gather_k, x_rows, xcd_group, dyn_split);
   return hipGetLastError();
@@ -1187,7 +1206,7 @@ hipError_t launch_gate_up(int bm, int variant, const uint16_t* x, const int32_t*
   // (Mixtral T=512 gate/up measured 360.8 -> 334.9 us).
   if (bm == 192 && variant == kGateUpLdsVariant) {
     if (x_tiled) return hipErrorInvalidValue;  // row-major activations only
-    return launch_lds_cfg<192, 7, kOutSwiGLU, kCpolNT, kLdsStages, 2, 128>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order,
+    return launch_lds_cfg<192, 7, kOutSwiGLU, kCpolNT, kLdsStages, 2, 128, 64>(x, w_gate_up, 2LL * ffn * d, blocks, nb, order,
                                               offsets, h, A, ffn, d, 1, d, nb_max, rotate,
                                               gather_perm, k, T, xcd_group, s);
   }
@@ -1305,7 +1324,7 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
     // of partials: down 1694 -> 1726, combination 188 -> 219).
     const bool nt = (long long)split * A * d * 4 <= (256LL << 20);
 #define MOE_DOWN_LDS(BMV, CP, ST, BMS)                                                           \
-  return launch_lds_cfg<BMV, 8, kOutF32Parts, CP, ST, 2, BMS>(h, w_down, (long long)d * ffn, blocks, nb, \
+  return launch_lds_cfg<BMV, 8, kOutF32Parts, CP, ST, 2, BMS, (BMS ? 64 : 0)>(h, w_down, (long long)d * ffn, blocks, nb, \
                                                   order, offsets, y, A, d, ffn, split, ksplit,    \
                                                   nb_max, rotate, nullptr, 1, A, xcd_group, s,    \
                                                   dyn_split)

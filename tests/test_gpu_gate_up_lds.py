@@ -225,13 +225,14 @@ def _exact_counts_case(counts, d, F, seed):
 
 
 @pytest.mark.parametrize("split", [1, 2])
-def test_192_row_tiles_switch_at_128_rows(split):
+def test_192_row_tiles_switch_at_64_and_128_rows(split):
     """The LDS-staged gate/up (224 columns) and down (256 columns) tiles of
-    BM = 192 run a block of at most 128 rows at 128 rows (the same columns,
-    fewer activation groups): blocks of 1, 64, 128 (128-row path), 129 and
-    192 rows (192-row path) give the same bytes as the register-ring tiles,
-    and meet the tolerance."""
-    x, lg, wgu, wd, ref = _exact_counts_case([128, 129, 1, 192, 64, 0], 512, 448, 43)
+    BM = 192 run a block of at most 64 rows at 64 rows and one of at most
+    128 at 128 (the same columns, fewer activation groups): blocks of 1 and
+    64 rows (64-row path), 65 and 128 (128-row path), 129 and 192 rows
+    (192-row path) give the same bytes as the register-ring tiles, and meet
+    the tolerance."""
+    x, lg, wgu, wd, ref = _exact_counts_case([128, 129, 1, 192, 64, 0, 65], 512, 448, 43)
     out = moe.moe_forward(x, lg, wgu, wd, 1, True, block_rows=192, tile_variant=LDS,
                           down_variant=3, split_k=split)
     parity.check_out(out, ref, f"192-row tiles split={split}")
