@@ -1323,21 +1323,21 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
     // 1336 -> 1284) and slower where they do not (DeepSeek-V3 T=4096, 940 MB
     // of partials: down 1694 -> 1726, combination 188 -> 219).
     const bool nt = (long long)split * A * d * 4 <= (256LL << 20);
-#define MOE_DOWN_LDS(BMV, CP, ST, BMS)                                                           \
-  return launch_lds_cfg<BMV, 8, kOutF32Parts, CP, ST, 2, BMS, (BMS ? 64 : 0)>(h, w_down, (long long)d * ffn, blocks, nb, \
+#define MOE_DOWN_LDS(BMV, CP, ST, BMS, BMS2)                                                     \
+  return launch_lds_cfg<BMV, 8, kOutF32Parts, CP, ST, 2, BMS, BMS2>(h, w_down, (long long)d * ffn, blocks, nb, \
                                                   order, offsets, y, A, d, ffn, split, ksplit,    \
                                                   nb_max, rotate, nullptr, 1, A, xcd_group, s,    \
                                                   dyn_split)
     if (bm == 192) {
-      if (nt) MOE_DOWN_LDS(192, kCpolNT, kLdsStages, 128);
-      MOE_DOWN_LDS(192, 0, kLdsStages, 128);
+      if (nt) MOE_DOWN_LDS(192, kCpolNT, kLdsStages, 128, 64);
+      MOE_DOWN_LDS(192, 0, kLdsStages, 128, 64);
     }
     if (bm == 256) {
-      if (nt) MOE_DOWN_LDS(256, kCpolNT, kLdsStages, 0);
-      MOE_DOWN_LDS(256, 0, kLdsStages, 0);
+      if (nt) MOE_DOWN_LDS(256, kCpolNT, kLdsStages, 0, 0);
+      MOE_DOWN_LDS(256, 0, kLdsStages, 0, 0);
     }
-    if (nt) MOE_DOWN_LDS(128, kCpolNT, kLdsStages, 0);
-    MOE_DOWN_LDS(128, 0, kLdsStages, 0);
+    if (nt) MOE_DOWN_LDS(128, kCpolNT, kLdsStages, 0, 0);
+    MOE_DOWN_LDS(128, 0, kLdsStages, 0, 0);
 #undef MOE_DOWN_LDS
   }
   // The wide LDS-staged tile: 64 columns per wave (7 waves at BM = 192, 8 at
