@@ -1348,7 +1348,7 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
   if ((bm == 192 || bm == 128) && variant == kDownLdsWideVariant) {
     if (fold.cnt) return hipErrorInvalidValue;
     if (bm == 192)
-      return launch_lds_cfg<192, 7, kOutF32Wide, kCpolNT>(h, w_down, (long long)d * ffn, blocks, nb,
+      return launch_lds_cfg<192, 7, kOutF32Wide, kCpolNT, kLdsStages, 2, 128>(h, w_down, (long long)d * ffn, blocks, nb,
                                                          order, offsets, y, A, d, ffn, split, ksplit,
                                                          nb_max, rotate, nullptr, 1, A, xcd_group, s,
                                                          dyn_split);
