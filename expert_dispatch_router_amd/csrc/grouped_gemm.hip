@@ -1193,6 +1193,8 @@ int down_tile_cols(int bm, int variant) {
     return LdsGemm<192, 7, kLdsBK, kLdsStages, kOutF32Wide>::kTileCols;  // 448
   if (bm == 128 && variant == kDownLdsWideVariant)
     return LdsGemm<128, 8, kLdsBK, kLdsStages, kOutF32Wide>::kTileCols;  // 512
+  if (bm == 128 && variant == kDownLdsWide7Variant)
+    return LdsGemm<128, 7, kLdsBK, kLdsStages, kOutF32Wide>::kTileCols;  // 448
   return 0;
 }
 
@@ -1353,6 +1355,14 @@ hipError_t launch_down(int bm, int variant, const uint16_t* h, const uint16_t* w
                                                          nb_max, rotate, nullptr, 1, A, xcd_group, s,
                                                          dyn_split);
     return launch_lds_cfg<128, 8, kOutF32Wide, kCpolNT>(h, w_down, (long long)d * ffn, blocks, nb,
+                                                       order, offsets, y, A, d, ffn, split, ksplit,
+                                                       nb_max, rotate, nullptr, 1, A, xcd_group, s,
+                                                       dyn_split);
+  }
+  // The same tile with 7 waves at BM = 128 (448 columns)
+  if (bm == 128 && variant == kDownLdsWide7Variant) {
+    if (fold.cnt) return hipErrorInvalidValue;
+    return launch_lds_cfg<128, 7, kOutF32Wide, kCpolNT>(h, w_down, (long long)d * ffn, blocks, nb,
                                                        order, offsets, y, A, d, ffn, split, ksplit,
                                                        nb_max, rotate, nullptr, 1, A, xcd_group, s,
                                                        dyn_split);

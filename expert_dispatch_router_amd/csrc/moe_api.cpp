@@ -297,12 +297,24 @@ bool down_lds_fits(int bm, int d, bool fold) {
 // else variant 0.
 constexpr int kWideDownMinTiles = 6;
 
+// At BM = 128 the wide tile comes in 8 waves (512 columns) and 7 (448): the
+// 7-wave one where its whole tiles fill the last round of 256 workgroups
+// better (Qwen2, d = 3584, 64 blocks: 7 x 64 = 448 workgroups, 1.75
+// rounds, against 8 x 64 = 512, two whole rounds).  Measured, pass ms,
+// interleaved: Qwen2 T=128/256/512 0.5751 -> 0.5667, 0.5886 -> 0.5825,
+// 0.6142 -> 0.6117 (down 203 -> 194 us at T=128); the same bytes.
 int auto_dn_variant(int A, int E, int bm, int d, int split, bool fold) {
   if (!fold && (bm == 128 || bm == 192)) {
     const int wc = down_tile_cols(bm, kDownLdsWideVariant);
     if (wc > 0 && tile_waste(d, wc) <= kMaxLdsTileWaste && (d + wc - 1) / wc >= kWideDownMinTiles &&
-        est_workgroups(A, E, bm, d, wc) * split >= 256)
+        est_workgroups(A, E, bm, d, wc) * split >= 256) {
+      const int w7 = bm == 128 ? down_tile_cols(bm, kDownLdsWide7Variant) : 0;
+      if (w7 > 0 && d % w7 == 0 &&
+          round_balance(est_workgroups(A, E, bm, d, w7) * split, 256) >
+              round_balance(est_workgroups(A, E, bm, d, wc) * split, 256) + 0.05)
+        return kDownLdsWide7Variant;
       return kDownLdsWideVariant;
+    }
   }
   return down_lds_fits(bm, d, fold) ? kDownLdsVariant : 0;
 }
@@ -378,7 +390,7 @@ void make_plan(int T, int d, int ffn, int E, int k, const moe_options* opt, Plan
                                                : auto_dn_variant(A, E, p->bm, d, p->split, p->fold);
     if (p->dn_variant == kDownLdsVariant && !down_lds_fits(p->bm, d, p->fold))
       p->plan_error = MOE_ERR_UNSUPPORTED;  // forced where it cannot run
-    if (p->dn_variant == kDownLdsWideVariant && p->fold)
+    if ((p->dn_variant == kDownLdsWideVariant || p->dn_variant == kDownLdsWide7Variant) && p->fold)
       p->plan_error = MOE_ERR_UNSUPPORTED;  // the fold lives in the register-ring tiles
     // 256-row blocks run only the LDS-staged tiles: the narrow gate/up tile
     // and the 256-column down tile (d a multiple of 256); not the unfused

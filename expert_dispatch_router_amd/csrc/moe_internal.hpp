@@ -316,6 +316,8 @@ constexpr int kDownLdsVariant = 2;
 // Tile variant of the down GEMM at BM = 128 and 192 that stages its weights in LDS with 64
 // columns per wave (8 waves, 512 columns at BM = 128; 7 waves, 448 at BM = 192).
 constexpr int kDownLdsWideVariant = 3;
+// The wide tile with 7 waves at BM = 128 (448 columns).
+constexpr int kDownLdsWide7Variant = 4;
 int down_tile_cols(int bm, int variant);
 
 }  // namespace moe

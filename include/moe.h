@@ -117,12 +117,15 @@ typedef struct moe_options {
      * at BM = 192), 2 (256 columns, 8 waves of 32, weights staged in LDS;
      * only when d is a multiple of 256) and 3 (64 columns per wave staged
      * in LDS: 512 columns, 8 waves at BM = 128; 448 columns, 7 waves at
-     * BM = 192; the last column tile may be partial); variants 2 and 3
-     * only when the combination is not folded into the down GEMM, else
-     * MOE_ERR_UNSUPPORTED.  Automatic: variant 3 on launches with many
-     * workgroups and at least six column tiles per block, else 2 where it
-     * fits; every other BM has variant 0 only.  0 = automatic.  All
-     * variants give the same bytes (the same per-output K order). */
+     * BM = 192; the last column tile may be partial) and, at BM = 128, 4
+     * (the same 64 columns per wave in 7 waves: 448 columns); variants 2
+     * to 4 only when the combination is not folded into the down GEMM,
+     * else MOE_ERR_UNSUPPORTED.  Automatic: variant 3 on launches with many
+     * workgroups and at least six column tiles per block -- at BM = 128
+     * variant 4 instead where d is a multiple of 448 and its workgroups
+     * fill whole rounds of 256 better -- else 2 where it fits; every other
+     * BM has variant 0 only.  0 = automatic.  All variants give the same
+     * bytes (the same per-output K order). */
     int down_variant;
     /* K-start rotation of the GEMMs: a workgroup starts its reduction at a
      * step derived from its schedule block (2), from its own id (3) or from

@@ -108,6 +108,14 @@ def test_options_checks():
         assert _ws(64, 320, 512, 8, 2, _o(bm, dvar=4))[0] == OK
         assert _ws(64, 256, 512, 8, 2, _o(bm, dvar=4, fold=2))[0] == UNSUP
     assert _ws(64, 256, 512, 8, 2, _o(64, dvar=4))[0] == UNSUP
+    # its 7-wave form (variant 4, option value 5): BM = 128 only
+    assert _ws(64, 320, 512, 8, 2, _o(128, dvar=5))[0] == OK
+    assert _ws(64, 256, 512, 8, 2, _o(128, dvar=5, fold=2))[0] == UNSUP
+    assert _ws(64, 256, 512, 8, 2, _o(192, dvar=5))[0] == UNSUP
+    assert _ws(64, 256, 512, 8, 2, _o(128, dvar=6))[0] == UNSUP
+    # automatic: the 7-wave tile where its whole tiles fill the rounds better
+    assert moe.moe_plan_ex(512, 3584, 2560, 64, 8)["down_variant"] == 4     # Qwen2 T=512
+    assert moe.moe_plan_ex(512, 7168, 2048, 256, 8)["down_variant"] == 3    # DeepSeek-V3 T=512
     for r in (1, 2, 3):
         assert _ws(64, 256, 512, 8, 2, _o(0, 0, 0, r))[0] == OK
 

@@ -256,17 +256,18 @@ WIDE_CASES = {
 
 
 @pytest.mark.parametrize("split", [1, 2, 3])
-@pytest.mark.parametrize("bm", [128, 192])
+@pytest.mark.parametrize("bm,variant", [(128, DOWN_WIDE), (192, DOWN_WIDE), (128, DOWN_WIDE + 1)])
 @pytest.mark.parametrize("name", sorted(WIDE_CASES))
-def test_lds_wide_down_matches_oracle_and_register_tile(name, bm, split):
+def test_lds_wide_down_matches_oracle_and_register_tile(name, bm, variant, split):
     """The down GEMM with 64 columns per wave staged in LDS (512 columns at
-    BM = 128, 448 at BM = 192, the last tile possibly partial): within the
-    tolerance, and the same bytes as the register-ring down tile (variant
-    0), which sums every output's K chunks in the same order."""
+    BM = 128, 448 at BM = 192 and in the 7-wave tile of BM = 128, the last
+    tile possibly partial): within the tolerance, and the same bytes as the
+    register-ring down tile (variant 0), which sums every output's K chunks
+    in the same order."""
     x, lg, wgu, wd, k, ref = _case(name, *WIDE_CASES[name])
     out = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, split_k=split,
-                          down_variant=DOWN_WIDE)
-    parity.check_out(out, ref, f"wide down {name} bm={bm} split={split}")
+                          down_variant=variant)
+    parity.check_out(out, ref, f"wide down {name} bm={bm} variant={variant} split={split}")
     base = moe.moe_forward(x, lg, wgu, wd, k, True, block_rows=bm, split_k=split, down_variant=1)
     assert torch.equal(out.view(torch.int16), base.view(torch.int16))
 

@@ -308,7 +308,7 @@ def _cases_all_options(n=60, seed=31337):
             if rng.random() < 0.5:
                 opts["tile_variant"] = int(rng.integers(0, 4))
             if rng.random() < 0.5:
-                opts["down_variant"] = int(rng.integers(0, 5))
+                opts["down_variant"] = int(rng.integers(0, 6))
         for key, hi in (("split_k", 5), ("rotate", 4), ("routing_kernels", 4), ("gather_mode", 4),
                         ("xcd_order", 4), ("fold_combine", 3), ("fuse_down", 3),
                         ("unfused_swiglu", 2)):
