@@ -349,24 +349,28 @@ __global__ __launch_bounds__(256) void gather_tiled_kernel(const uint16_t* __res
   }
 }
 
-// Small problems (T <= 1024 tokens, E <= 32 experts): the whole routing in
-// one workgroup of 1024 threads, thread t = token t.  Three launches (route,
-// histogram+scan+schedule, reorder) cost more than this work.
-//   1. route: the token's E logits in registers, k rounds of "best live
-//      candidate" in ascending expert order under the same rank rule as the
-//      lane-group route (so the same experts, in the same order);
-//   2. count: per expert, a ballot over each wave of "my token chose e"; the
+// Small problems (T <= 1024 tokens, E <= 64 experts; automatic up to 32):
+// the whole routing in one workgroup of 1024 threads, thread t = token t.
+// Three launches (route, histogram+scan+schedule, reorder) cost more than
+// this work.
+//   1. route: up to 32 experts (LPT = 1), the token's E logits in registers,
+//      k rounds of "best live candidate" in ascending expert order under the
+//      same rank rule as the lane-group route (so the same experts, in the
+//      same order); beyond, groups of LPT lanes per token run the lane-group
+//      route itself and pass the k experts to thread t through LDS;
+//   2. count: per expert and wave, the mask of lanes whose token chose e
+//      (a ballot per expert, or with lane groups k LDS ORs per token); the
 //      masks and their popcounts go to LDS;
 //   3. one exclusive scan over the (expert, wave) counts in expert-major
 //      order gives, for every wave, where its rows of expert e start; a
 //      token has at most one row per expert, so ascending token order within
 //      an expert is ascending flat index i = t*k + j, and a row's position is
-//      that start plus the rank of its lane in the wave's ballot;
+//      that start plus the rank of its lane in the wave's mask;
 //   4. counts, offsets, the block table and the block count.
 // Identical results to the general path.
 constexpr int kSmallWaves = kScanThreads / 64;
 
-template <int EMAX>
+template <int EMAX, int LPT>
 __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
     const LogitSrc logits, int T, int E, int k, int renorm, int score, int bm,
     int32_t* __restrict__ ids, float* __restrict__ w, int32_t* __restrict__ counts,
@@ -386,51 +390,74 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
   for (int i = t; i < zero.n; i += kScanThreads) zero.p[i] = 0;
 
   // 1. route
-  float v[EMAX];
-#pragma unroll
-  for (int e = 0; e < EMAX; ++e) v[e] = (ok && e < E) ? load_logit(logits, (size_t)t * E + e) : 0.0f;
-  const Mask valid = ok ? (E >= kMaskBits ? ~Mask(0) : (Mask(1) << E) - Mask(1)) : Mask(0);
-  Mask live = valid;
-  float sel_v[MOE_MAX_TOPK];
   int sel_e[MOE_MAX_TOPK];
+  Mask chosen = 0;  // one thread per token: the token's experts as bits
+  if constexpr (LPT == 1) {
+    float v[EMAX];
 #pragma unroll
-  for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-    float bv = 0.0f;
-    int be = -1;
-    if (j < k) {
+    for (int e = 0; e < EMAX; ++e) v[e] = (ok && e < E) ? load_logit(logits, (size_t)t * E + e) : 0.0f;
+    const Mask valid = ok ? (E >= kMaskBits ? ~Mask(0) : (Mask(1) << E) - Mask(1)) : Mask(0);
+    Mask live = valid;
+    float sel_v[MOE_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
+      float bv = 0.0f;
+      int be = -1;
+      if (j < k) {
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e)
+          if (((live >> e) & Mask(1)) && ranks_before(v[e], e, bv, be)) {
+            bv = v[e];
+            be = e;
+          }
+        if (be >= 0) live &= ~(Mask(1) << be);
+      }
+      sel_v[j] = bv;
+      sel_e[j] = be;
+    }
+    float z_all = 0.0f;
+    if (score == MOE_SCORE_SOFTMAX && !renorm) {
 #pragma unroll
       for (int e = 0; e < EMAX; ++e)
-        if (((live >> e) & Mask(1)) && ranks_before(v[e], e, bv, be)) {
-          bv = v[e];
-          be = e;
-        }
-      if (be >= 0) live &= ~(Mask(1) << be);
+        if ((valid >> e) & Mask(1)) z_all += expf(v[e] - sel_v[0]);
     }
-    sel_v[j] = bv;
-    sel_e[j] = be;
-  }
-  float z_all = 0.0f;
-  if (score == MOE_SCORE_SOFTMAX && !renorm) {
+    float wt[MOE_MAX_TOPK];
+    topk_weights(sel_v, k, renorm, score, z_all, wt);
+    if (ok) {
 #pragma unroll
-    for (int e = 0; e < EMAX; ++e)
-      if ((valid >> e) & Mask(1)) z_all += expf(v[e] - sel_v[0]);
-  }
-  float wt[MOE_MAX_TOPK];
-  topk_weights(sel_v, k, renorm, score, z_all, wt);
-  if (ok) {
+      for (int j = 0; j < MOE_MAX_TOPK; ++j)
+        if (j < k) {
+          ids[(size_t)t * k + j] = sel_e[j];
+          w[(size_t)t * k + j] = wt[j];
+        }
+    }
+    chosen = valid & ~live;
+  } else {
+    // LPT lanes per token: the lane-group route of the general path (the
+    // same experts and weights), T * LPT <= kScanThreads so every token in
+    // one pass; then thread t takes token t's experts from an LDS copy
+    static_assert(LPT <= 64 && (LPT & (LPT - 1)) == 0 && EMAX <= 256, "lane groups in a wave");
+    __shared__ uint8_t sel[(kScanThreads / LPT) * MOE_MAX_TOPK];  // [token][j] expert
+    if (t < EMAX * kSmallWaves) wmask[t] = 0ull;  // the count below ORs into it
+    const int tt = t / LPT;
+    route_token<LPT, (EMAX + LPT - 1) / LPT>(logits, tt, tt < T, t & (LPT - 1), E, k, renorm,
+                                             score, ids, w, sel);
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j)
-      if (j < k) {
-        ids[(size_t)t * k + j] = sel_e[j];
-        w[(size_t)t * k + j] = wt[j];
-      }
+    for (int j = 0; j < MOE_MAX_TOPK; ++j) sel_e[j] = (ok && j < k) ? (int)sel[t * k + j] : -1;
   }
 
-  // 2. count
-  const Mask chosen = valid & ~live;
-  for (int e = 0; e < E; ++e) {
-    const unsigned long long m = __ballot((int)((chosen >> e) & Mask(1)));
-    if (lane == 0) wmask[e * kSmallWaves + wave] = m;
+  // 2. count (with lane groups: each lane ORs its bit into the masks of its
+  // token's k experts instead of one ballot per expert)
+  if constexpr (LPT == 1) {
+    for (int e = 0; e < E; ++e) {
+      const unsigned long long m = __ballot((int)((chosen >> e) & Mask(1)));
+      if (lane == 0) wmask[e * kSmallWaves + wave] = m;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (sel_e[j] >= 0) atomicOr(&wmask[sel_e[j] * kSmallWaves + wave], 1ull << lane);
   }
   __syncthreads();
 
@@ -588,18 +615,32 @@ hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int
                                        hipStream_t s) {
   if (!small_routing_fits(T, E, k)) return hipErrorInvalidValue;
   if (var.blocks && (!var.nb || var.tiles < 1)) return hipErrorInvalidValue;
-#define MOE_LAUNCH_SMALL(EMAX)                                                               \
-  route_dispatch_small_kernel<EMAX><<<1, kScanThreads, 0, s>>>(                              \
+#define MOE_LAUNCH_SMALL(EMAX, LPT)                                                          \
+  route_dispatch_small_kernel<EMAX, LPT><<<1, kScanThreads, 0, s>>>(                         \
       logits, T, E, k, renorm, score, bm, ids, w, counts, offsets, perm, inv, blocks, nb, order, \
       zero, var)
+  // Up to 32 experts a thread routes its token alone; beyond, the largest
+  // lane group per token that still covers every token in one pass.
   if (E <= 8)
-    MOE_LAUNCH_SMALL(8);
+    MOE_LAUNCH_SMALL(8, 1);
   else if (E <= 16)
-    MOE_LAUNCH_SMALL(16);
+    MOE_LAUNCH_SMALL(16, 1);
   else if (E <= 32)
-    MOE_LAUNCH_SMALL(32);
+    MOE_LAUNCH_SMALL(32, 1);
+  else if (T <= 16)
+    MOE_LAUNCH_SMALL(64, 64);
+  else if (T <= 32)
+    MOE_LAUNCH_SMALL(64, 32);
+  else if (T <= 64)
+    MOE_LAUNCH_SMALL(64, 16);
+  else if (T <= 128)
+    MOE_LAUNCH_SMALL(64, 8);
+  else if (T <= 256)
+    MOE_LAUNCH_SMALL(64, 4);
+  else if (T <= 512)
+    MOE_LAUNCH_SMALL(64, 2);
   else
-    MOE_LAUNCH_SMALL(64);
+    MOE_LAUNCH_SMALL(64, 1);
 #undef MOE_LAUNCH_SMALL
   return hipGetLastError();
 }

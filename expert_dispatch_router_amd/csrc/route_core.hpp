@@ -13,9 +13,9 @@
 // IEEE equality, so -0 == +0 -- rank the lower expert first.  The order of
 // the k results is descending key.
 //
-// Mapping: a group of LPT lanes (a power of two, LPT = min(64, E rounded up))
-// owns one token; lane `sub` of the group holds experts sub, sub+LPT, ...
-// (EPL of them).  Each of the k rounds takes each lane's best unselected
+// Mapping: a group of LPT lanes (a power of two up to 64; the many-workgroup
+// route takes E rounded up, the one-workgroup kernel fewer) owns one token;
+// lane `sub` of the group holds experts sub, sub+LPT, ... (EPL of them).  Each of the k rounds takes each lane's best unselected
 // candidate and reduces it over the group with xor-butterfly shuffles; the
 // group agrees on the winner because the rank order is total.
 #pragma once
@@ -64,12 +64,15 @@ __device__ __forceinline__ void topk_weights(const float* sel_v, int k, int reno
 }
 
 // Routes token t (all LPT lanes of its group call this; tok_ok is false for
-// padding groups past the last token).  Lane j of the group writes entry j:
-// ids[t*k + j] and w[t*k + j].
+// padding groups past the last token).  The whole group ends with all k
+// results; lane j mod LPT writes entry j: ids[t*k + j] and w[t*k + j].
+// sel, if given: the ids also go to sel[t*k + j] (an LDS copy for the
+// one-workgroup kernel).
 template <int LPT, int EPL>
 __device__ __forceinline__ void route_token(const LogitSrc& logits, int t, bool tok_ok,
                                             int sub, int E, int k, int renorm, int score,
-                                            int32_t* __restrict__ ids, float* __restrict__ w) {
+                                            int32_t* __restrict__ ids, float* __restrict__ w,
+                                            uint8_t* sel = nullptr) {
   float v[EPL];
   unsigned live = 0;  // bit i set: expert sub + i*LPT exists and is not yet chosen
 #pragma unroll
@@ -131,17 +134,18 @@ __device__ __forceinline__ void route_token(const LogitSrc& logits, int t, bool 
   if (tok_ok) {
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      if (j < k && sub == j) {
+      if (j < k && (j & (LPT - 1)) == sub) {
         ids[(size_t)t * k + j] = sel_e[j];
         w[(size_t)t * k + j] = wt[j];
+        if (sel) sel[t * k + j] = (uint8_t)sel_e[j];
       }
     }
   }
 }
 
-// Expands CALL(LPT, EPL) for the lane-group shape of E experts: every lane of
-// a group must hold at least one candidate whenever k <= E (k <= 16 <= LPT
-// for E > 16, and k <= E <= LPT otherwise).
+// Expands CALL(LPT, EPL) for the lane-group shape of E experts used by the
+// many-workgroup route: LPT = E rounded up to a power of two, between 8 and
+// 64; EPL = the experts per lane.
 #define MOE_ROUTE_SHAPES(E, CALL) \
   do {                            \
     if ((E) <= 8) {               \

@@ -130,10 +130,17 @@ def test_route_two_launches_at_its_limit():
 def test_route_small_kernel_at_its_limits():
     """The one-workgroup kernel at its limits (1024 tokens, 64 experts, top-16),
     at 32 and 33 experts (the 32- and 64-bit expert masks) and at E=k: both
-    routing paths give the oracle's artefacts."""
+    routing paths give the oracle's artefacts.  Beyond 32 experts the kernel
+    routes with 64 / 32 / 16 / 8 / 4 / 2 lanes per token up to 16 / 32 / 64 /
+    128 / 256 / 512 tokens and one thread per token above: each lane-group
+    size at both ends of its range, with E = 33, 48 and 64 (lanes without
+    an expert), every score and normalisation."""
     gen = torch.Generator().manual_seed(21)
     for T, E, k in ((1024, 64, 16), (1024, 32, 16), (1000, 33, 8), (777, 64, 4), (64, 64, 64 // 4),
-                    (1024, 8, 2), (1000, 17, 5), (3, 4, 4), (1024, 1, 1), (5, 64, 16)):
+                    (1024, 8, 2), (1000, 17, 5), (3, 4, 4), (1024, 1, 1), (5, 64, 16),
+                    (16, 64, 4), (17, 64, 8), (32, 40, 3), (33, 64, 16), (65, 48, 6),
+                    (128, 33, 2), (129, 64, 8), (256, 48, 4), (257, 64, 4), (512, 33, 1),
+                    (513, 64, 4)):
         assert _small_routing_fits(T, E, k)
         lg = torch.randn(T, E, generator=gen).to(DEV)
         ref = None
@@ -141,6 +148,13 @@ def test_route_small_kernel_at_its_limits():
             g = moe.moe_route(lg, k, True, 0, routing_kernels=routing)
             if ref is None:
                 ref = parity.oracle_routing(lg, k, 0, True, g["bm"])
+            parity.check_routing(g, ref)
+    for T, E, k, score, renorm in ((20, 64, 8, 0, False), (100, 48, 6, 1, True),
+                                   (200, 40, 3, 1, False), (400, 64, 8, 0, False)):
+        lg = torch.randn(T, E, generator=gen).to(DEV)
+        ref = parity.oracle_routing(lg, k, score, renorm, 128)
+        for routing in (1, 2):
+            g = moe.moe_route(lg, k, renorm, score, block_rows=128, routing_kernels=routing)
             parity.check_routing(g, ref)
 
 
