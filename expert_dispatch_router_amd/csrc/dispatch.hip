@@ -401,9 +401,18 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
     float sel_v[MOE_MAX_TOPK];
 #pragma unroll
     for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      float bv = 0.0f;
-      int be = -1;
+      sel_v[j] = 0.0f;
+      sel_e[j] = -1;
+    }
+    // k rounds: a round past k (uniform over the launch) is skipped, not
+    // computed and discarded (the empty volatile asm keeps the compiler from
+    // speculating it)
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
       if (j < k) {
+        asm volatile("");
+        float bv = 0.0f;
+        int be = -1;
 #pragma unroll
         for (int e = 0; e < EMAX; ++e)
           if (((live >> e) & Mask(1)) && ranks_before(v[e], e, bv, be)) {
@@ -411,10 +420,9 @@ __global__ __launch_bounds__(kScanThreads) void route_dispatch_small_kernel(
             be = e;
           }
         if (be >= 0) live &= ~(Mask(1) << be);
+        sel_v[j] = bv;
+        sel_e[j] = be;
       }
-      sel_v[j] = bv;
-      sel_e[j] = be;
-    }
     float z_all = 0.0f;
     if (score == MOE_SCORE_SOFTMAX && !renorm) {
 #pragma unroll
@@ -619,8 +627,10 @@ hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int
   route_dispatch_small_kernel<EMAX, LPT><<<1, kScanThreads, 0, s>>>(                         \
       logits, T, E, k, renorm, score, bm, ids, w, counts, offsets, perm, inv, blocks, nb, order, \
       zero, var)
-  // Up to 32 experts a thread routes its token alone; beyond, the largest
-  // lane group per token that still covers every token in one pass.
+  // Up to 32 experts a thread routes its token alone; beyond, up to 256
+  // tokens, the largest lane group per token that still covers every token
+  // in one pass (with 2 lanes per token the kernel no longer fits its
+  // registers, and it was no faster than one thread per token).
   if (E <= 8)
     MOE_LAUNCH_SMALL(8, 1);
   else if (E <= 16)
@@ -637,8 +647,6 @@ hipError_t launch_route_dispatch_small(const LogitSrc& logits, int T, int E, int
     MOE_LAUNCH_SMALL(64, 8);
   else if (T <= 256)
     MOE_LAUNCH_SMALL(64, 4);
-  else if (T <= 512)
-    MOE_LAUNCH_SMALL(64, 2);
   else
     MOE_LAUNCH_SMALL(64, 1);
 #undef MOE_LAUNCH_SMALL

@@ -38,27 +38,50 @@ __device__ __forceinline__ bool ranks_before(float va, int ea, float vb, int eb)
 // optionally divided by the sum of the k sigmoids.
 __device__ __forceinline__ void topk_weights(const float* sel_v, int k, int renorm, int score,
                                              float z_all, float* wt) {
+  // Entries past k (uniform over the launch) are not computed: each block
+  // below holds an empty volatile asm statement, which the compiler may not
+  // speculate, so it stays a branch on k instead of becoming a computed
+  // exponential and a select.  Entries past k stay 0 and are never used; the
+  // sums and quotients are the same operations in the same order.
+#pragma unroll
+  for (int j = 0; j < MOE_MAX_TOPK; ++j) wt[j] = 0.0f;
   if (score == MOE_SCORE_SOFTMAX) {
     const float m = sel_v[0];  // the largest logit of the token
+#pragma unroll
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j < k) {
+        asm volatile("");
+        wt[j] = expf(sel_v[j] - m);
+      }
     float z = z_all;
     if (renorm) {
       z = 0.0f;
 #pragma unroll
       for (int j = 0; j < MOE_MAX_TOPK; ++j)
-        if (j < k) z += expf(sel_v[j] - m);
+        if (j < k) z += wt[j];
     }
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) wt[j] = (j < k) ? expf(sel_v[j] - m) / z : 0.0f;
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j < k) {
+        asm volatile("");
+        wt[j] = wt[j] / z;
+      }
   } else {
     float s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < MOE_MAX_TOPK; ++j) {
-      wt[j] = (j < k) ? 1.0f / (1.0f + expf(-sel_v[j])) : 0.0f;
-      s += wt[j];
-    }
+    for (int j = 0; j < MOE_MAX_TOPK; ++j)
+      if (j < k) {
+        asm volatile("");
+        wt[j] = 1.0f / (1.0f + expf(-sel_v[j]));
+        s += wt[j];
+      }
     if (renorm) {
 #pragma unroll
-      for (int j = 0; j < MOE_MAX_TOPK; ++j) wt[j] = wt[j] / s;
+      for (int j = 0; j < MOE_MAX_TOPK; ++j)
+        if (j < k) {
+          asm volatile("");
+          wt[j] = wt[j] / s;
+        }
     }
   }
 }

@@ -131,10 +131,10 @@ def test_route_small_kernel_at_its_limits():
     """The one-workgroup kernel at its limits (1024 tokens, 64 experts, top-16),
     at 32 and 33 experts (the 32- and 64-bit expert masks) and at E=k: both
     routing paths give the oracle's artefacts.  Beyond 32 experts the kernel
-    routes with 64 / 32 / 16 / 8 / 4 / 2 lanes per token up to 16 / 32 / 64 /
-    128 / 256 / 512 tokens and one thread per token above: each lane-group
-    size at both ends of its range, with E = 33, 48 and 64 (lanes without
-    an expert), every score and normalisation."""
+    routes with 64 / 32 / 16 / 8 / 4 lanes per token up to 16 / 32 / 64 /
+    128 / 256 tokens and one thread per token above: each lane-group size
+    at both ends of its range, with E = 33, 48 and 64 (lanes without an
+    expert), every score and normalisation."""
     gen = torch.Generator().manual_seed(21)
     for T, E, k in ((1024, 64, 16), (1024, 32, 16), (1000, 33, 8), (777, 64, 4), (64, 64, 64 // 4),
                     (1024, 8, 2), (1000, 17, 5), (3, 4, 4), (1024, 1, 1), (5, 64, 16),
