@@ -265,24 +265,36 @@ __global__ __launch_bounds__(kScanThreads) void hist_scan_kernel(
         const int i = (g0 + u * kWaves) * 64 + lane;
         ev[u] = i < A ? ids[i] : 0;
       }
+      int pos[kAhead];
 #pragma unroll
       for (int u = 0; u < kAhead; ++u) {
         const int g = g0 + u * kWaves;
         const int i = g * 64 + lane;
         const int e = ev[u];
         // the lanes of the group that hold each expert: OR is order-free, and
-        // a wave's LDS operations complete in program order
-        if (i < A) atomicOr(&wm[e], 1ull << lane);
-        asm volatile("" ::: "memory");
+        // a wave's LDS operations complete in program order.  Every access to
+        // the masks is atomic and any two may touch the same mask, so the
+        // compiler keeps their order (a fence or a memory-clobbering asm
+        // statement here would make it wait for every store in flight)
+        pos[u] = 0;
         if (i < A) {
-          const unsigned long long m = wm[e];
-          const int p = run[e] + chist[g * E + e] + __popcll(m & below);
-          perm[p] = i;
-          inv[i] = p;
+          atomicOr(&wm[e], 1ull << lane);
+          const unsigned long long m =
+              __hip_atomic_load(&wm[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
+          pos[u] = run[e] + chist[g * E + e] + __popcll(m & below);
+          // every lane that read it has read it
+          __hip_atomic_store(&wm[e], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WAVEFRONT);
         }
-        asm volatile("" ::: "memory");
-        if (i < A) wm[e] = 0ull;  // every lane that read it has read it
-        asm volatile("" ::: "memory");
+      }
+      // the stores after all the groups' LDS work: a store's registers are
+      // not reused while it is in flight, so nothing waits for it
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) {
+        const int i = (g0 + u * kWaves) * 64 + lane;
+        if (i < A) {
+          perm[pos[u]] = i;
+          inv[i] = pos[u];
+        }
       }
     }
   }
