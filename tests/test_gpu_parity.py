@@ -127,6 +127,33 @@ def test_route_two_launches_at_its_limit():
             assert torch.equal(g[key], g2[key]), key
 
 
+def test_route_random_sweep_every_path():
+    """80 seeded random routings (1-64 experts, top-1 to top-16, 1-1024
+    tokens around the lane-group and chunk boundaries, many ties in a third
+    of them, both scores and normalisations): every routing path gives the
+    oracle's artefacts bit for bit."""
+    rng = np.random.default_rng(9090)
+    sizes = [1, 2, 5, 16, 17, 31, 32, 33, 64, 65, 100, 128, 129, 200, 256, 257, 400, 512, 513,
+             700, 1024]
+    for _ in range(80):
+        E = int(rng.integers(1, 65))
+        k = int(rng.integers(1, min(E, 16) + 1))
+        T = int(rng.choice(sizes))
+        score, renorm = int(rng.integers(0, 2)), bool(rng.integers(0, 2))
+        if rng.random() < 0.3:
+            lg = torch.from_numpy(rng.integers(-2, 3, (T, E)).astype(np.float32))
+        else:
+            lg = torch.from_numpy((rng.standard_normal((T, E)) *
+                                   rng.choice([0.1, 1.0, 5.0])).astype(np.float32))
+        lg = lg.to(DEV)
+        ref = parity.oracle_routing(lg, k, score, renorm, 128)
+        for routing in (0, 1, 2, 3):
+            if routing == 3 and not _fused_reorder_fits(T * k, E):
+                continue
+            g = moe.moe_route(lg, k, renorm, score, block_rows=128, routing_kernels=routing)
+            parity.check_routing(g, ref)
+
+
 def test_route_small_kernel_at_its_limits():
     """The one-workgroup kernel at its limits (1024 tokens, 64 experts, top-16),
     at 32 and 33 experts (the 32- and 64-bit expert masks) and at E=k: both
